@@ -1,0 +1,139 @@
+"""Packed low-bit page tiers: encoder, decoder and byte layout (test infrastructure only).
+
+ARGUS (argus_cache 0.1.7.1 project page), section "Visual Architecture" and the
+tier legend under "Heatmap & Telemetry Legend": tiers INT8, INT4 ("2-way
+bit-packed"), INT2 ("4-way bit-packed") and 1-bit ("8-way sign-packed"), and
+section "Why It Works: Storage vs. Computation": packed pages are rebuilt in
+high precision on chip just before attention, never used in low-bit math.
+The page names bit widths and packing ratios only; everything below is a
+stated reading.
+
+Grouping: each token's K or V vector is cut into groups of 32 consecutive
+head-dim elements; every group stores a float16 (scale s, zero z) pair.
+
+Encoder, step-exact in IEEE float32 with every operation correctly rounded and
+no fused multiply-add (x is the float32 value of the 16-bit input, exact):
+  int-b (b = 8, 4, 2):
+    mn = min x, mx = max x
+    s  = fp16(fp32(mx - mn) / fp32(2^b - 1))
+    z  = fp16(mn)
+    c  = 0 if s == 0 else clamp(rint_even(fp32(x - z) / s), 0, 2^b - 1)
+  1-bit:
+    z  = fp16(T(x) / 32),  s = fp16(T(|x - z|) / 32),  c = (x >= z)
+    where T is the pairwise tree sum (level by level, pairs (2i, 2i+1)).
+  fp16() rounds to nearest even and saturates at +-65504.
+Decoder: int-b x^ = c*s + z; 1-bit x^ = z + (2c - 1)*s.  Both are exact in
+float64 for float16 s, z and b <= 8, and are returned rounded once to float32.
+Byte layout, LSB first in head-dim order: int8 one code per byte; int4 element
+2i in bits 0-3 and 2i+1 in bits 4-7; int2 element 4i+j in bits 2j..2j+1; 1-bit
+element 8i+j in bit j.  A vector's d*b/8 code bytes are contiguous; the
+(s, z) pairs live in a separate array.
+
+Pinned in tests/test_oracle_codec.py: hand-packed bytes (0xA3, 0xE4, 0x8D), the
+int4 ramp 0..31 (s = fp16(31/15) = 2.06640625), exactly representable inputs
+mapping back to their codes, the per-group error bound, the 1-bit value set
+and sign, and pack/unpack identity.
+"""
+
+import numpy as np
+
+from .rounding import round_fp16_sat
+
+TIER_NATIVE, TIER_I8, TIER_I4, TIER_I2, TIER_B1 = 0, 1, 2, 3, 4
+BITS_OF_TIER = {TIER_I8: 8, TIER_I4: 4, TIER_I2: 2, TIER_B1: 1}
+GROUP = 32
+
+
+def _f16(x32):
+    return round_fp16_sat(x32).astype(np.float32)
+
+
+def encode_group_int(x, bits):
+    """x: float32 (..., 32).  Returns (codes uint8 (..., 32), s f32 (...), z f32 (...))."""
+    x = np.asarray(x, dtype=np.float32)
+    qmax = np.float32(2 ** bits - 1)
+    mn = x.min(axis=-1)
+    mx = x.max(axis=-1)
+    with np.errstate(over="ignore"):
+        s = _f16((mx - mn) / qmax)
+    z = _f16(mn)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.rint((x - z[..., None]) / s[..., None])
+    c = np.clip(c, np.float32(0), qmax)
+    c = np.where((s == 0)[..., None], np.float32(0), c)
+    return c.astype(np.uint8), s, z
+
+
+def _tree_sum(v):
+    v = np.asarray(v, dtype=np.float32)
+    while v.shape[-1] > 1:
+        v = v[..., 0::2] + v[..., 1::2]
+    return v[..., 0]
+
+
+def encode_group_1bit(x):
+    """x: float32 (..., 32).  Returns (codes uint8 in {0,1}, s, z)."""
+    x = np.asarray(x, dtype=np.float32)
+    n = np.float32(GROUP)
+    z = _f16(_tree_sum(x) / n)
+    s = _f16(_tree_sum(np.abs(x - z[..., None])) / n)
+    c = (x >= z[..., None]).astype(np.uint8)
+    return c, s, z
+
+
+def pack_codes(codes, bits):
+    """codes uint8 (..., d) -> bytes uint8 (..., d*bits/8), LSB first."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if bits == 8:
+        return c.copy()
+    per = 8 // bits
+    out = np.zeros(c.shape[:-1] + (c.shape[-1] // per,), dtype=np.uint8)
+    for j in range(per):
+        out |= (c[..., j::per] << (bits * j)).astype(np.uint8)
+    return out
+
+
+def unpack_codes(packed, bits, d):
+    """Inverse of pack_codes."""
+    b = np.asarray(packed, dtype=np.uint8)
+    if bits == 8:
+        return b.copy()
+    per = 8 // bits
+    mask = (1 << bits) - 1
+    out = np.zeros(b.shape[:-1] + (d,), dtype=np.uint8)
+    for j in range(per):
+        out[..., j::per] = (b >> (bits * j)) & mask
+    return out
+
+
+def encode_vector(x16, tier):
+    """Encode token vectors.
+
+    x16: float32 (..., d) holding exact 16-bit values, d a multiple of 32.
+    Returns (packed bytes (..., d*bits/8), scale_zero float32 (..., d/32, 2)).
+    """
+    x = np.asarray(x16, dtype=np.float32)
+    d = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (d // GROUP, GROUP))
+    bits = BITS_OF_TIER[tier]
+    if tier == TIER_B1:
+        c, s, z = encode_group_1bit(g)
+    else:
+        c, s, z = encode_group_int(g, bits)
+    packed = pack_codes(c.reshape(x.shape), bits)
+    return packed, np.stack([s, z], axis=-1)
+
+
+def decode_vector(packed, scale_zero, tier, d):
+    """Decode token vectors to float32 (..., d) (exact float64 value rounded once)."""
+    bits = BITS_OF_TIER[tier]
+    c = unpack_codes(packed, bits, d).astype(np.float64)
+    sz = np.asarray(scale_zero, dtype=np.float64)
+    c = c.reshape(c.shape[:-1] + (d // GROUP, GROUP))
+    s = sz[..., 0][..., None]
+    z = sz[..., 1][..., None]
+    if tier == TIER_B1:
+        xh = z + (2.0 * c - 1.0) * s
+    else:
+        xh = c * s + z
+    return xh.reshape(xh.shape[:-2] + (d,)).astype(np.float32)

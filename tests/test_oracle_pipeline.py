@@ -1,0 +1,50 @@
+"""Oracle decode step on the seeded workloads (CPU only).
+
+A sanity check, not parity: on the tiny workload (4 planted high-mass pages per
+sequence, keys = 3 u_g + noise) the oracle's top-8 pages per KV head contain
+every planted page; and the generator reproduces any row on its own.
+"""
+
+import numpy as np
+
+from oracle.pipeline import decode_row
+from quantized_kv_cache_summary_amd import workloads as wl
+
+
+def test_planted_pages_are_selected_tiny():
+    w = wl.WORKLOADS["tiny"]
+    for b in range(w.B):
+        hp = set(wl.hot_pages(w, 0, b).tolist())
+        assert len(hp) == 4
+        for g in range(w.Hkv):
+            q = wl.queries(w, 0, b, g)
+            K = wl.row_keys(w, 0, b, g)
+            V = wl.row_values(w, 0, b, g)
+            r = decode_row(q, K, V, w.ctx, w.P, w.rank, w.tau, k_fixed=w.k_fixed)
+            assert r["k"] == 8
+            assert hp <= set(r["sel"].tolist())
+            assert abs(np.exp(r["S"]).sum() - 1) < 1e-12
+
+
+def test_generator_rows_are_independent_and_repeatable():
+    w = wl.WORKLOADS["llama8b_32k"].replace(ctx=1024, B=2)
+    a = wl.row_keys(w, 0, 1, 3)
+    b = wl.row_keys(w, 0, 1, 3)
+    np.testing.assert_array_equal(a, b)
+    c = wl.row_keys(w, 0, 1, 4)
+    assert not np.array_equal(a, c)
+    # values are exact bf16 numbers
+    np.testing.assert_array_equal(wl.round16(a, "bf16"), a)
+    bt = wl.block_table(w)
+    assert sorted(bt.ravel().tolist()) == list(range(w.n_phys))
+    kp = np.zeros((w.n_phys, w.Hkv, w.P, w.d), np.uint16)
+    wl.fill_pools(w, 0, kp, None, threads=2)
+    np.testing.assert_array_equal(wl.bits_to_f32(kp[bt[1], 3].reshape(-1, w.d), "bf16"), a)
+
+
+def test_tier_assignment_fractions():
+    w = wl.WORKLOADS["tiers_64k"].replace(ctx=16 * 1000, B=2)
+    t = wl.page_tiers(w)
+    for b in range(w.B):
+        counts = np.bincount(t[b], minlength=5)
+        assert list(counts) == [50, 150, 300, 400, 100]
