@@ -1,0 +1,247 @@
+/*
+ * kvsparse: importance-based sparse decode attention over a paged, optionally
+ * low-bit KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step for one layer is
+ *     kv_page_score  -> kv_page_topk  -> kv_sparse_decode_attn
+ * and, when a page is appended, kv_summary_build (and kv_pack_tier for pages
+ * stored in a packed low-bit tier).
+ *
+ * Method sources (no formulas are published; each call states the reading it
+ * implements):
+ *   AMASS, decode-time sparse KV-cache attention for vLLM (amass-kv 0.1.1
+ *     project page): section "AMASS" (attend only to pages that carry attention
+ *     mass; a sparse paged-attention kernel reads just those pages), section
+ *     "What is in the box" item 1 (quad, Gaussian-MGF page score from a tiny
+ *     per-page summary), section "Quickstart" (fixed budget / per-head
+ *     coverage selection), section "Benchmarking" (score, top-B and decode
+ *     stages; HBM roofline of the score stage).
+ *   ARGUS, virtual memory for transformers (argus_cache 0.1.7.1 project page):
+ *     sections "Visual Architecture" and the tier legend (INT8, INT4 2-way,
+ *     INT2 4-way, 1-bit 8-way sign-packed tiers) and "Why It Works: Storage
+ *     vs. Computation" (packed pages are rebuilt in high precision on chip just
+ *     before attention).
+ *
+ * Conventions for every call
+ *   - Plain C.  All array arguments are DEVICE pointers (device memory, or
+ *     pinned host memory mapped into the device address space where stated)
+ *     unless the name says "host".  The caller owns every buffer; the library
+ *     never allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *     call only enqueues work on it and returns.
+ *   - Every call validates its host-visible arguments (null pointers, shapes,
+ *     supported sizes, alignment, workspace size) BEFORE any HIP call and
+ *     returns a negative status without launching anything when they are
+ *     wrong.  A failed launch returns KV_ERR_HIP.  No C++ exception crosses
+ *     the ABI.
+ *   - No global mutable state: calls are thread-safe, and identical inputs give
+ *     bit-identical outputs (fixed reduction orders, no floating-point atomics).
+ *   - Values read from device memory (seq_lens, block tables, selections) are
+ *     not checked on the host; out-of-range values are clamped or skipped as
+ *     each call states, never dereferenced out of bounds except that block
+ *     table entries and page ids must name existing physical pages.
+ *   - Base pointers of 16-bit pools, queries, summaries and packed code pools
+ *     must be 16-byte aligned.
+ *
+ * Layout names: B sequences, Hq query heads, Hkv KV heads, G = Hq / Hkv query
+ * heads per KV head, d = head_dim, P = page_size, R = rank, max_pages = the
+ * block table's row length.  A "row" is one (sequence b, KV head g) pair,
+ * row = b * Hkv + g.  Logical page p of sequence b holds tokens
+ * [p*P, min((p+1)*P, seq_lens[b])); Np_b = ceil(seq_lens[b] / P), clamped to
+ * max_pages.  block_table[b * max_pages + p] is its physical page.
+ */
+#ifndef KVSPARSE_H
+#define KVSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KV_OK = 0,
+  KV_ERR_INVALID_ARG = -1,   /* null pointer, bad shape, misaligned pointer */
+  KV_ERR_UNSUPPORTED = -2,   /* valid but not compiled: d, P, R, G, dtype, tier */
+  KV_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+  KV_ERR_HIP = -4            /* the HIP runtime reported a launch error */
+};
+
+enum { KV_F16 = 0, KV_BF16 = 1 };   /* the cache's native 16-bit dtype (also q's) */
+
+/* Page tiers (ARGUS tier legend).  NATIVE is the cache's own 16-bit dtype. */
+enum { KV_TIER_NATIVE = 0, KV_TIER_I8 = 1, KV_TIER_I4 = 2, KV_TIER_I2 = 3, KV_TIER_B1 = 4 };
+
+/* page_entry word: tier in bits 29..31, slot in bits 0..28. */
+#define KV_PAGE_ENTRY(tier, slot) ((((uint32_t)(tier)) << 29) | ((uint32_t)(slot) & 0x1FFFFFFFu))
+
+/* One layer's paged cache geometry.
+ * Supported: head_dim in {64, 128}; page_size in {16, 32}; rank in {1, 2, 4, 8};
+ * num_q_heads a multiple of num_kv_heads with G = Hq / Hkv <= 16;
+ * kv_dtype KV_F16 or KV_BF16.  softmax_scale <= 0 selects 1/sqrt(head_dim). */
+typedef struct kv_layout {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t rank;
+  int32_t kv_dtype;
+  float softmax_scale;
+} kv_layout;
+
+/* Physical page pools read by attention.
+ *   page_entry == NULL: every physical page is native and lives at
+ *     k16/v16[phys] ([n_phys][Hkv][P][d] 16-bit).
+ *   page_entry != NULL: page_entry[phys] = KV_PAGE_ENTRY(tier, slot); native
+ *     pages live at k16/v16[slot]; a packed tier t (1..4, bits 8/4/2/1) keeps
+ *     codes at kq[t-1]/vq[t-1][slot] ([slots][Hkv][P][d*bits/8] bytes, codes
+ *     LSB-first in head-dim order) and one (scale, zero) float16 pair per
+ *     32-element group at ksz[t-1]/vsz[t-1][slot] ([slots][Hkv][P][d/32][2]).
+ *     A tier's K and V share the slot.  Decoding: int-b x = c*s + z rounded
+ *     once to float32 (fused multiply-add); 1-bit x = z + s if c else z - s.
+ *   v_hot_slot != NULL: V of physical page phys is read from
+ *     v_hot[v_hot_slot[phys]] ([hot][Hkv][P][d] 16-bit, device memory) when
+ *     v_hot_slot[phys] >= 0, else from v16[slot]; v16 may then be pinned host
+ *     memory mapped into the device address space (zero-copy reads over the
+ *     host link).  AMASS page, section "What is in the box" item 2 (the DRAM
+ *     value tier with a bounded resident hot buffer). */
+typedef struct kv_pages {
+  const void* k16;
+  const void* v16;
+  const uint8_t* kq[4];
+  const uint8_t* vq[4];
+  const void* ksz[4];
+  const void* vsz[4];
+  const uint32_t* page_entry;
+  const void* v_hot;
+  const int32_t* v_hot_slot;
+} kv_pages;
+
+/* ---------------------------------------------------------------------------
+ * kv_summary_build -- per-page key summary for the quad score, run when pages
+ * are appended (AMASS page, "What is in the box" item 1; the summary drops the
+ * per-key coordinates and keeps r' eigen-quantities of the page).
+ *
+ * For i in [0, n) and every KV head g, over the n_valid[i] first tokens of
+ * physical page phys = pages[i] of the 16-bit pool k16 ([n_phys][Hkv][P][d]):
+ *   mu = mean key; Xc = keys - mu; Gram = Xc Xc^T / n; (lam_j, v_j) its
+ *   eigenpairs, lam descending (cyclic Jacobi in float32);
+ *   w_j = Xc^T v_j / sqrt(n) for j = 1..R, set to 0 when j > n - 1 or
+ *   lam_j <= 1e-6 lam_1.
+ * Output record summary[phys][g] = [mu, w_1, ..., w_R], (1+R)*d bfloat16
+ * (round to nearest even), and log_n[phys] = log(n) as float32.
+ * Eigenvector signs and rotations inside degenerate eigenspaces are arbitrary.
+ * n_valid values are clamped to [0, P]; a page with 0 valid tokens gets a zero
+ * record and log_n = -inf.  pages[] entries must be distinct within a call.
+ * --------------------------------------------------------------------------- */
+int kv_summary_build(const kv_layout* layout, const void* k16, const int32_t* pages,
+                     const int32_t* n_valid, int32_t n, void* summary, float* log_n,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_page_score -- quad page score of every logical page for every query head
+ * (AMASS page, "What is in the box" item 1: quadratic, Gaussian-MGF score):
+ *   s[b][g][h][p] = log_n[phys] + tau q.mu + (tau^2/2) sum_j (q.w_j)^2
+ * with q = q[b][g*G + h] ([B][Hq][d], kv_dtype), phys = block_table[b][p],
+ * record = summary[phys][g], tau = softmax_scale.
+ * head_scores: float32 [B][Hkv][G][max_pages]; entries p >= Np_b are -inf.
+ * lse_partial: float32 pairs (max, sum exp(s - max)) per (row, page tile,
+ *   head) over the tile's valid pages; its size in bytes is
+ *   kv_page_score_partial_size().  It feeds kv_page_topk.
+ * --------------------------------------------------------------------------- */
+int kv_page_score(const kv_layout* layout, const void* q, const void* summary,
+                  const float* log_n, const int32_t* block_table, const int32_t* seq_lens,
+                  int32_t B, int32_t max_pages, float* head_scores, float* lse_partial,
+                  void* stream);
+
+size_t kv_page_score_partial_size(const kv_layout* layout, int32_t B, int32_t max_pages);
+
+/* ---------------------------------------------------------------------------
+ * kv_page_topk -- per row, select k pages (AMASS page, "Quickstart": budget,
+ * a fixed selected-page fraction; "Benchmarking": the top-B stage).
+ *   L_h  = logsumexp over valid p of s[h][p] (from lse_partial)
+ *   S_p  = log( (1/G) sum_h exp(s[h][p] - L_h) )   (group-mean mass fraction)
+ *   k    = min(Np_b, k_fixed) if k_fixed > 0, else
+ *          min(Np_b, max(1, ceil(keep_frac * Np_b))) (product in double)
+ * The first n_force_first and last n_force_last valid pages get S = +inf.
+ * Pages are ranked by (S descending, page index ascending), NaN as -inf; the
+ * first k are written to sel[row][0..k) in ascending page order, sel entries
+ * [k, k_max) are set to -1, sel_count[row] = k.
+ * sel: int32 [B][Hkv][k_max]; k_max must be >= the k of a row with max_pages
+ * pages.  page_S (optional, may be NULL): float32 [B][Hkv][max_pages], S_p for
+ * p < Np_b.  max_pages <= 15360.  ws/ws_bytes: kv_page_topk_workspace_size().
+ * --------------------------------------------------------------------------- */
+int kv_page_topk(const kv_layout* layout, const float* head_scores, const float* lse_partial,
+                 const int32_t* seq_lens, int32_t B, int32_t max_pages, float keep_frac,
+                 int32_t k_fixed, int32_t n_force_first, int32_t n_force_last,
+                 int32_t* sel, int32_t* sel_count, int32_t k_max, float* page_S,
+                 void* ws, size_t ws_bytes, void* stream);
+
+size_t kv_page_topk_workspace_size(const kv_layout* layout, int32_t B, int32_t max_pages);
+
+/* ---------------------------------------------------------------------------
+ * kv_sparse_decode_attn -- softmax attention of every query head over the
+ * tokens of its row's selected pages only (AMASS page, "AMASS": a sparse
+ * paged-attention kernel reads just the selected pages), renormalised over
+ * those tokens, with packed tiers decoded in registers (ARGUS page, "Why It
+ * Works"):
+ *   z_i = tau q.k_i, out = sum_i softmax(z)_i v_i, lse = log sum_i exp(z_i)
+ * over tokens i < seq_lens[b] of logical pages sel[row][0..sel_count[row]).
+ * sel entries outside [0, Np_b) are skipped; sel_count is clamped to
+ * [0, k_max].  out: float32 [B][Hq][d]; lse: float32 [B][Hq] (natural log);
+ * a row with no tokens gives out = 0, lse = -inf.
+ * Split-K: num_splits > 0 fixes the number of partial results per row (at
+ * most 256); 0 lets the library choose.  Results agree across split counts to
+ * float32 rounding.  ws/ws_bytes: kv_sparse_decode_attn_workspace_size() with
+ * the same num_splits.
+ * --------------------------------------------------------------------------- */
+int kv_sparse_decode_attn(const kv_layout* layout, const void* q, const kv_pages* pages,
+                          const int32_t* block_table, const int32_t* seq_lens, int32_t B,
+                          int32_t max_pages, const int32_t* sel, const int32_t* sel_count,
+                          int32_t k_max, int32_t num_splits, float* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream);
+
+size_t kv_sparse_decode_attn_workspace_size(const kv_layout* layout, int32_t B, int32_t k_max,
+                                            int32_t num_splits);
+
+/* The split count kv_sparse_decode_attn uses for num_splits = 0. */
+int32_t kv_sparse_decode_attn_num_splits(const kv_layout* layout, int32_t B, int32_t k_max);
+
+/* ---------------------------------------------------------------------------
+ * kv_dequant_tier -- the attention kernel's in-register tier decoding as a
+ * standalone call (for tests and tier migration): K and V of physical pages
+ * pages[0..n) decoded through `pages_desc` (page_entry, tiers, hot buffer) into
+ * out, float32 [n][2][Hkv][P][d] (index 0 = K, 1 = V).  ARGUS page, "Why It
+ * Works: Storage vs. Computation".
+ * --------------------------------------------------------------------------- */
+int kv_dequant_tier(const kv_layout* layout, const kv_pages* pages_desc, const int32_t* pages,
+                    int32_t n, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_pack_tier -- encode 16-bit pages into packed tier `tier` (1..4; ARGUS tier
+ * legend: INT8, INT4 2-way, INT2 4-way, 1-bit 8-way sign-packed).
+ * Per token vector, per group of 32 consecutive head-dim elements, x the
+ * float32 value of the 16-bit input, every step an IEEE float32 operation
+ * rounded to nearest even, no fused multiply-add:
+ *   int-b: s = f16(f32(max - min) / (2^b - 1)), z = f16(min),
+ *          c = 0 if s == 0 else clamp(rint(f32(x - z) / s), 0, 2^b - 1)
+ *   1-bit: z = f16(T(x) / 32), s = f16(T(|x - z|) / 32), c = (x >= z),
+ *          T the pairwise tree sum (level by level, pairs (2i, 2i+1))
+ *   f16() rounds to nearest even and saturates at +-65504.
+ * Source page src_pages[i] of src16 ([*][Hkv][P][d]) goes to slot dst_slots[i]
+ * of codes ([slots][Hkv][P][d*bits/8]) and scale_zero ([slots][Hkv][P][d/32][2]
+ * float16, scale first).  NULL src_pages / dst_slots mean i.
+ * --------------------------------------------------------------------------- */
+int kv_pack_tier(const kv_layout* layout, const void* src16, const int32_t* src_pages, int32_t n,
+                 int32_t tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
+                 void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSPARSE_H */

@@ -1,0 +1,215 @@
+// C ABI of libkvsparse: argument validation (before any HIP call), workspace
+// sizing, launch-shape choice and status codes.  Declared in include/kvsparse.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/kvsparse.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_layout(const kv_layout* L) {
+  if (!L) return KV_ERR_INVALID_ARG;
+  if (L->num_q_heads <= 0 || L->num_kv_heads <= 0) return KV_ERR_INVALID_ARG;
+  if (L->num_q_heads % L->num_kv_heads != 0) return KV_ERR_INVALID_ARG;
+  if (L->head_dim <= 0 || L->page_size <= 0 || L->rank <= 0) return KV_ERR_INVALID_ARG;
+  if (L->kv_dtype != KV_F16 && L->kv_dtype != KV_BF16) return KV_ERR_UNSUPPORTED;
+  if (L->head_dim != 64 && L->head_dim != 128) return KV_ERR_UNSUPPORTED;
+  if (L->page_size != 16 && L->page_size != 32) return KV_ERR_UNSUPPORTED;
+  if (L->rank != 1 && L->rank != 2 && L->rank != 4 && L->rank != 8) return KV_ERR_UNSUPPORTED;
+  if (L->num_q_heads / L->num_kv_heads > 16) return KV_ERR_UNSUPPORTED;
+  if (!(L->softmax_scale == L->softmax_scale)) return KV_ERR_INVALID_ARG;
+  return KV_OK;
+}
+
+float scale_of(const kv_layout* L) {
+  return L->softmax_scale > 0.f ? L->softmax_scale : 1.0f / std::sqrt((float)L->head_dim);
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? KV_OK : KV_ERR_HIP; }
+
+int topk_bound(int max_pages, float keep, int k_fixed) {
+  if (max_pages <= 0) return 0;
+  if (k_fixed > 0) return k_fixed < max_pages ? k_fixed : max_pages;
+  int k = (int)std::ceil((double)keep * (double)max_pages);
+  k = k < 1 ? 1 : k;
+  return k > max_pages ? max_pages : k;
+}
+
+int auto_splits(int rows, int k_max) {
+  if (rows <= 0) return 1;
+  int s = (1024 + rows - 1) / rows;            // about four blocks per CU
+  int cap = k_max / 4;                         // at least ~4 pages per split
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s > kvs::kMaxSplits) s = kvs::kMaxSplits;
+  return s < 1 ? 1 : s;
+}
+
+int check_pages(const kv_layout* L, const kv_pages* pg) {
+  if (!pg) return KV_ERR_INVALID_ARG;
+  if (!pg->k16 || !pg->v16) return KV_ERR_INVALID_ARG;
+  if (!aligned16(pg->k16) || !aligned16(pg->v16)) return KV_ERR_INVALID_ARG;
+  if (pg->page_entry) {
+    for (int t = 0; t < 4; ++t) {
+      if (!pg->kq[t] || !pg->vq[t] || !pg->ksz[t] || !pg->vsz[t]) return KV_ERR_INVALID_ARG;
+      if (!aligned16(pg->kq[t]) || !aligned16(pg->vq[t])) return KV_ERR_INVALID_ARG;
+      if ((reinterpret_cast<uintptr_t>(pg->ksz[t]) & 3u) || (reinterpret_cast<uintptr_t>(pg->vsz[t]) & 3u))
+        return KV_ERR_INVALID_ARG;
+    }
+  }
+  if (pg->v_hot_slot && (!pg->v_hot || !aligned16(pg->v_hot))) return KV_ERR_INVALID_ARG;
+  (void)L;
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv_status_string(int status) {
+  switch (status) {
+    case KV_OK: return "ok";
+    case KV_ERR_INVALID_ARG: return "invalid argument";
+    case KV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KV_ERR_WORKSPACE: return "workspace missing or too small";
+    case KV_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int kv_summary_build(const kv_layout* L, const void* k16, const int32_t* pages, const int32_t* n_valid,
+                     int32_t n, void* summary, float* log_n, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (n < 0) return KV_ERR_INVALID_ARG;
+  if (n == 0) return KV_OK;
+  if (!k16 || !pages || !n_valid || !summary || !log_n) return KV_ERR_INVALID_ARG;
+  if (!aligned16(k16)) return KV_ERR_INVALID_ARG;
+  if ((int64_t)n * L->num_kv_heads > 0x7FFFFFFF) return KV_ERR_UNSUPPORTED;
+  return from_hip(kvs::launch_summary_build(*L, k16, pages, n_valid, n, summary, log_n,
+                                            (hipStream_t)stream));
+}
+
+size_t kv_page_score_partial_size(const kv_layout* L, int32_t B, int32_t max_pages) {
+  if (check_layout(L) || B <= 0 || max_pages <= 0) return 0;
+  const size_t G = (size_t)(L->num_q_heads / L->num_kv_heads);
+  return (size_t)B * L->num_kv_heads * kvs::score_tiles(max_pages) * G * 2 * sizeof(float);
+}
+
+int kv_page_score(const kv_layout* L, const void* q, const void* summary, const float* log_n,
+                  const int32_t* block_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                  float* head_scores, float* lse_partial, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
+  if (B == 0 || max_pages == 0) return KV_OK;
+  if (!q || !summary || !log_n || !block_table || !seq_lens || !head_scores || !lse_partial)
+    return KV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(summary)) return KV_ERR_INVALID_ARG;
+  if ((int64_t)B * L->num_kv_heads > 65535) return KV_ERR_UNSUPPORTED;
+  return from_hip(kvs::launch_page_score(*L, q, summary, log_n, block_table, seq_lens, B, max_pages,
+                                         scale_of(L), head_scores, lse_partial, (hipStream_t)stream));
+}
+
+size_t kv_page_topk_workspace_size(const kv_layout* L, int32_t B, int32_t max_pages) {
+  (void)L; (void)B; (void)max_pages;
+  return 0;
+}
+
+int kv_page_topk(const kv_layout* L, const float* head_scores, const float* lse_partial,
+                 const int32_t* seq_lens, int32_t B, int32_t max_pages, float keep_frac,
+                 int32_t k_fixed, int32_t n_force_first, int32_t n_force_last, int32_t* sel,
+                 int32_t* sel_count, int32_t k_max, float* page_S, void* ws, size_t ws_bytes,
+                 void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  (void)ws; (void)ws_bytes;
+  if (B < 0 || max_pages < 0 || k_max < 0 || k_fixed < 0 || n_force_first < 0 || n_force_last < 0)
+    return KV_ERR_INVALID_ARG;
+  if (!(keep_frac >= 0.f) || !std::isfinite(keep_frac)) return KV_ERR_INVALID_ARG;
+  if (B == 0) return KV_OK;
+  if (max_pages > kvs::kMaxTopkPages) return KV_ERR_UNSUPPORTED;
+  if (!seq_lens || !sel_count) return KV_ERR_INVALID_ARG;
+  if (max_pages > 0 && (!head_scores || !lse_partial)) return KV_ERR_INVALID_ARG;
+  if (k_max > 0 && !sel) return KV_ERR_INVALID_ARG;
+  if (k_max < topk_bound(max_pages, keep_frac, k_fixed)) return KV_ERR_INVALID_ARG;
+  if ((int64_t)B * L->num_kv_heads > 0x7FFFFFFF) return KV_ERR_UNSUPPORTED;
+  return from_hip(kvs::launch_page_topk(*L, head_scores, lse_partial, seq_lens, B, max_pages,
+                                        keep_frac, k_fixed, n_force_first, n_force_last, sel,
+                                        sel_count, k_max, page_S, (hipStream_t)stream));
+}
+
+int32_t kv_sparse_decode_attn_num_splits(const kv_layout* L, int32_t B, int32_t k_max) {
+  if (check_layout(L) || B <= 0) return 1;
+  return auto_splits(B * L->num_kv_heads, k_max);
+}
+
+size_t kv_sparse_decode_attn_workspace_size(const kv_layout* L, int32_t B, int32_t k_max,
+                                            int32_t num_splits) {
+  if (check_layout(L) || B <= 0 || num_splits < 0) return 0;
+  const int rows = B * L->num_kv_heads;
+  const int s = num_splits > 0 ? num_splits : auto_splits(rows, k_max);
+  const size_t G = (size_t)(L->num_q_heads / L->num_kv_heads);
+  return (size_t)rows * s * G * (L->head_dim + 2) * sizeof(float);
+}
+
+int kv_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages* pg,
+                          const int32_t* block_table, const int32_t* seq_lens, int32_t B,
+                          int32_t max_pages, const int32_t* sel, const int32_t* sel_count,
+                          int32_t k_max, int32_t num_splits, float* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0 || k_max < 0 || num_splits < 0) return KV_ERR_INVALID_ARG;
+  if (num_splits > kvs::kMaxSplits) return KV_ERR_UNSUPPORTED;
+  if (B == 0) return KV_OK;
+  if (!q || !block_table || !seq_lens || !sel_count || !out || !lse) return KV_ERR_INVALID_ARG;
+  if (k_max > 0 && !sel) return KV_ERR_INVALID_ARG;
+  if (!aligned16(q)) return KV_ERR_INVALID_ARG;
+  rc = check_pages(L, pg);
+  if (rc) return rc;
+  const int rows = B * L->num_kv_heads;
+  if ((int64_t)rows > 65535) return KV_ERR_UNSUPPORTED;
+  const int s = num_splits > 0 ? num_splits : auto_splits(rows, k_max);
+  const size_t need = kv_sparse_decode_attn_workspace_size(L, B, k_max, s);
+  if (!ws || ws_bytes < need) return KV_ERR_WORKSPACE;
+  return from_hip(kvs::launch_sparse_attn(*L, q, *pg, block_table, seq_lens, B, max_pages, sel,
+                                          sel_count, k_max, s, scale_of(L), out, lse, (float*)ws,
+                                          (hipStream_t)stream));
+}
+
+int kv_dequant_tier(const kv_layout* L, const kv_pages* pg, const int32_t* pages, int32_t n,
+                    float* out, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (n < 0) return KV_ERR_INVALID_ARG;
+  if (n == 0) return KV_OK;
+  if (!pages || !out) return KV_ERR_INVALID_ARG;
+  rc = check_pages(L, pg);
+  if (rc) return rc;
+  return from_hip(kvs::launch_dequant_tier(*L, *pg, pages, n, out, (hipStream_t)stream));
+}
+
+int kv_pack_tier(const kv_layout* L, const void* src16, const int32_t* src_pages, int32_t n,
+                 int32_t tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
+                 void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (tier < KV_TIER_I8 || tier > KV_TIER_B1) return KV_ERR_UNSUPPORTED;
+  if (n < 0) return KV_ERR_INVALID_ARG;
+  if (n == 0) return KV_OK;
+  if (!src16 || !codes || !scale_zero) return KV_ERR_INVALID_ARG;
+  if (!aligned16(src16) || (reinterpret_cast<uintptr_t>(codes) & 3u) ||
+      (reinterpret_cast<uintptr_t>(scale_zero) & 3u))
+    return KV_ERR_INVALID_ARG;
+  return from_hip(kvs::launch_pack_tier(*L, src16, src_pages, n, tier, codes, scale_zero, dst_slots,
+                                        (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Packed low-bit page tiers: encoder.  ARGUS (argus_cache 0.1.7.1 project
+// page), "Visual Architecture" and the tier legend: INT8, INT4 (2-way
+// bit-packed), INT2 (4-way bit-packed), 1-bit (8-way sign-packed).
+//
+// Per token vector, per group of 32 consecutive head-dim elements, with every
+// operation an IEEE float32 operation rounded to nearest even and no fused
+// multiply-add (this file is compiled with -ffp-contract=off; division and
+// square root are the correctly rounded ones):
+//   int-b: s = f16(f32(max - min) / (2^b - 1)), z = f16(min),
+//          c = 0 if s == 0 else clamp(rint(f32(x - z) / s), 0, 2^b - 1)
+//   1-bit: z = f16(T(x) / 32), s = f16(T(|x - z|) / 32), c = (x >= z)
+//          with T the pairwise tree sum, level by level, pairs (2i, 2i+1)
+//   f16(): round to nearest even, saturating at +-65504.
+// Codes are packed LSB first in head-dim order; (s, z) are stored as a float16
+// pair per group.  One thread encodes one group.
+
+#include "device.h"
+#include "launch.h"
+
+namespace kvs {
+
+__device__ __forceinline__ float f16_sat(float x) {
+  x = fminf(fmaxf(x, -65504.f), 65504.f);
+  return (float)(_Float16)x;
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+template <int D, bool F16>
+__global__ __launch_bounds__(256) void pack_tier_kernel(const uint16_t* __restrict__ src16,
+                                                        const int32_t* __restrict__ src_pages,
+                                                        const int32_t* __restrict__ dst_slots, int n,
+                                                        int Hkv, int P, int bits,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint16_t* __restrict__ scale_zero) {
+  constexpr int NG = D / 32;
+  const size_t total = (size_t)n * Hkv * P * NG;
+  for (size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x; id < total;
+       id += (size_t)gridDim.x * blockDim.x) {
+    size_t r = id;
+    const int grp = (int)(r % NG); r /= NG;
+    const int tk = (int)(r % P); r /= P;
+    const int g = (int)(r % Hkv); r /= Hkv;
+    const int i = (int)r;
+    const int sp = src_pages ? src_pages[i] : i;
+    const int ds = dst_slots ? dst_slots[i] : i;
+    const uint16_t* xs = src16 + (((size_t)sp * Hkv + g) * P + tk) * D + grp * 32;
+    float x[32];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u32x4_t w = ld16(xs + 8 * v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * v + 2 * j] = lo16<F16>(w[j]);
+        x[8 * v + 2 * j + 1] = hi16<F16>(w[j]);
+      }
+    }
+    uint32_t c[32];
+    float s, z;
+    if (bits == 1) {
+      float t[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) t[j] = x[2 * j] + x[2 * j + 1];
+#pragma unroll
+      for (int len = 8; len >= 1; len >>= 1)
+#pragma unroll
+        for (int j = 0; j < len; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+      z = f16_sat(t[0] / 32.f);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) t[j] = fabsf(x[2 * j] - z) + fabsf(x[2 * j + 1] - z);
+#pragma unroll
+      for (int len = 8; len >= 1; len >>= 1)
+#pragma unroll
+        for (int j = 0; j < len; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+      s = f16_sat(t[0] / 32.f);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) c[j] = x[j] >= z ? 1u : 0u;
+    } else {
+      const float qmax = (float)((1 << bits) - 1);
+      float mn = x[0], mx = x[0];
+#pragma unroll
+      for (int j = 1; j < 32; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
+      s = f16_sat((mx - mn) / qmax);
+      z = f16_sat(mn);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        float cj = 0.f;
+        if (s != 0.f) cj = fminf(fmaxf(__builtin_rintf((x[j] - z) / s), 0.f), qmax);
+        c[j] = (uint32_t)cj;
+      }
+    }
+    // pack: 32 codes of `bits` bits -> bits 32-bit words, LSB first
+    const size_t row = ((size_t)ds * Hkv + g) * P + tk;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * (D * bits / 8) + grp * 4 * bits);
+    const int per_word = 32 / bits;
+    for (int wdx = 0; wdx < bits; ++wdx) {
+      uint32_t word = 0;
+      for (int j = 0; j < per_word; ++j) word |= c[wdx * per_word + j] << (j * bits);
+      dst[wdx] = word;
+    }
+    uint16_t* szp = scale_zero + (row * NG + grp) * 2;
+    szp[0] = f16_bits(s);
+    szp[1] = f16_bits(z);
+  }
+}
+
+hipError_t launch_pack_tier(const kv_layout& L, const void* src16, const int32_t* src_pages, int n,
+                            int tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
+                            hipStream_t st) {
+  static const int kBits[5] = {16, 8, 4, 2, 1};
+  const int bits = kBits[tier];
+  const size_t total = (size_t)n * L.num_kv_heads * L.page_size * (L.head_dim / 32);
+  const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+  const uint16_t* s = (const uint16_t*)src16;
+  uint16_t* sz = (uint16_t*)scale_zero;
+  const bool f16 = L.kv_dtype == KV_F16;
+  if (L.head_dim == 64) {
+    if (f16) hipLaunchKernelGGL((pack_tier_kernel<64, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, codes, sz);
+    else hipLaunchKernelGGL((pack_tier_kernel<64, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, codes, sz);
+  } else {
+    if (f16) hipLaunchKernelGGL((pack_tier_kernel<128, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, codes, sz);
+    else hipLaunchKernelGGL((pack_tier_kernel<128, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, codes, sz);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -1,0 +1,47 @@
+// Internal launchers: the C ABI (capi.cpp) validates arguments, then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvsparse.h"
+
+namespace kvs {
+
+// Pages of 16 logical pages per MFMA tile; a score block covers this many pages.
+constexpr int kScorePagesPerBlock = 128;
+constexpr int kTopkThreads = 512;
+constexpr int kMaxTopkPages = 15360;   // keys in LDS stay under 64 KB
+constexpr int kMaxSplits = 256;
+
+inline int score_tiles(int max_pages) { return (max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock; }
+
+hipError_t launch_summary_build(const kv_layout& L, const void* k16, const int32_t* pages,
+                                const int32_t* n_valid, int n, void* summary, float* log_n,
+                                hipStream_t st);
+
+hipError_t launch_page_score(const kv_layout& L, const void* q, const void* summary,
+                             const float* log_n, const int32_t* block_table, const int32_t* seq_lens,
+                             int B, int max_pages, float tau, float* head_scores, float* lse_partial,
+                             hipStream_t st);
+
+hipError_t launch_page_topk(const kv_layout& L, const float* head_scores, const float* lse_partial,
+                            const int32_t* seq_lens, int B, int max_pages, float keep, int k_fixed,
+                            int n_force_first, int n_force_last, int32_t* sel, int32_t* sel_count,
+                            int k_max, float* page_S, hipStream_t st);
+
+hipError_t launch_sparse_attn(const kv_layout& L, const void* q, const kv_pages& pg,
+                              const int32_t* block_table, const int32_t* seq_lens, int B,
+                              int max_pages, const int32_t* sel, const int32_t* sel_count, int k_max,
+                              int n_splits, float tau, float* out, float* lse, float* partials,
+                              hipStream_t st);
+
+hipError_t launch_dequant_tier(const kv_layout& L, const kv_pages& pg, const int32_t* pages, int n,
+                               float* out, hipStream_t st);
+
+hipError_t launch_pack_tier(const kv_layout& L, const void* src16, const int32_t* src_pages, int n,
+                            int tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
+                            hipStream_t st);
+
+}  // namespace kvs

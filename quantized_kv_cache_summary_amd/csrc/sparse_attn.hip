@@ -1,0 +1,495 @@
+// Sparse paged decode attention over the selected pages only, split-K with a
+// log-sum-exp merge.  AMASS (amass-kv 0.1.1 project page), "AMASS": each decode
+// step attends only to the pages that carry attention mass, read by a sparse
+// paged-attention kernel.  Packed tiers are rebuilt in registers just before
+// use (ARGUS, argus_cache 0.1.7.1 project page, "Why It Works: Storage vs.
+// Computation"); the arithmetic stays float32.
+//
+// gfx950 design.  One block (4 waves) per (row, split); the split's selected
+// pages are dealt round-robin to the waves; a wave handles 16 tokens at a time.
+//   QK^T: the G query heads of the group are the 16 B columns of a 16x16x32
+//     MFMA, the 16 tokens its A rows.  Each lane loads d/4 contiguous elements
+//     (64 bytes) of one token's key.  A packed page is decoded to float32 and
+//     fed as an exact bf16 (or f16) hi + lo pair, two MFMAs per step.
+//   softmax: the MFMA leaves head h / tokens 4g'+i in lane h + 16g'.  The
+//     running max is shared by the four lane groups and only raised when a
+//     chunk exceeds it by more than 2^8 (the stale max cancels exactly in
+//     out = acc / l), so rescaling is rare.
+//   PV: lane (token slot ts, element chunk ec) loads d/16 values of token
+//     4j + ts, so the V page is read with 16-byte coalesced loads; the
+//     probabilities reach it through a 1 KB per-wave LDS tile; acc[head][d/16]
+//     accumulates in float32 FMAs.
+// The four waves merge in LDS; a second kernel merges the splits.
+
+#include "device.h"
+#include "launch.h"
+
+namespace kvs {
+
+constexpr int kAttnWaves = 4;
+
+struct PagesDev {
+  const uint16_t* k16;
+  const uint16_t* v16;
+  const uint8_t* kq[4];
+  const uint8_t* vq[4];
+  const uint16_t* ksz[4];
+  const uint16_t* vsz[4];
+  const uint32_t* page_entry;
+  const uint16_t* v_hot;
+  const int32_t* v_hot_slot;
+};
+
+// ---------------------------------------------------------------- packed decode
+
+// Loads `EL` consecutive codes of `BITS` bits starting at element e0 of a code row.
+template <int EL, int BITS>
+__device__ __forceinline__ void load_code_words(const uint8_t* rowp, int e0, uint32_t* w, int& shift0) {
+  constexpr int NB = EL * BITS;   // bits to load
+  const int bitoff = e0 * BITS;
+  const uint8_t* p = rowp + (bitoff >> 3);
+  shift0 = bitoff & 7;
+  if constexpr (NB >= 32) {
+#pragma unroll
+    for (int i = 0; i < NB / 32; ++i) w[i] = reinterpret_cast<const uint32_t*>(p)[i];
+  } else if constexpr (NB == 16) {
+    w[0] = *reinterpret_cast<const uint16_t*>(p);
+  } else {
+    w[0] = *p;
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t code_at(const uint32_t* w, int shift0, int e) {
+  const int bit = shift0 + e * BITS;
+  return (w[bit >> 5] >> (bit & 31)) & ((1u << BITS) - 1u);
+}
+
+// Decodes EL elements starting at e0 of token row `tokrow` of a packed page.
+template <int D, int EL, int BITS>
+__device__ __forceinline__ void decode_run(const uint8_t* codes, const uint16_t* sz, size_t tokrow,
+                                           int e0, float* x) {
+  uint32_t w[(EL * BITS + 31) / 32];
+  int sh;
+  load_code_words<EL, BITS>(codes + tokrow * (D * BITS / 8), e0, w, sh);
+  const uint32_t szw = *reinterpret_cast<const uint32_t*>(sz + (tokrow * (D / 32) + e0 / 32) * 2);
+  const float s = f16_bits_to_f32(szw & 0xFFFFu), z = f16_bits_to_f32(szw >> 16);
+  if constexpr (BITS == 1) {
+    const float zp = z + s, zm = z - s;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) x[e] = code_at<1>(w, sh, e) ? zp : zm;
+  } else {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) x[e] = __builtin_fmaf((float)code_at<BITS>(w, sh, e), s, z);
+  }
+}
+
+// Exact split of float32 values into a 16-bit hi part and a 16-bit lo part.
+template <bool F16>
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  if constexpr (F16) {
+    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+    const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+    hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+  } else {
+    const uint32_t u0 = __float_as_uint(x0) & 0xFFFF0000u, u1 = __float_as_uint(x1) & 0xFFFF0000u;
+    hi = (u0 >> 16) | u1;
+    const uint32_t r0 = __float_as_uint(x0 - __uint_as_float(u0)), r1 = __float_as_uint(x1 - __uint_as_float(u1));
+    lo = (r0 >> 16) | (r1 & 0xFFFF0000u);
+  }
+}
+
+// ---------------------------------------------------------------- the kernel
+
+template <int D, int GM, bool F16, bool TIERED>
+__global__ __launch_bounds__(256) void sparse_attn_kernel(
+    const uint16_t* __restrict__ q, PagesDev pg, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int Hkv, int G, int P, int max_pages,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int k_max, int n_splits,
+    float scale_log2, float* __restrict__ partials) {
+  constexpr int KS = D / 32;     // MFMA k-steps
+  constexpr int EK = D / 4;      // key elements per lane
+  constexpr int EV = D / 16;     // value elements per lane
+  constexpr float kRescale = 8.0f;
+
+  __shared__ float ptile[kAttnWaves][16][16];       // [wave][token][head]
+  __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
+  __shared__ float wacc[kAttnWaves][GM][D];
+
+  const int row = blockIdx.y, split = blockIdx.x;
+  const int b = row / Hkv, g = row - b * Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+
+  const int L = seq_lens[b];
+  int Np = L > 0 ? (L + P - 1) / P : 0;
+  Np = Np < max_pages ? Np : max_pages;
+  int cnt = sel_count[row];
+  cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
+  const int beg = (int)(((long long)split * cnt) / n_splits);
+  const int end = (int)(((long long)(split + 1) * cnt) / n_splits);
+
+  // B operand: query head `col`, elements grp*EK + 8s + [0, 8)
+  u32x4_t qop[KS];
+  {
+    const int Hq = Hkv * G;
+    const uint16_t* qp = q + ((size_t)b * Hq + (size_t)g * G + (col < G ? col : 0)) * D + grp * EK;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qop[s] = col < G ? ld16(qp + 8 * s) : u32x4_t{0, 0, 0, 0};
+  }
+
+  float m_run = -INFINITY;   // per head (col), identical in the 4 lane groups
+  float l_run = 0.f;         // per lane: its own tokens
+  float acc[GM][EV];
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[h][e] = 0.f;
+
+  const int32_t* srow = sel + (size_t)row * k_max;
+  const int32_t* bt = block_table + (size_t)b * max_pages;
+  const size_t page_elems = (size_t)P * D;
+
+  for (int it = beg + wave; it < end; it += kAttnWaves) {
+    const int p = srow[it];
+    if (p < 0 || p >= Np) continue;
+    const int phys = bt[p];
+    uint32_t tier = 0, slot = (uint32_t)phys;
+    if constexpr (TIERED) {
+      if (pg.page_entry) {
+        const uint32_t e = pg.page_entry[phys];
+        tier = e >> 29;
+        slot = e & 0x1FFFFFFFu;
+      }
+    }
+    const size_t pr = (size_t)slot * Hkv + g;   // (slot, head) page record index
+    const uint16_t* kbase = pg.k16 + pr * page_elems;
+    const uint16_t* vbase = pg.v16 + pr * page_elems;
+    if (pg.v_hot_slot) {
+      const int hs = pg.v_hot_slot[phys];
+      if (hs >= 0) vbase = pg.v_hot + ((size_t)hs * Hkv + g) * page_elems;
+    }
+
+    for (int c = 0; c < P / 16; ++c) {
+      const int tok0 = p * P + c * 16;
+      // ---- logits
+      f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
+      if (!TIERED || tier == KV_TIER_NATIVE) {
+        const uint16_t* kp = kbase + (size_t)(c * 16 + col) * D + grp * EK;
+        u32x4_t a[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[s] = ld16(kp + 8 * s);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(a[s], qop[s], zacc);
+      } else {
+        float x[EK];
+        const size_t tokrow = pr * P + c * 16 + col;
+        const int t = (int)tier - 1;
+        switch (tier) {
+          case KV_TIER_I8: decode_run<D, EK, 8>(pg.kq[t], pg.ksz[t], tokrow, grp * EK, x); break;
+          case KV_TIER_I4: decode_run<D, EK, 4>(pg.kq[t], pg.ksz[t], tokrow, grp * EK, x); break;
+          case KV_TIER_I2: decode_run<D, EK, 2>(pg.kq[t], pg.ksz[t], tokrow, grp * EK, x); break;
+          default: decode_run<D, EK, 1>(pg.kq[t], pg.ksz[t], tokrow, grp * EK, x); break;
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          u32x4_t ah, al;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t hw, lw;
+            split_pair<F16>(x[8 * s + 2 * w], x[8 * s + 2 * w + 1], hw, lw);
+            ah[w] = hw;
+            al[w] = lw;
+          }
+          zacc = mfma16<F16>(ah, qop[s], zacc);
+          zacc = mfma16<F16>(al, qop[s], zacc);
+        }
+      }
+      float z[4];
+      float cm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tpos = tok0 + 4 * grp + i;
+        z[i] = tpos < L ? zacc[i] * scale_log2 : -INFINITY;
+        cm = nan_max(cm, z[i]);
+      }
+      cm = nan_max(cm, __shfl_xor(cm, 16));
+      cm = nan_max(cm, __shfl_xor(cm, 32));
+      // a NaN logit (NaN query) makes the running max NaN, so the head's
+      // output and lse come out NaN instead of being dropped
+      const float m_new = nan_max(m_run, cm);
+      const bool need = (m_new > m_run + kRescale) || (m_new != m_new && m_run == m_run);
+      if (__ballot(need)) {
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+        if (m_new != -INFINITY) m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+          const float ah = readlane_f(alpha, h);
+#pragma unroll
+          for (int e = 0; e < EV; ++e) acc[h][e] *= ah;
+        }
+      }
+      float pz[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pz[i] = (m_run == -INFINITY) ? 0.f : exp2f(z[i] - m_run);
+        l_run += pz[i];
+        ptile[wave][4 * grp + i][col] = pz[i];
+      }
+      wave_lds_sync();
+      // ---- values
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tk = 4 * j + grp;
+        const bool valid = tok0 + tk < L;
+        float v[EV];
+        if (!TIERED || tier == KV_TIER_NATIVE) {
+          const uint16_t* vp = vbase + (size_t)(c * 16 + tk) * D + col * EV;
+          if constexpr (EV == 8) {
+            const u32x4_t r = valid ? ld16(vp) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) { v[2 * w] = lo16<F16>(r[w]); v[2 * w + 1] = hi16<F16>(r[w]); }
+          } else {
+            const u32x2_t r = valid ? *reinterpret_cast<const u32x2_t*>(vp) : u32x2_t{0, 0};
+#pragma unroll
+            for (int w = 0; w < 2; ++w) { v[2 * w] = lo16<F16>(r[w]); v[2 * w + 1] = hi16<F16>(r[w]); }
+          }
+        } else {
+          const size_t tokrow = pr * P + c * 16 + tk;
+          const int t = (int)tier - 1;
+          switch (tier) {
+            case KV_TIER_I8: decode_run<D, EV, 8>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
+            case KV_TIER_I4: decode_run<D, EV, 4>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
+            case KV_TIER_I2: decode_run<D, EV, 2>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
+            default: decode_run<D, EV, 1>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
+          }
+          if (!valid) {
+#pragma unroll
+            for (int e = 0; e < EV; ++e) v[e] = 0.f;
+          }
+        }
+        float pv[GM];
+#pragma unroll
+        for (int h4 = 0; h4 < GM; h4 += 4) {
+          const float4 t4 = *reinterpret_cast<const float4*>(&ptile[wave][tk][h4]);
+          pv[h4] = t4.x; pv[h4 + 1] = t4.y; pv[h4 + 2] = t4.z; pv[h4 + 3] = t4.w;
+        }
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+#pragma unroll
+          for (int e = 0; e < EV; ++e) acc[h][e] = __builtin_fmaf(pv[h], v[e], acc[h][e]);
+      }
+      wave_lds_sync();
+    }
+  }
+
+  // ---- wave totals: l over lane groups, acc over token slots
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      float a = acc[h][e];
+      a += __shfl_xor(a, 16);
+      a += __shfl_xor(a, 32);
+      acc[h][e] = a;
+    }
+  if (lane < 16) { wm[wave][lane] = m_run; wl[wave][lane] = l_run; }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+#pragma unroll
+      for (int e = 0; e < EV; ++e) wacc[wave][h][col * EV + e] = acc[h][e];
+  }
+  __syncthreads();
+
+  // ---- merge the waves (fixed order) and write this split's partial
+  float* dst = partials + ((size_t)row * n_splits + split) * G * (D + 2);
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int h = idx / D, e = idx - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = nan_max(M, wm[w][h]);
+    float a = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float f = exp2f(wm[w][h] - M);
+        a += wacc[w][h][e] * f;
+        l += wl[w][h] * f;
+      }
+    }
+    dst[(size_t)h * (D + 2) + e] = a;
+    if (e == 0) {
+      dst[(size_t)h * (D + 2) + D] = M;
+      dst[(size_t)h * (D + 2) + D + 1] = l;
+    }
+  }
+}
+
+// Split merge: one block of D threads per (row, head).
+template <int D>
+__global__ __launch_bounds__(D) void split_reduce_kernel(const float* __restrict__ partials, int Hkv,
+                                                          int G, int n_splits, float* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  const int rh = blockIdx.x;
+  const int row = rh / G, h = rh - row * G;
+  const int b = row / Hkv, g = row - b * Hkv;
+  const int e = threadIdx.x;
+  const float* src = partials + (size_t)row * n_splits * G * (D + 2) + (size_t)h * (D + 2);
+  const size_t stride = (size_t)G * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) M = nan_max(M, src[s * stride + D]);
+  float a = 0.f, l = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float f = exp2f(src[s * stride + D] - M);
+      a += src[s * stride + e] * f;
+      l += src[s * stride + D + 1] * f;
+    }
+  }
+  const size_t hq = (size_t)b * Hkv * G + (size_t)g * G + h;
+  const bool empty = l == 0.f;
+  out[hq * D + e] = empty ? 0.f : a / l;
+  if (e == 0) lse[hq] = empty ? -INFINITY : (M + log2f(l)) * kLn2;
+}
+
+template <int D, int GM, bool F16, bool TIERED>
+static hipError_t launch_attn_t(const kv_layout& L, const void* q, const PagesDev& pd,
+                                const int32_t* bt, const int32_t* sl, int B, int max_pages,
+                                const int32_t* sel, const int32_t* cnt, int k_max, int n_splits,
+                                float tau, float* out, float* lse, float* partials, hipStream_t st) {
+  const int G = L.num_q_heads / L.num_kv_heads;
+  const int rows = B * L.num_kv_heads;
+  hipLaunchKernelGGL((sparse_attn_kernel<D, GM, F16, TIERED>), dim3(n_splits, rows), dim3(256), 0, st,
+                     (const uint16_t*)q, pd, bt, sl, L.num_kv_heads, G, L.page_size, max_pages, sel, cnt,
+                     k_max, n_splits, tau * kLog2e, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((split_reduce_kernel<D>), dim3(rows * G), dim3(D), 0, st, partials,
+                     L.num_kv_heads, G, n_splits, out, lse);
+  return hipGetLastError();
+}
+
+template <int D, bool F16, bool TIERED>
+static hipError_t launch_attn_g(const kv_layout& L, const void* q, const PagesDev& pd,
+                                const int32_t* bt, const int32_t* sl, int B, int max_pages,
+                                const int32_t* sel, const int32_t* cnt, int k_max, int n_splits,
+                                float tau, float* out, float* lse, float* partials, hipStream_t st) {
+  const int G = L.num_q_heads / L.num_kv_heads;
+  if (G <= 4) return launch_attn_t<D, 4, F16, TIERED>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
+  if (G <= 8) return launch_attn_t<D, 8, F16, TIERED>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
+  return launch_attn_t<D, 16, F16, TIERED>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
+}
+
+template <int D, bool F16>
+static hipError_t launch_attn_d(const kv_layout& L, const void* q, const PagesDev& pd, bool tiered,
+                                const int32_t* bt, const int32_t* sl, int B, int max_pages,
+                                const int32_t* sel, const int32_t* cnt, int k_max, int n_splits,
+                                float tau, float* out, float* lse, float* partials, hipStream_t st) {
+  if (tiered) return launch_attn_g<D, F16, true>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
+  return launch_attn_g<D, F16, false>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
+}
+
+static PagesDev to_dev(const kv_pages& pg) {
+  PagesDev d;
+  d.k16 = (const uint16_t*)pg.k16;
+  d.v16 = (const uint16_t*)pg.v16;
+  for (int t = 0; t < 4; ++t) {
+    d.kq[t] = pg.kq[t];
+    d.vq[t] = pg.vq[t];
+    d.ksz[t] = (const uint16_t*)pg.ksz[t];
+    d.vsz[t] = (const uint16_t*)pg.vsz[t];
+  }
+  d.page_entry = pg.page_entry;
+  d.v_hot = (const uint16_t*)pg.v_hot;
+  d.v_hot_slot = pg.v_hot_slot;
+  return d;
+}
+
+hipError_t launch_sparse_attn(const kv_layout& L, const void* q, const kv_pages& pg,
+                              const int32_t* block_table, const int32_t* seq_lens, int B,
+                              int max_pages, const int32_t* sel, const int32_t* sel_count, int k_max,
+                              int n_splits, float tau, float* out, float* lse, float* partials,
+                              hipStream_t st) {
+  const PagesDev pd = to_dev(pg);
+  const bool tiered = pg.page_entry != nullptr;
+  const bool f16 = L.kv_dtype == KV_F16;
+  if (L.head_dim == 64)
+    return f16 ? launch_attn_d<64, true>(L, q, pd, tiered, block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits, tau, out, lse, partials, st)
+               : launch_attn_d<64, false>(L, q, pd, tiered, block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits, tau, out, lse, partials, st);
+  return f16 ? launch_attn_d<128, true>(L, q, pd, tiered, block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits, tau, out, lse, partials, st)
+             : launch_attn_d<128, false>(L, q, pd, tiered, block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits, tau, out, lse, partials, st);
+}
+
+// ---------------------------------------------------------------- standalone decode
+
+template <int D, bool F16>
+__global__ __launch_bounds__(256) void dequant_kernel(PagesDev pg, const int32_t* __restrict__ pages,
+                                                      int n, int Hkv, int P, float* __restrict__ out) {
+  // one thread per (page i, K/V, head, token, 8-element run)
+  constexpr int RUN = 8;
+  const size_t total = (size_t)n * 2 * Hkv * P * (D / RUN);
+  for (size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x; id < total;
+       id += (size_t)gridDim.x * blockDim.x) {
+    size_t r = id;
+    const int run = (int)(r % (D / RUN)); r /= (D / RUN);
+    const int tk = (int)(r % P); r /= P;
+    const int g = (int)(r % Hkv); r /= Hkv;
+    const int kv = (int)(r % 2); r /= 2;
+    const int i = (int)r;
+    const int phys = pages[i];
+    uint32_t tier = 0, slot = (uint32_t)phys;
+    if (pg.page_entry) {
+      const uint32_t e = pg.page_entry[phys];
+      tier = e >> 29;
+      slot = e & 0x1FFFFFFFu;
+    }
+    const size_t prow = ((size_t)slot * Hkv + g) * P + tk;
+    float x[RUN];
+    if (tier == KV_TIER_NATIVE) {
+      const uint16_t* src = (kv == 0 ? pg.k16 : pg.v16) + prow * D;
+      if (kv == 1 && pg.v_hot_slot) {
+        const int hs = pg.v_hot_slot[phys];
+        if (hs >= 0) src = pg.v_hot + (((size_t)hs * Hkv + g) * P + tk) * D;
+      }
+      const u32x4_t w = ld16(src + run * RUN);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { x[2 * j] = lo16<F16>(w[j]); x[2 * j + 1] = hi16<F16>(w[j]); }
+    } else {
+      const int t = (int)tier - 1;
+      const uint8_t* codes = kv == 0 ? pg.kq[t] : pg.vq[t];
+      const uint16_t* sz = kv == 0 ? pg.ksz[t] : pg.vsz[t];
+      switch (tier) {
+        case KV_TIER_I8: decode_run<D, RUN, 8>(codes, sz, prow, run * RUN, x); break;
+        case KV_TIER_I4: decode_run<D, RUN, 4>(codes, sz, prow, run * RUN, x); break;
+        case KV_TIER_I2: decode_run<D, RUN, 2>(codes, sz, prow, run * RUN, x); break;
+        default: decode_run<D, RUN, 1>(codes, sz, prow, run * RUN, x); break;
+      }
+    }
+    float* dst = out + ((((size_t)i * 2 + kv) * Hkv + g) * P + tk) * D + run * RUN;
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) dst[j] = x[j];
+  }
+}
+
+hipError_t launch_dequant_tier(const kv_layout& L, const kv_pages& pg, const int32_t* pages, int n,
+                               float* out, hipStream_t st) {
+  const PagesDev pd = to_dev(pg);
+  const size_t total = (size_t)n * 2 * L.num_kv_heads * L.page_size * (L.head_dim / 8);
+  const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+  const bool f16 = L.kv_dtype == KV_F16;
+  if (L.head_dim == 64) {
+    if (f16) hipLaunchKernelGGL((dequant_kernel<64, true>), dim3(blocks), dim3(256), 0, st, pd, pages, n, L.num_kv_heads, L.page_size, out);
+    else hipLaunchKernelGGL((dequant_kernel<64, false>), dim3(blocks), dim3(256), 0, st, pd, pages, n, L.num_kv_heads, L.page_size, out);
+  } else {
+    if (f16) hipLaunchKernelGGL((dequant_kernel<128, true>), dim3(blocks), dim3(256), 0, st, pd, pages, n, L.num_kv_heads, L.page_size, out);
+    else hipLaunchKernelGGL((dequant_kernel<128, false>), dim3(blocks), dim3(256), 0, st, pd, pages, n, L.num_kv_heads, L.page_size, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -1,0 +1,191 @@
+// Per-page key summary for the quad score, built when a page is appended.
+// AMASS (amass-kv 0.1.1 project page), "What is in the box" item 1: the quad
+// selector keeps a tiny per-page summary with r' eigen-quantities instead of
+// the per-key coordinates.  Per (physical page, KV head), over n valid keys:
+//   mu = mean key, Xc = keys - mu, Gram = Xc Xc^T / n (n <= 32),
+//   eigenpairs of Gram by cyclic Jacobi in float32, lam descending,
+//   w_j = Xc^T v_j / sqrt(n) (= sqrt(lam_j) u_j), zero when j > n-1 or
+//   lam_j <= 1e-6 lam_1;
+// stored as bfloat16 [mu, w_1..w_R] and float32 log n.
+//
+// One wave per (page, KV head).  The keys are centred into LDS once; the
+// n x n Gram comes from LDS dot products; Jacobi runs with the round-robin
+// ("circle") pair schedule, so the n/2 rotations of a step are disjoint and
+// the whole step is a set of independent 2x2 block updates A <- J^T A J plus
+// the column update V <- V J.  A sweep applies every pair once; sweeps stop
+// when no off-diagonal element is above float32 noise (at most 16 sweeps).
+
+#include "device.h"
+#include "launch.h"
+
+namespace kvs {
+
+template <int D, int PS, bool F16>
+__global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __restrict__ k16,
+                                                           const int32_t* __restrict__ pages,
+                                                           const int32_t* __restrict__ n_valid,
+                                                           int Hkv, int R, uint16_t* __restrict__ summary,
+                                                           float* __restrict__ log_n) {
+  constexpr int CPL = D / 64;   // columns per lane
+  __shared__ float X[PS][D + 1];
+  __shared__ float A[PS][PS + 1];
+  __shared__ float V[PS][PS + 1];
+  __shared__ float rot_c[PS / 2], rot_s[PS / 2];
+  __shared__ int rot_p[PS / 2], rot_q[PS / 2];
+  __shared__ int order[PS];
+  __shared__ int n_rot;
+
+  const int lane = threadIdx.x;
+  const int i = blockIdx.x / Hkv, g = blockIdx.x - (blockIdx.x / Hkv) * Hkv;
+  const int phys = pages[i];
+  int nv = n_valid[i];
+  nv = nv < 0 ? 0 : (nv > PS ? PS : nv);
+  const uint16_t* src = k16 + ((size_t)phys * Hkv + g) * PS * D;
+  uint16_t* dst = summary + ((size_t)phys * Hkv + g) * (size_t)(1 + R) * D;
+
+  if (nv == 0) {
+    for (int e = lane; e < (1 + R) * D; e += 64) dst[e] = 0;
+    if (g == 0 && lane == 0) log_n[phys] = -INFINITY;
+    return;
+  }
+
+  // mean (token order, float32) and centred keys
+  float mu[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = lane + 64 * c;
+    float s = 0.f;
+    for (int t = 0; t < nv; ++t) s += h16_to_f32<F16>(src[(size_t)t * D + e]);
+    mu[c] = s / (float)nv;
+    dst[e] = (uint16_t)f32_to_bf16_rne(mu[c]);
+    for (int t = 0; t < PS; ++t)
+      X[t][e] = t < nv ? h16_to_f32<F16>(src[(size_t)t * D + e]) - mu[c] : 0.f;
+  }
+  int m = nv + (nv & 1);
+  if (m < 2) m = 2;
+  const int half = m / 2;
+  __syncthreads();
+
+  // Gram / n
+  const float inv_n = 1.f / (float)nv;
+  for (int idx = lane; idx < m * m; idx += 64) {
+    const int a = idx / m, bb = idx - a * m;
+    if (a <= bb) {
+      float s = 0.f;
+      for (int e = 0; e < D; ++e) s += X[a][e] * X[bb][e];
+      s *= inv_n;
+      A[a][bb] = s;
+      A[bb][a] = s;
+    }
+    V[a][bb] = a == bb ? 1.f : 0.f;
+  }
+  __syncthreads();
+  float trace = 0.f;
+  for (int a = 0; a < m; ++a) trace += A[a][a];
+  const float tiny = 1e-12f * trace;
+
+  for (int sweep = 0; sweep < 16; ++sweep) {
+    if (lane == 0) n_rot = 0;
+    __syncthreads();
+    for (int step = 0; step < m - 1; ++step) {
+      if (lane < half) {
+        // circle method: player 0 fixed, players 1..m-1 rotate
+        int x, y;
+        if (lane == 0) { x = 0; y = 1 + (step % (m - 1)); }
+        else {
+          x = 1 + ((step + lane) % (m - 1));
+          y = 1 + ((step + m - 1 - lane) % (m - 1));
+        }
+        const int p = x < y ? x : y, qq = x < y ? y : x;
+        const float app = A[p][p], aqq = A[qq][qq], apq = A[p][qq];
+        float c = 1.f, s = 0.f;
+        if (fabsf(apq) > 1e-7f * sqrtf(fabsf(app * aqq)) + tiny) {
+          const float theta = (aqq - app) / (2.f * apq);
+          const float t = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
+          c = 1.f / sqrtf(t * t + 1.f);
+          s = t * c;
+          atomicAdd(&n_rot, 1);
+        }
+        rot_p[lane] = p; rot_q[lane] = qq; rot_c[lane] = c; rot_s[lane] = s;
+      }
+      __syncthreads();
+      for (int blk = lane; blk < half * half; blk += 64) {
+        const int a = blk / half, bb = blk - a * half;
+        const int pa = rot_p[a], qa = rot_q[a], pb = rot_p[bb], qb = rot_q[bb];
+        const float ca = rot_c[a], sa = rot_s[a], cb = rot_c[bb], sb = rot_s[bb];
+        const float b00 = A[pa][pb], b01 = A[pa][qb], b10 = A[qa][pb], b11 = A[qa][qb];
+        const float t00 = ca * b00 - sa * b10, t01 = ca * b01 - sa * b11;
+        const float t10 = sa * b00 + ca * b10, t11 = sa * b01 + ca * b11;
+        A[pa][pb] = t00 * cb - t01 * sb;
+        A[pa][qb] = t00 * sb + t01 * cb;
+        A[qa][pb] = t10 * cb - t11 * sb;
+        A[qa][qb] = t10 * sb + t11 * cb;
+      }
+      for (int idx = lane; idx < m * half; idx += 64) {
+        const int r = idx / half, bb = idx - r * half;
+        const int pb = rot_p[bb], qb = rot_q[bb];
+        const float cb = rot_c[bb], sb = rot_s[bb];
+        const float vp = V[r][pb], vq = V[r][qb];
+        V[r][pb] = cb * vp - sb * vq;
+        V[r][qb] = sb * vp + cb * vq;
+      }
+      __syncthreads();
+    }
+    const int applied = n_rot;
+    __syncthreads();
+    if (applied == 0) break;
+  }
+
+  // eigenvalues descending (ties by index) -> order[rank] = column
+  if (lane < m) {
+    const float lj = A[lane][lane];
+    int pos = 0;
+    for (int j = 0; j < m; ++j) {
+      const float li = A[j][j];
+      pos += (li > lj) || (li == lj && j < lane);
+    }
+    order[pos] = lane;
+  }
+  __syncthreads();
+  const float lam1 = fmaxf(A[order[0]][order[0]], 0.f);
+  const float inv_sqrt_n = 1.f / sqrtf((float)nv);
+  for (int j = 0; j < R; ++j) {
+    float lam = 0.f;
+    int colj = 0;
+    if (j < m) { colj = order[j]; lam = fmaxf(A[colj][colj], 0.f); }
+    const bool zero = (j + 1 > nv - 1) || !(lam > 1e-6f * lam1);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = lane + 64 * c;
+      float w = 0.f;
+      if (!zero) {
+        for (int t = 0; t < nv; ++t) w += X[t][e] * V[t][colj];
+        w *= inv_sqrt_n;
+      }
+      dst[(size_t)(1 + j) * D + e] = (uint16_t)f32_to_bf16_rne(w);
+    }
+  }
+  if (g == 0 && lane == 0) log_n[phys] = logf((float)nv);
+}
+
+hipError_t launch_summary_build(const kv_layout& L, const void* k16, const int32_t* pages,
+                                const int32_t* n_valid, int n, void* summary, float* log_n,
+                                hipStream_t st) {
+  const dim3 grid(n * L.num_kv_heads);
+  const bool f16 = L.kv_dtype == KV_F16;
+  const uint16_t* k = (const uint16_t*)k16;
+  uint16_t* s = (uint16_t*)summary;
+#define KVS_SB(D_, PS_, F_) hipLaunchKernelGGL((summary_build_kernel<D_, PS_, F_>), grid, dim3(64), 0, st, \
+                                               k, pages, n_valid, L.num_kv_heads, L.rank, s, log_n)
+  if (L.head_dim == 64) {
+    if (L.page_size == 16) { if (f16) KVS_SB(64, 16, true); else KVS_SB(64, 16, false); }
+    else { if (f16) KVS_SB(64, 32, true); else KVS_SB(64, 32, false); }
+  } else {
+    if (L.page_size == 16) { if (f16) KVS_SB(128, 16, true); else KVS_SB(128, 16, false); }
+    else { if (f16) KVS_SB(128, 32, true); else KVS_SB(128, 32, false); }
+  }
+#undef KVS_SB
+  return hipGetLastError();
+}
+
+}  // namespace kvs

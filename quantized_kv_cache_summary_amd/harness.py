@@ -1,0 +1,225 @@
+"""Device-side set-up of a synthetic decode layer and one decode step through the C ABI.
+
+Allocation and upload only (torch for device memory and streams); every step of
+the method runs in libkvsparse.  Used by the GPU tests and bench.py.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import numpy as np
+import torch
+
+from . import kvsparse as kv
+from . import workloads as wl
+
+TORCH16 = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def to_device16(bits, dtype, device="cuda"):
+    """uint16 numpy bits -> torch 16-bit tensor on the device."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(TORCH16[dtype]).to(device)
+
+
+def layout_of(w: wl.Workload, softmax_scale=0.0):
+    return kv.layout(w.Hq, w.Hkv, w.d, w.P, w.rank, w.dtype, softmax_scale)
+
+
+# ------------------------------------------------------------------ pinned, mapped host memory
+
+class MappedHostBuffer:
+    """hipHostMalloc(..., hipHostMallocMapped) buffer with its device address."""
+
+    def __init__(self, nbytes):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self.host = ctypes.c_void_p()
+        rc = self._hip.hipHostMalloc(ctypes.byref(self.host), ctypes.c_size_t(nbytes), ctypes.c_uint(0x2))
+        if rc != 0:
+            raise RuntimeError(f"hipHostMalloc({nbytes}) failed: {rc}")
+        self.dev = ctypes.c_void_p()
+        rc = self._hip.hipHostGetDevicePointer(ctypes.byref(self.dev), self.host, ctypes.c_uint(0))
+        if rc != 0:
+            raise RuntimeError(f"hipHostGetDevicePointer failed: {rc}")
+        self.nbytes = nbytes
+
+    def numpy(self, dtype, shape):
+        buf = (ctypes.c_char * self.nbytes).from_address(self.host.value)
+        return np.frombuffer(buf, dtype=dtype).reshape(shape)
+
+    def free(self):
+        if self.host:
+            self._hip.hipHostFree(self.host)
+            self.host = ctypes.c_void_p()
+
+
+# ------------------------------------------------------------------ one layer
+
+class DeviceLayer:
+    """K/V pools, block table, summaries (and tier pools / host V) of one layer."""
+
+    def __init__(self, w: wl.Workload, layer=0, summaries="build", device="cuda", host_v=None,
+                 hot_mode="warm", seq_lens=None, threads=None):
+        self.w, self.layer, self.device = w, layer, device
+        self.L = layout_of(w)
+        host_v = w.v_host if host_v is None else host_v
+        shape = (w.n_phys, w.Hkv, w.P, w.d)
+        self.bt_np = wl.block_table(w, layer)
+        self.bt = torch.from_numpy(self.bt_np).to(device)
+        self.seq_lens_np = wl.seq_lens(w) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+        self.seq_lens = torch.from_numpy(self.seq_lens_np).to(device)
+        kbits = np.empty(shape, dtype=np.uint16)
+        self.host_v = None
+        if host_v:
+            self.host_v = MappedHostBuffer(int(np.prod(shape)) * 2)
+            vbits = self.host_v.numpy(np.uint16, shape)
+        else:
+            vbits = np.empty(shape, dtype=np.uint16)
+        wl.fill_pools(w, layer, kbits, vbits, self.bt_np, threads=threads)
+        self.k16 = to_device16(kbits, w.dtype, device)
+        del kbits
+        self.v16 = None if host_v else to_device16(vbits, w.dtype, device)
+        del vbits
+        self.summary = torch.empty((w.n_phys, w.Hkv, (1 + w.rank) * w.d), dtype=torch.bfloat16, device=device)
+        self.log_n = torch.empty(w.n_phys, dtype=torch.float32, device=device)
+        if summaries == "build":
+            self.build_summaries()
+        elif summaries == "synthetic":
+            rec, n_valid = wl.synthetic_summary(w, layer)
+            self.summary.copy_(to_device16(rec.reshape(w.n_phys, w.Hkv, -1), "bf16", device))
+            self.log_n.copy_(torch.from_numpy(np.log(n_valid.astype(np.float64)).astype(np.float32)))
+        self.tiers = None
+        self.page_entry = None
+        if w.tier_fracs is not None:
+            self._pack_tiers()
+        self.v_hot = None
+        self.v_hot_slot = None
+        if host_v:
+            self._init_hot_buffer(hot_mode)
+        self.pages = self._make_pages()
+
+    def valid_tokens_per_phys(self):
+        """Valid tokens of every physical page under the current seq_lens (P when unused)."""
+        w = self.w
+        nv = np.full(w.n_phys, w.P, dtype=np.int32)
+        for b in range(w.B):
+            starts = np.arange(w.Np) * w.P
+            nv[self.bt_np[b]] = np.clip(self.seq_lens_np[b] - starts, 0, w.P)
+        return nv
+
+    # summary of every physical page, over its valid tokens
+    def build_summaries(self, stream=None):
+        w = self.w
+        ids = torch.arange(w.n_phys, dtype=torch.int32, device=self.device)
+        nv = torch.from_numpy(self.valid_tokens_per_phys()).to(self.device)
+        kv.summary_build(self.L, self.k16, ids, nv, self.summary, self.log_n, stream)
+
+    def _pack_tiers(self):
+        w = self.w
+        tiers_logical = wl.page_tiers(w, self.layer)              # (B, Np)
+        tier_phys = np.zeros(w.n_phys, dtype=np.int64)
+        tier_phys[self.bt_np.ravel()] = tiers_logical.ravel()
+        self.tier_phys = tier_phys
+        entry = np.zeros(w.n_phys, dtype=np.uint32)
+        self.kq, self.vq, self.ksz, self.vsz = [], [], [], []
+        for t in range(1, 5):
+            phys = np.nonzero(tier_phys == t)[0].astype(np.int32)
+            n = max(1, phys.size)
+            bits = kv.TIER_BITS[t]
+            kc = torch.zeros((n, w.Hkv, w.P, w.d * bits // 8), dtype=torch.uint8, device=self.device)
+            vc = torch.zeros_like(kc)
+            ks = torch.zeros((n, w.Hkv, w.P, w.d // 32, 2), dtype=torch.float16, device=self.device)
+            vs = torch.zeros_like(ks)
+            if phys.size:
+                src = torch.from_numpy(phys).to(self.device)
+                kv.pack_tier(self.L, self.k16, phys.size, t, kc, ks, src_pages=src)
+                kv.pack_tier(self.L, self.v16, phys.size, t, vc, vs, src_pages=src)
+                entry[phys] = (np.uint32(t) << np.uint32(29)) | np.arange(phys.size, dtype=np.uint32)
+            self.kq.append(kc); self.vq.append(vc); self.ksz.append(ks); self.vsz.append(vs)
+        native = np.nonzero(tier_phys == 0)[0]
+        entry[native] = native.astype(np.uint32)                  # native slot = physical page
+        self.page_entry = torch.from_numpy(entry.view(np.int32)).to(self.device)
+        self.tiers = tier_phys
+
+    def _init_hot_buffer(self, hot_mode, sel_pages=None):
+        w = self.w
+        n_slots = max(1, int(round(w.hot_buffer_frac * w.n_phys)))
+        self.n_hot = n_slots
+        self.v_hot = torch.empty((n_slots, w.Hkv, w.P, w.d), dtype=TORCH16[w.dtype], device=self.device)
+        self.set_hot_pages(np.zeros(0, np.int64) if sel_pages is None else sel_pages, fill_random=True)
+
+    def set_hot_pages(self, must_include, fill_random=True):
+        """Hot buffer = must_include pages (then a seeded random fill); copies their V."""
+        w = self.w
+        slot, chosen = wl.hot_buffer_slots(w, self.n_hot if fill_random else min(self.n_hot, len(must_include)),
+                                           self.layer, must_include)
+        self.v_hot_slot = torch.from_numpy(slot).to(self.device)
+        vh = self.host_v.numpy(np.uint16, (w.n_phys, w.Hkv, w.P, w.d))
+        stage = torch.from_numpy(np.ascontiguousarray(vh[chosen]).view(np.int16)).view(TORCH16[w.dtype])
+        self.v_hot[: len(chosen)].copy_(stage.to(self.device))
+        self.hot_pages = chosen
+        self.pages = self._make_pages()
+
+    def _make_pages(self):
+        v16 = self.v16
+        v16_ptr = self.host_v.dev.value if self.host_v is not None else None
+        if self.page_entry is not None:
+            return kv.make_pages(self.k16, v16, self.kq, self.vq, self.ksz, self.vsz, self.page_entry,
+                                 self.v_hot, self.v_hot_slot, v16_ptr=v16_ptr)
+        return kv.make_pages(self.k16, v16, page_entry=None, v_hot=self.v_hot, v_hot_slot=self.v_hot_slot,
+                             v16_ptr=v16_ptr)
+
+    def release(self):
+        if self.host_v is not None:
+            torch.cuda.synchronize()
+            self.host_v.free()
+            self.host_v = None
+
+
+# ------------------------------------------------------------------ step buffers
+
+class StepBuffers:
+    def __init__(self, w: wl.Workload, device="cuda", num_splits=0, with_S=False):
+        L = layout_of(w)
+        self.k_max = w.k_of(w.Np)
+        self.num_splits = num_splits
+        self.head_scores = torch.empty((w.B, w.Hkv, w.G, w.Np), dtype=torch.float32, device=device)
+        nb = kv.page_score_partial_size(L, w.B, w.Np)
+        self.lse_partial = torch.empty(nb // 4, dtype=torch.float32, device=device)
+        self.sel = torch.empty((w.B, w.Hkv, max(1, self.k_max)), dtype=torch.int32, device=device)
+        self.sel_count = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=device)
+        self.page_S = torch.empty((w.B, w.Hkv, w.Np), dtype=torch.float32, device=device) if with_S else None
+        self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=device)
+        nws = kv.attn_workspace_size(L, w.B, self.sel.shape[-1], num_splits)
+        self.ws = torch.empty(max(1, nws // 4), dtype=torch.float32, device=device)
+
+
+def queries_device(w: wl.Workload, layer=0, qidx=0, device="cuda"):
+    return to_device16(wl.query_tensor(w, layer, qidx), w.dtype, device)
+
+
+def score(layer: DeviceLayer, q, bufs: StepBuffers, stream=None):
+    kv.page_score(layer.L, q, layer.summary, layer.log_n, layer.bt, layer.seq_lens, bufs.head_scores,
+                  bufs.lse_partial, stream)
+
+
+def topk(layer: DeviceLayer, bufs: StepBuffers, n_force_first=0, n_force_last=0, stream=None):
+    w = layer.w
+    kv.page_topk(layer.L, bufs.head_scores, bufs.lse_partial, layer.seq_lens, w.Np, w.keep, w.k_fixed,
+                 bufs.sel, bufs.sel_count, n_force_first, n_force_last, bufs.page_S, None, stream)
+
+
+def attend(layer: DeviceLayer, q, bufs: StepBuffers, sel=None, sel_count=None, stream=None):
+    kv.sparse_decode_attn(layer.L, q, layer.pages, layer.bt, layer.seq_lens,
+                          bufs.sel if sel is None else sel, bufs.sel_count if sel_count is None else sel_count,
+                          bufs.out, bufs.lse, bufs.ws, bufs.num_splits, stream)
+
+
+def decode_step(layer: DeviceLayer, q, bufs: StepBuffers, stream=None):
+    """score -> top-k -> sparse attention for one layer of the whole batch."""
+    score(layer, q, bufs, stream)
+    topk(layer, bufs, stream=stream)
+    attend(layer, q, bufs, stream=stream)

@@ -1,0 +1,204 @@
+"""ctypes binding of libkvsparse (include/kvsparse.h).  Argument marshalling only.
+
+Every function takes torch tensors for device buffers, passes their data
+pointers, sizes and torch's current HIP stream to the C ABI, and raises
+``KvError`` on a non-zero status.  The library is loaded on first use; if it has
+not been built the call raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvsparse.so")
+
+KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_HIP = 0, -1, -2, -3, -4
+KV_F16, KV_BF16 = 0, 1
+KV_TIER_NATIVE, KV_TIER_I8, KV_TIER_I4, KV_TIER_I2, KV_TIER_B1 = range(5)
+TIER_BITS = {KV_TIER_I8: 8, KV_TIER_I4: 4, KV_TIER_I2: 2, KV_TIER_B1: 1}
+
+# every entry point declared in include/kvsparse.h
+SYMBOLS = (
+    "kv_summary_build", "kv_page_score", "kv_page_score_partial_size", "kv_page_topk",
+    "kv_page_topk_workspace_size", "kv_sparse_decode_attn", "kv_sparse_decode_attn_workspace_size",
+    "kv_sparse_decode_attn_num_splits", "kv_dequant_tier", "kv_pack_tier", "kv_status_string",
+)
+
+
+class KvError(RuntimeError):
+    def __init__(self, status, fn):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+class KvLayout(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("rank", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class KvPages(ctypes.Structure):
+    _fields_ = [
+        ("k16", ctypes.c_void_p), ("v16", ctypes.c_void_p),
+        ("kq", ctypes.c_void_p * 4), ("vq", ctypes.c_void_p * 4),
+        ("ksz", ctypes.c_void_p * 4), ("vsz", ctypes.c_void_p * 4),
+        ("page_entry", ctypes.c_void_p), ("v_hot", ctypes.c_void_p), ("v_hot_slot", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_LP = ctypes.POINTER(KvLayout)
+_PP = ctypes.POINTER(KvPages)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "kv_summary_build": (_I, [_LP, _P, _P, _P, _I, _P, _P, _P]),
+            "kv_page_score": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
+            "kv_page_score_partial_size": (_SZ, [_LP, _I, _I]),
+            "kv_page_topk": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _I, _P, _P, _I, _P,
+                                  _P, _SZ, _P]),
+            "kv_page_topk_workspace_size": (_SZ, [_LP, _I, _I]),
+            "kv_sparse_decode_attn": (_I, [_LP, _P, _PP, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _P,
+                                           _SZ, _P]),
+            "kv_sparse_decode_attn_workspace_size": (_SZ, [_LP, _I, _I, _I]),
+            "kv_sparse_decode_attn_num_splits": (_I, [_LP, _I, _I]),
+            "kv_dequant_tier": (_I, [_LP, _PP, _P, _I, _P, _P]),
+            "kv_pack_tier": (_I, [_LP, _P, _P, _I, _I, _P, _P, _P, _P]),
+            "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().kv_status_string(int(status)).decode()
+
+
+def layout(num_q_heads, num_kv_heads, head_dim, page_size, rank, dtype, softmax_scale=0.0):
+    d = {"f16": KV_F16, "bf16": KV_BF16, torch.float16: KV_F16, torch.bfloat16: KV_BF16}[dtype]
+    return KvLayout(num_q_heads, num_kv_heads, head_dim, page_size, rank, d, softmax_scale)
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return stream
+
+
+def _check(rc, fn):
+    if rc != KV_OK:
+        raise KvError(rc, fn)
+
+
+def make_pages(k16, v16, kq=None, vq=None, ksz=None, vsz=None, page_entry=None, v_hot=None,
+               v_hot_slot=None, v16_ptr=None):
+    """KvPages struct; keeps the tensors alive on the returned object.
+
+    v16_ptr overrides v16's pointer (a device-mapped host address)."""
+    pg = KvPages()
+    pg.k16 = _p(k16)
+    pg.v16 = v16_ptr if v16_ptr is not None else _p(v16)
+    for t in range(4):
+        pg.kq[t] = _p(kq[t]) if kq else None
+        pg.vq[t] = _p(vq[t]) if vq else None
+        pg.ksz[t] = _p(ksz[t]) if ksz else None
+        pg.vsz[t] = _p(vsz[t]) if vsz else None
+    pg.page_entry = _p(page_entry)
+    pg.v_hot = _p(v_hot)
+    pg.v_hot_slot = _p(v_hot_slot)
+    pg._keep = (k16, v16, kq, vq, ksz, vsz, page_entry, v_hot, v_hot_slot)
+    return pg
+
+
+def summary_build(L, k16, pages, n_valid, summary, log_n, stream=None):
+    rc = lib().kv_summary_build(ctypes.byref(L), _p(k16), _p(pages), _p(n_valid), int(pages.numel()),
+                                _p(summary), _p(log_n), _stream(stream))
+    _check(rc, "kv_summary_build")
+
+
+def page_score_partial_size(L, B, max_pages):
+    return int(lib().kv_page_score_partial_size(ctypes.byref(L), int(B), int(max_pages)))
+
+
+def page_score(L, q, summary, log_n, block_table, seq_lens, head_scores, lse_partial, stream=None):
+    B, max_pages = block_table.shape
+    rc = lib().kv_page_score(ctypes.byref(L), _p(q), _p(summary), _p(log_n), _p(block_table),
+                             _p(seq_lens), int(B), int(max_pages), _p(head_scores), _p(lse_partial),
+                             _stream(stream))
+    _check(rc, "kv_page_score")
+
+
+def page_topk_workspace_size(L, B, max_pages):
+    return int(lib().kv_page_topk_workspace_size(ctypes.byref(L), int(B), int(max_pages)))
+
+
+def page_topk(L, head_scores, lse_partial, seq_lens, max_pages, keep_frac, k_fixed, sel, sel_count,
+              n_force_first=0, n_force_last=0, page_S=None, ws=None, stream=None):
+    B = seq_lens.shape[0]
+    k_max = sel.shape[-1]
+    rc = lib().kv_page_topk(ctypes.byref(L), _p(head_scores), _p(lse_partial), _p(seq_lens), int(B),
+                            int(max_pages), float(keep_frac), int(k_fixed), int(n_force_first),
+                            int(n_force_last), _p(sel), _p(sel_count), int(k_max), _p(page_S), _p(ws),
+                            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "kv_page_topk")
+
+
+def attn_num_splits(L, B, k_max):
+    return int(lib().kv_sparse_decode_attn_num_splits(ctypes.byref(L), int(B), int(k_max)))
+
+
+def attn_workspace_size(L, B, k_max, num_splits=0):
+    return int(lib().kv_sparse_decode_attn_workspace_size(ctypes.byref(L), int(B), int(k_max),
+                                                          int(num_splits)))
+
+
+def sparse_decode_attn(L, q, pages, block_table, seq_lens, sel, sel_count, out, lse, ws,
+                       num_splits=0, stream=None):
+    B, max_pages = block_table.shape
+    k_max = sel.shape[-1]
+    rc = lib().kv_sparse_decode_attn(ctypes.byref(L), _p(q), ctypes.byref(pages), _p(block_table),
+                                     _p(seq_lens), int(B), int(max_pages), _p(sel), _p(sel_count),
+                                     int(k_max), int(num_splits), _p(out), _p(lse), _p(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(stream))
+    _check(rc, "kv_sparse_decode_attn")
+
+
+def dequant_tier(L, pages, page_ids, out, stream=None):
+    rc = lib().kv_dequant_tier(ctypes.byref(L), ctypes.byref(pages), _p(page_ids), int(page_ids.numel()),
+                               _p(out), _stream(stream))
+    _check(rc, "kv_dequant_tier")
+
+
+def pack_tier(L, src16, n, tier, codes, scale_zero, src_pages=None, dst_slots=None, stream=None):
+    rc = lib().kv_pack_tier(ctypes.byref(L), _p(src16), _p(src_pages), int(n), int(tier), _p(codes),
+                            _p(scale_zero), _p(dst_slots), _stream(stream))
+    _check(rc, "kv_pack_tier")

@@ -168,14 +168,17 @@ def plant_direction(w: Workload, layer: int, b: int, g: int):
 
 
 def row_keys(w: Workload, layer: int, b: int, g: int):
-    """(ctx, d) float32 keys of one (sequence, KV head), logical token order."""
+    """(Np*P, d) float32 keys of one (sequence, KV head), logical token order.
+
+    Rows cover whole pages; tokens at or beyond ctx fill the last page's unused
+    slots and are never valid."""
     rng = rng_for(w, layer, b, g, T_K)
     if w.keys == "gmm":
         centers = rng_for(w, layer, b, g, T_CENTERS).standard_normal((w.gmm_centers, w.d), dtype=np.float32)
-        assign = rng.integers(0, w.gmm_centers, w.ctx)
-        x = centers[assign] + np.float32(w.gmm_std) * rng.standard_normal((w.ctx, w.d), dtype=np.float32)
+        assign = rng.integers(0, w.gmm_centers, w.Np * w.P)
+        x = centers[assign] + np.float32(w.gmm_std) * rng.standard_normal((w.Np * w.P, w.d), dtype=np.float32)
     else:
-        x = rng.standard_normal((w.ctx, w.d), dtype=np.float32)
+        x = rng.standard_normal((w.Np * w.P, w.d), dtype=np.float32)
         hp = hot_pages(w, layer, b)
         if hp.size:
             u = (w.plant_scale * plant_direction(w, layer, b, g)).astype(np.float32)
@@ -185,7 +188,7 @@ def row_keys(w: Workload, layer: int, b: int, g: int):
 
 
 def row_values(w: Workload, layer: int, b: int, g: int):
-    x = rng_for(w, layer, b, g, T_V).standard_normal((w.ctx, w.d), dtype=np.float32)
+    x = rng_for(w, layer, b, g, T_V).standard_normal((w.Np * w.P, w.d), dtype=np.float32)
     return round16(x, w.dtype)
 
 

@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad host
+arguments with the documented status before any HIP call (CPU only: no call
+here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_kv_cache_summary_amd import kvsparse as kv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvsparse.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kv.LIB_PATH), reason="libkvsparse.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(kv_[a-z0-9_]+)\s*\(", text)) - {"kv_layout", "kv_pages"}
+
+
+def test_header_and_binding_agree():
+    assert _declared() == set(kv.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kv.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert kv.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert kv.status_string(s) not in ("ok", "unknown status")
+    assert kv.status_string(17) == "unknown status"
+
+
+def _L(**kw):
+    a = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, rank=4, dtype="bf16")
+    a.update(kw)
+    return kv.layout(**a)
+
+
+FAKE = 0x10000   # a 16-byte aligned non-null address; never dereferenced (validation fails first)
+
+
+def _score(L, **over):
+    a = dict(q=FAKE, summary=FAKE, log_n=FAKE, bt=FAKE, sl=FAKE, B=2, max_pages=10, hs=FAKE, lp=FAKE)
+    a.update(over)
+    return kv.lib().kv_page_score(ctypes.byref(L), a["q"], a["summary"], a["log_n"], a["bt"], a["sl"],
+                                  a["B"], a["max_pages"], a["hs"], a["lp"], None)
+
+
+def test_layout_validation():
+    assert _score(_L(head_dim=96)) == kv.KV_ERR_UNSUPPORTED
+    assert _score(_L(page_size=8)) == kv.KV_ERR_UNSUPPORTED
+    assert _score(_L(rank=3)) == kv.KV_ERR_UNSUPPORTED
+    assert _score(_L(num_q_heads=12, num_kv_heads=8)) == kv.KV_ERR_INVALID_ARG
+    assert _score(_L(num_q_heads=34, num_kv_heads=2)) == kv.KV_ERR_UNSUPPORTED   # G = 17
+    assert _score(_L(num_kv_heads=0)) == kv.KV_ERR_INVALID_ARG
+    L = _L()
+    L.kv_dtype = 7
+    assert _score(L) == kv.KV_ERR_UNSUPPORTED
+    assert kv.lib().kv_page_score(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+
+
+def test_score_argument_validation():
+    L = _L()
+    assert _score(L, q=None) == kv.KV_ERR_INVALID_ARG
+    assert _score(L, lp=None) == kv.KV_ERR_INVALID_ARG
+    assert _score(L, q=FAKE + 2) == kv.KV_ERR_INVALID_ARG          # misaligned
+    assert _score(L, B=-1) == kv.KV_ERR_INVALID_ARG
+    assert _score(L, B=0) == kv.KV_OK                              # nothing to do, no launch
+
+
+def test_topk_validation():
+    L = _L()
+    f = kv.lib().kv_page_topk
+    ok = dict(hs=FAKE, lp=FAKE, sl=FAKE, B=2, mp=100, keep=0.08, kf=0, ff=0, fl=0, sel=FAKE, cnt=FAKE,
+              kmax=8, S=None)
+
+    def call(**o):
+        a = dict(ok)
+        a.update(o)
+        return f(ctypes.byref(L), a["hs"], a["lp"], a["sl"], a["B"], a["mp"], a["keep"], a["kf"], a["ff"],
+                 a["fl"], a["sel"], a["cnt"], a["kmax"], a["S"], None, 0, None)
+
+    assert call(kmax=7) == kv.KV_ERR_INVALID_ARG                   # ceil(0.08 * 100) = 8 > 7
+    assert call(kf=20, kmax=19) == kv.KV_ERR_INVALID_ARG
+    assert call(keep=float("nan")) == kv.KV_ERR_INVALID_ARG
+    assert call(keep=-0.5) == kv.KV_ERR_INVALID_ARG
+    assert call(mp=20000, kmax=2000) == kv.KV_ERR_UNSUPPORTED
+    assert call(sel=None) == kv.KV_ERR_INVALID_ARG
+    assert call(ff=-1) == kv.KV_ERR_INVALID_ARG
+    assert call(B=0) == kv.KV_OK
+
+
+def test_attention_validation_and_workspace():
+    L = _L()
+    pg = kv.KvPages()
+    pg.k16 = FAKE
+    pg.v16 = FAKE
+    f = kv.lib().kv_sparse_decode_attn
+
+    def call(pages=pg, ws=FAKE, ws_bytes=1 << 40, splits=0, q=FAKE):
+        return f(ctypes.byref(L), q, ctypes.byref(pages) if pages is not None else None, FAKE, FAKE, 8, 2048,
+                 FAKE, FAKE, 164, splits, FAKE, FAKE, ws, ws_bytes, None)
+
+    need = kv.attn_workspace_size(L, 8, 164)
+    s = kv.attn_num_splits(L, 8, 164)
+    assert s == 16 and need == 64 * s * 4 * 130 * 4
+    assert kv.attn_workspace_size(L, 8, 164, 3) == 64 * 3 * 4 * 130 * 4
+    assert call(ws_bytes=need - 1) == kv.KV_ERR_WORKSPACE
+    assert call(ws=None) == kv.KV_ERR_WORKSPACE
+    assert call(pages=None) == kv.KV_ERR_INVALID_ARG
+    assert call(splits=300) == kv.KV_ERR_UNSUPPORTED
+    assert call(q=FAKE + 8) == kv.KV_ERR_INVALID_ARG
+    tiered = kv.KvPages()
+    tiered.k16 = FAKE
+    tiered.v16 = FAKE
+    tiered.page_entry = FAKE
+    assert call(pages=tiered) == kv.KV_ERR_INVALID_ARG              # tier pools missing
+    hot = kv.KvPages()
+    hot.k16 = FAKE
+    hot.v16 = FAKE
+    hot.v_hot_slot = FAKE
+    assert call(pages=hot) == kv.KV_ERR_INVALID_ARG                 # hot buffer missing
+
+
+def test_pack_build_dequant_validation():
+    L = _L()
+    lib = kv.lib()
+    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 4, 0, FAKE, FAKE, None, None) == kv.KV_ERR_UNSUPPORTED
+    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 4, 5, FAKE, FAKE, None, None) == kv.KV_ERR_UNSUPPORTED
+    assert lib.kv_pack_tier(ctypes.byref(L), None, None, 4, 1, FAKE, FAKE, None, None) == kv.KV_ERR_INVALID_ARG
+    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 0, 1, FAKE, FAKE, None, None) == kv.KV_OK
+    assert lib.kv_summary_build(ctypes.byref(L), FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert lib.kv_summary_build(ctypes.byref(L), FAKE + 4, FAKE, FAKE, 3, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert lib.kv_summary_build(ctypes.byref(L), FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == kv.KV_OK
+    assert lib.kv_dequant_tier(ctypes.byref(L), None, FAKE, 2, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert kv.page_score_partial_size(L, 8, 2048) == 64 * 16 * 4 * 2 * 4
+    assert kv.page_topk_workspace_size(L, 8, 2048) == 0
