@@ -123,37 +123,40 @@ typedef struct kv_pages {
  * are appended (AMASS page, "What is in the box" item 1; the summary drops the
  * per-key coordinates and keeps r' eigen-quantities of the page).
  *
- * For i in [0, n) and every KV head g, over the n_valid[i] first tokens of
- * physical page phys = pages[i] of the 16-bit pool k16 ([n_phys][Hkv][P][d]):
+ * For every entry i in [0, n), (b, p) = (entries[2i], entries[2i+1]), and every
+ * KV head g, over the first n_valid[i] tokens of the page's keys in the 16-bit
+ * pool k16 ([n_phys][Hkv][P][d], physical page block_table[b * max_pages + p]):
  *   mu = mean key; Xc = keys - mu; Gram = Xc Xc^T / n; (lam_j, v_j) its
  *   eigenpairs, lam descending (cyclic Jacobi in float32);
  *   w_j = Xc^T v_j / sqrt(n) for j = 1..R, set to 0 when j > n - 1 or
  *   lam_j <= 1e-6 lam_1.
- * Output record summary[phys][g] = [mu, w_1, ..., w_R], (1+R)*d bfloat16
- * (round to nearest even), and log_n[phys] = log(n) as float32.
+ * Summaries are stored in LOGICAL page order per (sequence, KV head), so the
+ * scorer streams them without a block-table lookup:
+ *   summary: bfloat16 [B][Hkv][max_pages][(1+R)*d], record = [mu, w_1..w_R]
+ *            (round to nearest even);
+ *   log_n:   float32 [B][max_pages], log(n).
  * Eigenvector signs and rotations inside degenerate eigenspaces are arbitrary.
  * n_valid values are clamped to [0, P]; a page with 0 valid tokens gets a zero
- * record and log_n = -inf.  pages[] entries must be distinct within a call.
+ * record and log_n = -inf.  Entries must be distinct within a call.
  * --------------------------------------------------------------------------- */
-int kv_summary_build(const kv_layout* layout, const void* k16, const int32_t* pages,
-                     const int32_t* n_valid, int32_t n, void* summary, float* log_n,
-                     void* stream);
+int kv_summary_build(const kv_layout* layout, const void* k16, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* entries, const int32_t* n_valid, int32_t n,
+                     void* summary, float* log_n, void* stream);
 
 /* ---------------------------------------------------------------------------
  * kv_page_score -- quad page score of every logical page for every query head
  * (AMASS page, "What is in the box" item 1: quadratic, Gaussian-MGF score):
- *   s[b][g][h][p] = log_n[phys] + tau q.mu + (tau^2/2) sum_j (q.w_j)^2
- * with q = q[b][g*G + h] ([B][Hq][d], kv_dtype), phys = block_table[b][p],
- * record = summary[phys][g], tau = softmax_scale.
+ *   s[b][g][h][p] = log_n[b][p] + tau q.mu + (tau^2/2) sum_j (q.w_j)^2
+ * with q = q[b][g*G + h] ([B][Hq][d], kv_dtype), record summary[b][g][p]
+ * (layout of kv_summary_build), tau = softmax_scale.
  * head_scores: float32 [B][Hkv][G][max_pages]; entries p >= Np_b are -inf.
- * lse_partial: float32 pairs (max, sum exp(s - max)) per (row, page tile,
+ * lse_partial: float32 pairs (max, sum exp(s - max)) per (row, 64-page tile,
  *   head) over the tile's valid pages; its size in bytes is
  *   kv_page_score_partial_size().  It feeds kv_page_topk.
  * --------------------------------------------------------------------------- */
 int kv_page_score(const kv_layout* layout, const void* q, const void* summary,
-                  const float* log_n, const int32_t* block_table, const int32_t* seq_lens,
-                  int32_t B, int32_t max_pages, float* head_scores, float* lse_partial,
-                  void* stream);
+                  const float* log_n, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                  float* head_scores, float* lse_partial, void* stream);
 
 size_t kv_page_score_partial_size(const kv_layout* layout, int32_t B, int32_t max_pages);
 
@@ -194,7 +197,7 @@ size_t kv_page_topk_workspace_size(const kv_layout* layout, int32_t B, int32_t m
  * Split-K: num_splits > 0 fixes the number of partial results per row (at
  * most 256); 0 lets the library choose.  Results agree across split counts to
  * float32 rounding.  ws/ws_bytes: kv_sparse_decode_attn_workspace_size() with
- * the same num_splits.
+ * the same num_splits.  Calls that share a workspace must not overlap in time.
  * --------------------------------------------------------------------------- */
 int kv_sparse_decode_attn(const kv_layout* layout, const void* q, const kv_pages* pages,
                           const int32_t* block_table, const int32_t* seq_lens, int32_t B,

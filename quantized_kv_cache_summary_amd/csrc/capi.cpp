@@ -83,17 +83,19 @@ const char* kv_status_string(int status) {
   }
 }
 
-int kv_summary_build(const kv_layout* L, const void* k16, const int32_t* pages, const int32_t* n_valid,
-                     int32_t n, void* summary, float* log_n, void* stream) {
+int kv_summary_build(const kv_layout* L, const void* k16, const int32_t* block_table, int32_t max_pages,
+                     const int32_t* entries, const int32_t* n_valid, int32_t n, void* summary,
+                     float* log_n, void* stream) {
   int rc = check_layout(L);
   if (rc) return rc;
-  if (n < 0) return KV_ERR_INVALID_ARG;
+  if (n < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
   if (n == 0) return KV_OK;
-  if (!k16 || !pages || !n_valid || !summary || !log_n) return KV_ERR_INVALID_ARG;
-  if (!aligned16(k16)) return KV_ERR_INVALID_ARG;
+  if (max_pages == 0) return KV_ERR_INVALID_ARG;
+  if (!k16 || !block_table || !entries || !n_valid || !summary || !log_n) return KV_ERR_INVALID_ARG;
+  if (!aligned16(k16) || !aligned16(summary)) return KV_ERR_INVALID_ARG;
   if ((int64_t)n * L->num_kv_heads > 0x7FFFFFFF) return KV_ERR_UNSUPPORTED;
-  return from_hip(kvs::launch_summary_build(*L, k16, pages, n_valid, n, summary, log_n,
-                                            (hipStream_t)stream));
+  return from_hip(kvs::launch_summary_build(*L, k16, block_table, max_pages, entries, n_valid, n,
+                                            summary, log_n, (hipStream_t)stream));
 }
 
 size_t kv_page_score_partial_size(const kv_layout* L, int32_t B, int32_t max_pages) {
@@ -103,18 +105,17 @@ size_t kv_page_score_partial_size(const kv_layout* L, int32_t B, int32_t max_pag
 }
 
 int kv_page_score(const kv_layout* L, const void* q, const void* summary, const float* log_n,
-                  const int32_t* block_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,
-                  float* head_scores, float* lse_partial, void* stream) {
+                  const int32_t* seq_lens, int32_t B, int32_t max_pages, float* head_scores,
+                  float* lse_partial, void* stream) {
   int rc = check_layout(L);
   if (rc) return rc;
   if (B < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
   if (B == 0 || max_pages == 0) return KV_OK;
-  if (!q || !summary || !log_n || !block_table || !seq_lens || !head_scores || !lse_partial)
-    return KV_ERR_INVALID_ARG;
+  if (!q || !summary || !log_n || !seq_lens || !head_scores || !lse_partial) return KV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(summary)) return KV_ERR_INVALID_ARG;
   if ((int64_t)B * L->num_kv_heads > 65535) return KV_ERR_UNSUPPORTED;
-  return from_hip(kvs::launch_page_score(*L, q, summary, log_n, block_table, seq_lens, B, max_pages,
-                                         scale_of(L), head_scores, lse_partial, (hipStream_t)stream));
+  return from_hip(kvs::launch_page_score(*L, q, summary, log_n, seq_lens, B, max_pages, scale_of(L),
+                                         head_scores, lse_partial, (hipStream_t)stream));
 }
 
 size_t kv_page_topk_workspace_size(const kv_layout* L, int32_t B, int32_t max_pages) {

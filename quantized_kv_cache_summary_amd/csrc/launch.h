@@ -10,21 +10,20 @@
 namespace kvs {
 
 // Pages of 16 logical pages per MFMA tile; a score block covers this many pages.
-constexpr int kScorePagesPerBlock = 128;
+constexpr int kScorePagesPerBlock = 64;
 constexpr int kTopkThreads = 512;
 constexpr int kMaxTopkPages = 15360;   // keys in LDS stay under 64 KB
 constexpr int kMaxSplits = 256;
 
 inline int score_tiles(int max_pages) { return (max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock; }
 
-hipError_t launch_summary_build(const kv_layout& L, const void* k16, const int32_t* pages,
-                                const int32_t* n_valid, int n, void* summary, float* log_n,
-                                hipStream_t st);
+hipError_t launch_summary_build(const kv_layout& L, const void* k16, const int32_t* block_table,
+                                int max_pages, const int32_t* entries, const int32_t* n_valid, int n,
+                                void* summary, float* log_n, hipStream_t st);
 
 hipError_t launch_page_score(const kv_layout& L, const void* q, const void* summary,
-                             const float* log_n, const int32_t* block_table, const int32_t* seq_lens,
-                             int B, int max_pages, float tau, float* head_scores, float* lse_partial,
-                             hipStream_t st);
+                             const float* log_n, const int32_t* seq_lens, int B, int max_pages,
+                             float tau, float* head_scores, float* lse_partial, hipStream_t st);
 
 hipError_t launch_page_topk(const kv_layout& L, const float* head_scores, const float* lse_partial,
                             const int32_t* seq_lens, int B, int max_pages, float keep, int k_fixed,

@@ -7,8 +7,11 @@
 //   S_p = log((1/G) sum_h exp(s[h][p] - L_h))  (group-mean mass fraction)
 //
 // Selection is an exact k-th-largest search on order-preserving uint32 keys:
-// four 8-bit radix passes with LDS histograms (integer counts, so the result
-// does not depend on thread timing), then one ordered compaction that keeps
+// 8-bit radix passes with LDS histograms (integer counts, so the result does
+// not depend on thread timing) that start at the highest bit in which the
+// row's largest and smallest keys differ -- the scores of a row share sign and
+// exponent bits, and a first digit taken there would pile every key onto one
+// or two histogram bins -- then one ordered compaction that keeps
 // every key above the threshold and the lowest-index pages among keys equal
 // to it.  Pages come out in ascending order with no sort.  Ties therefore
 // break by (S descending, page ascending) exactly.
@@ -31,7 +34,8 @@ __device__ __forceinline__ uint32_t order_key(float S) {
 
 // Exclusive prefix sum over the block (kTopkThreads threads); also returns the total.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   int x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -52,6 +56,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
   return before + x - v;
 }
 
+template <int GM>
 __global__ __launch_bounds__(kTopkThreads) void page_topk_kernel(
     const float* __restrict__ head_scores, const float* __restrict__ lse_partial,
     const int32_t* __restrict__ seq_lens, int Hkv, int G, int P, int max_pages, int n_tiles,
@@ -59,13 +64,15 @@ __global__ __launch_bounds__(kTopkThreads) void page_topk_kernel(
     int32_t* __restrict__ sel_count, int k_max, float* __restrict__ page_S) {
   extern __shared__ uint32_t keys[];   // max_pages
   __shared__ float Lh[16];
-  __shared__ int hist[256];
+  __shared__ int hist[2][256];
   __shared__ int wave_tot[kTopkWaves];
+  __shared__ uint32_t wave_max[kTopkWaves], wave_min[kTopkWaves];
   __shared__ int digit_sel, digit_above;
 
   const int row = blockIdx.x;
   const int b = row / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int L = seq_lens[b];
   int Np = L > 0 ? (L + P - 1) / P : 0;
   Np = Np < max_pages ? Np : max_pages;
@@ -82,7 +89,21 @@ __global__ __launch_bounds__(kTopkThreads) void page_topk_kernel(
   if (tid == 0) sel_count[row] = k;
   if (k == 0) return;
 
-  // 1. per-head normaliser from the score blocks' partials (fixed merge order)
+  // 1. the first round of head scores is requested before the per-head
+  //    normalisers are merged, so the two loads overlap
+  const float* hs = head_scores + (size_t)row * G * max_pages;
+  constexpr int U = 4;
+  float v[U][GM];
+  auto load_round = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * kTopkThreads;
+#pragma unroll
+      for (int h = 0; h < GM; ++h)   // clamped, always in bounds; extra values are ignored
+        v[u][h] = hs[(size_t)(h < G ? h : 0) * max_pages + (p < Np ? p : Np - 1)];
+    }
+  };
+  load_round(tid);
   for (int h = wave; h < G; h += kTopkWaves) {
     float m = -INFINITY, s = 0.f;
     for (int t = lane; t < n_tiles; t += 64) {
@@ -98,72 +119,118 @@ __global__ __launch_bounds__(kTopkThreads) void page_topk_kernel(
   }
   __syncthreads();
 
-  // 2. group aggregate and keys
+  // 2. group aggregate and keys, U pages per thread per round
   const float logG = __logf((float)G);
-  const float* hs = head_scores + (size_t)row * G * max_pages;
-  for (int p = tid; p < Np; p += kTopkThreads) {
-    float a[16];
-    float M = -INFINITY;
-    for (int h = 0; h < G; ++h) {
-      a[h] = hs[(size_t)h * max_pages + p] - Lh[h];
-      M = fmaxf(M, a[h]);
-    }
-    float S;
-    if (M == -INFINITY) {
-      S = -INFINITY;
-      for (int h = 0; h < G; ++h) if (a[h] != a[h]) S = a[h];
-    } else {
-      float sum = 0.f;
-      for (int h = 0; h < G; ++h) sum += __expf(a[h] - M);
-      S = M + __logf(sum) - logG;
-    }
-    if (p < n_force_first || p >= Np - n_force_last) S = INFINITY;
-    keys[p] = order_key(S);
-    if (page_S) page_S[(size_t)row * max_pages + p] = S;
-  }
-  __syncthreads();
-
-  // 3. k-th largest key by four 8-bit radix passes
-  uint32_t prefix = 0, pmask = 0;
-  int rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int p = tid; p < Np; p += kTopkThreads) {
-      const uint32_t key = keys[p];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      int c[4], tot = 0;
+  float Lr[GM];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; tot += c[i]; }
-      int incl = tot;
+  for (int h = 0; h < GM; ++h) Lr[h] = h < G ? Lh[h] : 0.f;
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+  for (int p0 = tid; p0 < Np; p0 += kTopkThreads * U) {
+    if (p0 != tid) load_round(p0);
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const unsigned long long hit = __ballot(incl >= rem);
-      const int first = __ffsll((long long)hit) - 1;
-      if (lane == first) {
-        int cum = incl - tot;
-        int dsel = 255 - 4 * lane - 3;
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * kTopkThreads;
+      if (p >= Np) break;
+      float M = -INFINITY;
+      bool nan = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (cum + c[i] >= rem) { dsel = 255 - 4 * lane - i; break; }
-          cum += c[i];
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          v[u][h] -= Lr[h];
+          nan |= v[u][h] != v[u][h];
+          M = fmaxf(M, v[u][h]);
         }
-        digit_sel = dsel;
-        digit_above = cum;
       }
+      float S;
+      if (nan) S = __int_as_float(0x7FC00000);
+      else if (M == -INFINITY) S = -INFINITY;
+      else {
+        float sum = 0.f;
+#pragma unroll
+        for (int h = 0; h < GM; ++h) if (h < G) sum += __expf(v[u][h] - M);
+        S = M + __logf(sum) - logG;
+      }
+      if (p < n_force_first || p >= Np - n_force_last) S = INFINITY;
+      const uint32_t key = order_key(S);
+      keys[p] = key;
+      kmax = key > kmax ? key : kmax;
+      kmin = key < kmin ? key : kmin;
+      if (page_S) page_S[(size_t)row * max_pages + p] = S;
     }
+  }
+  // block max / min of the keys: the radix passes start below their common prefix
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t a = (uint32_t)__shfl_xor((int)kmax, off), c = (uint32_t)__shfl_xor((int)kmin, off);
+    kmax = a > kmax ? a : kmax;
+    kmin = c < kmin ? c : kmin;
+  }
+  if (lane == 0) { wave_max[wave] = kmax; wave_min[wave] = kmin; }
+  __syncthreads();
+  kmax = wave_max[0];
+  kmin = wave_min[0];
+#pragma unroll
+  for (int w = 1; w < kTopkWaves; ++w) {
+    kmax = wave_max[w] > kmax ? wave_max[w] : kmax;
+    kmin = wave_min[w] < kmin ? wave_min[w] : kmin;
+  }
+
+  // 3. k-th largest key: 8-bit radix passes from the highest differing bit down
+  uint32_t prefix = kmax & ~0u, pmask = 0;
+  int rem = k;
+  const uint32_t diff = kmax ^ kmin;
+  if (diff == 0) {
+    prefix = kmax;               // every key equal
+  } else {
+    const int hb = 31 - __clz((int)diff);
+    pmask = hb >= 31 ? 0u : ~((2u << hb) - 1u);   // common prefix bits
+    prefix = kmax & pmask;
+    int top = hb;                                   // highest bit of the next digit
+    int buf = 0;
+    if (tid < 256) hist[0][tid] = 0;
     __syncthreads();
-    prefix |= (uint32_t)digit_sel << shift;
-    pmask |= 0xFFu << shift;
-    rem -= digit_above;
-    __syncthreads();
+    while (top >= 0) {
+      const int width = top + 1 < 8 ? top + 1 : 8;
+      const int shift = top + 1 - width;
+      const uint32_t dmask = (1u << width) - 1u;
+      for (int p = tid; p < Np; p += kTopkThreads) {
+        const uint32_t key = keys[p];
+        if ((key & pmask) == prefix) atomicAdd(&hist[buf][(key >> shift) & dmask], 1);
+      }
+      if (tid < 256) hist[buf ^ 1][tid] = 0;     // clear the other buffer for the next pass
+      __syncthreads();
+      if (wave == 0) {
+        // lane l owns digits 255-4l .. 252-4l (descending); unused digits are 0
+        int c[4], tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { c[i] = hist[buf][255 - 4 * lane - i]; tot += c[i]; }
+        int incl = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off);
+          if (lane >= off) incl += y;
+        }
+        const unsigned long long hit = __ballot(incl >= rem);
+        const int first = __ffsll((long long)hit) - 1;
+        if (lane == first) {
+          int cum = incl - tot;
+          int dsel = 255 - 4 * lane - 3;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (cum + c[i] >= rem) { dsel = 255 - 4 * lane - i; break; }
+            cum += c[i];
+          }
+          digit_sel = dsel;
+          digit_above = cum;
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)digit_sel << shift;
+      pmask |= dmask << shift;
+      rem -= digit_above;
+      buf ^= 1;
+      top -= width;
+    }
   }
   const uint32_t T = prefix;   // k-th largest key; take `rem` of the keys equal to it
 
@@ -199,10 +266,14 @@ hipError_t launch_page_topk(const kv_layout& L, const float* head_scores, const 
   const int G = L.num_q_heads / L.num_kv_heads;
   const int rows = B * L.num_kv_heads;
   const size_t lds = (size_t)(max_pages > 0 ? max_pages : 1) * sizeof(uint32_t);
-  hipLaunchKernelGGL(page_topk_kernel, dim3(rows), dim3(kTopkThreads), lds, st, head_scores,
-                     lse_partial, seq_lens, L.num_kv_heads, G, L.page_size, max_pages,
-                     score_tiles(max_pages), keep, k_fixed, n_force_first, n_force_last, sel,
-                     sel_count, k_max, page_S);
+#define KVS_TOPK(GM_) hipLaunchKernelGGL((page_topk_kernel<GM_>), dim3(rows), dim3(kTopkThreads), lds, st, \
+                     head_scores, lse_partial, seq_lens, L.num_kv_heads, G, L.page_size, max_pages,     \
+                     score_tiles(max_pages), keep, k_fixed, n_force_first, n_force_last, sel,           \
+                     sel_count, k_max, page_S)
+  if (G <= 4) KVS_TOPK(4);
+  else if (G <= 8) KVS_TOPK(8);
+  else KVS_TOPK(16);
+#undef KVS_TOPK
   return hipGetLastError();
 }
 

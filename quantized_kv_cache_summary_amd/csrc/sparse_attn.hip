@@ -19,7 +19,9 @@
 //     4j + ts, so the V page is read with 16-byte coalesced loads; the
 //     probabilities reach it through a 1 KB per-wave LDS tile; acc[head][d/16]
 //     accumulates in float32 FMAs.
-// The four waves merge in LDS; a second kernel merges the splits.
+// The four waves merge in LDS; a small second kernel merges the splits (a
+// kernel boundary is the cheap way to make every split's partial visible
+// across the chip's L2 slices).
 
 #include "device.h"
 #include "launch.h"
@@ -27,6 +29,7 @@
 namespace kvs {
 
 constexpr int kAttnWaves = 4;
+constexpr int kBatch = 2;   // 16-token chunks per load batch; two batches are in flight
 
 struct PagesDev {
   const uint16_t* k16;
@@ -102,6 +105,113 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
 
 // ---------------------------------------------------------------- the kernel
 
+// Per-wave attention state: running max (per head, shared by the four lane
+// groups), this lane's partial softmax sum, and acc[head][d/16] of the
+// token slot / element chunk this lane owns.
+template <int D, int GM>
+struct AttnState {
+  static constexpr int EV = D / 16;
+  float m_run;
+  float l_run;
+  float acc[GM][EV];
+};
+
+// Softmax update for one 16-token chunk given its raw logits (head col,
+// tokens 4*grp + i); writes the probabilities to the wave's LDS tile.
+template <int D, int GM>
+__device__ __forceinline__ void softmax_chunk(AttnState<D, GM>& st, const f32x4_t& zacc, int tok0, int L,
+                                              bool page_ok, float scale_log2, float (*ptile)[16],
+                                              int grp, int col) {
+  constexpr int EV = D / 16;
+  constexpr float kRescale = 8.0f;
+  float z[4];
+  float cm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tpos = tok0 + 4 * grp + i;
+    z[i] = (page_ok && tpos < L) ? zacc[i] * scale_log2 : -INFINITY;
+    cm = nan_max(cm, z[i]);
+  }
+  cm = nan_max(cm, __shfl_xor(cm, 16));
+  cm = nan_max(cm, __shfl_xor(cm, 32));
+  // a NaN logit (NaN query) makes the running max NaN, so the head's output
+  // and lse come out NaN instead of being dropped
+  const float m_new = nan_max(st.m_run, cm);
+  const bool need = (m_new > st.m_run + kRescale) || (m_new != m_new && st.m_run == st.m_run);
+  if (__ballot(need)) {
+    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+    if (m_new != -INFINITY) st.m_run = m_new;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      const float ah = readlane_f(alpha, h);
+#pragma unroll
+      for (int e = 0; e < EV; ++e) st.acc[h][e] *= ah;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float pz = (st.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[i] - st.m_run);
+    st.l_run += pz;
+    ptile[4 * grp + i][col] = pz;
+  }
+  wave_lds_sync();
+}
+
+// acc[h][:] += p[h][token] * v for one token slot of the chunk.
+template <int D, int GM>
+__device__ __forceinline__ void pv_accumulate(AttnState<D, GM>& st, const float* v, const float (*ptile)[16], int tk) {
+  constexpr int EV = D / 16;
+  float pv[GM];
+#pragma unroll
+  for (int h4 = 0; h4 < GM; h4 += 4) {
+    const float4 t4 = *reinterpret_cast<const float4*>(&ptile[tk][h4]);
+    pv[h4] = t4.x; pv[h4 + 1] = t4.y; pv[h4 + 2] = t4.z; pv[h4 + 3] = t4.w;
+  }
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int e = 0; e < EV; ++e) st.acc[h][e] = __builtin_fmaf(pv[h], v[e], st.acc[h][e]);
+}
+
+template <bool F16, int EV>
+__device__ __forceinline__ void unpack_v(const u32x4_t& r, float* v) {
+  if constexpr (EV == 8) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { v[2 * w] = lo16<F16>(r[w]); v[2 * w + 1] = hi16<F16>(r[w]); }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) { v[2 * w] = lo16<F16>(r[w]); v[2 * w + 1] = hi16<F16>(r[w]); }
+  }
+}
+
+// Raw loads of one 16-token chunk of a native page: K rows for the MFMA (key
+// row `col`, 64 contiguous bytes per k-step), V rows for the PV lanes (token
+// 4j + grp, 16 contiguous bytes per lane).
+template <int D>
+struct ChunkRaw {
+  u32x4_t k[D / 32];
+  u32x4_t v[4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_native_chunk(ChunkRaw<D>& r, const uint16_t* kbase, const uint16_t* vbase,
+                                                  int c, int col, int grp) {
+  constexpr int KS = D / 32, EV = D / 16;
+  const uint16_t* kp = kbase + (size_t)(c * 16 + col) * D + 8 * grp;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) r.k[s] = ld16(kp + 32 * s);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint16_t* vp = vbase + (size_t)(c * 16 + 4 * j + grp) * D + col * EV;
+    if constexpr (EV == 8) r.v[j] = ld16(vp);
+    else {
+      const u32x2_t t = *reinterpret_cast<const u32x2_t*>(vp);
+      r.v[j] = u32x4_t{t[0], t[1], 0, 0};
+    }
+  }
+}
+
 template <int D, int GM, bool F16, bool TIERED>
 __global__ __launch_bounds__(256) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, PagesDev pg, const int32_t* __restrict__ block_table,
@@ -111,7 +221,6 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   constexpr int KS = D / 32;     // MFMA k-steps
   constexpr int EK = D / 4;      // key elements per lane
   constexpr int EV = D / 16;     // value elements per lane
-  constexpr float kRescale = 8.0f;
 
   __shared__ float ptile[kAttnWaves][16][16];       // [wave][token][head]
   __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
@@ -119,7 +228,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
 
   const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / Hkv, g = row - b * Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int col = lane & 15, grp = lane >> 4;
 
   const int L = seq_lens[b];
@@ -129,180 +239,232 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
   const int beg = (int)(((long long)split * cnt) / n_splits);
   const int end = (int)(((long long)(split + 1) * cnt) / n_splits);
+  const int n_mine = end - beg > wave ? (end - beg - wave + kAttnWaves - 1) / kAttnWaves : 0;
 
-  // B operand: query head `col`, elements grp*EK + 8s + [0, 8)
+  // B operand: query head `col`, at k-step s the elements [32s + 8grp, +8)
+  // (the same assignment as the key rows); heads past G are zero.
   u32x4_t qop[KS];
   {
     const int Hq = Hkv * G;
-    const uint16_t* qp = q + ((size_t)b * Hq + (size_t)g * G + (col < G ? col : 0)) * D + grp * EK;
+    const uint32_t keep = col < G ? 0xFFFFFFFFu : 0u;
+    const uint16_t* qp = q + ((size_t)b * Hq + (size_t)g * G + (col < G ? col : 0)) * D + 8 * grp;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qop[s] = col < G ? ld16(qp + 8 * s) : u32x4_t{0, 0, 0, 0};
+    for (int s = 0; s < KS; ++s) {
+      qop[s] = ld16(qp + 32 * s);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qop[s][w] &= keep;
+    }
   }
 
-  float m_run = -INFINITY;   // per head (col), identical in the 4 lane groups
-  float l_run = 0.f;         // per lane: its own tokens
-  float acc[GM][EV];
+  AttnState<D, GM> st;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
 #pragma unroll
   for (int h = 0; h < GM; ++h)
 #pragma unroll
-    for (int e = 0; e < EV; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < EV; ++e) st.acc[h][e] = 0.f;
 
   const int32_t* srow = sel + (size_t)row * k_max;
   const int32_t* bt = block_table + (size_t)b * max_pages;
   const size_t page_elems = (size_t)P * D;
+  const int cpp = P / 16;   // 16-token chunks per page
+  float (*pt)[16] = ptile[wave];
 
-  for (int it = beg + wave; it < end; it += kAttnWaves) {
-    const int p = srow[it];
-    if (p < 0 || p >= Np) continue;
-    const int phys = bt[p];
-    uint32_t tier = 0, slot = (uint32_t)phys;
-    if constexpr (TIERED) {
-      if (pg.page_entry) {
-        const uint32_t e = pg.page_entry[phys];
-        tier = e >> 29;
-        slot = e & 0x1FFFFFFFu;
-      }
-    }
-    const size_t pr = (size_t)slot * Hkv + g;   // (slot, head) page record index
-    const uint16_t* kbase = pg.k16 + pr * page_elems;
-    const uint16_t* vbase = pg.v16 + pr * page_elems;
-    if (pg.v_hot_slot) {
-      const int hs = pg.v_hot_slot[phys];
-      if (hs >= 0) vbase = pg.v_hot + ((size_t)hs * Hkv + g) * page_elems;
-    }
-
-    for (int c = 0; c < P / 16; ++c) {
-      const int tok0 = p * P + c * 16;
-      // ---- logits
-      f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
-      if (!TIERED || tier == KV_TIER_NATIVE) {
-        const uint16_t* kp = kbase + (size_t)(c * 16 + col) * D + grp * EK;
-        u32x4_t a[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) a[s] = ld16(kp + 8 * s);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(a[s], qop[s], zacc);
-      } else {
-        float x[EK];
-        const size_t tokrow = pr * P + c * 16 + col;
-        const int t = (int)tier - 1;
-        switch (tier) {
-          case KV_TIER_I8: decode_run<D, EK, 8>(pg.kq[t], pg.ksz[t], tokrow, grp * EK, x); break;
-          case KV_TIER_I4: decode_run<D, EK, 4>(pg.kq[t], pg.ksz[t], tokrow, grp * EK, x); break;
-          case KV_TIER_I2: decode_run<D, EK, 2>(pg.kq[t], pg.ksz[t], tokrow, grp * EK, x); break;
-          default: decode_run<D, EK, 1>(pg.kq[t], pg.ksz[t], tokrow, grp * EK, x); break;
-        }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          u32x4_t ah, al;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            uint32_t hw, lw;
-            split_pair<F16>(x[8 * s + 2 * w], x[8 * s + 2 * w + 1], hw, lw);
-            ah[w] = hw;
-            al[w] = lw;
+  for (int j0 = 0; j0 < n_mine; j0 += 64) {
+    const int nb = n_mine - j0 < 64 ? n_mine - j0 : 64;
+    // this wave's pages, one per lane: logical page, slot, hot-buffer slot
+    int l_p = -1, l_hot = -1;
+    uint32_t l_tier = 0, l_slot = 0;
+    if (lane < nb) {
+      const int p = srow[beg + wave + kAttnWaves * (j0 + lane)];
+      if (p >= 0 && p < Np) {
+        l_p = p;
+        const int phys = bt[p];
+        l_slot = (uint32_t)phys;
+        if constexpr (TIERED) {
+          if (pg.page_entry) {
+            const uint32_t e = pg.page_entry[phys];
+            l_tier = e >> 29;
+            l_slot = e & 0x1FFFFFFFu;
           }
-          zacc = mfma16<F16>(ah, qop[s], zacc);
-          zacc = mfma16<F16>(al, qop[s], zacc);
+        }
+        if (pg.v_hot_slot) l_hot = pg.v_hot_slot[phys];
+      }
+    }
+    const unsigned long long valid = __ballot(l_p >= 0);
+    if (valid == 0) continue;
+
+    if constexpr (!TIERED) {
+      // skipped entries read the first valid page of the list instead (and are
+      // masked), so every load of a batch is unconditional straight-line code
+      const int first = __ffsll((long long)valid) - 1;
+      if (l_p < 0) {
+        l_slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, first);
+        l_hot = __builtin_amdgcn_readlane(l_hot, first);
+      }
+      const int nch = nb * cpp;
+      // issue the loads of chunks [cb, cb + NB) into r (the last chunk is
+      // re-read past the end; those extra chunks are never computed)
+      auto issue = [&](ChunkRaw<D> (&r)[kBatch], int (&pp)[kBatch], int cb) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int ci = cb + u < nch ? cb + u : nch - 1;
+          const int jj = ci / cpp;
+          pp[u] = __builtin_amdgcn_readlane(l_p, jj);
+          const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, jj);
+          const int hot = __builtin_amdgcn_readlane(l_hot, jj);
+          const size_t pr = (size_t)slot * Hkv + g;
+          const uint16_t* kb = pg.k16 + pr * page_elems;
+          const uint16_t* vb = hot >= 0 ? pg.v_hot + ((size_t)hot * Hkv + g) * page_elems : pg.v16 + pr * page_elems;
+          load_native_chunk<D>(r[u], kb, vb, ci - jj * cpp, col, grp);
+        }
+      };
+      auto compute = [&](const ChunkRaw<D> (&r)[kBatch], const int (&pp)[kBatch], int cb) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (cb + u >= nch) break;
+          const int ci = cb + u;
+          const int c = ci - (ci / cpp) * cpp;
+          const int p = pp[u];
+          f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(r[u].k[s], qop[s], zacc);
+          const int tok0 = p * P + c * 16;
+          softmax_chunk<D, GM>(st, zacc, tok0, L, p >= 0, scale_log2, pt, grp, col);
+          // values of tokens that do not exist (past seq_len, skipped entries)
+          // are zeroed: their probability is 0 but the memory may hold NaN
+          const bool full = p >= 0 && tok0 + 16 <= L;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v[EV];
+            unpack_v<F16, EV>(r[u].v[j], v);
+            if (!full) {
+              const uint32_t vk = (p >= 0 && tok0 + 4 * j + grp < L) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+              for (int e = 0; e < EV; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) & vk);
+            }
+            pv_accumulate<D, GM>(st, v, pt, 4 * j + grp);
+          }
+          wave_lds_sync();
+        }
+      };
+      ChunkRaw<D> ra[kBatch], rb[kBatch];
+      int pa[kBatch], pb[kBatch];
+      issue(ra, pa, 0);
+      for (int cb = 0; cb < nch; cb += 2 * kBatch) {
+        if (cb + kBatch < nch) issue(rb, pb, cb + kBatch);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ra, pa, cb);
+        if (cb + kBatch < nch) {
+          if (cb + 2 * kBatch < nch) issue(ra, pa, cb + 2 * kBatch);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(rb, pb, cb + kBatch);
         }
       }
-      float z[4];
-      float cm = -INFINITY;
+    } else {
+      // tiered pages: decode in registers, one chunk at a time
+      for (int jj = 0; jj < nb; ++jj) {
+        const int p = __builtin_amdgcn_readlane(l_p, jj);
+        if (p < 0) continue;
+        const uint32_t tier = (uint32_t)__builtin_amdgcn_readlane((int)l_tier, jj);
+        const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, jj);
+        const int hot = __builtin_amdgcn_readlane(l_hot, jj);
+        const size_t pr = (size_t)slot * Hkv + g;
+        const uint16_t* kbase = pg.k16 + pr * page_elems;
+        const uint16_t* vbase = hot >= 0 ? pg.v_hot + ((size_t)hot * Hkv + g) * page_elems : pg.v16 + pr * page_elems;
+        for (int c = 0; c < cpp; ++c) {
+          const int tok0 = p * P + c * 16;
+          f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
+          if (tier == KV_TIER_NATIVE) {
+            const uint16_t* kp = kbase + (size_t)(c * 16 + col) * D + 8 * grp;
+            u32x4_t a[KS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tpos = tok0 + 4 * grp + i;
-        z[i] = tpos < L ? zacc[i] * scale_log2 : -INFINITY;
-        cm = nan_max(cm, z[i]);
-      }
-      cm = nan_max(cm, __shfl_xor(cm, 16));
-      cm = nan_max(cm, __shfl_xor(cm, 32));
-      // a NaN logit (NaN query) makes the running max NaN, so the head's
-      // output and lse come out NaN instead of being dropped
-      const float m_new = nan_max(m_run, cm);
-      const bool need = (m_new > m_run + kRescale) || (m_new != m_new && m_run == m_run);
-      if (__ballot(need)) {
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-        if (m_new != -INFINITY) m_run = m_new;
-        l_run *= alpha;
+            for (int s = 0; s < KS; ++s) a[s] = ld16(kp + 32 * s);
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          const float ah = readlane_f(alpha, h);
-#pragma unroll
-          for (int e = 0; e < EV; ++e) acc[h][e] *= ah;
-        }
-      }
-      float pz[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pz[i] = (m_run == -INFINITY) ? 0.f : exp2f(z[i] - m_run);
-        l_run += pz[i];
-        ptile[wave][4 * grp + i][col] = pz[i];
-      }
-      wave_lds_sync();
-      // ---- values
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tk = 4 * j + grp;
-        const bool valid = tok0 + tk < L;
-        float v[EV];
-        if (!TIERED || tier == KV_TIER_NATIVE) {
-          const uint16_t* vp = vbase + (size_t)(c * 16 + tk) * D + col * EV;
-          if constexpr (EV == 8) {
-            const u32x4_t r = valid ? ld16(vp) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-            for (int w = 0; w < 4; ++w) { v[2 * w] = lo16<F16>(r[w]); v[2 * w + 1] = hi16<F16>(r[w]); }
+            for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(a[s], qop[s], zacc);
           } else {
-            const u32x2_t r = valid ? *reinterpret_cast<const u32x2_t*>(vp) : u32x2_t{0, 0};
+            // decode the elements this lane feeds at each k-step, [32s + 8grp, +8)
+            const size_t tokrow = pr * P + c * 16 + col;
+            const int t = (int)tier - 1;
 #pragma unroll
-            for (int w = 0; w < 2; ++w) { v[2 * w] = lo16<F16>(r[w]); v[2 * w + 1] = hi16<F16>(r[w]); }
-          }
-        } else {
-          const size_t tokrow = pr * P + c * 16 + tk;
-          const int t = (int)tier - 1;
-          switch (tier) {
-            case KV_TIER_I8: decode_run<D, EV, 8>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
-            case KV_TIER_I4: decode_run<D, EV, 4>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
-            case KV_TIER_I2: decode_run<D, EV, 2>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
-            default: decode_run<D, EV, 1>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
-          }
-          if (!valid) {
+            for (int s = 0; s < KS; ++s) {
+              float x[8];
+              switch (tier) {
+                case KV_TIER_I8: decode_run<D, 8, 8>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
+                case KV_TIER_I4: decode_run<D, 8, 4>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
+                case KV_TIER_I2: decode_run<D, 8, 2>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
+                default: decode_run<D, 8, 1>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
+              }
+              u32x4_t ah, al;
 #pragma unroll
-            for (int e = 0; e < EV; ++e) v[e] = 0.f;
+              for (int w = 0; w < 4; ++w) {
+                uint32_t hw, lw;
+                split_pair<F16>(x[2 * w], x[2 * w + 1], hw, lw);
+                ah[w] = hw;
+                al[w] = lw;
+              }
+              zacc = mfma16<F16>(ah, qop[s], zacc);
+              zacc = mfma16<F16>(al, qop[s], zacc);
+            }
           }
+          softmax_chunk<D, GM>(st, zacc, tok0, L, true, scale_log2, pt, grp, col);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int tk = 4 * j + grp;
+            const bool valid = tok0 + tk < L;
+            float v[EV];
+            if (tier == KV_TIER_NATIVE) {
+              const uint16_t* vp = vbase + (size_t)(c * 16 + tk) * D + col * EV;
+              u32x4_t r = u32x4_t{0, 0, 0, 0};
+              if (valid) {
+                if constexpr (EV == 8) r = ld16(vp);
+                else {
+                  const u32x2_t t2 = *reinterpret_cast<const u32x2_t*>(vp);
+                  r = u32x4_t{t2[0], t2[1], 0, 0};
+                }
+              }
+              unpack_v<F16, EV>(r, v);
+            } else {
+              const size_t tokrow = pr * P + c * 16 + tk;
+              const int t = (int)tier - 1;
+              switch (tier) {
+                case KV_TIER_I8: decode_run<D, EV, 8>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
+                case KV_TIER_I4: decode_run<D, EV, 4>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
+                case KV_TIER_I2: decode_run<D, EV, 2>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
+                default: decode_run<D, EV, 1>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
+              }
+              if (!valid) {
+#pragma unroll
+                for (int e = 0; e < EV; ++e) v[e] = 0.f;
+              }
+            }
+            pv_accumulate<D, GM>(st, v, pt, tk);
+          }
+          wave_lds_sync();
         }
-        float pv[GM];
-#pragma unroll
-        for (int h4 = 0; h4 < GM; h4 += 4) {
-          const float4 t4 = *reinterpret_cast<const float4*>(&ptile[wave][tk][h4]);
-          pv[h4] = t4.x; pv[h4 + 1] = t4.y; pv[h4 + 2] = t4.z; pv[h4 + 3] = t4.w;
-        }
-#pragma unroll
-        for (int h = 0; h < GM; ++h)
-#pragma unroll
-          for (int e = 0; e < EV; ++e) acc[h][e] = __builtin_fmaf(pv[h], v[e], acc[h][e]);
       }
-      wave_lds_sync();
     }
   }
 
   // ---- wave totals: l over lane groups, acc over token slots
+  float l_run = st.l_run;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 #pragma unroll
   for (int h = 0; h < GM; ++h)
 #pragma unroll
     for (int e = 0; e < EV; ++e) {
-      float a = acc[h][e];
+      float a = st.acc[h][e];
       a += __shfl_xor(a, 16);
       a += __shfl_xor(a, 32);
-      acc[h][e] = a;
+      st.acc[h][e] = a;
     }
-  if (lane < 16) { wm[wave][lane] = m_run; wl[wave][lane] = l_run; }
+  if (lane < 16) { wm[wave][lane] = st.m_run; wl[wave][lane] = l_run; }
   if (grp == 0) {
 #pragma unroll
     for (int h = 0; h < GM; ++h)
 #pragma unroll
-      for (int e = 0; e < EV; ++e) wacc[wave][h][col * EV + e] = acc[h][e];
+      for (int e = 0; e < EV; ++e) wacc[wave][h][col * EV + e] = st.acc[h][e];
   }
   __syncthreads();
 
@@ -328,27 +490,44 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
       dst[(size_t)h * (D + 2) + D + 1] = l;
     }
   }
+
 }
 
-// Split merge: one block of D threads per (row, head).
+// Split merge: one thread per (row, head, element); every split's (max, sum,
+// acc) is requested before any is used, so the kernel waits on memory once.
 template <int D>
-__global__ __launch_bounds__(D) void split_reduce_kernel(const float* __restrict__ partials, int Hkv,
-                                                          int G, int n_splits, float* __restrict__ out,
-                                                          float* __restrict__ lse) {
-  const int rh = blockIdx.x;
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ partials, int rows,
+                                                           int Hkv, int G, int n_splits,
+                                                           float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int U = 16;
+  const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (long long)rows * G * D) return;
+  const int e = (int)(id % D);
+  const int rh = (int)(id / D);
   const int row = rh / G, h = rh - row * G;
   const int b = row / Hkv, g = row - b * Hkv;
-  const int e = threadIdx.x;
-  const float* src = partials + (size_t)row * n_splits * G * (D + 2) + (size_t)h * (D + 2);
+  const float* sh = partials + (size_t)row * n_splits * G * (D + 2) + (size_t)h * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = nan_max(M, src[s * stride + D]);
-  float a = 0.f, l = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float f = exp2f(src[s * stride + D] - M);
-      a += src[s * stride + e] * f;
-      l += src[s * stride + D + 1] * f;
+  float M = -INFINITY, a = 0.f, l = 0.f;
+  for (int s0 = 0; s0 < n_splits; s0 += U) {
+    float av[U], mv[U], lv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int si = s0 + u < n_splits ? s0 + u : n_splits - 1;
+      av[u] = sh[si * stride + e];
+      mv[u] = sh[si * stride + D];
+      lv[u] = sh[si * stride + D + 1];
+    }
+    // running merge in split order: fixed, so the result does not depend on timing
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u >= n_splits) break;
+      const float Mn = nan_max(M, mv[u]);
+      if (Mn == -INFINITY) continue;
+      const float fo = exp2f(M - Mn), fn = exp2f(mv[u] - Mn);
+      a = a * fo + av[u] * fn;
+      l = l * fo + lv[u] * fn;
+      M = Mn;
     }
   }
   const size_t hq = (size_t)b * Hkv * G + (size_t)g * G + h;
@@ -369,8 +548,9 @@ static hipError_t launch_attn_t(const kv_layout& L, const void* q, const PagesDe
                      k_max, n_splits, tau * kLog2e, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((split_reduce_kernel<D>), dim3(rows * G), dim3(D), 0, st, partials,
-                     L.num_kv_heads, G, n_splits, out, lse);
+  const long long n = (long long)rows * G * D;
+  hipLaunchKernelGGL((split_reduce_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partials,
+                     rows, L.num_kv_heads, G, n_splits, out, lse);
   return hipGetLastError();
 }
 

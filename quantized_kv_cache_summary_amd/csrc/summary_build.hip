@@ -6,7 +6,8 @@
 //   eigenpairs of Gram by cyclic Jacobi in float32, lam descending,
 //   w_j = Xc^T v_j / sqrt(n) (= sqrt(lam_j) u_j), zero when j > n-1 or
 //   lam_j <= 1e-6 lam_1;
-// stored as bfloat16 [mu, w_1..w_R] and float32 log n.
+// stored as bfloat16 [mu, w_1..w_R] and float32 log n at the page's logical
+// position (sequence, KV head, page), where the scorer streams them in order.
 //
 // One wave per (page, KV head).  The keys are centred into LDS once; the
 // n x n Gram comes from LDS dot products; Jacobi runs with the round-robin
@@ -22,7 +23,9 @@ namespace kvs {
 
 template <int D, int PS, bool F16>
 __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __restrict__ k16,
-                                                           const int32_t* __restrict__ pages,
+                                                           const int32_t* __restrict__ block_table,
+                                                           int max_pages,
+                                                           const int32_t* __restrict__ entries,
                                                            const int32_t* __restrict__ n_valid,
                                                            int Hkv, int R, uint16_t* __restrict__ summary,
                                                            float* __restrict__ log_n) {
@@ -37,15 +40,17 @@ __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __res
 
   const int lane = threadIdx.x;
   const int i = blockIdx.x / Hkv, g = blockIdx.x - (blockIdx.x / Hkv) * Hkv;
-  const int phys = pages[i];
+  const int sb = entries[2 * i], sp = entries[2 * i + 1];   // sequence, logical page
+  const int phys = block_table[(size_t)sb * max_pages + sp];
   int nv = n_valid[i];
   nv = nv < 0 ? 0 : (nv > PS ? PS : nv);
   const uint16_t* src = k16 + ((size_t)phys * Hkv + g) * PS * D;
-  uint16_t* dst = summary + ((size_t)phys * Hkv + g) * (size_t)(1 + R) * D;
+  uint16_t* dst = summary + (((size_t)sb * Hkv + g) * max_pages + sp) * (size_t)(1 + R) * D;
+  float* ln = log_n + (size_t)sb * max_pages + sp;
 
   if (nv == 0) {
     for (int e = lane; e < (1 + R) * D; e += 64) dst[e] = 0;
-    if (g == 0 && lane == 0) log_n[phys] = -INFINITY;
+    if (g == 0 && lane == 0) *ln = -INFINITY;
     return;
   }
 
@@ -165,18 +170,19 @@ __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __res
       dst[(size_t)(1 + j) * D + e] = (uint16_t)f32_to_bf16_rne(w);
     }
   }
-  if (g == 0 && lane == 0) log_n[phys] = logf((float)nv);
+  if (g == 0 && lane == 0) *ln = logf((float)nv);
 }
 
-hipError_t launch_summary_build(const kv_layout& L, const void* k16, const int32_t* pages,
-                                const int32_t* n_valid, int n, void* summary, float* log_n,
-                                hipStream_t st) {
+hipError_t launch_summary_build(const kv_layout& L, const void* k16, const int32_t* block_table,
+                                int max_pages, const int32_t* entries, const int32_t* n_valid, int n,
+                                void* summary, float* log_n, hipStream_t st) {
   const dim3 grid(n * L.num_kv_heads);
   const bool f16 = L.kv_dtype == KV_F16;
   const uint16_t* k = (const uint16_t*)k16;
   uint16_t* s = (uint16_t*)summary;
 #define KVS_SB(D_, PS_, F_) hipLaunchKernelGGL((summary_build_kernel<D_, PS_, F_>), grid, dim3(64), 0, st, \
-                                               k, pages, n_valid, L.num_kv_heads, L.rank, s, log_n)
+                                               k, block_table, max_pages, entries, n_valid, L.num_kv_heads, \
+                                               L.rank, s, log_n)
   if (L.head_dim == 64) {
     if (L.page_size == 16) { if (f16) KVS_SB(64, 16, true); else KVS_SB(64, 16, false); }
     else { if (f16) KVS_SB(64, 32, true); else KVS_SB(64, 32, false); }

@@ -82,13 +82,14 @@ class DeviceLayer:
         del kbits
         self.v16 = None if host_v else to_device16(vbits, w.dtype, device)
         del vbits
-        self.summary = torch.empty((w.n_phys, w.Hkv, (1 + w.rank) * w.d), dtype=torch.bfloat16, device=device)
-        self.log_n = torch.empty(w.n_phys, dtype=torch.float32, device=device)
+        # summaries in logical page order per (sequence, KV head)
+        self.summary = torch.empty((w.B, w.Hkv, w.Np, (1 + w.rank) * w.d), dtype=torch.bfloat16, device=device)
+        self.log_n = torch.empty((w.B, w.Np), dtype=torch.float32, device=device)
         if summaries == "build":
             self.build_summaries()
         elif summaries == "synthetic":
             rec, n_valid = wl.synthetic_summary(w, layer)
-            self.summary.copy_(to_device16(rec.reshape(w.n_phys, w.Hkv, -1), "bf16", device))
+            self.summary.copy_(to_device16(rec.reshape(w.B, w.Hkv, w.Np, -1), "bf16", device))
             self.log_n.copy_(torch.from_numpy(np.log(n_valid.astype(np.float64)).astype(np.float32)))
         self.tiers = None
         self.page_entry = None
@@ -100,21 +101,19 @@ class DeviceLayer:
             self._init_hot_buffer(hot_mode)
         self.pages = self._make_pages()
 
-    def valid_tokens_per_phys(self):
-        """Valid tokens of every physical page under the current seq_lens (P when unused)."""
+    def valid_tokens(self):
+        """(B, Np) valid tokens of every logical page under the current seq_lens."""
         w = self.w
-        nv = np.full(w.n_phys, w.P, dtype=np.int32)
-        for b in range(w.B):
-            starts = np.arange(w.Np) * w.P
-            nv[self.bt_np[b]] = np.clip(self.seq_lens_np[b] - starts, 0, w.P)
-        return nv
+        starts = np.arange(w.Np, dtype=np.int64) * w.P
+        return np.clip(self.seq_lens_np[:, None].astype(np.int64) - starts[None, :], 0, w.P).astype(np.int32)
 
-    # summary of every physical page, over its valid tokens
+    # summary of every logical page, over its valid tokens (0 -> empty record)
     def build_summaries(self, stream=None):
         w = self.w
-        ids = torch.arange(w.n_phys, dtype=torch.int32, device=self.device)
-        nv = torch.from_numpy(self.valid_tokens_per_phys()).to(self.device)
-        kv.summary_build(self.L, self.k16, ids, nv, self.summary, self.log_n, stream)
+        bb, pp = np.meshgrid(np.arange(w.B), np.arange(w.Np), indexing="ij")
+        entries = torch.from_numpy(np.stack([bb.ravel(), pp.ravel()], 1).astype(np.int32)).to(self.device)
+        nv = torch.from_numpy(self.valid_tokens().ravel()).to(self.device)
+        kv.summary_build(self.L, self.k16, self.bt, entries, nv, self.summary, self.log_n, stream)
 
     def _pack_tiers(self):
         w = self.w
@@ -194,7 +193,8 @@ class StepBuffers:
         self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=device)
         self.lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=device)
         nws = kv.attn_workspace_size(L, w.B, self.sel.shape[-1], num_splits)
-        self.ws = torch.empty(max(1, nws // 4), dtype=torch.float32, device=device)
+        # zeroed once: its per-row counters must start at zero (each call leaves them at zero)
+        self.ws = torch.zeros(max(1, nws // 4), dtype=torch.float32, device=device)
 
 
 def queries_device(w: wl.Workload, layer=0, qidx=0, device="cuda"):
@@ -202,7 +202,7 @@ def queries_device(w: wl.Workload, layer=0, qidx=0, device="cuda"):
 
 
 def score(layer: DeviceLayer, q, bufs: StepBuffers, stream=None):
-    kv.page_score(layer.L, q, layer.summary, layer.log_n, layer.bt, layer.seq_lens, bufs.head_scores,
+    kv.page_score(layer.L, q, layer.summary, layer.log_n, layer.seq_lens, bufs.head_scores,
                   bufs.lse_partial, stream)
 
 
@@ -223,3 +223,62 @@ def decode_step(layer: DeviceLayer, q, bufs: StepBuffers, stream=None):
     score(layer, q, bufs, stream)
     topk(layer, bufs, stream=stream)
     attend(layer, q, bufs, stream=stream)
+
+
+# ------------------------------------------------------------------ overlapped row groups
+
+class _View:
+    pass
+
+
+class SplitStep:
+    """One decode step with the batch cut into row groups, each group's
+    score -> top-k -> attention chain on its own HIP stream.
+
+    Rows are independent, so a group's selection and attention can run while
+    another group is still being scored; the C ABI is called per group with
+    pointers offset to that group's sequences (no library change).  All
+    streams keep the default priority."""
+
+    def __init__(self, layer: DeviceLayer, bufs: StepBuffers, n_groups=2, num_splits=0):
+        w = layer.w
+        self.layer, self.bufs = layer, bufs
+        n_groups = max(1, min(n_groups, w.B))
+        edges = [round(i * w.B / n_groups) for i in range(n_groups + 1)]
+        self.streams = [torch.cuda.Stream() for _ in range(n_groups)]
+        lp = bufs.lse_partial.view(w.B, -1)
+        self.groups = []
+        for b0, b1 in zip(edges[:-1], edges[1:]):
+            v = _View()
+            v.b0, v.b1 = b0, b1
+            v.summary = layer.summary[b0:b1]
+            v.log_n = layer.log_n[b0:b1]
+            v.seq_lens = layer.seq_lens[b0:b1]
+            v.bt = layer.bt[b0:b1]
+            v.head_scores = bufs.head_scores[b0:b1]
+            v.lse_partial = lp[b0:b1]
+            v.sel = bufs.sel[b0:b1]
+            v.sel_count = bufs.sel_count[b0:b1]
+            v.page_S = None if bufs.page_S is None else bufs.page_S[b0:b1]
+            v.out = bufs.out[b0:b1]
+            v.lse = bufs.lse[b0:b1]
+            nws = kv.attn_workspace_size(layer.L, b1 - b0, bufs.sel.shape[-1], num_splits)
+            v.ws = torch.zeros(max(1, nws // 4), dtype=torch.float32, device=layer.device)
+            self.groups.append(v)
+        self.num_splits = num_splits
+
+    def __call__(self, q):
+        layer, w = self.layer, self.layer.w
+        main = torch.cuda.current_stream()
+        for s in self.streams:
+            s.wait_stream(main)
+        for v, s in zip(self.groups, self.streams):
+            with torch.cuda.stream(s):
+                qg = q[v.b0:v.b1]
+                kv.page_score(layer.L, qg, v.summary, v.log_n, v.seq_lens, v.head_scores, v.lse_partial, s)
+                kv.page_topk(layer.L, v.head_scores, v.lse_partial, v.seq_lens, w.Np, w.keep, w.k_fixed,
+                             v.sel, v.sel_count, 0, 0, v.page_S, None, s)
+                kv.sparse_decode_attn(layer.L, qg, layer.pages, v.bt, v.seq_lens, v.sel, v.sel_count,
+                                      v.out, v.lse, v.ws, self.num_splits, s)
+        for s in self.streams:
+            main.wait_stream(s)

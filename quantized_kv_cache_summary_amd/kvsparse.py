@@ -66,8 +66,8 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
         L = ctypes.CDLL(LIB_PATH)
         sig = {
-            "kv_summary_build": (_I, [_LP, _P, _P, _P, _I, _P, _P, _P]),
-            "kv_page_score": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
+            "kv_summary_build": (_I, [_LP, _P, _P, _I, _P, _P, _I, _P, _P, _P]),
+            "kv_page_score": (_I, [_LP, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
             "kv_page_score_partial_size": (_SZ, [_LP, _I, _I]),
             "kv_page_topk": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _I, _P, _P, _I, _P,
                                   _P, _SZ, _P]),
@@ -138,9 +138,11 @@ def make_pages(k16, v16, kq=None, vq=None, ksz=None, vsz=None, page_entry=None, 
     return pg
 
 
-def summary_build(L, k16, pages, n_valid, summary, log_n, stream=None):
-    rc = lib().kv_summary_build(ctypes.byref(L), _p(k16), _p(pages), _p(n_valid), int(pages.numel()),
-                                _p(summary), _p(log_n), _stream(stream))
+def summary_build(L, k16, block_table, entries, n_valid, summary, log_n, stream=None):
+    """entries: int32 (n, 2) of (sequence, logical page); summary [B, Hkv, max_pages, (1+R)*d]."""
+    max_pages = block_table.shape[1]
+    rc = lib().kv_summary_build(ctypes.byref(L), _p(k16), _p(block_table), int(max_pages), _p(entries),
+                                _p(n_valid), int(entries.shape[0]), _p(summary), _p(log_n), _stream(stream))
     _check(rc, "kv_summary_build")
 
 
@@ -148,11 +150,11 @@ def page_score_partial_size(L, B, max_pages):
     return int(lib().kv_page_score_partial_size(ctypes.byref(L), int(B), int(max_pages)))
 
 
-def page_score(L, q, summary, log_n, block_table, seq_lens, head_scores, lse_partial, stream=None):
-    B, max_pages = block_table.shape
-    rc = lib().kv_page_score(ctypes.byref(L), _p(q), _p(summary), _p(log_n), _p(block_table),
-                             _p(seq_lens), int(B), int(max_pages), _p(head_scores), _p(lse_partial),
-                             _stream(stream))
+def page_score(L, q, summary, log_n, seq_lens, head_scores, lse_partial, stream=None):
+    """summary [B, Hkv, max_pages, (1+R)*d]; head_scores [B, Hkv, G, max_pages]."""
+    B, max_pages = seq_lens.shape[0], summary.shape[2]
+    rc = lib().kv_page_score(ctypes.byref(L), _p(q), _p(summary), _p(log_n), _p(seq_lens), int(B),
+                             int(max_pages), _p(head_scores), _p(lse_partial), _stream(stream))
     _check(rc, "kv_page_score")
 
 

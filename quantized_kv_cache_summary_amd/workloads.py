@@ -259,22 +259,21 @@ def synthetic_selection(w: Workload, k: int, layer: int = 0, ragged: bool = Fals
 def synthetic_summary(w: Workload, layer: int = 0, lam=(12.0, 10.0, 9.0, 8.0, 7.0, 6.0, 5.0, 4.0)):
     """Random stored summaries shaped like real ones, for score/select tests.
 
-    Returns (records uint16 [n_phys, Hkv, 1+rank, d] 16-bit bf16 bits,
-    n_valid int32 [n_phys]).  mu ~ N(0, 1/P); direction j ~ N(0, lam_j/d)."""
+    Returns (records uint16 [B, Hkv, Np, 1+rank, d] bf16 bits in logical page
+    order, n_valid int32 [B, Np]).  mu ~ N(0, 1/P); direction j ~ N(0, lam_j/d);
+    the planted pages carry a mean along their group's query direction."""
     rng = rng_for(w, layer, 0, 0, T_SUMMARY)
-    rec = np.empty((w.n_phys, w.Hkv, 1 + w.rank, w.d), dtype=np.float32)
-    rec[:, :, 0] = rng.standard_normal((w.n_phys, w.Hkv, w.d), dtype=np.float32) / np.float32(math.sqrt(w.P))
+    rec = np.empty((w.B, w.Hkv, w.Np, 1 + w.rank, w.d), dtype=np.float32)
+    rec[:, :, :, 0] = rng.standard_normal((w.B, w.Hkv, w.Np, w.d), dtype=np.float32) / np.float32(math.sqrt(w.P))
     for j in range(w.rank):
         sd = np.float32(math.sqrt(lam[j % len(lam)] / w.d))
-        rec[:, :, 1 + j] = rng.standard_normal((w.n_phys, w.Hkv, w.d), dtype=np.float32) * sd
-    # a few pages carry a mean along their group's query direction, for spread
+        rec[:, :, :, 1 + j] = rng.standard_normal((w.B, w.Hkv, w.Np, w.d), dtype=np.float32) * sd
     for b in range(w.B):
         hp = hot_pages(w, layer, b)
         if hp.size:
-            bt = block_table(w, layer)[b]
             for g in range(w.Hkv):
-                rec[bt[hp], g, 0] += np.float32(w.plant_scale) * plant_direction(w, layer, b, g).astype(np.float32)
-    n_valid = np.full(w.n_phys, w.P, dtype=np.int32)
+                rec[b, g, hp, 0] += np.float32(w.plant_scale) * plant_direction(w, layer, b, g).astype(np.float32)
+    n_valid = np.full((w.B, w.Np), w.P, dtype=np.int32)
     return bf16_bits(rec), n_valid
 
 

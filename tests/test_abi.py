@@ -48,9 +48,9 @@ FAKE = 0x10000   # a 16-byte aligned non-null address; never dereferenced (valid
 
 
 def _score(L, **over):
-    a = dict(q=FAKE, summary=FAKE, log_n=FAKE, bt=FAKE, sl=FAKE, B=2, max_pages=10, hs=FAKE, lp=FAKE)
+    a = dict(q=FAKE, summary=FAKE, log_n=FAKE, sl=FAKE, B=2, max_pages=10, hs=FAKE, lp=FAKE)
     a.update(over)
-    return kv.lib().kv_page_score(ctypes.byref(L), a["q"], a["summary"], a["log_n"], a["bt"], a["sl"],
+    return kv.lib().kv_page_score(ctypes.byref(L), a["q"], a["summary"], a["log_n"], a["sl"],
                                   a["B"], a["max_pages"], a["hs"], a["lp"], None)
 
 
@@ -64,13 +64,14 @@ def test_layout_validation():
     L = _L()
     L.kv_dtype = 7
     assert _score(L) == kv.KV_ERR_UNSUPPORTED
-    assert kv.lib().kv_page_score(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert kv.lib().kv_page_score(None, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
 
 
 def test_score_argument_validation():
     L = _L()
     assert _score(L, q=None) == kv.KV_ERR_INVALID_ARG
     assert _score(L, lp=None) == kv.KV_ERR_INVALID_ARG
+    assert _score(L, summary=FAKE + 4) == kv.KV_ERR_INVALID_ARG    # misaligned
     assert _score(L, q=FAKE + 2) == kv.KV_ERR_INVALID_ARG          # misaligned
     assert _score(L, B=-1) == kv.KV_ERR_INVALID_ARG
     assert _score(L, B=0) == kv.KV_OK                              # nothing to do, no launch
@@ -137,9 +138,12 @@ def test_pack_build_dequant_validation():
     assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 4, 5, FAKE, FAKE, None, None) == kv.KV_ERR_UNSUPPORTED
     assert lib.kv_pack_tier(ctypes.byref(L), None, None, 4, 1, FAKE, FAKE, None, None) == kv.KV_ERR_INVALID_ARG
     assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 0, 1, FAKE, FAKE, None, None) == kv.KV_OK
-    assert lib.kv_summary_build(ctypes.byref(L), FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
-    assert lib.kv_summary_build(ctypes.byref(L), FAKE + 4, FAKE, FAKE, 3, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
-    assert lib.kv_summary_build(ctypes.byref(L), FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == kv.KV_OK
+    sb = lib.kv_summary_build
+    assert sb(ctypes.byref(L), FAKE, FAKE, 8, FAKE, FAKE, -1, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert sb(ctypes.byref(L), FAKE + 4, FAKE, 8, FAKE, FAKE, 3, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert sb(ctypes.byref(L), FAKE, None, 8, FAKE, FAKE, 3, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert sb(ctypes.byref(L), FAKE, FAKE, 0, FAKE, FAKE, 3, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
+    assert sb(ctypes.byref(L), FAKE, FAKE, 8, FAKE, FAKE, 0, FAKE, FAKE, None) == kv.KV_OK
     assert lib.kv_dequant_tier(ctypes.byref(L), None, FAKE, 2, FAKE, None) == kv.KV_ERR_INVALID_ARG
-    assert kv.page_score_partial_size(L, 8, 2048) == 64 * 16 * 4 * 2 * 4
+    assert kv.page_score_partial_size(L, 8, 2048) == 64 * 32 * 4 * 2 * 4
     assert kv.page_topk_workspace_size(L, 8, 2048) == 0

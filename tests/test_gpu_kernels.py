@@ -60,14 +60,13 @@ def test_score_and_select_parity(hz, name):
     sel = bufs.sel.cpu().numpy()
     cnt = bufs.sel_count.cpu().numpy()
     rec_bits, n_valid = wl.synthetic_summary(w)
-    rec = bits_to_f64(rec_bits)
+    rec = bits_to_f64(rec_bits)                    # [B, Hkv, Np, 1+R, d], logical page order
     log_n = np.log(n_valid.astype(np.float64)).astype(np.float32).astype(np.float64)
     swaps = 0
     for b in range(w.B):
         Np = oracle.num_pages(lens[b], w.P)
-        pages = layer.bt_np[b, :Np]
         for g in range(w.Hkv):
-            s_ref = oracle.page_score(_q_ref(w, b, g), rec[pages, g, 0], rec[pages, g, 1:], log_n[pages], w.tau)
+            s_ref = oracle.page_score(_q_ref(w, b, g), rec[b, g, :Np, 0], rec[b, g, :Np, 1:], log_n[b, :Np], w.tau)
             assert_scores_close(hs[b, g, :, :Np], s_ref)
             assert np.all(hs[b, g, :, Np:] == -np.inf)
             S_ref = oracle.group_aggregate(s_ref)
@@ -97,9 +96,8 @@ def test_forced_pages_and_fixed_k(hz):
     rec = bits_to_f64(rec_bits)
     log_n = np.log(n_valid.astype(np.float64)).astype(np.float32).astype(np.float64)
     for b in range(w.B):
-        pages = layer.bt_np[b]
         for g in range(w.Hkv):
-            s_ref = oracle.page_score(_q_ref(w, b, g), rec[pages, g, 0], rec[pages, g, 1:], log_n[pages], w.tau)
+            s_ref = oracle.page_score(_q_ref(w, b, g), rec[b, g, :, 0], rec[b, g, :, 1:], log_n[b], w.tau)
             S_ref = oracle.group_aggregate(s_ref)
             forced = [0, 1, w.Np - 3, w.Np - 2, w.Np - 1]
             assert all(np.isinf(S[b, g, p]) for p in forced)
@@ -191,25 +189,26 @@ def test_summary_builder_invariants(hz, name):
     announce(f"summary build {name}")
     layer = hz.DeviceLayer(w, summaries="build", seq_lens=lens)
     torch.cuda.synchronize()
-    rec = layer.summary.float().cpu().numpy().astype(np.float64).reshape(w.n_phys, w.Hkv, 1 + w.rank, w.d)
+    rec = layer.summary.float().cpu().numpy().astype(np.float64).reshape(w.B, w.Hkv, w.Np, 1 + w.rank, w.d)
     log_n = layer.log_n.cpu().numpy()
-    nv_phys = layer.valid_tokens_per_phys()
+    nv = layer.valid_tokens()
     skipped = checked = 0
     for b in range(w.B):
         Np = oracle.num_pages(lens[b], w.P)
+        assert np.all(log_n[b, Np:] == -np.inf) and not rec[b, :, Np:].any()
         for g in range(w.Hkv):
             K = wl.row_keys(w, 0, b, g)
             for p in range(Np):
-                phys = layer.bt_np[b, p]
                 keys = K[p * w.P: min((p + 1) * w.P, lens[b])]
                 n = keys.shape[0]
-                assert nv_phys[phys] == n
-                assert log_n[phys] == np.float32(math.log(n)) or abs(log_n[phys] - math.log(n)) <= 2 ** -22 * math.log(n)
+                assert nv[b, p] == n
+                ln = log_n[b, p]
+                assert ln == np.float32(math.log(n)) or abs(ln - math.log(n)) <= 2 ** -22 * max(1.0, math.log(n))
                 mu, wv, lam, _ = oracle.summarize_page(keys, w.rank)
                 mu_b = oracle.round_bf16(mu)
                 ulp = np.maximum(np.abs(mu_b), 2.0 ** -126) * 2.0 ** -7
-                assert np.all(np.abs(rec[phys, g, 0] - mu_b) <= ulp * 1.01)
-                wg = rec[phys, g, 1:]
+                assert np.all(np.abs(rec[b, g, p, 0] - mu_b) <= ulp * 1.01)
+                wg = rec[b, g, p, 1:]
                 # full spectrum for the gap test
                 Xc = keys.astype(np.float64) - mu
                 lam_all = np.sort(np.linalg.eigvalsh(Xc @ Xc.T / n))[::-1]
