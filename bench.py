@@ -12,7 +12,6 @@ Prints one JSON line on stdout; progress goes to stderr.
 """
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -24,8 +23,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode attn steps/sec & effective HBM GB/s (% peak) at 32k-128k ctx, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "page_score_llama8b_32k_traffic.json")
-SCORE_SRC = os.path.join(ROOT, "quantized_kv_cache_summary_amd", "csrc", "page_score.hip")
 
 
 def log(*a):
@@ -43,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 512 MiB device copy (known bytes) for scaling counter readings")
     ap.add_argument("--groups", type=int, default=1,
                     help="row groups per step, each on its own stream (1 = one chain for the batch)")
     return ap.parse_args()
@@ -55,15 +54,16 @@ def algorithmic_bytes(w, sel_counts):
     return summary, selected
 
 
-def traffic_for(per_launch_bytes_alg):
-    """HBM bytes of the score kernel from the committed counter runs, if they
-    were taken on the current kernel source; else None."""
+def traffic_for(workload):
+    """HBM bytes per launch of the score kernel from the committed counter runs
+    (profiles/), if they were taken on the current kernel source; else None."""
+    from quantized_kv_cache_summary_amd import traffic
+    path = os.path.join(ROOT, "profiles", f"page_score_{workload}_traffic.json")
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(path))
     except (OSError, ValueError):
         return None
-    src_hash = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
-    if t.get("kernel_source_sha256") != src_hash:
+    if t.get("kernel_source_sha256") != traffic.score_kernel_hash():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -145,6 +145,15 @@ def main():
         li = i % n_layers
         q = qs[li][(i // n_layers) % args.queries]
         steps_split[li](q)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copy calibration: 3 x 512 MiB device-to-device copies")
 
     for i in range(args.warmup):
         step(i)
@@ -241,7 +250,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic_for(summary_b),
+            "traffic": traffic_for(w.name),
             "avg_launch_us": score_avg_s * 1e6,
             "bytes_per_launch": summary_b,
         },
