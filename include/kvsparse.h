@@ -197,7 +197,10 @@ size_t kv_page_topk_workspace_size(const kv_layout* layout, int32_t B, int32_t m
  * Split-K: num_splits > 0 fixes the number of partial results per row (at
  * most 256); 0 lets the library choose.  Results agree across split counts to
  * float32 rounding.  ws/ws_bytes: kv_sparse_decode_attn_workspace_size() with
- * the same num_splits.  Calls that share a workspace must not overlap in time.
+ * the same num_splits.  The workspace ends with one counter per row that must
+ * be zero when a call starts: zero it once after allocating; every completed
+ * call leaves the counters at zero.  Calls that share a workspace must not
+ * overlap in time.
  * --------------------------------------------------------------------------- */
 int kv_sparse_decode_attn(const kv_layout* layout, const void* q, const kv_pages* pages,
                           const int32_t* block_table, const int32_t* seq_lens, int32_t B,
@@ -205,11 +208,15 @@ int kv_sparse_decode_attn(const kv_layout* layout, const void* q, const kv_pages
                           int32_t k_max, int32_t num_splits, float* out, float* lse,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of workspace for num_splits partials per row; num_splits = 0 gives
+ * enough for the automatic count of either page kind. */
 size_t kv_sparse_decode_attn_workspace_size(const kv_layout* layout, int32_t B, int32_t k_max,
                                             int32_t num_splits);
 
-/* The split count kv_sparse_decode_attn uses for num_splits = 0. */
-int32_t kv_sparse_decode_attn_num_splits(const kv_layout* layout, int32_t B, int32_t k_max);
+/* The split count kv_sparse_decode_attn uses for num_splits = 0: tiered != 0
+ * for a pool with packed tiers (pages->page_entry set), 0 for native pages. */
+int32_t kv_sparse_decode_attn_num_splits(const kv_layout* layout, int32_t B, int32_t k_max,
+                                         int32_t tiered);
 
 /* ---------------------------------------------------------------------------
  * kv_dequant_tier -- the attention kernel's in-register tier decoding as a

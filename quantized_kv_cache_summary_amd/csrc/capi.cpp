@@ -41,14 +41,28 @@ int topk_bound(int max_pages, float keep, int k_fixed) {
   return k > max_pages ? max_pages : k;
 }
 
-int auto_splits(int rows, int k_max) {
+// Splits per row.  A native-page block streams K/V at the gather rate with one
+// wave per SIMD, and every further split only lengthens the latency-bound head
+// (page list) and tail (merge) of the kernel, so native pages get about one
+// 4-wave block per CU (256 blocks).  Packed tiers spend VALU time decoding, so
+// they get as many blocks as stay resident (three 4-wave blocks per CU).  At
+// least two pages per wave either way.
+int auto_splits(int rows, int k_max, bool tiered) {
   if (rows <= 0) return 1;
-  int s = (1024 + rows - 1) / rows;            // about four blocks per CU
-  int cap = k_max / 4;                         // at least ~4 pages per split
+  const int waves = 4;
+  const int target = tiered ? 768 : 256;
+  int s = (target + rows - 1) / rows;
+  int cap = k_max / (2 * waves);
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
   if (s > kvs::kMaxSplits) s = kvs::kMaxSplits;
   return s < 1 ? 1 : s;
+}
+
+// Workspace for num_splits = 0 covers whichever automatic count the pages need.
+int auto_splits_any(int rows, int k_max) {
+  const int a = auto_splits(rows, k_max, false), b = auto_splits(rows, k_max, true);
+  return a > b ? a : b;
 }
 
 int check_pages(const kv_layout* L, const kv_pages* pg) {
@@ -146,18 +160,17 @@ int kv_page_topk(const kv_layout* L, const float* head_scores, const float* lse_
                                         sel_count, k_max, page_S, (hipStream_t)stream));
 }
 
-int32_t kv_sparse_decode_attn_num_splits(const kv_layout* L, int32_t B, int32_t k_max) {
+int32_t kv_sparse_decode_attn_num_splits(const kv_layout* L, int32_t B, int32_t k_max, int32_t tiered) {
   if (check_layout(L) || B <= 0) return 1;
-  return auto_splits(B * L->num_kv_heads, k_max);
+  return auto_splits(B * L->num_kv_heads, k_max, tiered != 0);
 }
 
 size_t kv_sparse_decode_attn_workspace_size(const kv_layout* L, int32_t B, int32_t k_max,
                                             int32_t num_splits) {
   if (check_layout(L) || B <= 0 || num_splits < 0) return 0;
   const int rows = B * L->num_kv_heads;
-  const int s = num_splits > 0 ? num_splits : auto_splits(rows, k_max);
-  const size_t G = (size_t)(L->num_q_heads / L->num_kv_heads);
-  return (size_t)rows * s * G * (L->head_dim + 2) * sizeof(float);
+  const int s = num_splits > 0 ? num_splits : auto_splits_any(rows, k_max);
+  return kvs::attn_workspace_bytes(rows, s, L->num_q_heads / L->num_kv_heads, L->head_dim);
 }
 
 int kv_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages* pg,
@@ -177,7 +190,7 @@ int kv_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages* pg,
   if (rc) return rc;
   const int rows = B * L->num_kv_heads;
   if ((int64_t)rows > 65535) return KV_ERR_UNSUPPORTED;
-  const int s = num_splits > 0 ? num_splits : auto_splits(rows, k_max);
+  const int s = num_splits > 0 ? num_splits : auto_splits(rows, k_max, pg->page_entry != nullptr);
   const size_t need = kv_sparse_decode_attn_workspace_size(L, B, k_max, s);
   if (!ws || ws_bytes < need) return KV_ERR_WORKSPACE;
   return from_hip(kvs::launch_sparse_attn(*L, q, *pg, block_table, seq_lens, B, max_pages, sel,

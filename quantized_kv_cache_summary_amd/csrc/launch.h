@@ -17,6 +17,16 @@ constexpr int kMaxSplits = 256;
 
 inline int score_tiles(int max_pages) { return (max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock; }
 
+// Attention workspace: per (row, split, head) partials [d + 2] floats, then one
+// uint32 counter per row (zero between calls).
+inline size_t attn_partial_floats(int rows, int splits, int G, int d) {
+  const size_t n = (size_t)rows * splits * G * (d + 2);
+  return (n + 3) & ~(size_t)3;   // keeps the counters 16-byte aligned
+}
+inline size_t attn_workspace_bytes(int rows, int splits, int G, int d) {
+  return attn_partial_floats(rows, splits, G, d) * sizeof(float) + (size_t)rows * sizeof(unsigned);
+}
+
 hipError_t launch_summary_build(const kv_layout& L, const void* k16, const int32_t* block_table,
                                 int max_pages, const int32_t* entries, const int32_t* n_valid, int n,
                                 void* summary, float* log_n, hipStream_t st);

@@ -5,7 +5,7 @@
 // use (ARGUS, argus_cache 0.1.7.1 project page, "Why It Works: Storage vs.
 // Computation"); the arithmetic stays float32.
 //
-// gfx950 design.  One block (4 waves) per (row, split); the split's selected
+// gfx950 design.  One block of 4 waves per (row, split); the split's selected
 // pages are dealt round-robin to the waves; a wave handles 16 tokens at a time.
 //   QK^T: the G query heads of the group are the 16 B columns of a 16x16x32
 //     MFMA, the 16 tokens its A rows.  Each lane loads d/4 contiguous elements
@@ -19,16 +19,19 @@
 //     4j + ts, so the V page is read with 16-byte coalesced loads; the
 //     probabilities reach it through a 1 KB per-wave LDS tile; acc[head][d/16]
 //     accumulates in float32 FMAs.
-// The four waves merge in LDS; a small second kernel merges the splits (a
-// kernel boundary is the cheap way to make every split's partial visible
-// across the chip's L2 slices).
+// The four waves merge in LDS; the last block of a row to finish (a counter per
+// row in the workspace) merges the row's splits into out and lse.  Partials
+// cross blocks through device-coherent stores and loads: a release fence
+// would write back the whole L2 and costs far more than the merge.
 
 #include "device.h"
 #include "launch.h"
 
 namespace kvs {
 
-constexpr int kAttnWaves = 4;
+// waves per block: enough that a CU holds four waves per SIMD with few splits
+template <int GM>
+constexpr int attn_waves() { return 4; }
 constexpr int kBatch = 2;   // 16-token chunks per load batch; two batches are in flight
 
 struct PagesDev {
@@ -213,14 +216,17 @@ __device__ __forceinline__ void load_native_chunk(ChunkRaw<D>& r, const uint16_t
 }
 
 template <int D, int GM, bool F16, bool TIERED>
-__global__ __launch_bounds__(256) void sparse_attn_kernel(
+__global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, PagesDev pg, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int Hkv, int G, int P, int max_pages,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int k_max, int n_splits,
-    float scale_log2, float* __restrict__ partials) {
+    float scale_log2, float* __restrict__ partials, unsigned* __restrict__ counters,
+    float* __restrict__ out, float* __restrict__ lse) {
   constexpr int KS = D / 32;     // MFMA k-steps
   constexpr int EK = D / 4;      // key elements per lane
   constexpr int EV = D / 16;     // value elements per lane
+  constexpr int kAttnWaves = attn_waves<GM>();
+  constexpr int kThreads = 64 * kAttnWaves;
 
   __shared__ float ptile[kAttnWaves][16][16];       // [wave][token][head]
   __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
 
   // ---- merge the waves (fixed order) and write this split's partial
   float* dst = partials + ((size_t)row * n_splits + split) * G * (D + 2);
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, e = idx - h * D;
     float M = -INFINITY;
 #pragma unroll
@@ -484,56 +490,60 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
         l += wl[w][h] * f;
       }
     }
-    dst[(size_t)h * (D + 2) + e] = a;
+    // device-coherent stores (written through to the chip's coherence point),
+    // so another block may read them after the counter below says so
+    __hip_atomic_store(dst + (size_t)h * (D + 2) + e, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (e == 0) {
-      dst[(size_t)h * (D + 2) + D] = M;
-      dst[(size_t)h * (D + 2) + D + 1] = l;
+      __hip_atomic_store(dst + (size_t)h * (D + 2) + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + (size_t)h * (D + 2) + D + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
-}
-
-// Split merge: one thread per (row, head, element); every split's (max, sum,
-// acc) is requested before any is used, so the kernel waits on memory once.
-template <int D>
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ partials, int rows,
-                                                           int Hkv, int G, int n_splits,
-                                                           float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int U = 16;
-  const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (id >= (long long)rows * G * D) return;
-  const int e = (int)(id % D);
-  const int rh = (int)(id / D);
-  const int row = rh / G, h = rh - row * G;
-  const int b = row / Hkv, g = row - b * Hkv;
-  const float* sh = partials + (size_t)row * n_splits * G * (D + 2) + (size_t)h * (D + 2);
+  // ---- the last split of the row to finish merges all splits in split order.
+  // Every partial store above has completed before the count is raised, and
+  // the merging block reads partials with device-coherent loads; no cache
+  // write-back fence is needed because nothing else crosses blocks.
+  __shared__ int is_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(&counters[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned)(n_splits - 1);
+  __syncthreads();
+  if (!is_last) return;
+  const float* src = partials + (size_t)row * n_splits * G * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
-  float M = -INFINITY, a = 0.f, l = 0.f;
-  for (int s0 = 0; s0 < n_splits; s0 += U) {
-    float av[U], mv[U], lv[U];
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, e = idx - h * D;
+    const float* sh = src + (size_t)h * (D + 2);
+    constexpr int U = 8;
+    float M = -INFINITY, a = 0.f, l = 0.f;
+    for (int s0 = 0; s0 < n_splits; s0 += U) {
+      float av[U], mv[U], lv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int si = s0 + u < n_splits ? s0 + u : n_splits - 1;
-      av[u] = sh[si * stride + e];
-      mv[u] = sh[si * stride + D];
-      lv[u] = sh[si * stride + D + 1];
-    }
-    // running merge in split order: fixed, so the result does not depend on timing
+      for (int u = 0; u < U; ++u) {
+        const int si = s0 + u < n_splits ? s0 + u : n_splits - 1;
+        av[u] = __hip_atomic_load(sh + si * stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mv[u] = __hip_atomic_load(sh + si * stride + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lv[u] = __hip_atomic_load(sh + si * stride + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (s0 + u >= n_splits) break;
-      const float Mn = nan_max(M, mv[u]);
-      if (Mn == -INFINITY) continue;
-      const float fo = exp2f(M - Mn), fn = exp2f(mv[u] - Mn);
-      a = a * fo + av[u] * fn;
-      l = l * fo + lv[u] * fn;
-      M = Mn;
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u >= n_splits) break;
+        const float Mn = nan_max(M, mv[u]);
+        if (Mn == -INFINITY) continue;
+        const float fo = exp2f(M - Mn), fn = exp2f(mv[u] - Mn);
+        a = a * fo + av[u] * fn;
+        l = l * fo + lv[u] * fn;
+        M = Mn;
+      }
     }
+    const size_t hq = (size_t)b * Hkv * G + (size_t)g * G + h;
+    const bool empty = l == 0.f;
+    out[hq * D + e] = empty ? 0.f : a / l;
+    if (e == 0) lse[hq] = empty ? -INFINITY : (M + log2f(l)) * kLn2;
   }
-  const size_t hq = (size_t)b * Hkv * G + (size_t)g * G + h;
-  const bool empty = l == 0.f;
-  out[hq * D + e] = empty ? 0.f : a / l;
-  if (e == 0) lse[hq] = empty ? -INFINITY : (M + log2f(l)) * kLn2;
+  if (threadIdx.x == 0) __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int GM, bool F16, bool TIERED>
@@ -543,14 +553,10 @@ static hipError_t launch_attn_t(const kv_layout& L, const void* q, const PagesDe
                                 float tau, float* out, float* lse, float* partials, hipStream_t st) {
   const int G = L.num_q_heads / L.num_kv_heads;
   const int rows = B * L.num_kv_heads;
-  hipLaunchKernelGGL((sparse_attn_kernel<D, GM, F16, TIERED>), dim3(n_splits, rows), dim3(256), 0, st,
+  unsigned* counters = reinterpret_cast<unsigned*>(partials + attn_partial_floats(rows, n_splits, G, D));
+  hipLaunchKernelGGL((sparse_attn_kernel<D, GM, F16, TIERED>), dim3(n_splits, rows), dim3(64 * attn_waves<GM>()), 0, st,
                      (const uint16_t*)q, pd, bt, sl, L.num_kv_heads, G, L.page_size, max_pages, sel, cnt,
-                     k_max, n_splits, tau * kLog2e, partials);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long long n = (long long)rows * G * D;
-  hipLaunchKernelGGL((split_reduce_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partials,
-                     rows, L.num_kv_heads, G, n_splits, out, lse);
+                     k_max, n_splits, tau * kLog2e, partials, counters, out, lse);
   return hipGetLastError();
 }
 

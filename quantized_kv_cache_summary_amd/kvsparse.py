@@ -75,7 +75,7 @@ def lib():
             "kv_sparse_decode_attn": (_I, [_LP, _P, _PP, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _P,
                                            _SZ, _P]),
             "kv_sparse_decode_attn_workspace_size": (_SZ, [_LP, _I, _I, _I]),
-            "kv_sparse_decode_attn_num_splits": (_I, [_LP, _I, _I]),
+            "kv_sparse_decode_attn_num_splits": (_I, [_LP, _I, _I, _I]),
             "kv_dequant_tier": (_I, [_LP, _PP, _P, _I, _P, _P]),
             "kv_pack_tier": (_I, [_LP, _P, _P, _I, _I, _P, _P, _P, _P]),
             "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -173,8 +173,8 @@ def page_topk(L, head_scores, lse_partial, seq_lens, max_pages, keep_frac, k_fix
     _check(rc, "kv_page_topk")
 
 
-def attn_num_splits(L, B, k_max):
-    return int(lib().kv_sparse_decode_attn_num_splits(ctypes.byref(L), int(B), int(k_max)))
+def attn_num_splits(L, B, k_max, tiered=False):
+    return int(lib().kv_sparse_decode_attn_num_splits(ctypes.byref(L), int(B), int(k_max), int(bool(tiered))))
 
 
 def attn_workspace_size(L, B, k_max, num_splits=0):

@@ -110,10 +110,13 @@ def test_attention_validation_and_workspace():
         return f(ctypes.byref(L), q, ctypes.byref(pages) if pages is not None else None, FAKE, FAKE, 8, 2048,
                  FAKE, FAKE, 164, splits, FAKE, FAKE, ws, ws_bytes, None)
 
-    need = kv.attn_workspace_size(L, 8, 164)
-    s = kv.attn_num_splits(L, 8, 164)
-    assert s == 16 and need == 64 * s * 4 * 130 * 4
-    assert kv.attn_workspace_size(L, 8, 164, 3) == 64 * 3 * 4 * 130 * 4
+    s = kv.attn_num_splits(L, 8, 164)                  # native pages: one block per CU
+    st = kv.attn_num_splits(L, 8, 164, tiered=True)    # packed tiers: three blocks per CU
+    assert (s, st) == (4, 12)
+    assert kv.attn_num_splits(L, 8, 16) == 2           # at least two pages per wave
+    need = kv.attn_workspace_size(L, 8, 164, s)
+    assert need == 64 * s * 4 * 130 * 4 + 64 * 4       # partials + one counter per row
+    assert kv.attn_workspace_size(L, 8, 164) == kv.attn_workspace_size(L, 8, 164, st)
     assert call(ws_bytes=need - 1) == kv.KV_ERR_WORKSPACE
     assert call(ws=None) == kv.KV_ERR_WORKSPACE
     assert call(pages=None) == kv.KV_ERR_INVALID_ARG
