@@ -70,6 +70,59 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Cross-lane steps through DPP (row_shr within 16-lane rows, row_bcast:15/31
+// across rows) instead of LDS permutes.  Lanes whose source lies outside the
+// pattern take `old`, the identity of the operation.  Every lane of the wave
+// must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive prefix sum in lane order.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += dpp<0x111, 0xF>(0, x);   // row_shr:1
+  x += dpp<0x112, 0xF>(0, x);   // row_shr:2
+  x += dpp<0x114, 0xF>(0, x);   // row_shr:4
+  x += dpp<0x118, 0xF>(0, x);   // row_shr:8
+  x += dpp<0x142, 0xA>(0, x);   // row_bcast:15 into rows 1 and 3
+  x += dpp<0x143, 0xC>(0, x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Wave-wide reductions; the result is wave-uniform.
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i32(int x, int identity, Op op) {
+  x = op(x, dpp<0x111, 0xF>(identity, x));
+  x = op(x, dpp<0x112, 0xF>(identity, x));
+  x = op(x, dpp<0x114, 0xF>(identity, x));
+  x = op(x, dpp<0x118, 0xF>(identity, x));
+  x = op(x, dpp<0x142, 0xA>(identity, x));
+  x = op(x, dpp<0x143, 0xC>(identity, x));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  return wave_reduce_i32(x, 0, [](int a, int b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return (uint32_t)wave_reduce_i32((int)x, 0, [](int a, int b) { return (uint32_t)a > (uint32_t)b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return (uint32_t)wave_reduce_i32((int)x, -1, [](int a, int b) { return (uint32_t)a < (uint32_t)b ? a : b; });
+}
+// fmaxf semantics: a NaN lane is dropped unless every lane is NaN.
+__device__ __forceinline__ float wave_max_f32(float x) {
+  return __int_as_float(wave_reduce_i32(__float_as_int(x), (int)0xFF800000u, [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  return __int_as_float(wave_reduce_i32(__float_as_int(x), 0, [](int a, int b) {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  }));
+}
+
 // max that propagates NaN from either side (fmaxf drops it).
 __device__ __forceinline__ float nan_max(float a, float b) {
   return (a != a || a > b) ? a : b;

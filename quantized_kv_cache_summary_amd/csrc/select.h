@@ -1,0 +1,343 @@
+// Exact top-k page selection for one (sequence, KV head) row, by one block of
+// NT threads.  AMASS (amass-kv 0.1.1 project page), "Quickstart" (budget: a
+// fixed selected page fraction) and "Benchmarking" (the top-B stage).
+//
+//   L_h = logsumexp_p s[h][p]                 (merged from the score blocks'
+//                                              (max, sum exp) partials)
+//   S_p = log((1/G) sum_h exp(s[h][p] - L_h))  (group-mean mass fraction)
+//
+// The k-th largest S is found exactly on order-preserving uint32 keys.  The
+// +inf keys (forced pages) and -inf keys (empty or NaN scores) are counted
+// apart, so the radix passes start at the highest bit in which the row's
+// finite keys differ: scores of one row share sign and most exponent bits,
+// and a digit taken above that would put nearly every key in one bin.  Each
+// pass is an 8-bit LDS histogram with integer counts (independent of thread
+// timing); once the bin holding the k-th key has at most kDirectMax keys they
+// are ranked against each other directly instead of by further passes.  An
+// ordered compaction then keeps every key above the threshold and the
+// lowest-index pages among keys equal to it, so pages come out ascending with
+// no sort and ties break by (S descending, page ascending) exactly.
+#pragma once
+
+#include "device.h"
+
+namespace kvs {
+
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // key of -inf; NaN scores take it too
+constexpr uint32_t kKeyPosInf = 0xFF800000u;   // key of +inf (forced pages)
+constexpr int kDirectMax = 64;                  // bin size finished by direct ranking
+
+__device__ __forceinline__ uint32_t order_key(float S) {
+  if (S != S) return kKeyNegInf;
+  S = S + 0.0f;   // -0 -> +0
+  const uint32_t u = __float_as_uint(S);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ bool finite_key(uint32_t key) { return key > kKeyNegInf && key < kKeyPosInf; }
+
+// Pages kept for a row of Np pages: k_fixed if set, else ceil(keep * Np), in [1, Np].
+__device__ __forceinline__ int selection_count(int Np, float keep, int k_fixed) {
+  if (Np <= 0) return 0;
+  if (k_fixed > 0) return k_fixed < Np ? k_fixed : Np;
+  int k = (int)ceil((double)keep * (double)Np);
+  return k < 1 ? 1 : (k > Np ? Np : k);
+}
+
+template <int NT>
+struct SelectLds {
+  static_assert(NT >= 256 && NT % 64 == 0, "every lane scans four of the 256 bins");
+  static constexpr int NW = NT / 64;
+  float Lh[16];
+  int hist[3][256];   // three buffers: one pass fills one, clears the next, reads back the one it filled
+  int wave_tot[NW];
+  uint32_t wmax[NW], wmin[NW];
+  int wpos[NW], wneg[NW];
+  uint32_t cand[kDirectMax];
+  int n_cand;
+};
+
+// Register-held inputs: the first round of head scores (U pages per thread,
+// strided by NT) and the score blocks' (max, sum exp) partials of the heads
+// this wave normalises (tiles lane + 64 i).
+template <int NT, int GM>
+struct SelectLoads {
+  static constexpr int NW = NT / 64;
+  static constexpr int U0 = 2048 / NT, U1 = 32 / GM;
+  static constexpr int U = U0 < U1 ? U0 : U1;
+  static constexpr int HJ = (GM + NW - 1) / NW;
+  static constexpr int TI = 4;   // up to 256 score tiles per row
+  float v[U][GM];
+  float2 part[HJ][TI];
+};
+
+template <int NT, int GM, int U>
+__device__ __forceinline__ void select_load_round(float (&v)[U][GM], const float* hs, int G, int max_pages,
+                                                  int p0) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int p = p0 + u * NT;
+    const int pc = p < max_pages ? p : max_pages - 1;   // in bounds; values past the row are ignored
+#pragma unroll
+    for (int h = 0; h < GM; ++h) v[u][h] = hs[(size_t)(h < G ? h : 0) * max_pages + pc];
+  }
+}
+
+// Requests every input the threshold search starts from.  No address depends
+// on the row length, so the loads leave before it is known.  hs: the row's
+// [G][max_pages] head scores; lsep: its [n_tiles][G] partial pairs.
+// max_pages >= 1, n_tiles <= 256.
+template <int NT, int GM>
+__device__ __forceinline__ void select_issue(SelectLoads<NT, GM>& ld, const float* hs, const float* lsep,
+                                             int G, int max_pages, int n_tiles) {
+  using SL = SelectLoads<NT, GM>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  select_load_round<NT, GM>(ld.v, hs, G, max_pages, threadIdx.x);
+#pragma unroll
+  for (int j = 0; j < SL::HJ; ++j) {
+    const int h = wave + SL::NW * j;
+    const int hc = h < G ? h : 0;
+#pragma unroll
+    for (int i = 0; i < SL::TI; ++i) {
+      if (64 * i < n_tiles) {
+        const int t = lane + 64 * i < n_tiles ? lane + 64 * i : n_tiles - 1;
+        ld.part[j][i] = *reinterpret_cast<const float2*>(lsep + ((size_t)t * G + hc) * 2);
+      }
+    }
+  }
+}
+
+// Threshold of the row: the k-th largest key T and how many keys equal to T
+// are kept (the lowest-index ones).  Leaves the keys of pages [0, Np) in
+// keys[].  select_issue must have been called.  k >= 1.  Block-uniform results.
+template <int NT, int GM>
+__device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<NT, GM>& ld,
+                                 const float* hs, int G, int max_pages, int n_tiles, int Np, int k,
+                                 int n_force_first, int n_force_last, float* page_S_row,
+                                 uint32_t& T_out, int& take_out) {
+  using SL = SelectLoads<NT, GM>;
+  constexpr int NW = NT / 64;
+  constexpr int U = SL::U;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // 1. per-head normalisers L_h from the partials
+#pragma unroll
+  for (int j = 0; j < SL::HJ; ++j) {
+    const int h = wave + NW * j;
+    if (h < G) {
+      float m = -INFINITY, s = 0.f;
+#pragma unroll
+      for (int i = 0; i < SL::TI; ++i)
+        if (64 * i < n_tiles && lane + 64 * i < n_tiles) lse_merge(m, s, ld.part[j][i].x, ld.part[j][i].y);
+      const float M = wave_max_f32(m);
+      const float S = wave_sum_f32(m == -INFINITY ? 0.f : s * __expf(m - M));
+      if (lane == 0) sh.Lh[h] = (S > 0.f || S != S) ? M + __logf(S) : -INFINITY;
+    }
+  }
+  if (tid == 0) sh.n_cand = 0;
+  if (tid < 256) sh.hist[0][tid] = 0;
+  __syncthreads();
+
+  // 2. group aggregate and keys, the next round of scores in flight while one
+  //    is reduced; extremes of the finite keys, counts of the infinite ones
+  const float logG = __logf((float)G);
+  float Lr[GM];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) Lr[h] = h < G ? sh.Lh[h] : 0.f;
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+  int npos = 0, nneg = 0;
+  for (int r0 = 0; r0 < Np; r0 += NT * U) {
+    const bool more = r0 + NT * U < Np;
+    float nx[U][GM];
+    if (more) select_load_round<NT, GM>(nx, hs, G, max_pages, r0 + NT * U + tid);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = r0 + tid + u * NT;
+      if (p >= Np) break;
+      float x[GM];
+      float M = -INFINITY;
+      bool nan = false;
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          x[h] = ld.v[u][h] - Lr[h];
+          nan |= x[h] != x[h];
+          M = fmaxf(M, x[h]);
+        }
+      }
+      float S;
+      if (nan) S = __int_as_float(0x7FC00000);
+      else if (M == -INFINITY) S = -INFINITY;
+      else {
+        float sum = 0.f;
+#pragma unroll
+        for (int h = 0; h < GM; ++h) if (h < G) sum += __expf(x[h] - M);
+        S = M + __logf(sum) - logG;
+      }
+      if (p < n_force_first || p >= Np - n_force_last) S = INFINITY;
+      const uint32_t key = order_key(S);
+      keys[p] = key;
+      if (finite_key(key)) {
+        kmax = key > kmax ? key : kmax;
+        kmin = key < kmin ? key : kmin;
+      }
+      npos += key == kKeyPosInf;
+      nneg += key == kKeyNegInf;
+      if (page_S_row) page_S_row[p] = S;
+    }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < GM; ++h) ld.v[u][h] = nx[u][h];
+    }
+  }
+  kmax = wave_max_u32(kmax);
+  kmin = wave_min_u32(kmin);
+  npos = wave_sum_i32(npos);
+  nneg = wave_sum_i32(nneg);
+  if (lane == 0) { sh.wmax[wave] = kmax; sh.wmin[wave] = kmin; sh.wpos[wave] = npos; sh.wneg[wave] = nneg; }
+  __syncthreads();
+  kmax = sh.wmax[0];
+  kmin = sh.wmin[0];
+  npos = sh.wpos[0];
+  nneg = sh.wneg[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    kmax = sh.wmax[w] > kmax ? sh.wmax[w] : kmax;
+    kmin = sh.wmin[w] < kmin ? sh.wmin[w] : kmin;
+    npos += sh.wpos[w];
+    nneg += sh.wneg[w];
+  }
+
+  // 3. the k-th largest key
+  int rem = k;
+  if (rem <= npos) {                         // only forced (+inf) pages are kept
+    T_out = kKeyPosInf;
+    take_out = rem;
+    return;
+  }
+  rem -= npos;
+  const int nfin = Np - npos - nneg;
+  if (rem > nfin) {                          // every finite page is kept, and some -inf ones
+    T_out = kKeyNegInf;
+    take_out = rem - nfin;
+    return;
+  }
+  if (kmax == kmin) {                        // all finite keys equal
+    T_out = kmax;
+    take_out = rem;
+    return;
+  }
+  const uint32_t diff = kmax ^ kmin;
+  const int hb = 31 - __clz((int)diff);
+  uint32_t pmask = hb >= 31 ? 0u : ~((2u << hb) - 1u);   // common prefix of the finite keys
+  uint32_t prefix = kmax & pmask;
+  int top = hb;                                          // highest bit of the next digit
+  int buf = 0;
+  for (;;) {
+    const int width = top + 1 < 8 ? top + 1 : 8;
+    const int shift = top + 1 - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int p = tid; p < Np; p += NT) {
+      const uint32_t key = keys[p];
+      if ((key & pmask) == prefix && finite_key(key)) atomicAdd(&sh.hist[buf][(key >> shift) & dmask], 1);
+    }
+    const int nb = buf == 2 ? 0 : buf + 1;
+    if (tid < 256) sh.hist[nb][tid] = 0;
+    __syncthreads();
+    // every wave finds the digit itself, so no second barrier is needed:
+    // lane l owns digits 255-4l .. 252-4l (descending); unused digits count 0
+    int c[4], tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { c[i] = sh.hist[buf][255 - 4 * lane - i]; tot += c[i]; }
+    const int incl = wave_incl_sum(tot);
+    const int first = __ffsll((long long)__ballot(incl >= rem)) - 1;
+    int cum = incl - tot, dsel = 252 - 4 * lane, dcnt = c[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (cum + c[i] >= rem) { dsel = 255 - 4 * lane - i; dcnt = c[i]; break; }
+      cum += c[i];
+    }
+    dsel = __builtin_amdgcn_readlane(dsel, first);
+    cum = __builtin_amdgcn_readlane(cum, first);
+    dcnt = __builtin_amdgcn_readlane(dcnt, first);
+    prefix |= (uint32_t)dsel << shift;
+    pmask |= dmask << shift;
+    rem -= cum;
+    buf = nb;
+    top -= width;
+    if (top < 0) {                             // every bit fixed: T is the prefix
+      T_out = prefix;
+      take_out = rem;
+      return;
+    }
+    if (dcnt <= kDirectMax) break;
+  }
+
+  // 4. direct finish: every wave ranks the (at most kDirectMax) keys left in the bin
+  for (int p = tid; p < Np; p += NT) {
+    const uint32_t key = keys[p];
+    if ((key & pmask) == prefix && finite_key(key)) {
+      const int slot = atomicAdd(&sh.n_cand, 1);
+      if (slot < kDirectMax) sh.cand[slot] = key;
+    }
+  }
+  __syncthreads();
+  const int nc = sh.n_cand < kDirectMax ? sh.n_cand : kDirectMax;
+  const uint32_t x = lane < nc ? sh.cand[lane] : 0u;
+  int gt = 0, ge = 0;
+  for (int j = 0; j < nc; ++j) {
+    const uint32_t y = sh.cand[j];
+    gt += y > x;
+    ge += y >= x;
+  }
+  const int first = __ffsll((long long)__ballot(lane < nc && gt < rem && rem <= ge)) - 1;
+  T_out = (uint32_t)__builtin_amdgcn_readlane((int)x, first);
+  take_out = rem - __builtin_amdgcn_readlane(gt, first);
+}
+
+// Calls emit(p, pos) for every kept page p of [0, Np), pos = its rank in
+// ascending page order.  Each thread walks a contiguous run of pages.
+// Uses sh.wave_tot once (no barrier after it).
+template <int NT, typename Emit>
+__device__ __forceinline__ void select_compact(SelectLds<NT>& sh, const uint32_t* keys, int Np, uint32_t T,
+                                               int take, Emit&& emit) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int chunk = (Np + NT - 1) / NT;
+  const int lo = tid * chunk;
+  const int hi = lo + chunk < Np ? lo + chunk : Np;
+  int n_gt = 0, n_eq = 0;
+  for (int p = lo; p < hi; ++p) {
+    const uint32_t key = keys[p];
+    n_gt += key > T;
+    n_eq += key == T;
+  }
+  // one scan of both counts (each total is at most Np < 2^15)
+  const int v = (n_gt << 16) | n_eq;
+  const int incl = wave_incl_sum(v);
+  if (lane == 63) sh.wave_tot[wave] = incl;
+  __syncthreads();
+  int before = incl - v;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+    if (w < wave) before += sh.wave_tot[w];
+  const int gt_before = before >> 16, eq_before = before & 0xFFFF;
+  int take_eq = take - eq_before;
+  take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
+  int pos = gt_before + (eq_before < take ? eq_before : take);
+  int taken = 0;
+  for (int p = lo; p < hi; ++p) {
+    const uint32_t key = keys[p];
+    if (key > T || (key == T && taken < take_eq)) {
+      emit(p, pos++);
+      taken += key == T;
+    }
+  }
+}
+
+}  // namespace kvs

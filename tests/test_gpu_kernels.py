@@ -105,6 +105,87 @@ def test_forced_pages_and_fixed_k(hz):
             assert set(forced) <= set(sel[b, g, :20].tolist())
 
 
+def _tile_partials(hs, Np, n_tiles, tile=64):
+    """(max, sum exp(x - max)) of every 64-page tile and head over the finite
+    scores of pages < Np: the per-block partials the score kernel leaves."""
+    rows, G, _ = hs.shape
+    part = np.zeros((rows, n_tiles, G, 2), np.float32)
+    for r in range(rows):
+        for t in range(n_tiles):
+            for h in range(G):
+                x = hs[r, h, t * tile:min((t + 1) * tile, Np[r])].astype(np.float64)
+                x = x[np.isfinite(x)]
+                if x.size == 0:
+                    part[r, t, h] = (-np.inf, 0.0)
+                else:
+                    m = x.max()
+                    part[r, t, h] = (m, np.exp(x - m).sum())
+    return part
+
+
+def _crafted_scores(G, max_pages, rng):
+    """Rows that reach every branch of the selector: heavy exact ties, a wide
+    range, keys that differ only in the last mantissa bits, mostly -inf, NaN
+    scores, all equal, an empty row and a short one."""
+    Np = np.array([max_pages, 577, 600, 590, 512, 333, 0, 3])
+    hs = np.full((8, G, max_pages), -np.inf, np.float32)
+    hs[0, :, :Np[0]] = rng.integers(0, 4, (G, Np[0]))
+    hs[1, :, :Np[1]] = rng.standard_normal((G, Np[1])) * 30
+    base = np.float32(5.0)
+    steps = (np.arange(Np[2]) % 37).astype(np.float32)
+    hs[2, :, :Np[2]] = base + steps * np.float32(2.0 ** -20)
+    fin = rng.choice(Np[3], 5, replace=False)
+    hs[3, :, fin] = rng.standard_normal((5, G))
+    hs[4, :, :Np[4]] = rng.standard_normal((G, Np[4]))
+    hs[4, 1, rng.choice(Np[4], 40, replace=False)] = np.nan
+    hs[5, :, :Np[5]] = 2.5
+    hs[7, :, :Np[7]] = rng.standard_normal((G, Np[7]))
+    return hs, Np
+
+
+def _expected_selection(S, Np, k):
+    """Top k of float32 scores by (S descending, page ascending), NaN as -inf."""
+    x = np.where(np.isnan(S[:Np]), -np.inf, S[:Np]).astype(np.float64)
+    order = np.lexsort((np.arange(Np), -x))
+    return np.sort(order[:k])
+
+
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_selection_branches_exact(G):
+    """Selection on crafted head scores, checked bit-exactly against an
+    exhaustive sort of the kernel's own float32 S (the order is unique given S)."""
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    announce(f"crafted selection G={G}")
+    rng = np.random.default_rng(17 + G)
+    max_pages = 600
+    n_tiles = (max_pages + 63) // 64
+    L = kv.layout(G, 1, 128, 16, 4, "bf16")
+    hs, Np = _crafted_scores(G, max_pages, rng)
+    part = _tile_partials(hs, Np, n_tiles)
+    seq = torch.tensor(Np * 16 - (Np > 0) * 5, dtype=torch.int32, device="cuda")   # ragged last page
+    hs_d = torch.from_numpy(hs).cuda()
+    part_d = torch.from_numpy(part).cuda()
+    cases = [(0.1, 0, 0, 0), (0.0, 7, 0, 0), (0.0, 5, 6, 4), (0.0, 12, 6, 4), (1.0, 0, 0, 0)]
+    for keep, k_fixed, nff, nfl in cases:
+        k_max = oracle.selection_count(max_pages, keep, k_fixed)
+        sel = torch.full((8, k_max), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(8, dtype=torch.int32, device="cuda")
+        S = torch.zeros((8, max_pages), dtype=torch.float32, device="cuda")
+        kv.page_topk(L, hs_d, part_d, seq, max_pages, keep, k_fixed, sel, cnt, n_force_first=nff,
+                     n_force_last=nfl, page_S=S)
+        torch.cuda.synchronize()
+        S_h, sel_h, cnt_h = S.cpu().numpy(), sel.cpu().numpy(), cnt.cpu().numpy()
+        for r in range(8):
+            k = oracle.selection_count(int(Np[r]), keep, k_fixed)
+            assert cnt_h[r] == k, (keep, k_fixed, r)
+            if Np[r] > 0:
+                forced = [p for p in range(Np[r]) if p < nff or p >= Np[r] - nfl]
+                assert np.all(np.isposinf(S_h[r, forced]))
+            exp = _expected_selection(S_h[r], int(Np[r]), k)
+            assert np.array_equal(sel_h[r, :k], exp), (keep, k_fixed, nff, nfl, r)
+            assert np.all(sel_h[r, k:] == -1)
+
+
 # ---------------------------------------------------------------- attention
 
 @pytest.mark.parametrize("name", list(SMALL))
