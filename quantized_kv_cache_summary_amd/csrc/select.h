@@ -53,7 +53,7 @@ struct SelectLds {
   int wave_tot[NW];
   uint32_t wmax[NW], wmin[NW];
   int wpos[NW], wneg[NW];
-  uint32_t cand[kDirectMax];
+  alignas(16) uint32_t cand[kDirectMax];
   int n_cand;
 };
 
@@ -108,6 +108,21 @@ __device__ __forceinline__ void select_issue(SelectLoads<NT, GM>& ld, const floa
   }
 }
 
+// Calls f(key) for the keys of pages [0, Np) this thread owns (p = tid + j NT).
+// Reads are issued KB at a time before any is used, so a pass costs a few LDS
+// round trips rather than one per key.
+template <int NT, typename F>
+__device__ __forceinline__ void for_own_keys(const uint32_t* keys, int Np, F&& f) {
+  constexpr int KB = 4;
+  for (int p0 = threadIdx.x; p0 < Np; p0 += KB * NT) {
+    uint32_t kv[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) kv[i] = p0 + i * NT < Np ? keys[p0 + i * NT] : kKeyNegInf;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) f(kv[i]);
+  }
+}
+
 // Threshold of the row: the k-th largest key T and how many keys equal to T
 // are kept (the lowest-index ones).  Leaves the keys of pages [0, Np) in
 // keys[].  select_issue must have been called.  k >= 1.  Block-uniform results.
@@ -137,6 +152,7 @@ __device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<
     }
   }
   if (tid == 0) sh.n_cand = 0;
+  if (tid < kDirectMax) sh.cand[tid] = 0u;   // below every finite key
   if (tid < 256) sh.hist[0][tid] = 0;
   __syncthreads();
 
@@ -241,10 +257,9 @@ __device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<
     const int width = top + 1 < 8 ? top + 1 : 8;
     const int shift = top + 1 - width;
     const uint32_t dmask = (1u << width) - 1u;
-    for (int p = tid; p < Np; p += NT) {
-      const uint32_t key = keys[p];
+    for_own_keys<NT>(keys, Np, [&](uint32_t key) {
       if ((key & pmask) == prefix && finite_key(key)) atomicAdd(&sh.hist[buf][(key >> shift) & dmask], 1);
-    }
+    });
     const int nb = buf == 2 ? 0 : buf + 1;
     if (tid < 256) sh.hist[nb][tid] = 0;
     __syncthreads();
@@ -278,21 +293,21 @@ __device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<
   }
 
   // 4. direct finish: every wave ranks the (at most kDirectMax) keys left in the bin
-  for (int p = tid; p < Np; p += NT) {
-    const uint32_t key = keys[p];
+  for_own_keys<NT>(keys, Np, [&](uint32_t key) {
     if ((key & pmask) == prefix && finite_key(key)) {
       const int slot = atomicAdd(&sh.n_cand, 1);
       if (slot < kDirectMax) sh.cand[slot] = key;
     }
-  }
+  });
   __syncthreads();
   const int nc = sh.n_cand < kDirectMax ? sh.n_cand : kDirectMax;
   const uint32_t x = lane < nc ? sh.cand[lane] : 0u;
   int gt = 0, ge = 0;
-  for (int j = 0; j < nc; ++j) {
-    const uint32_t y = sh.cand[j];
-    gt += y > x;
-    ge += y >= x;
+  // four slots per read; unused slots hold 0, which no finite key is below
+  for (int j = 0; j < nc; j += 4) {
+    const uint4 y = *reinterpret_cast<const uint4*>(&sh.cand[j]);
+    gt += (y.x > x) + (y.y > x) + (y.z > x) + (y.w > x);
+    ge += (y.x >= x) + (y.y >= x) + (y.z >= x) + (y.w >= x);
   }
   const int first = __ffsll((long long)__ballot(lane < nc && gt < rem && rem <= ge)) - 1;
   T_out = (uint32_t)__builtin_amdgcn_readlane((int)x, first);
@@ -312,10 +327,15 @@ __device__ __forceinline__ void select_compact(SelectLds<NT>& sh, const uint32_t
   const int lo = tid * chunk;
   const int hi = lo + chunk < Np ? lo + chunk : Np;
   int n_gt = 0, n_eq = 0;
-  for (int p = lo; p < hi; ++p) {
-    const uint32_t key = keys[p];
-    n_gt += key > T;
-    n_eq += key == T;
+  for (int p0 = lo; p0 < hi; p0 += 4) {
+    uint32_t kv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kv[i] = p0 + i < hi ? keys[p0 + i] : 0u;   // 0: below every key
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      n_gt += kv[i] > T;
+      n_eq += kv[i] == T;
+    }
   }
   // one scan of both counts (each total is at most Np < 2^15)
   const int v = (n_gt << 16) | n_eq;
@@ -331,11 +351,16 @@ __device__ __forceinline__ void select_compact(SelectLds<NT>& sh, const uint32_t
   take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
   int pos = gt_before + (eq_before < take ? eq_before : take);
   int taken = 0;
-  for (int p = lo; p < hi; ++p) {
-    const uint32_t key = keys[p];
-    if (key > T || (key == T && taken < take_eq)) {
-      emit(p, pos++);
-      taken += key == T;
+  for (int p0 = lo; p0 < hi; p0 += 4) {
+    uint32_t kv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kv[i] = p0 + i < hi ? keys[p0 + i] : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kv[i] > T || (kv[i] == T && taken < take_eq)) {
+        emit(p0 + i, pos++);
+        taken += kv[i] == T;
+      }
     }
   }
 }
