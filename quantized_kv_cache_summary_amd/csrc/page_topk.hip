@@ -7,38 +7,38 @@
 
 namespace kvs {
 
-template <int GM>
-__global__ __launch_bounds__(kTopkThreads) void page_topk_kernel(
+template <int GM, int NT>
+__global__ __launch_bounds__(NT) void page_topk_kernel(
     const float* __restrict__ head_scores, const float* __restrict__ lse_partial,
     const int32_t* __restrict__ seq_lens, int Hkv, int G, int P, int max_pages, int n_tiles,
     float keep, int k_fixed, int n_force_first, int n_force_last, int32_t* __restrict__ sel,
     int32_t* __restrict__ sel_count, int k_max, float* __restrict__ page_S) {
   extern __shared__ uint32_t keys[];   // max_pages
-  __shared__ SelectLds<kTopkThreads> sh;
+  __shared__ SelectLds<NT> sh;
 
   const int row = blockIdx.x;
   const int b = row / Hkv;
   const int tid = threadIdx.x;
   const float* hs = head_scores + (size_t)row * G * max_pages;
   const float* lsep = lse_partial + (size_t)row * n_tiles * G * 2;
-  SelectLoads<kTopkThreads, GM> ld;
-  if (max_pages > 0) select_issue<kTopkThreads, GM>(ld, hs, lsep, G, max_pages, n_tiles);
+  SelectLoads<NT, GM> ld;
+  if (max_pages > 0) select_issue<NT, GM>(ld, hs, lsep, G, max_pages, n_tiles);
 
   const int L = seq_lens[b];
   int Np = L > 0 ? (L + P - 1) / P : 0;
   Np = Np < max_pages ? Np : max_pages;
   const int k = selection_count(Np, keep, k_fixed);
   int32_t* out = sel + (size_t)row * k_max;
-  for (int i = k + tid; i < k_max; i += kTopkThreads) out[i] = -1;
+  for (int i = k + tid; i < k_max; i += NT) out[i] = -1;
   if (tid == 0) sel_count[row] = k;
   if (k == 0) return;
 
   uint32_t T;
   int take;
-  select_threshold<kTopkThreads, GM>(sh, keys, ld, hs, G, max_pages, n_tiles, Np, k, n_force_first,
+  select_threshold<NT, GM>(sh, keys, ld, hs, G, max_pages, n_tiles, Np, k, n_force_first,
                                      n_force_last, page_S ? page_S + (size_t)row * max_pages : nullptr,
                                      T, take);
-  select_compact<kTopkThreads>(sh, keys, Np, T, take, [&](int p, int pos) {
+  select_compact<NT>(sh, keys, Np, T, take, [&](int p, int pos) {
     if (pos < k) out[pos] = p;
   });
 }
@@ -50,13 +50,15 @@ hipError_t launch_page_topk(const kv_layout& L, const float* head_scores, const 
   const int G = L.num_q_heads / L.num_kv_heads;
   const int rows = B * L.num_kv_heads;
   const size_t lds = (size_t)(max_pages > 0 ? max_pages : 1) * sizeof(uint32_t);
-#define KVS_TOPK(GM_) hipLaunchKernelGGL((page_topk_kernel<GM_>), dim3(rows), dim3(kTopkThreads), lds, st, \
+  // long rows: twice the threads, so twice the head scores are in flight at once
+#define KVS_TOPK(GM_, NT_) hipLaunchKernelGGL((page_topk_kernel<GM_, NT_>), dim3(rows), dim3(NT_), lds, st,  \
                      head_scores, lse_partial, seq_lens, L.num_kv_heads, G, L.page_size, max_pages,     \
                      score_tiles(max_pages), keep, k_fixed, n_force_first, n_force_last, sel,           \
                      sel_count, k_max, page_S)
-  if (G <= 4) KVS_TOPK(4);
-  else if (G <= 8) KVS_TOPK(8);
-  else KVS_TOPK(16);
+  const bool wide = max_pages > kTopkWideFrom;
+  if (G <= 4) { if (wide) KVS_TOPK(4, 2 * kTopkThreads); else KVS_TOPK(4, kTopkThreads); }
+  else if (G <= 8) { if (wide) KVS_TOPK(8, 2 * kTopkThreads); else KVS_TOPK(8, kTopkThreads); }
+  else { if (wide) KVS_TOPK(16, 2 * kTopkThreads); else KVS_TOPK(16, kTopkThreads); }
 #undef KVS_TOPK
   return hipGetLastError();
 }

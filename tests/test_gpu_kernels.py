@@ -150,14 +150,14 @@ def _expected_selection(S, Np, k):
     return np.sort(order[:k])
 
 
-@pytest.mark.parametrize("G", [4, 8, 16])
-def test_selection_branches_exact(G):
+@pytest.mark.parametrize("G,max_pages", [(4, 600), (8, 600), (16, 600), (4, 5000), (16, 5000)])
+def test_selection_branches_exact(G, max_pages):
     """Selection on crafted head scores, checked bit-exactly against an
-    exhaustive sort of the kernel's own float32 S (the order is unique given S)."""
+    exhaustive sort of the kernel's own float32 S (the order is unique given S).
+    Rows over 4096 pages take the selector's wide-block variant."""
     from quantized_kv_cache_summary_amd import kvsparse as kv
-    announce(f"crafted selection G={G}")
+    announce(f"crafted selection G={G} max_pages={max_pages}")
     rng = np.random.default_rng(17 + G)
-    max_pages = 600
     n_tiles = (max_pages + 63) // 64
     L = kv.layout(G, 1, 128, 16, 4, "bf16")
     hs, Np = _crafted_scores(G, max_pages, rng)
