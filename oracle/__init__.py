@@ -31,6 +31,8 @@ from .rounding import round_bf16, round_fp16_sat, as_float32
 from .paging import page_token_counts, num_pages, logical_page_tokens
 from .summary import summarize_page, store_summary, summarize_and_store
 from .score import page_score, exact_page_logmass
+from .basis import (row_basis, row_covariance, store_basis, basis_page_stats, store_basis_summary,
+                    page_score_basis)
 from .select import group_aggregate, selection_count, select_pages
 from .attention import sparse_attention, dense_attention
 from .codec import (
@@ -45,6 +47,8 @@ __all__ = [
     "page_token_counts", "num_pages", "logical_page_tokens",
     "summarize_page", "store_summary", "summarize_and_store",
     "page_score", "exact_page_logmass",
+    "row_basis", "row_covariance", "store_basis", "basis_page_stats", "store_basis_summary",
+    "page_score_basis",
     "group_aggregate", "selection_count", "select_pages",
     "sparse_attention", "dense_attention",
     "BITS_OF_TIER", "TIER_NATIVE", "TIER_I8", "TIER_I4", "TIER_I2", "TIER_B1",

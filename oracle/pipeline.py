@@ -14,6 +14,7 @@ import numpy as np
 from .paging import num_pages, page_token_counts
 from .summary import summarize_and_store
 from .score import page_score
+from .basis import row_basis, store_basis, basis_page_stats, store_basis_summary, page_score_basis
 from .select import group_aggregate, selection_count, select_pages
 from .attention import sparse_attention
 from .codec import TIER_NATIVE, encode_vector, decode_vector
@@ -33,6 +34,27 @@ def build_row_summaries(keys, seq_len, page_size, rank):
     return mu, w, log_n
 
 
+def build_row_basis_summaries(keys, seq_len, page_size, rank, basis=None):
+    """Shared-basis stored summaries of every logical page of one row.
+
+    basis: the stored (r', d) basis to use; by default the row's own
+    (row_basis over its seq_len valid keys, stored as float32).
+    Returns (U, mu, lam, log_n).
+    """
+    keys = np.asarray(keys, dtype=np.float64)[:seq_len]
+    U = store_basis(row_basis(keys, rank)) if basis is None else np.asarray(basis, dtype=np.float64)
+    npg = num_pages(seq_len, page_size)
+    d = keys.shape[1]
+    mu = np.zeros((npg, d))
+    lam = np.zeros((npg, U.shape[0]))
+    log_n = np.zeros(npg)
+    for p in range(npg):
+        lo = p * page_size
+        mu[p], lam[p], log_n[p] = store_basis_summary(
+            *basis_page_stats(keys[lo:min(lo + page_size, seq_len)], U))
+    return U, mu, lam, log_n
+
+
 def reconstruct_tiers(x, seq_len, page_size, page_tiers):
     """Encode and decode every token vector of the non-native pages (float64 out)."""
     x = np.array(x, dtype=np.float64)
@@ -49,19 +71,28 @@ def reconstruct_tiers(x, seq_len, page_size, page_tiers):
 
 
 def decode_row(q, keys, values, seq_len, page_size, rank, tau, keep_frac=0.0, k_fixed=0,
-               n_force_first=0, n_force_last=0, page_tiers=None, summary=None):
+               n_force_first=0, n_force_last=0, page_tiers=None, summary=None, shared_basis=False,
+               basis=None):
     """Full step for one row.
 
     q: (G, d); keys, values: (>= seq_len, d) 16-bit values in logical token order.
-    summary: optional stored (mu, w, log_n) to score from; built here otherwise.
+    summary: optional stored summary to score from -- (mu, w, log_n) per page,
+    or (U, mu, lam, log_n) with shared_basis -- built here otherwise (with
+    shared_basis, from `basis` if given, else the row's own basis).
     """
     keys = np.asarray(keys, dtype=np.float64)[:seq_len]
     values = np.asarray(values, dtype=np.float64)[:seq_len]
-    if summary is None:
-        summary = build_row_summaries(keys, seq_len, page_size, rank)
-    mu, w, log_n = summary
     npg = num_pages(seq_len, page_size)
-    s_hat = page_score(q, mu[:npg], w[:npg], log_n[:npg], tau)
+    if shared_basis:
+        if summary is None:
+            summary = build_row_basis_summaries(keys, seq_len, page_size, rank, basis)
+        U, mu, w, log_n = summary                # w holds the per-page variances here
+        s_hat = page_score_basis(q, mu[:npg], w[:npg], U, log_n[:npg], tau)
+    else:
+        if summary is None:
+            summary = build_row_summaries(keys, seq_len, page_size, rank)
+        mu, w, log_n = summary
+        s_hat = page_score(q, mu[:npg], w[:npg], log_n[:npg], tau)
     S = group_aggregate(s_hat) if npg else np.zeros(0)
     k = selection_count(npg, keep_frac, k_fixed)
     sel = select_pages(S, k, n_force_first, n_force_last) if npg else np.zeros(0, np.int64)

@@ -27,7 +27,7 @@ import numpy as np
 
 SEED = 2026
 
-T_Q, T_K, T_V, T_HOT, T_TABLE, T_TIER, T_SEL, T_SUMMARY, T_CENTERS, T_HOTBUF = range(10)
+T_Q, T_K, T_V, T_HOT, T_TABLE, T_TIER, T_SEL, T_SUMMARY, T_CENTERS, T_HOTBUF, T_BASIS = range(11)
 
 TIER_NAMES = ("native", "int8", "int4", "int2", "1bit")
 
@@ -275,6 +275,32 @@ def synthetic_summary(w: Workload, layer: int = 0, lam=(12.0, 10.0, 9.0, 8.0, 7.
                 rec[b, g, hp, 0] += np.float32(w.plant_scale) * plant_direction(w, layer, b, g).astype(np.float32)
     n_valid = np.full((w.B, w.Np), w.P, dtype=np.int32)
     return bf16_bits(rec), n_valid
+
+
+def synthetic_basis_summary(w: Workload, layer: int = 0, lam_scale=(3.0, 2.0, 1.5, 1.2, 1.0, 0.9, 0.8, 0.7)):
+    """Random stored shared-basis summaries, for score/select tests.
+
+    Returns (basis float32 [B, Hkv, rank, d] with orthonormal rows before
+    rounding, mu uint16 bf16 bits [B, Hkv, Np, d] in logical page order,
+    lam float32 [B, Hkv, Np, rank] >= 0, n_valid int32 [B, Np]).  mu is drawn as
+    in synthetic_summary (planted pages carry a mean along their group's query
+    direction); lam_j = lam_scale_j * (chi-square with P degrees of freedom) / P."""
+    rng = rng_for(w, layer, 0, 0, T_BASIS)
+    basis = np.empty((w.B, w.Hkv, w.rank, w.d), dtype=np.float32)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            Q, _ = np.linalg.qr(rng.standard_normal((w.d, w.rank)))
+            basis[b, g] = Q.T.astype(np.float32)
+    mu = rng.standard_normal((w.B, w.Hkv, w.Np, w.d), dtype=np.float32) / np.float32(math.sqrt(w.P))
+    for b in range(w.B):
+        hp = hot_pages(w, layer, b)
+        if hp.size:
+            for g in range(w.Hkv):
+                mu[b, g, hp] += np.float32(w.plant_scale) * plant_direction(w, layer, b, g).astype(np.float32)
+    scale = np.array([lam_scale[j % len(lam_scale)] for j in range(w.rank)], dtype=np.float32)
+    lam = (rng.chisquare(w.P, (w.B, w.Hkv, w.Np, w.rank)).astype(np.float32) / np.float32(w.P)) * scale
+    n_valid = np.full((w.B, w.Np), w.P, dtype=np.int32)
+    return basis, bf16_bits(mu), lam.astype(np.float32), n_valid
 
 
 # ---------------------------------------------------------------- whole pools

@@ -2,7 +2,8 @@
 
 A sanity check, not parity: on the tiny workload (4 planted high-mass pages per
 sequence, keys = 3 u_g + noise) the oracle's top-8 pages per KV head contain
-every planted page; and the generator reproduces any row on its own.
+every planted page, with per-page summaries and with the shared-basis ones; and
+the generator reproduces any row on its own.
 """
 
 import numpy as np
@@ -22,6 +23,18 @@ def test_planted_pages_are_selected_tiny():
             V = wl.row_values(w, 0, b, g)
             r = decode_row(q, K, V, w.ctx, w.P, w.rank, w.tau, k_fixed=w.k_fixed)
             assert r["k"] == 8
+            assert hp <= set(r["sel"].tolist())
+            assert abs(np.exp(r["S"]).sum() - 1) < 1e-12
+
+
+def test_planted_pages_are_selected_tiny_shared_basis():
+    w = wl.WORKLOADS["tiny"]
+    for b in range(w.B):
+        hp = set(wl.hot_pages(w, 0, b).tolist())
+        for g in range(w.Hkv):
+            q = wl.queries(w, 0, b, g)
+            r = decode_row(q, wl.row_keys(w, 0, b, g), wl.row_values(w, 0, b, g), w.ctx, w.P, w.rank,
+                           w.tau, k_fixed=w.k_fixed, shared_basis=True)
             assert hp <= set(r["sel"].tolist())
             assert abs(np.exp(r["S"]).sum() - 1) < 1e-12
 
