@@ -5,7 +5,9 @@
  * One decode step for one layer is
  *     kv_page_score  -> kv_page_topk  -> kv_sparse_decode_attn
  * and, when a page is appended, kv_summary_build (and kv_pack_tier for pages
- * stored in a packed low-bit tier).
+ * stored in a packed low-bit tier).  With shared-basis summaries the score is
+ * kv_page_score_basis, the basis comes from kv_basis_build at prefill and the
+ * page statistics from kv_summary_build_basis.
  *
  * Method sources (no formulas are published; each call states the reading it
  * implements):
@@ -159,6 +161,53 @@ int kv_page_score(const kv_layout* layout, const void* q, const void* summary,
                   float* head_scores, float* lse_partial, void* stream);
 
 size_t kv_page_score_partial_size(const kv_layout* layout, int32_t B, int32_t max_pages);
+
+/* ---------------------------------------------------------------------------
+ * Shared-basis summaries (AMASS page, "What is in the box" item 1: the quad
+ * summary keeps only r' eigenvalues per page).  The r' directions are shared by
+ * every page of a row; a page keeps its mean and the variances of its keys
+ * along them.  Record: 2d + 4R + 4 bytes per (page, KV head) against
+ * 2(1+R)d + 4 for kv_summary_build's per-page directions.
+ *
+ * kv_basis_build -- the row basis, at prefill.  For every row, over the keys of
+ * its tokens t < seq_lens[b] (clamped to max_pages * P) in k16 through
+ * block_table:
+ *   C = population covariance of those keys;
+ *   basis[row][j] = unit eigenvector of C for its j-th largest eigenvalue
+ *   (j < R; cyclic Jacobi in float32), its largest-magnitude entry positive
+ *   (the first such entry on ties).
+ * basis: float32 [B][Hkv][R][d].  Eigenvectors inside a degenerate eigenspace
+ * are arbitrary.  A row with no tokens gets the first R unit vectors.
+ * ws/ws_bytes: kv_basis_build_workspace_size() (no state kept between calls).
+ * --------------------------------------------------------------------------- */
+int kv_basis_build(const kv_layout* layout, const void* k16, const int32_t* block_table,
+                   const int32_t* seq_lens, int32_t B, int32_t max_pages, float* basis,
+                   void* ws, size_t ws_bytes, void* stream);
+
+size_t kv_basis_build_workspace_size(const kv_layout* layout, int32_t B, int32_t max_pages);
+
+/* kv_summary_build_basis -- page statistics in the row basis, when pages are
+ * appended.  For every entry i, (b, p) = (entries[2i], entries[2i+1]), and KV
+ * head g, over the first n_valid[i] keys of the page (as kv_summary_build):
+ *   mu    = mean key (float32), stored bfloat16 (round to nearest even);
+ *   lam_j = mean of (u_j . (k - mu))^2 with u_j = basis[b][g][j], float32;
+ *   log_n = log(n), float32 [B][max_pages].
+ * mu: bfloat16 [B][Hkv][max_pages][d] and lam: float32 [B][Hkv][max_pages][R],
+ * both in LOGICAL page order.  A page with 0 valid tokens gets zeros and
+ * log_n = -inf.  Entries must be distinct within a call. */
+int kv_summary_build_basis(const kv_layout* layout, const void* k16, const int32_t* block_table,
+                           int32_t max_pages, const int32_t* entries, const int32_t* n_valid,
+                           int32_t n, const float* basis, void* mu, float* lam, float* log_n,
+                           void* stream);
+
+/* kv_page_score_basis -- quad page score from shared-basis summaries:
+ *   s[b][g][h][p] = log_n[b][p] + tau q.mu + (tau^2/2) sum_j lam_j (q.u_j)^2
+ * with the layouts above; outputs exactly as kv_page_score (head_scores,
+ * lse_partial of kv_page_score_partial_size()), so kv_page_topk follows
+ * unchanged.  basis must be 16-byte aligned. */
+int kv_page_score_basis(const kv_layout* layout, const void* q, const void* mu, const float* lam,
+                        const float* basis, const float* log_n, const int32_t* seq_lens, int32_t B,
+                        int32_t max_pages, float* head_scores, float* lse_partial, void* stream);
 
 /* ---------------------------------------------------------------------------
  * kv_page_topk -- per row, select k pages (AMASS page, "Quickstart": budget,

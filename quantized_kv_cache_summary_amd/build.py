@@ -25,6 +25,8 @@ SOURCES = {
     "page_topk.hip": [],
     "sparse_attn.hip": [],
     "summary_build.hip": [],
+    "basis_build.hip": [],
+    "score_basis.hip": [],
     "codec.hip": ["-ffp-contract=off"],
 }
 

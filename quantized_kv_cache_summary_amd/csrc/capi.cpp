@@ -132,6 +132,58 @@ int kv_page_score(const kv_layout* L, const void* q, const void* summary, const 
                                          head_scores, lse_partial, (hipStream_t)stream));
 }
 
+size_t kv_basis_build_workspace_size(const kv_layout* L, int32_t B, int32_t max_pages) {
+  if (check_layout(L) || B <= 0 || max_pages <= 0) return 0;
+  return kvs::basis_workspace_bytes(B * L->num_kv_heads, max_pages, L->head_dim);
+}
+
+int kv_basis_build(const kv_layout* L, const void* k16, const int32_t* block_table, const int32_t* seq_lens,
+                   int32_t B, int32_t max_pages, float* basis, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
+  if (B == 0) return KV_OK;
+  if (max_pages == 0 || !k16 || !block_table || !seq_lens || !basis) return KV_ERR_INVALID_ARG;
+  if (!aligned16(k16)) return KV_ERR_INVALID_ARG;
+  if ((int64_t)B * L->num_kv_heads > 65535) return KV_ERR_UNSUPPORTED;
+  if ((int64_t)max_pages * L->page_size > 0x3FFFFFFF) return KV_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < kv_basis_build_workspace_size(L, B, max_pages)) return KV_ERR_WORKSPACE;
+  return from_hip(kvs::launch_basis_build(*L, k16, block_table, seq_lens, B, max_pages, basis, (float*)ws,
+                                          (hipStream_t)stream));
+}
+
+int kv_summary_build_basis(const kv_layout* L, const void* k16, const int32_t* block_table, int32_t max_pages,
+                           const int32_t* entries, const int32_t* n_valid, int32_t n, const float* basis,
+                           void* mu, float* lam, float* log_n, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (n < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
+  if (n == 0) return KV_OK;
+  if (max_pages == 0) return KV_ERR_INVALID_ARG;
+  if (!k16 || !block_table || !entries || !n_valid || !basis || !mu || !lam || !log_n) return KV_ERR_INVALID_ARG;
+  if (!aligned16(k16)) return KV_ERR_INVALID_ARG;
+  if ((int64_t)n * L->num_kv_heads > 0x7FFFFFFF) return KV_ERR_UNSUPPORTED;
+  return from_hip(kvs::launch_summary_build_basis(*L, k16, block_table, max_pages, entries, n_valid, n, basis,
+                                                  mu, lam, log_n, (hipStream_t)stream));
+}
+
+int kv_page_score_basis(const kv_layout* L, const void* q, const void* mu, const float* lam, const float* basis,
+                        const float* log_n, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                        float* head_scores, float* lse_partial, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
+  if (B == 0 || max_pages == 0) return KV_OK;
+  if (!q || !mu || !lam || !basis || !log_n || !seq_lens || !head_scores || !lse_partial)
+    return KV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(mu) || !aligned16(basis)) return KV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lam) & 3u) || (reinterpret_cast<uintptr_t>(log_n) & 3u))
+    return KV_ERR_INVALID_ARG;
+  if ((int64_t)B * L->num_kv_heads > 65535) return KV_ERR_UNSUPPORTED;
+  return from_hip(kvs::launch_page_score_basis(*L, q, mu, lam, basis, log_n, seq_lens, B, max_pages,
+                                               scale_of(L), head_scores, lse_partial, (hipStream_t)stream));
+}
+
 size_t kv_page_topk_workspace_size(const kv_layout* L, int32_t B, int32_t max_pages) {
   (void)L; (void)B; (void)max_pages;
   return 0;

@@ -28,6 +28,28 @@ inline size_t attn_workspace_bytes(int rows, int splits, int G, int d) {
   return attn_partial_floats(rows, splits, G, d) * sizeof(float) + (size_t)rows * sizeof(unsigned);
 }
 
+// Shared-basis build: covariance statistics per (row, chunk of pages), then
+// one merge + eigen block per row.  Workspace: [rows][chunks][1 + d + d*d] floats.
+constexpr int kBasisChunkPages = 256;
+inline int basis_chunks(int max_pages) { return (max_pages + kBasisChunkPages - 1) / kBasisChunkPages; }
+inline size_t basis_workspace_bytes(int rows, int max_pages, int d) {
+  return (size_t)rows * basis_chunks(max_pages) * (size_t)(1 + d + d * d) * sizeof(float);
+}
+
+hipError_t launch_basis_build(const kv_layout& L, const void* k16, const int32_t* block_table,
+                              const int32_t* seq_lens, int B, int max_pages, float* basis, float* part,
+                              hipStream_t st);
+
+hipError_t launch_summary_build_basis(const kv_layout& L, const void* k16, const int32_t* block_table,
+                                      int max_pages, const int32_t* entries, const int32_t* n_valid, int n,
+                                      const float* basis, void* mu, float* lam, float* log_n,
+                                      hipStream_t st);
+
+hipError_t launch_page_score_basis(const kv_layout& L, const void* q, const void* mu, const float* lam,
+                                   const float* basis, const float* log_n, const int32_t* seq_lens, int B,
+                                   int max_pages, float tau, float* head_scores, float* lse_partial,
+                                   hipStream_t st);
+
 hipError_t launch_summary_build(const kv_layout& L, const void* k16, const int32_t* block_table,
                                 int max_pages, const int32_t* entries, const int32_t* n_valid, int n,
                                 void* summary, float* log_n, hipStream_t st);

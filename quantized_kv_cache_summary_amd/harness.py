@@ -82,14 +82,32 @@ class DeviceLayer:
         del kbits
         self.v16 = None if host_v else to_device16(vbits, w.dtype, device)
         del vbits
-        # summaries in logical page order per (sequence, KV head)
-        self.summary = torch.empty((w.B, w.Hkv, w.Np, (1 + w.rank) * w.d), dtype=torch.bfloat16, device=device)
+        # summaries in logical page order per (sequence, KV head): per-page
+        # directions ("build", "synthetic") or a shared row basis with per-page
+        # means and variances ("basis_build", "basis_synthetic")
+        self.summary = self.basis = self.mu = self.lam = None
         self.log_n = torch.empty((w.B, w.Np), dtype=torch.float32, device=device)
+        if summaries in ("build", "synthetic"):
+            self.summary = torch.empty((w.B, w.Hkv, w.Np, (1 + w.rank) * w.d), dtype=torch.bfloat16,
+                                       device=device)
+        elif summaries in ("basis_build", "basis_synthetic"):
+            self.basis = torch.empty((w.B, w.Hkv, w.rank, w.d), dtype=torch.float32, device=device)
+            self.mu = torch.empty((w.B, w.Hkv, w.Np, w.d), dtype=torch.bfloat16, device=device)
+            self.lam = torch.empty((w.B, w.Hkv, w.Np, w.rank), dtype=torch.float32, device=device)
         if summaries == "build":
             self.build_summaries()
         elif summaries == "synthetic":
             rec, n_valid = wl.synthetic_summary(w, layer)
             self.summary.copy_(to_device16(rec.reshape(w.B, w.Hkv, w.Np, -1), "bf16", device))
+            self.log_n.copy_(torch.from_numpy(np.log(n_valid.astype(np.float64)).astype(np.float32)))
+        elif summaries == "basis_build":
+            self.build_basis()
+            self.build_basis_summaries()
+        elif summaries == "basis_synthetic":
+            U, mu_bits, lam, n_valid = wl.synthetic_basis_summary(w, layer)
+            self.basis.copy_(torch.from_numpy(U))
+            self.mu.copy_(to_device16(mu_bits, "bf16", device))
+            self.lam.copy_(torch.from_numpy(lam))
             self.log_n.copy_(torch.from_numpy(np.log(n_valid.astype(np.float64)).astype(np.float32)))
         self.tiers = None
         self.page_entry = None
@@ -109,11 +127,31 @@ class DeviceLayer:
 
     # summary of every logical page, over its valid tokens (0 -> empty record)
     def build_summaries(self, stream=None):
+        entries, nv = self._all_entries()
+        kv.summary_build(self.L, self.k16, self.bt, entries, nv, self.summary, self.log_n, stream)
+
+    def _all_entries(self):
         w = self.w
         bb, pp = np.meshgrid(np.arange(w.B), np.arange(w.Np), indexing="ij")
         entries = torch.from_numpy(np.stack([bb.ravel(), pp.ravel()], 1).astype(np.int32)).to(self.device)
         nv = torch.from_numpy(self.valid_tokens().ravel()).to(self.device)
-        kv.summary_build(self.L, self.k16, self.bt, entries, nv, self.summary, self.log_n, stream)
+        return entries, nv
+
+    # the row basis over every valid key (prefill)
+    def build_basis(self, stream=None):
+        w = self.w
+        nb = kv.basis_build_workspace_size(self.L, w.B, w.Np)
+        ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device=self.device)
+        kv.basis_build(self.L, self.k16, self.bt, self.seq_lens, self.basis, ws, stream)
+        if stream is None:
+            torch.cuda.current_stream().synchronize()
+        del ws
+
+    # shared-basis statistics of every logical page (0 valid tokens -> zeros)
+    def build_basis_summaries(self, stream=None):
+        entries, nv = self._all_entries()
+        kv.summary_build_basis(self.L, self.k16, self.bt, entries, nv, self.basis, self.mu, self.lam,
+                               self.log_n, stream)
 
     def _pack_tiers(self):
         w = self.w
@@ -202,8 +240,12 @@ def queries_device(w: wl.Workload, layer=0, qidx=0, device="cuda"):
 
 
 def score(layer: DeviceLayer, q, bufs: StepBuffers, stream=None):
-    kv.page_score(layer.L, q, layer.summary, layer.log_n, layer.seq_lens, bufs.head_scores,
-                  bufs.lse_partial, stream)
+    if layer.basis is not None:
+        kv.page_score_basis(layer.L, q, layer.mu, layer.lam, layer.basis, layer.log_n, layer.seq_lens,
+                            bufs.head_scores, bufs.lse_partial, stream)
+    else:
+        kv.page_score(layer.L, q, layer.summary, layer.log_n, layer.seq_lens, bufs.head_scores,
+                      bufs.lse_partial, stream)
 
 
 def topk(layer: DeviceLayer, bufs: StepBuffers, n_force_first=0, n_force_last=0, stream=None):
@@ -251,7 +293,10 @@ class SplitStep:
         for b0, b1 in zip(edges[:-1], edges[1:]):
             v = _View()
             v.b0, v.b1 = b0, b1
-            v.summary = layer.summary[b0:b1]
+            v.summary = None if layer.summary is None else layer.summary[b0:b1]
+            v.basis = None if layer.basis is None else layer.basis[b0:b1]
+            v.mu = None if layer.mu is None else layer.mu[b0:b1]
+            v.lam = None if layer.lam is None else layer.lam[b0:b1]
             v.log_n = layer.log_n[b0:b1]
             v.seq_lens = layer.seq_lens[b0:b1]
             v.bt = layer.bt[b0:b1]
@@ -275,7 +320,11 @@ class SplitStep:
         for v, s in zip(self.groups, self.streams):
             with torch.cuda.stream(s):
                 qg = q[v.b0:v.b1]
-                kv.page_score(layer.L, qg, v.summary, v.log_n, v.seq_lens, v.head_scores, v.lse_partial, s)
+                if v.basis is not None:
+                    kv.page_score_basis(layer.L, qg, v.mu, v.lam, v.basis, v.log_n, v.seq_lens, v.head_scores,
+                                        v.lse_partial, s)
+                else:
+                    kv.page_score(layer.L, qg, v.summary, v.log_n, v.seq_lens, v.head_scores, v.lse_partial, s)
                 kv.page_topk(layer.L, v.head_scores, v.lse_partial, v.seq_lens, w.Np, w.keep, w.k_fixed,
                              v.sel, v.sel_count, 0, 0, v.page_S, None, s)
                 kv.sparse_decode_attn(layer.L, qg, layer.pages, v.bt, v.seq_lens, v.sel, v.sel_count,

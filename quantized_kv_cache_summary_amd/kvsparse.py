@@ -25,6 +25,7 @@ SYMBOLS = (
     "kv_summary_build", "kv_page_score", "kv_page_score_partial_size", "kv_page_topk",
     "kv_page_topk_workspace_size", "kv_sparse_decode_attn", "kv_sparse_decode_attn_workspace_size",
     "kv_sparse_decode_attn_num_splits", "kv_dequant_tier", "kv_pack_tier", "kv_status_string",
+    "kv_basis_build", "kv_basis_build_workspace_size", "kv_summary_build_basis", "kv_page_score_basis",
 )
 
 
@@ -79,6 +80,10 @@ def lib():
             "kv_dequant_tier": (_I, [_LP, _PP, _P, _I, _P, _P]),
             "kv_pack_tier": (_I, [_LP, _P, _P, _I, _I, _P, _P, _P, _P]),
             "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "kv_basis_build": (_I, [_LP, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+            "kv_basis_build_workspace_size": (_SZ, [_LP, _I, _I]),
+            "kv_summary_build_basis": (_I, [_LP, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
+            "kv_page_score_basis": (_I, [_LP, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -144,6 +149,33 @@ def summary_build(L, k16, block_table, entries, n_valid, summary, log_n, stream=
     rc = lib().kv_summary_build(ctypes.byref(L), _p(k16), _p(block_table), int(max_pages), _p(entries),
                                 _p(n_valid), int(entries.shape[0]), _p(summary), _p(log_n), _stream(stream))
     _check(rc, "kv_summary_build")
+
+
+def basis_build_workspace_size(L, B, max_pages):
+    return int(lib().kv_basis_build_workspace_size(ctypes.byref(L), int(B), int(max_pages)))
+
+
+def basis_build(L, k16, block_table, seq_lens, basis, ws, stream=None):
+    B, max_pages = block_table.shape
+    rc = lib().kv_basis_build(ctypes.byref(L), _p(k16), _p(block_table), _p(seq_lens), int(B), int(max_pages),
+                              _p(basis), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "kv_basis_build")
+
+
+def summary_build_basis(L, k16, block_table, entries, n_valid, basis, mu, lam, log_n, stream=None):
+    max_pages = block_table.shape[1]
+    rc = lib().kv_summary_build_basis(ctypes.byref(L), _p(k16), _p(block_table), int(max_pages), _p(entries),
+                                      _p(n_valid), int(n_valid.shape[0]), _p(basis), _p(mu), _p(lam),
+                                      _p(log_n), _stream(stream))
+    _check(rc, "kv_summary_build_basis")
+
+
+def page_score_basis(L, q, mu, lam, basis, log_n, seq_lens, head_scores, lse_partial, stream=None):
+    B = seq_lens.shape[0]
+    max_pages = log_n.shape[1]
+    rc = lib().kv_page_score_basis(ctypes.byref(L), _p(q), _p(mu), _p(lam), _p(basis), _p(log_n), _p(seq_lens),
+                                   int(B), int(max_pages), _p(head_scores), _p(lse_partial), _stream(stream))
+    _check(rc, "kv_page_score_basis")
 
 
 def page_score_partial_size(L, B, max_pages):

@@ -150,3 +150,30 @@ def test_pack_build_dequant_validation():
     assert lib.kv_dequant_tier(ctypes.byref(L), None, FAKE, 2, FAKE, None) == kv.KV_ERR_INVALID_ARG
     assert kv.page_score_partial_size(L, 8, 2048) == 64 * 32 * 4 * 2 * 4
     assert kv.page_topk_workspace_size(L, 8, 2048) == 0
+
+
+def test_shared_basis_validation():
+    L = _L()
+    lib = kv.lib()
+    need = kv.basis_build_workspace_size(L, 2, 300)
+    assert need == 16 * 2 * (1 + 128 + 128 * 128) * 4           # rows x 256-page chunks x statistics
+    bb = lambda **o: lib.kv_basis_build(ctypes.byref(L), o.get("k", FAKE), FAKE, FAKE, 2, 300,
+                                        o.get("basis", FAKE), o.get("ws", FAKE), o.get("wsb", need), None)
+    assert bb(wsb=need - 1) == kv.KV_ERR_WORKSPACE
+    assert bb(ws=None) == kv.KV_ERR_WORKSPACE
+    assert bb(basis=None) == kv.KV_ERR_INVALID_ARG
+    assert bb(k=FAKE + 2) == kv.KV_ERR_INVALID_ARG
+    assert lib.kv_basis_build(ctypes.byref(L), FAKE, FAKE, FAKE, 0, 300, FAKE, None, 0, None) == kv.KV_OK
+    sb = lambda **o: lib.kv_summary_build_basis(ctypes.byref(L), FAKE, FAKE, 300, FAKE, FAKE, o.get("n", 4),
+                                                o.get("basis", FAKE), o.get("mu", FAKE), FAKE, FAKE, None)
+    assert sb(basis=None) == kv.KV_ERR_INVALID_ARG
+    assert sb(mu=None) == kv.KV_ERR_INVALID_ARG
+    assert sb(n=-1) == kv.KV_ERR_INVALID_ARG
+    assert sb(n=0) == kv.KV_OK
+    ps = lambda **o: lib.kv_page_score_basis(ctypes.byref(L), FAKE, o.get("mu", FAKE), o.get("lam", FAKE),
+                                             o.get("basis", FAKE), FAKE, FAKE, 2, 300, FAKE, FAKE, None)
+    assert ps(mu=FAKE + 4) == kv.KV_ERR_INVALID_ARG
+    assert ps(basis=FAKE + 4) == kv.KV_ERR_INVALID_ARG
+    assert ps(lam=FAKE + 2) == kv.KV_ERR_INVALID_ARG
+    assert ps(lam=None) == kv.KV_ERR_INVALID_ARG
+    assert _score(_L(head_dim=96)) == kv.KV_ERR_UNSUPPORTED
