@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--queries", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-basis", action="store_true",
+                    help="skip the shared-basis summary variant (reported beside the headline)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy (known bytes) for scaling counter readings")
@@ -51,6 +53,13 @@ def algorithmic_bytes(w, sel_counts):
     rec = (1 + w.rank) * w.d * 2 + 4                       # bf16 record + float32 log n
     summary = w.rows * w.Np * rec
     selected = int(sel_counts.sum()) * w.P * w.d * 2 * 2   # K and V, 16-bit
+    return summary, selected
+
+
+def basis_algorithmic_bytes(w, sel_counts):
+    rec = w.d * 2 + w.rank * 4 + 4                          # bf16 mean + float32 variances + log n
+    summary = w.rows * w.Np * rec + w.rows * w.rank * w.d * 4   # + the float32 row bases
+    selected = int(sel_counts.sum()) * w.P * w.d * 2 * 2
     return summary, selected
 
 
@@ -279,6 +288,47 @@ def main():
             "bytes_per_launch": summary_b,
         },
     }
+    if not args.no_basis:
+        # the same layers scored from shared-basis summaries (row basis built
+        # from each layer's keys, then per-page means and variances), same
+        # rotation, queries, selection rule, attention and timing
+        t0 = time.time()
+        blayers = [l.with_basis_summaries() for l in layers]
+        torch.cuda.synchronize()
+        log(f"[bench] shared-basis summaries built in {time.time() - t0:.1f}s")
+        bsteps = [hz.SplitStep(blayers[i], bufs[i], 1) for i in range(n_layers)]
+        n_cap = n_layers * min(args.queries, 4)
+        for i in range(args.warmup):
+            bsteps[i % n_layers](qs[i % n_layers][(i // n_layers) % args.queries])
+        gb = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gb):
+            for i in range(n_cap):
+                bsteps[i % n_layers](qs[i % n_layers][(i // n_layers) % args.queries])
+        for _ in range(3):
+            gb.replay()
+        torch.cuda.synchronize()
+        reps = max(1, K // n_cap)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            gb.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        b_ms = a.elapsed_time(b) / (reps * n_cap)
+        bscore_us, _ = graph_avg_us(lambda li, q: hz.score(blayers[li], q, bufs[li]))
+        bsel = bufs[0].sel_count.cpu().numpy()
+        bsum, bselb = basis_algorithmic_bytes(w, bsel)
+        log(f"[bench] shared-basis step {b_ms * 1e3:.1f} us, score {bscore_us:.2f} us")
+        result["shared_basis"] = {
+            "value": 1e3 / b_ms, "unit": "steps/s", "ms_per_step": b_ms, "steps": reps * n_cap,
+            "effective_GBps": (bsum + bselb) / (b_ms / 1e3) / 1e9,
+            "pct_hbm_peak": 100.0 * (bsum + bselb) / (b_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_step": {"summaries": bsum, "selected_kv": bselb},
+            "score_kernel": {"avg_launch_us": bscore_us, "achieved_GBps": bsum / (bscore_us * 1e3),
+                             "frac": bsum / (bscore_us * 1e3) / HBM_PEAK_GBS},
+            "note": "same layers, queries and attention; summaries = shared row basis + per-page mean "
+                    "and variances (not the headline's per-page directions)",
+        }
     if not args.no_cpu_baseline:
         log("[bench] oracle baseline on the host ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

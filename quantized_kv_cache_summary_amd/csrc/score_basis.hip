@@ -58,23 +58,9 @@ __global__ __launch_bounds__(64 * kBasisScoreWaves) void page_score_basis_kernel
   const int base = chunk * kScorePagesPerBlock;
   auto clampp = [&](int p) { return p < max_pages ? p : max_pages - 1; };
 
-  // ---- every load of the wave, before any math
+  // ---- every load of the wave, before any math: first the small ones the
+  //      basis projections need, so that work overlaps the means in flight
   const size_t rrow = (size_t)row * max_pages;
-  const uint16_t* mrow = mu + rrow * D + 8 * kg;
-  u32x4_t a[SUB][KS];
-#pragma unroll
-  for (int t = 0; t < SUB; ++t) {
-    const uint16_t* src = mrow + (size_t)clampp(base + 16 * t + (col & 3) * 4 + (col >> 2)) * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) a[t][s] = ld16(src + 32 * s);
-  }
-  float lv[R];
-  {
-    const float* lp = lam + (rrow + clampp(base + lane)) * R;
-#pragma unroll
-    for (int j = 0; j < R; ++j) lv[j] = lp[j];
-  }
-  const float lnv = log_n[(size_t)b * max_pages + clampp(base + lane)];
   // query operand: head `col`, elements [32s + 8kg, +8); heads past G are zero
   u32x4_t qraw[KS];
   {
@@ -94,7 +80,22 @@ __global__ __launch_bounds__(64 * kBasisScoreWaves) void page_score_basis_kernel
       ub[s][4] = x1.x; ub[s][5] = x1.y; ub[s][6] = x1.z; ub[s][7] = x1.w;
     }
   }
+  float lv[R];
+  {
+    const float* lp = lam + (rrow + clampp(base + lane)) * R;
+#pragma unroll
+    for (int j = 0; j < R; ++j) lv[j] = lp[j];
+  }
+  const float lnv = log_n[(size_t)b * max_pages + clampp(base + lane)];
   const int L = seq_lens[b];
+  const uint16_t* mrow = mu + rrow * D + 8 * kg;
+  u32x4_t a[SUB][KS];
+#pragma unroll
+  for (int t = 0; t < SUB; ++t) {
+    const uint16_t* src = mrow + (size_t)clampp(base + 16 * t + (col & 3) * 4 + (col >> 2)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a[t][s] = ld16(src + 32 * s);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- page variances and log n of the wave's 64 pages through LDS

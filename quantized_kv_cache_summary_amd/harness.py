@@ -130,6 +130,22 @@ class DeviceLayer:
         entries, nv = self._all_entries()
         kv.summary_build(self.L, self.k16, self.bt, entries, nv, self.summary, self.log_n, stream)
 
+    def with_basis_summaries(self, stream=None):
+        """The same layer (pools, block table, tiers, host V shared) scored from
+        shared-basis summaries built from its keys; release() the original only."""
+        import copy
+        w = self.w
+        v = copy.copy(self)
+        v.summary = None
+        v.basis = torch.empty((w.B, w.Hkv, w.rank, w.d), dtype=torch.float32, device=self.device)
+        v.mu = torch.empty((w.B, w.Hkv, w.Np, w.d), dtype=torch.bfloat16, device=self.device)
+        v.lam = torch.empty((w.B, w.Hkv, w.Np, w.rank), dtype=torch.float32, device=self.device)
+        v.log_n = torch.empty_like(self.log_n)
+        v.host_v = None
+        v.build_basis(stream)
+        v.build_basis_summaries(stream)
+        return v
+
     def _all_entries(self):
         w = self.w
         bb, pp = np.meshgrid(np.arange(w.B), np.arange(w.Np), indexing="ij")
