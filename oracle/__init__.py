@@ -33,7 +33,7 @@ from .summary import summarize_page, store_summary, summarize_and_store
 from .score import page_score, exact_page_logmass
 from .basis import (row_basis, row_covariance, store_basis, basis_page_stats, store_basis_summary,
                     page_score_basis)
-from .select import group_aggregate, selection_count, select_pages
+from .select import group_aggregate, selection_count, select_pages, coverage_count
 from .attention import sparse_attention, dense_attention
 from .codec import (
     BITS_OF_TIER, TIER_NATIVE, TIER_I8, TIER_I4, TIER_I2, TIER_B1,
@@ -49,7 +49,7 @@ __all__ = [
     "page_score", "exact_page_logmass",
     "row_basis", "row_covariance", "store_basis", "basis_page_stats", "store_basis_summary",
     "page_score_basis",
-    "group_aggregate", "selection_count", "select_pages",
+    "group_aggregate", "selection_count", "select_pages", "coverage_count",
     "sparse_attention", "dense_attention",
     "BITS_OF_TIER", "TIER_NATIVE", "TIER_I8", "TIER_I4", "TIER_I2", "TIER_B1",
     "encode_group_int", "encode_group_1bit", "encode_vector", "decode_vector",

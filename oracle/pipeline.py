@@ -15,7 +15,7 @@ from .paging import num_pages, page_token_counts
 from .summary import summarize_and_store
 from .score import page_score
 from .basis import row_basis, store_basis, basis_page_stats, store_basis_summary, page_score_basis
-from .select import group_aggregate, selection_count, select_pages
+from .select import group_aggregate, selection_count, select_pages, coverage_count
 from .attention import sparse_attention
 from .codec import TIER_NATIVE, encode_vector, decode_vector
 
@@ -72,13 +72,15 @@ def reconstruct_tiers(x, seq_len, page_size, page_tiers):
 
 def decode_row(q, keys, values, seq_len, page_size, rank, tau, keep_frac=0.0, k_fixed=0,
                n_force_first=0, n_force_last=0, page_tiers=None, summary=None, shared_basis=False,
-               basis=None):
+               basis=None, coverage=None, k_cap=None):
     """Full step for one row.
 
     q: (G, d); keys, values: (>= seq_len, d) 16-bit values in logical token order.
     summary: optional stored summary to score from -- (mu, w, log_n) per page,
     or (U, mu, lam, log_n) with shared_basis -- built here otherwise (with
     shared_basis, from `basis` if given, else the row's own basis).
+    coverage: coverage mode (k from the mass prefix, capped at k_cap) instead of
+    keep_frac / k_fixed.
     """
     keys = np.asarray(keys, dtype=np.float64)[:seq_len]
     values = np.asarray(values, dtype=np.float64)[:seq_len]
@@ -94,7 +96,10 @@ def decode_row(q, keys, values, seq_len, page_size, rank, tau, keep_frac=0.0, k_
         mu, w, log_n = summary
         s_hat = page_score(q, mu[:npg], w[:npg], log_n[:npg], tau)
     S = group_aggregate(s_hat) if npg else np.zeros(0)
-    k = selection_count(npg, keep_frac, k_fixed)
+    if coverage is None:
+        k = selection_count(npg, keep_frac, k_fixed)
+    else:
+        k = coverage_count(S, coverage, npg if k_cap is None else k_cap, n_force_first, n_force_last)
     sel = select_pages(S, k, n_force_first, n_force_last) if npg else np.zeros(0, np.int64)
     k_hat = reconstruct_tiers(keys, seq_len, page_size, page_tiers)
     v_hat = reconstruct_tiers(values, seq_len, page_size, page_tiers)

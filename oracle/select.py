@@ -18,9 +18,18 @@ Selection keeps k pages per (sequence, KV head):
   order by (S descending, page index ascending), NaN ranking as -inf;
   take the first k and return them in ascending page order.
 
+Coverage mode (the ``coverage`` field: the smallest set of pages holding a given
+share of the attention mass).  S_p is a log-distribution (sum_p exp(S_p) = 1),
+so with the same ranking (forced pages first by index, then S descending, page
+ascending) k is the shortest prefix whose total mass exp(S) reaches the
+coverage; forced pages count with their own mass and are always kept, NaN
+pages have mass 0; k is then clamped to [max(1, forced pages), min(k_cap, Np)]
+and a prefix that never reaches the coverage keeps every page (up to the cap).
+
 Pinned in tests/test_oracle_select.py: sum_p exp(S_p) = 1; G = 1 reduces to the
 order of s_hat; a brute-force full sort on tiny inputs over 10^4 seeds; constant
-scores select {0..k-1}; forced pages and NaN ranks.
+scores select {0..k-1}; forced pages and NaN ranks; coverage counts against a
+brute-force loop and closed forms (uniform masses, one dominant page).
 """
 
 import math
@@ -50,6 +59,34 @@ def selection_count(num_valid_pages, keep_frac, k_fixed=0):
         return min(npg, int(k_fixed))
     keep = float(np.float32(keep_frac))
     return min(npg, max(1, math.ceil(keep * npg)))
+
+
+def _forced_mask(npg, n_force_first, n_force_last):
+    forced = np.zeros(npg, dtype=bool)
+    if n_force_first > 0:
+        forced[: min(n_force_first, npg)] = True
+    if n_force_last > 0:
+        forced[max(0, npg - n_force_last):] = True
+    return forced
+
+
+def coverage_count(S, coverage, k_cap, n_force_first=0, n_force_last=0):
+    """k for one row in coverage mode (see the module header); S is (Np,)."""
+    S = np.array(S, dtype=np.float64)
+    npg = S.shape[0]
+    if npg == 0:
+        return 0
+    forced = _forced_mask(npg, n_force_first, n_force_last)
+    with np.errstate(over="ignore"):
+        mass = np.where(np.isnan(S), 0.0, np.minimum(np.exp(S), 1.0))
+    rank_key = np.where(np.isnan(S), -np.inf, S)
+    rank_key[forced] = np.inf
+    order = np.lexsort((np.arange(npg), -rank_key))
+    cum = np.cumsum(mass[order])
+    hit = np.nonzero(cum >= coverage)[0]
+    k = int(hit[0]) + 1 if hit.size else npg
+    k = max(k, int(forced.sum()), 1)
+    return min(k, int(k_cap), npg)
 
 
 def select_pages(S, k, n_force_first=0, n_force_last=0):
