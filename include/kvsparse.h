@@ -233,6 +233,26 @@ int kv_page_topk(const kv_layout* layout, const float* head_scores, const float*
 size_t kv_page_topk_workspace_size(const kv_layout* layout, int32_t B, int32_t max_pages);
 
 /* ---------------------------------------------------------------------------
+ * kv_page_topk_coverage -- kv_page_topk with k chosen per row by attention-mass
+ * coverage (AMASS page, "Quickstart": the `coverage` field, the default
+ * selection rule, against the fixed `budget`).  With S_p as in kv_page_topk
+ * (sum_p exp(S_p) = 1 over the row's valid pages) and the same order (forced
+ * pages first by index, then S descending, page ascending), k is the length of
+ * the shortest prefix whose total mass exp(S) reaches `coverage`; forced pages
+ * count with their own mass and are always kept, NaN pages have mass 0, and a
+ * prefix that never reaches `coverage` keeps every page.  k is then clamped to
+ * [max(1, forced pages), min(k_max, Np_b)].  Masses are summed in fixed point
+ * with 40 fraction bits (exact integer sums, so the result does not depend on
+ * thread timing).  coverage >= 0 (a value above 1 keeps every page); k_max >= 1
+ * is the cap and the row length of sel.  Other arguments and outputs as for
+ * kv_page_topk.
+ * --------------------------------------------------------------------------- */
+int kv_page_topk_coverage(const kv_layout* layout, const float* head_scores, const float* lse_partial,
+                          const int32_t* seq_lens, int32_t B, int32_t max_pages, float coverage,
+                          int32_t n_force_first, int32_t n_force_last, int32_t* sel, int32_t* sel_count,
+                          int32_t k_max, float* page_S, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * kv_sparse_decode_attn -- softmax attention of every query head over the
  * tokens of its row's selected pages only (AMASS page, "AMASS": a sparse
  * paged-attention kernel reads just the selected pages), renormalised over

@@ -208,13 +208,32 @@ int kv_page_topk(const kv_layout* L, const float* head_scores, const float* lse_
   if (k_max < topk_bound(max_pages, keep_frac, k_fixed)) return KV_ERR_INVALID_ARG;
   if ((int64_t)B * L->num_kv_heads > 0x7FFFFFFF) return KV_ERR_UNSUPPORTED;
   return from_hip(kvs::launch_page_topk(*L, head_scores, lse_partial, seq_lens, B, max_pages,
-                                        keep_frac, k_fixed, n_force_first, n_force_last, sel,
+                                        keep_frac, k_fixed, -1.f, n_force_first, n_force_last, sel,
                                         sel_count, k_max, page_S, (hipStream_t)stream));
 }
 
 int32_t kv_sparse_decode_attn_num_splits(const kv_layout* L, int32_t B, int32_t k_max, int32_t tiered) {
   if (check_layout(L) || B <= 0) return 1;
   return auto_splits(B * L->num_kv_heads, k_max, tiered != 0);
+}
+
+int kv_page_topk_coverage(const kv_layout* L, const float* head_scores, const float* lse_partial,
+                          const int32_t* seq_lens, int32_t B, int32_t max_pages, float coverage,
+                          int32_t n_force_first, int32_t n_force_last, int32_t* sel, int32_t* sel_count,
+                          int32_t k_max, float* page_S, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  (void)ws; (void)ws_bytes;
+  if (B < 0 || max_pages < 0 || k_max < 1 || n_force_first < 0 || n_force_last < 0) return KV_ERR_INVALID_ARG;
+  if (!(coverage >= 0.f) || !std::isfinite(coverage)) return KV_ERR_INVALID_ARG;
+  if (B == 0) return KV_OK;
+  if (max_pages > kvs::kMaxTopkPages) return KV_ERR_UNSUPPORTED;
+  if (!seq_lens || !sel_count || !sel) return KV_ERR_INVALID_ARG;
+  if (max_pages > 0 && (!head_scores || !lse_partial)) return KV_ERR_INVALID_ARG;
+  if ((int64_t)B * L->num_kv_heads > 0x7FFFFFFF) return KV_ERR_UNSUPPORTED;
+  return from_hip(kvs::launch_page_topk(*L, head_scores, lse_partial, seq_lens, B, max_pages, 0.f, 0,
+                                        coverage, n_force_first, n_force_last, sel, sel_count, k_max,
+                                        page_S, (hipStream_t)stream));
 }
 
 size_t kv_sparse_decode_attn_workspace_size(const kv_layout* L, int32_t B, int32_t k_max,

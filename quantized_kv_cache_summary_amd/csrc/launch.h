@@ -58,10 +58,11 @@ hipError_t launch_page_score(const kv_layout& L, const void* q, const void* summ
                              const float* log_n, const int32_t* seq_lens, int B, int max_pages,
                              float tau, float* head_scores, float* lse_partial, hipStream_t st);
 
+// coverage < 0: budget mode (keep / k_fixed); coverage >= 0: coverage mode.
 hipError_t launch_page_topk(const kv_layout& L, const float* head_scores, const float* lse_partial,
                             const int32_t* seq_lens, int B, int max_pages, float keep, int k_fixed,
-                            int n_force_first, int n_force_last, int32_t* sel, int32_t* sel_count,
-                            int k_max, float* page_S, hipStream_t st);
+                            float coverage, int n_force_first, int n_force_last, int32_t* sel,
+                            int32_t* sel_count, int k_max, float* page_S, hipStream_t st);
 
 hipError_t launch_sparse_attn(const kv_layout& L, const void* q, const kv_pages& pg,
                               const int32_t* block_table, const int32_t* seq_lens, int B,

@@ -55,7 +55,29 @@ struct SelectLds {
   int wpos[NW], wneg[NW];
   alignas(16) uint32_t cand[kDirectMax];
   int n_cand;
+  // coverage mode: per-bin masses in fixed point, forced pages' mass
+  unsigned long long hmass[3][256];
+  unsigned long long forced_mass;
 };
+
+// Row statistics of the keys (block-uniform).
+struct SelectStats {
+  uint32_t kmax, kmin;   // extremes of the finite keys
+  int npos, nneg;        // +inf keys (forced pages), -inf keys (empty or NaN)
+};
+
+// Page mass exp(S) in fixed point with 40 fraction bits (S <= 0 for a
+// log-distribution; larger values clamp at 1).  Integer sums are exact, so the
+// coverage count does not depend on the order of accumulation.
+constexpr float kMassScale = 1099511627776.0f;   // 2^40
+__device__ __forceinline__ unsigned long long mass_fixed(float S) {
+  if (!(S == S)) return 0ull;
+  const float m = fminf(__expf(S), 1.0f);
+  return (unsigned long long)(m * kMassScale);
+}
+__device__ __forceinline__ float key_to_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
 
 // Register-held inputs: the first round of head scores (U pages per thread,
 // strided by NT) and the score blocks' (max, sum exp) partials of the heads
@@ -126,11 +148,13 @@ __device__ __forceinline__ void for_own_keys(const uint32_t* keys, int Np, F&& f
 // Threshold of the row: the k-th largest key T and how many keys equal to T
 // are kept (the lowest-index ones).  Leaves the keys of pages [0, Np) in
 // keys[].  select_issue must have been called.  k >= 1.  Block-uniform results.
+// Keys of pages [0, Np) into keys[] and their statistics.  select_issue must
+// have been called.  With with_mass, the forced pages' own masses (before their
+// score is raised to +inf) are summed into sh.forced_mass.
 template <int NT, int GM>
-__device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<NT, GM>& ld,
-                                 const float* hs, int G, int max_pages, int n_tiles, int Np, int k,
-                                 int n_force_first, int n_force_last, float* page_S_row,
-                                 uint32_t& T_out, int& take_out) {
+__device__ SelectStats select_keys(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<NT, GM>& ld,
+                                   const float* hs, int G, int max_pages, int n_tiles, int Np,
+                                   int n_force_first, int n_force_last, float* page_S_row, bool with_mass) {
   using SL = SelectLoads<NT, GM>;
   constexpr int NW = NT / 64;
   constexpr int U = SL::U;
@@ -151,9 +175,9 @@ __device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<
       if (lane == 0) sh.Lh[h] = (S > 0.f || S != S) ? M + __logf(S) : -INFINITY;
     }
   }
-  if (tid == 0) sh.n_cand = 0;
+  if (tid == 0) { sh.n_cand = 0; sh.forced_mass = 0ull; }
   if (tid < kDirectMax) sh.cand[tid] = 0u;   // below every finite key
-  if (tid < 256) sh.hist[0][tid] = 0;
+  if (tid < 256) { sh.hist[0][tid] = 0; sh.hmass[0][tid] = 0ull; }
   __syncthreads();
 
   // 2. group aggregate and keys, the next round of scores in flight while one
@@ -164,6 +188,7 @@ __device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<
   for (int h = 0; h < GM; ++h) Lr[h] = h < G ? sh.Lh[h] : 0.f;
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
   int npos = 0, nneg = 0;
+  unsigned long long fmass = 0ull;
   for (int r0 = 0; r0 < Np; r0 += NT * U) {
     const bool more = r0 + NT * U < Np;
     float nx[U][GM];
@@ -192,7 +217,10 @@ __device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<
         for (int h = 0; h < GM; ++h) if (h < G) sum += __expf(x[h] - M);
         S = M + __logf(sum) - logG;
       }
-      if (p < n_force_first || p >= Np - n_force_last) S = INFINITY;
+      if (p < n_force_first || p >= Np - n_force_last) {
+        if (with_mass) fmass += mass_fixed(S);
+        S = INFINITY;
+      }
       const uint32_t key = order_key(S);
       keys[p] = key;
       if (finite_key(key)) {
@@ -210,23 +238,36 @@ __device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<
         for (int h = 0; h < GM; ++h) ld.v[u][h] = nx[u][h];
     }
   }
+  if (with_mass && fmass) atomicAdd(&sh.forced_mass, fmass);
   kmax = wave_max_u32(kmax);
   kmin = wave_min_u32(kmin);
   npos = wave_sum_i32(npos);
   nneg = wave_sum_i32(nneg);
   if (lane == 0) { sh.wmax[wave] = kmax; sh.wmin[wave] = kmin; sh.wpos[wave] = npos; sh.wneg[wave] = nneg; }
   __syncthreads();
-  kmax = sh.wmax[0];
-  kmin = sh.wmin[0];
-  npos = sh.wpos[0];
-  nneg = sh.wneg[0];
+  SelectStats st;
+  st.kmax = sh.wmax[0];
+  st.kmin = sh.wmin[0];
+  st.npos = sh.wpos[0];
+  st.nneg = sh.wneg[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
-    kmax = sh.wmax[w] > kmax ? sh.wmax[w] : kmax;
-    kmin = sh.wmin[w] < kmin ? sh.wmin[w] : kmin;
-    npos += sh.wpos[w];
-    nneg += sh.wneg[w];
+    st.kmax = sh.wmax[w] > st.kmax ? sh.wmax[w] : st.kmax;
+    st.kmin = sh.wmin[w] < st.kmin ? sh.wmin[w] : st.kmin;
+    st.npos += sh.wpos[w];
+    st.nneg += sh.wneg[w];
   }
+  return st;
+}
+
+// Threshold of the row: the k-th largest key T and how many keys equal to T
+// are kept (the lowest-index ones).  1 <= k <= Np.  Block-uniform results.
+template <int NT>
+__device__ void select_kth(SelectLds<NT>& sh, const uint32_t* keys, int Np, const SelectStats& stt, int k,
+                           uint32_t& T_out, int& take_out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t kmax = stt.kmax, kmin = stt.kmin;
+  const int npos = stt.npos, nneg = stt.nneg;
 
   // 3. the k-th largest key
   int rem = k;
@@ -312,6 +353,116 @@ __device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<
   const int first = __ffsll((long long)__ballot(lane < nc && gt < rem && rem <= ge)) - 1;
   T_out = (uint32_t)__builtin_amdgcn_readlane((int)x, first);
   take_out = rem - __builtin_amdgcn_readlane(gt, first);
+}
+
+// Keys and the threshold for a fixed k (>= 1).
+template <int NT, int GM>
+__device__ void select_threshold(SelectLds<NT>& sh, uint32_t* keys, SelectLoads<NT, GM>& ld,
+                                 const float* hs, int G, int max_pages, int n_tiles, int Np, int k,
+                                 int n_force_first, int n_force_last, float* page_S_row,
+                                 uint32_t& T_out, int& take_out) {
+  const SelectStats st = select_keys<NT, GM>(sh, keys, ld, hs, G, max_pages, n_tiles, Np, n_force_first,
+                                             n_force_last, page_S_row, false);
+  select_kth<NT>(sh, keys, Np, st, k, T_out, take_out);
+}
+
+// Coverage mode: the length of the shortest prefix of the selection order
+// (forced pages first, then keys descending, equal keys by page) whose total
+// mass exp(S) reaches `coverage` (forced pages with their own mass, -inf keys
+// with none); every page if it is never reached.  Then clamped to
+// [max(1, forced pages), min(k_cap, Np)].  The crossing is found by radix
+// passes over the finite keys with per-bin counts and fixed-point masses; the
+// keys equal to the final threshold share one mass, so the count needed among
+// them is a division.  Block-uniform result.
+template <int NT>
+__device__ int select_coverage_k(SelectLds<NT>& sh, const uint32_t* keys, int Np, const SelectStats& stt,
+                                 float coverage, int k_cap) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int npos = stt.npos, nfin = Np - stt.npos - stt.nneg;
+  int lo = npos > 1 ? npos : 1;
+  int hi = k_cap < Np ? k_cap : Np;
+  auto clampk = [&](int k) { k = k < lo ? lo : k; return k > hi ? hi : k; };
+  if (!(coverage <= 1.0f)) return clampk(Np);               // never reached (or NaN coverage)
+  const unsigned long long target = (unsigned long long)(fmaxf(coverage, 0.f) * kMassScale);
+  if (target == 0ull) return clampk(1);
+  const unsigned long long fm = sh.forced_mass;
+  if (fm >= target) return clampk(npos);
+  unsigned long long rem = target - fm;
+  int above = npos;
+  if (nfin == 0) return clampk(Np);
+  if (stt.kmax == stt.kmin) {                               // all finite keys equal
+    const unsigned long long m = mass_fixed(key_to_score(stt.kmax));
+    if (m == 0ull || m * (unsigned long long)nfin < rem) return clampk(Np);
+    return clampk(above + (int)((rem + m - 1) / m));
+  }
+  const uint32_t diff = stt.kmax ^ stt.kmin;
+  const int hb = 31 - __clz((int)diff);
+  uint32_t pmask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = stt.kmax & pmask;
+  int top = hb;
+  int buf = 0;
+  for (;;) {
+    const int width = top + 1 < 8 ? top + 1 : 8;
+    const int shift = top + 1 - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    for_own_keys<NT>(keys, Np, [&](uint32_t key) {
+      if ((key & pmask) == prefix && finite_key(key)) {
+        const int bin = (key >> shift) & dmask;
+        atomicAdd(&sh.hist[buf][bin], 1);
+        atomicAdd(&sh.hmass[buf][bin], mass_fixed(key_to_score(key)));
+      }
+    });
+    const int nb = buf == 2 ? 0 : buf + 1;
+    if (tid < 256) { sh.hist[nb][tid] = 0; sh.hmass[nb][tid] = 0ull; }
+    __syncthreads();
+    // every wave scans the masses (digits descending) and finds the crossing bin
+    int c[4], ctot = 0;
+    unsigned long long mb[4], mtot = 0ull;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = sh.hist[buf][255 - 4 * lane - i];
+      mb[i] = sh.hmass[buf][255 - 4 * lane - i];
+      ctot += c[i];
+      mtot += mb[i];
+    }
+    unsigned long long minc = mtot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned long long y = __shfl_up(minc, off);
+      if (lane >= off) minc += y;
+    }
+    const int cinc = wave_incl_sum(ctot);
+    const unsigned long long hit = __ballot(minc >= rem);
+    if (hit == 0ull) return clampk(Np);                    // the finite keys never reach it
+    const int first = __ffsll((long long)hit) - 1;
+    unsigned long long mcum = minc - mtot;
+    int ccum = cinc - ctot, dsel = 252 - 4 * lane, dcnt = c[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (mcum + mb[i] >= rem) { dsel = 255 - 4 * lane - i; dcnt = c[i]; break; }
+      mcum += mb[i];
+      ccum += c[i];
+    }
+    dsel = __builtin_amdgcn_readlane(dsel, first);
+    dcnt = __builtin_amdgcn_readlane(dcnt, first);
+    ccum = __builtin_amdgcn_readlane(ccum, first);
+    const unsigned long long mc_lo = (unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mcum, first);
+    const unsigned long long mc_hi = (unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mcum >> 32), first);
+    mcum = mc_lo | (mc_hi << 32);
+    prefix |= (uint32_t)dsel << shift;
+    pmask |= dmask << shift;
+    rem -= mcum;
+    above += ccum;
+    buf = nb;
+    top -= width;
+    if (top < 0) {
+      // the crossing key: dcnt keys equal to `prefix`, each of mass m
+      const unsigned long long m = mass_fixed(key_to_score(prefix));
+      int need = m ? (int)((rem + m - 1) / m) : dcnt;
+      need = need < dcnt ? need : dcnt;
+      return clampk(above + need);
+    }
+  }
 }
 
 // Calls emit(p, pos) for every kept page p of [0, Np), pos = its rank in

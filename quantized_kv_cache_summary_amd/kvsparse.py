@@ -26,6 +26,7 @@ SYMBOLS = (
     "kv_page_topk_workspace_size", "kv_sparse_decode_attn", "kv_sparse_decode_attn_workspace_size",
     "kv_sparse_decode_attn_num_splits", "kv_dequant_tier", "kv_pack_tier", "kv_status_string",
     "kv_basis_build", "kv_basis_build_workspace_size", "kv_summary_build_basis", "kv_page_score_basis",
+    "kv_page_topk_coverage",
 )
 
 
@@ -73,6 +74,8 @@ def lib():
             "kv_page_topk": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _I, _P, _P, _I, _P,
                                   _P, _SZ, _P]),
             "kv_page_topk_workspace_size": (_SZ, [_LP, _I, _I]),
+            "kv_page_topk_coverage": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P, _I, _P,
+                                           _P, _SZ, _P]),
             "kv_sparse_decode_attn": (_I, [_LP, _P, _PP, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _P,
                                            _SZ, _P]),
             "kv_sparse_decode_attn_workspace_size": (_SZ, [_LP, _I, _I, _I]),
@@ -203,6 +206,17 @@ def page_topk(L, head_scores, lse_partial, seq_lens, max_pages, keep_frac, k_fix
                             int(n_force_last), _p(sel), _p(sel_count), int(k_max), _p(page_S), _p(ws),
                             0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "kv_page_topk")
+
+
+def page_topk_coverage(L, head_scores, lse_partial, seq_lens, max_pages, coverage, sel, sel_count,
+                       n_force_first=0, n_force_last=0, page_S=None, ws=None, stream=None):
+    B = seq_lens.shape[0]
+    k_max = sel.shape[-1]
+    rc = lib().kv_page_topk_coverage(ctypes.byref(L), _p(head_scores), _p(lse_partial), _p(seq_lens), int(B),
+                                     int(max_pages), float(coverage), int(n_force_first), int(n_force_last),
+                                     _p(sel), _p(sel_count), int(k_max), _p(page_S), _p(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "kv_page_topk_coverage")
 
 
 def attn_num_splits(L, B, k_max, tiered=False):

@@ -186,6 +186,94 @@ def test_selection_branches_exact(G, max_pages):
             assert np.all(sel_h[r, k:] == -1)
 
 
+def _coverage_bounds(S, Np, cov, cap, nff, nfl, delta):
+    """Range of coverage counts for coverages within +-delta (counts are monotone)."""
+    lo = oracle.coverage_count(S[:Np], max(0.0, cov - delta), cap, nff, nfl)
+    hi = oracle.coverage_count(S[:Np], cov + delta, cap, nff, nfl)
+    return lo, hi
+
+
+@pytest.mark.parametrize("G,max_pages", [(4, 600), (8, 600), (4, 5000)])
+def test_coverage_selection_crafted(G, max_pages):
+    """Coverage mode on crafted head scores: k within the counts for coverages
+    +-1e-6 around the asked one, computed from the kernel's own float32 S
+    (masses are summed in 2^-40 fixed point), and the kept pages are exactly
+    the top k of that S."""
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    announce(f"coverage selection G={G} max_pages={max_pages}")
+    rng = np.random.default_rng(29 + G)
+    n_tiles = (max_pages + 63) // 64
+    L = kv.layout(G, 1, 128, 16, 4, "bf16")
+    hs, Np = _crafted_scores(G, max_pages, rng)
+    part = _tile_partials(hs, Np, n_tiles)
+    seq = torch.tensor(Np * 16 - (Np > 0) * 5, dtype=torch.int32, device="cuda")
+    hs_d = torch.from_numpy(hs).cuda()
+    part_d = torch.from_numpy(part).cuda()
+    cases = [(0.95, max_pages, 0, 0), (0.5, max_pages, 0, 0), (0.0, max_pages, 0, 0), (1.0, max_pages, 0, 0),
+             (1.5, 40, 0, 0), (0.9, 25, 0, 0), (0.95, max_pages, 3, 2), (0.2, max_pages, 6, 0)]
+    seen = set()
+    for cov, cap, nff, nfl in cases:
+        sel = torch.full((8, cap), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((8,), -7, dtype=torch.int32, device="cuda")
+        S = torch.zeros((8, max_pages), dtype=torch.float32, device="cuda")
+        kv.page_topk_coverage(L, hs_d, part_d, seq, max_pages, cov, sel, cnt, n_force_first=nff,
+                              n_force_last=nfl, page_S=S)
+        torch.cuda.synchronize()
+        S_h, sel_h, cnt_h = S.cpu().numpy(), sel.cpu().numpy(), cnt.cpu().numpy()
+        for r in range(8):
+            n = int(Np[r])
+            k = int(cnt_h[r])
+            if n == 0:
+                assert k == 0 and np.all(sel_h[r] == -1)
+                continue
+            # forced pages hold +inf in page_S and their own masses are not reported, so rows
+            # with forced pages are only checked for k's clamp range
+            Sr = S_h[r].astype(np.float64)
+            if nff or nfl:
+                forced = [p for p in range(n) if p < nff or p >= n - nfl]
+                assert np.all(np.isposinf(Sr[forced]))
+                assert max(1, len(forced)) <= k <= min(cap, n)
+            else:
+                lo, hi = _coverage_bounds(Sr, n, cov, cap, 0, 0, 1e-6)
+                assert lo <= k <= hi, (cov, cap, r, k, lo, hi)
+            seen.add(k)
+            exp = _expected_selection(S_h[r], n, k)
+            assert np.array_equal(sel_h[r, :k], exp), (cov, r)
+            assert np.all(sel_h[r, k:] == -1)
+    assert len(seen) > 4
+
+
+def test_coverage_selection_on_scores(hz):
+    """Coverage mode from real scores against the oracle's coverage count on its
+    own S, within a 1e-5 mass band, and the band-exact selection."""
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    w = SMALL["llama_small"]
+    lens = [w.ctx, w.ctx - 3 * w.P - 5]
+    announce("coverage selection on llama_small scores")
+    layer = hz.DeviceLayer(w, summaries="synthetic", seq_lens=lens)
+    q = hz.queries_device(w)
+    bufs = hz.StepBuffers(w, with_S=True)
+    hz.score(layer, q, bufs)
+    rec_bits, n_valid = wl.synthetic_summary(w)
+    rec = bits_to_f64(rec_bits)
+    log_n = np.log(n_valid.astype(np.float64)).astype(np.float32).astype(np.float64)
+    for cov in (0.3, 0.8, 0.95):
+        sel = torch.full((w.B, w.Hkv, w.Np), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((w.B, w.Hkv), dtype=torch.int32, device="cuda")
+        kv.page_topk_coverage(layer.L, bufs.head_scores, bufs.lse_partial, layer.seq_lens, w.Np, cov, sel, cnt)
+        torch.cuda.synchronize()
+        sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+        for b in range(w.B):
+            Np = oracle.num_pages(lens[b], w.P)
+            for g in range(w.Hkv):
+                s_ref = oracle.page_score(_q_ref(w, b, g), rec[b, g, :Np, 0], rec[b, g, :Np, 1:], log_n[b, :Np], w.tau)
+                S_ref = oracle.group_aggregate(s_ref)
+                k = int(cnt_h[b, g])
+                lo, hi = _coverage_bounds(S_ref, Np, cov, w.Np, 0, 0, 1e-5)
+                assert lo <= k <= hi, (cov, b, g, k, lo, hi)
+                check_selection(S_ref, k, sel_h[b, g, :k])
+
+
 # ---------------------------------------------------------------- attention
 
 @pytest.mark.parametrize("name", list(SMALL))
