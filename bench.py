@@ -329,6 +329,23 @@ def main():
             "note": "same layers, queries and attention; summaries = shared row basis + per-page mean "
                     "and variances (not the headline's per-page directions)",
         }
+    # coverage-mode selection (k per row from the mass prefix) on the headline
+    # layers' scores: its kernel time and the k it picks, for context
+    from quantized_kv_cache_summary_amd import kvsparse as kvs
+    cov_sel = [torch.empty((w.B, w.Hkv, w.Np), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+    cov_cnt = [torch.empty((w.B, w.Hkv), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+    for li in range(n_layers):
+        hz.score(layers[li], qs[li][0], bufs[li])
+    cov = {}
+    for c in (0.5, 0.95):
+        us, _ = graph_avg_us(lambda li, q: kvs.page_topk_coverage(layers[li].L, bufs[li].head_scores,
+                                                                  bufs[li].lse_partial, layers[li].seq_lens, w.Np,
+                                                                  c, cov_sel[li], cov_cnt[li]))
+        kk = cov_cnt[0].cpu().numpy()
+        cov[str(c)] = {"avg_launch_us": us, "k_mean": float(kk.mean()), "k_min": int(kk.min()),
+                       "k_max": int(kk.max())}
+    result["coverage_topk"] = cov
+    log(f"[bench] coverage-mode top-k: {cov}")
     if not args.no_cpu_baseline:
         log("[bench] oracle baseline on the host ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
