@@ -40,6 +40,7 @@ from .codec import (
     encode_group_int, encode_group_1bit, encode_vector, decode_vector,
     pack_codes, unpack_codes,
 )
+from .hotbuffer import HotBuffer, selected_physical_pages
 from .pipeline import decode_row
 
 __all__ = [
@@ -54,5 +55,6 @@ __all__ = [
     "BITS_OF_TIER", "TIER_NATIVE", "TIER_I8", "TIER_I4", "TIER_I2", "TIER_B1",
     "encode_group_int", "encode_group_1bit", "encode_vector", "decode_vector",
     "pack_codes", "unpack_codes",
+    "HotBuffer", "selected_physical_pages",
     "decode_row",
 ]

@@ -1,0 +1,75 @@
+"""Hot-buffer admission for a host-resident value pool (test infrastructure only).
+
+AMASS (amass-kv 0.1.1 project page), "What is in the box" item 2 and the
+AMASS-mem variant: the value cache lives in pinned, device-mapped host memory
+with a bounded resident hot buffer plus a staging pool, and only the pages a
+step actually calls stay in device memory.  Reading for the admission rule,
+applied once per decode step after its selection (plain LRU over buffer slots):
+
+  state:  slot_page[s]  physical page held by slot s, or -1
+          slot_stamp[s] step at which slot s was last used (0 = never)
+          hot[p]        slot holding physical page p, or -1
+  step t with selected physical pages U (every row's selection mapped through
+  the block table, duplicates removed):
+    1. every page of U that is hot has its slot stamped t;
+    2. the pages of U that are not hot, ascending by page id, are admitted into
+       the slots with the smallest (stamp, slot index) among slots whose stamp
+       is below t, one page per slot, paired in ascending order of slot index
+       with the pages in ascending order; if there are fewer such slots than
+       pages, the lowest page ids are admitted;
+    3. an admitted slot drops its old page (hot[old] = -1), takes the new one
+       and is stamped t; its V data is copied from the host pool.
+
+Pinned in tests/test_oracle_hotbuffer.py: hand-worked sequences (fill, hit,
+eviction of the least recently used, ties by slot index, more misses than free
+slots), and invariants over seeded random sequences (hot and slot_page are
+inverse maps, no more than n_slots pages hot, every page of the step hot when
+it fits).
+"""
+
+import numpy as np
+
+
+class HotBuffer:
+    def __init__(self, n_phys, n_slots):
+        self.slot_page = np.full(n_slots, -1, dtype=np.int64)
+        self.slot_stamp = np.zeros(n_slots, dtype=np.int64)
+        self.hot = np.full(n_phys, -1, dtype=np.int64)
+
+    def step(self, pages, t):
+        """Apply one step's admission; returns the (page, slot) copies, in slot order."""
+        U = np.unique(np.asarray(pages, dtype=np.int64))
+        hit = self.hot[U] >= 0
+        self.slot_stamp[self.hot[U[hit]]] = t
+        miss = U[~hit]                                   # ascending
+        free = np.nonzero(self.slot_stamp < t)[0]
+        order = np.lexsort((free, self.slot_stamp[free]))   # (stamp, slot) ascending
+        n = min(miss.size, free.size)
+        victims = np.sort(free[order[:n]])
+        admit = miss[:n]
+        copies = []
+        for p, s in zip(admit, victims):
+            old = self.slot_page[s]
+            if old >= 0:
+                self.hot[old] = -1
+            self.slot_page[s] = p
+            self.hot[p] = s
+            self.slot_stamp[s] = t
+            copies.append((int(p), int(s)))
+        return copies
+
+
+def selected_physical_pages(sel, sel_count, block_table, Hkv, seq_lens, page_size):
+    """Physical pages a step selected and attention reads: entries i < sel_count
+    (clamped to [0, k_max]) of sel [B, Hkv, k_max] with 0 <= p < Np_b."""
+    out = []
+    B, max_pages = block_table.shape
+    k_max = sel.shape[-1]
+    for b in range(B):
+        npg = min(max_pages, -(-int(seq_lens[b]) // page_size)) if seq_lens[b] > 0 else 0
+        for g in range(Hkv):
+            k = min(max(int(sel_count[b, g]), 0), k_max)
+            lp = np.asarray(sel[b, g, :k], dtype=np.int64)
+            lp = lp[(lp >= 0) & (lp < npg)]
+            out.append(block_table[b, lp])
+    return np.unique(np.concatenate(out)) if out else np.zeros(0, np.int64)
