@@ -288,6 +288,40 @@ int32_t kv_sparse_decode_attn_num_splits(const kv_layout* layout, int32_t B, int
                                          int32_t tiered);
 
 /* ---------------------------------------------------------------------------
+ * kv_hot_admit -- hot-buffer admission for a host-resident V pool (AMASS page,
+ * "What is in the box" item 2 and the AMASS-mem variant: V in pinned,
+ * device-mapped host memory, a bounded resident hot buffer plus a staging
+ * pool).  Run once per step after its attention, on a stream the next step's
+ * attention waits for.  With U = the physical pages of the step's selection
+ * (entries i < sel_count, clamped to [0, k_max], of pages 0 <= p < Np_b,
+ * through block_table; duplicates removed):
+ *   1. a page of U already hot (v_hot_slot[p] = s >= 0) stamps its slot:
+ *      slot_stamp[s] = step;
+ *   2. the pages of U that are not hot, ascending by page id, are admitted
+ *      into the slots least recently used before this step -- the smallest
+ *      (slot_stamp, slot index) among slots with slot_stamp < step -- one page
+ *      per slot, paired in ascending slot order; with fewer such slots than
+ *      pages the lowest page ids are admitted;
+ *   3. an admitted slot s drops its old page (v_hot_slot[old] = -1), takes p
+ *      (slot_page[s] = p, v_hot_slot[p] = s, slot_stamp[s] = step) and p's V
+ *      for every KV head, [Hkv][P][d] 16-bit, is copied from v16 (the pool,
+ *      [n_phys][Hkv][P][d], device-mapped host memory or device memory) into
+ *      v_hot ([n_slots][Hkv][P][d]).
+ * State, device memory owned by the caller: v_hot_slot int32 [n_phys],
+ * slot_page int32 [n_slots], slot_stamp uint32 [n_slots] (0 = never used).
+ * Initialise them consistently (all -1 / 0 for an empty buffer).  step >= 1
+ * and increasing across calls.  n_phys <= 2^19, n_slots <= 2^14.
+ * ws/ws_bytes: kv_hot_admit_workspace_size(n_slots).
+ * --------------------------------------------------------------------------- */
+int kv_hot_admit(const kv_layout* layout, const void* v16, void* v_hot, int32_t* v_hot_slot,
+                 int32_t n_phys, int32_t* slot_page, uint32_t* slot_stamp, int32_t n_slots,
+                 const int32_t* block_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                 const int32_t* sel, const int32_t* sel_count, int32_t k_max, uint32_t step,
+                 void* ws, size_t ws_bytes, void* stream);
+
+size_t kv_hot_admit_workspace_size(int32_t n_slots);
+
+/* ---------------------------------------------------------------------------
  * kv_dequant_tier -- the attention kernel's in-register tier decoding as a
  * standalone call (for tests and tier migration): K and V of physical pages
  * pages[0..n) decoded through `pages_desc` (page_entry, tiers, hot buffer) into

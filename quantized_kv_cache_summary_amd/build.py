@@ -27,6 +27,7 @@ SOURCES = {
     "summary_build.hip": [],
     "basis_build.hip": [],
     "score_basis.hip": [],
+    "hot_admit.hip": [],
     "codec.hip": ["-ffp-contract=off"],
 }
 

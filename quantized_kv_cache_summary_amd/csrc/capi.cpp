@@ -269,6 +269,29 @@ int kv_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages* pg,
                                           (hipStream_t)stream));
 }
 
+size_t kv_hot_admit_workspace_size(int32_t n_slots) {
+  return n_slots > 0 ? kvs::hot_admit_workspace_bytes(n_slots) : 0;
+}
+
+int kv_hot_admit(const kv_layout* L, const void* v16, void* v_hot, int32_t* v_hot_slot, int32_t n_phys,
+                 int32_t* slot_page, uint32_t* slot_stamp, int32_t n_slots, const int32_t* block_table,
+                 const int32_t* seq_lens, int32_t B, int32_t max_pages, const int32_t* sel,
+                 const int32_t* sel_count, int32_t k_max, uint32_t step, void* ws, size_t ws_bytes,
+                 void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0 || k_max < 0 || n_phys < 1 || n_slots < 1 || step == 0) return KV_ERR_INVALID_ARG;
+  if (n_phys > kvs::kAdmitMaxPhys || n_slots > kvs::kAdmitMaxSlots) return KV_ERR_UNSUPPORTED;
+  if (!v16 || !v_hot || !v_hot_slot || !slot_page || !slot_stamp) return KV_ERR_INVALID_ARG;
+  if (!aligned16(v16) || !aligned16(v_hot)) return KV_ERR_INVALID_ARG;
+  if (B > 0 && k_max > 0 && (!block_table || !seq_lens || !sel || !sel_count)) return KV_ERR_INVALID_ARG;
+  if ((int64_t)B * L->num_kv_heads * k_max > 0x7FFFFFFF) return KV_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < kv_hot_admit_workspace_size(n_slots)) return KV_ERR_WORKSPACE;
+  return from_hip(kvs::launch_hot_admit(*L, v16, v_hot, v_hot_slot, n_phys, slot_page, slot_stamp, n_slots,
+                                        block_table, seq_lens, B, max_pages, sel, sel_count, k_max, step,
+                                        (int32_t*)ws, (hipStream_t)stream));
+}
+
 int kv_dequant_tier(const kv_layout* L, const kv_pages* pg, const int32_t* pages, int32_t n,
                     float* out, void* stream) {
   int rc = check_layout(L);

@@ -26,7 +26,7 @@ SYMBOLS = (
     "kv_page_topk_workspace_size", "kv_sparse_decode_attn", "kv_sparse_decode_attn_workspace_size",
     "kv_sparse_decode_attn_num_splits", "kv_dequant_tier", "kv_pack_tier", "kv_status_string",
     "kv_basis_build", "kv_basis_build_workspace_size", "kv_summary_build_basis", "kv_page_score_basis",
-    "kv_page_topk_coverage",
+    "kv_page_topk_coverage", "kv_hot_admit", "kv_hot_admit_workspace_size",
 )
 
 
@@ -74,6 +74,9 @@ def lib():
             "kv_page_topk": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _I, _P, _P, _I, _P,
                                   _P, _SZ, _P]),
             "kv_page_topk_workspace_size": (_SZ, [_LP, _I, _I]),
+            "kv_hot_admit": (_I, [_LP, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, ctypes.c_uint32,
+                                  _P, _SZ, _P]),
+            "kv_hot_admit_workspace_size": (_SZ, [_I]),
             "kv_page_topk_coverage": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P, _I, _P,
                                            _P, _SZ, _P]),
             "kv_sparse_decode_attn": (_I, [_LP, _P, _PP, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _P,
@@ -217,6 +220,22 @@ def page_topk_coverage(L, head_scores, lse_partial, seq_lens, max_pages, coverag
                                      _p(sel), _p(sel_count), int(k_max), _p(page_S), _p(ws),
                                      0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "kv_page_topk_coverage")
+
+
+def hot_admit_workspace_size(n_slots):
+    return int(lib().kv_hot_admit_workspace_size(int(n_slots)))
+
+
+def hot_admit(L, v16_ptr, v_hot, v_hot_slot, slot_page, slot_stamp, block_table, seq_lens, sel, sel_count, step,
+              ws, stream=None):
+    """v16_ptr: device address (int) of the V pool, which may be device-mapped host memory."""
+    B, max_pages = block_table.shape
+    rc = lib().kv_hot_admit(ctypes.byref(L), ctypes.c_void_p(v16_ptr), _p(v_hot), _p(v_hot_slot),
+                            int(v_hot_slot.shape[0]), _p(slot_page), _p(slot_stamp), int(slot_page.shape[0]),
+                            _p(block_table), _p(seq_lens), int(B), int(max_pages), _p(sel), _p(sel_count),
+                            int(sel.shape[-1]), int(step), _p(ws), ws.numel() * ws.element_size(),
+                            _stream(stream))
+    _check(rc, "kv_hot_admit")
 
 
 def attn_num_splits(L, B, k_max, tiered=False):

@@ -1,0 +1,120 @@
+"""GPU parity of hot-buffer admission (kv_hot_admit) against the oracle's rule.
+
+Over a sequence of steps with seeded selections, after every step the three
+state arrays (page -> slot, slot -> page, slot stamps) must equal the oracle's
+exactly, and every hot slot must hold its page's V bit for bit.  With the V pool
+in pinned, device-mapped host memory, attention results must not depend on
+which pages are hot (the same bits are read from either place).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_kv_cache_summary_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+W = wl.WORKLOADS
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def hz():
+    from quantized_kv_cache_summary_amd import harness
+    return harness
+
+
+def _step_selection(w, rng, k_max, lens):
+    """A step's selection: per row a random count in [0, k_max] of sorted distinct pages
+    (some past the row's length, some -1 padding), as the top-k would leave it."""
+    sel = np.full((w.B, w.Hkv, k_max), -1, dtype=np.int32)
+    cnt = np.zeros((w.B, w.Hkv), dtype=np.int32)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            k = int(rng.integers(0, k_max + 1))
+            pick = np.sort(rng.choice(w.Np, size=min(k, w.Np), replace=False))
+            sel[b, g, :pick.size] = pick
+            cnt[b, g] = pick.size + (1 if rng.random() < 0.1 else 0)   # a count past the list
+    return sel, cnt
+
+
+@pytest.mark.parametrize("name,n_slots", [("llama_small", 40), ("heavy_small", 13), ("heavy_small", 400)])
+def test_admission_matches_oracle(hz, name, n_slots):
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    w = {"llama_small": W["llama8b_32k"].replace(B=2, ctx=16 * 300 + 7),
+         "heavy_small": W["heavy70b_128k"].replace(B=2, Hq=16, Hkv=2, ctx=32 * 150 + 5, v_host=False)}[name]
+    announce(f"hot admission {name} slots={n_slots}")
+    lens = [w.ctx, w.ctx - 7 * w.P]
+    layer = hz.DeviceLayer(w, summaries=None, seq_lens=lens)
+    L = layer.L
+    n_phys = w.n_phys
+    hot = torch.full((n_phys,), -1, dtype=torch.int32, device="cuda")
+    slot_page = torch.full((n_slots,), -1, dtype=torch.int32, device="cuda")
+    slot_stamp = torch.zeros((n_slots,), dtype=torch.int32, device="cuda")
+    v_hot = torch.zeros((n_slots, w.Hkv, w.P, w.d), dtype=layer.v16.dtype, device="cuda")
+    ws = torch.zeros(kv.hot_admit_workspace_size(n_slots) // 4, dtype=torch.int32, device="cuda")
+    ref = oracle.HotBuffer(n_phys, n_slots)
+    rng = np.random.default_rng(41 + n_slots)
+    k_max = 12
+    v_all = layer.v16.view(torch.int16).cpu().numpy().reshape(n_phys, -1)
+    for t in range(1, 16):
+        sel, cnt = _step_selection(w, rng, k_max, lens)
+        kv.hot_admit(L, layer.v16.data_ptr(), v_hot, hot, slot_page, slot_stamp, layer.bt, layer.seq_lens,
+                     torch.from_numpy(sel).cuda(), torch.from_numpy(cnt).cuda(), t, ws)
+        torch.cuda.synchronize()
+        U = oracle.selected_physical_pages(sel, cnt, layer.bt_np, w.Hkv, np.array(lens), w.P)
+        copies = ref.step(U, t)
+        assert np.array_equal(hot.cpu().numpy(), ref.hot), t
+        assert np.array_equal(slot_page.cpu().numpy(), ref.slot_page), t
+        assert np.array_equal(slot_stamp.cpu().numpy().astype(np.int64), ref.slot_stamp), t
+        wsn = ws.cpu().numpy()
+        assert wsn[0] == len(copies) and [tuple(x) for x in wsn[1:1 + 2 * len(copies)].reshape(-1, 2)] == copies
+        vh = v_hot.view(torch.int16).cpu().numpy().reshape(n_slots, -1)
+        for s, p in enumerate(ref.slot_page):
+            if p >= 0:
+                assert np.array_equal(vh[s], v_all[p]), (t, s, p)
+
+
+def test_admission_from_host_mapped_pool_keeps_attention(hz):
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    w = W["heavy70b_128k"].replace(B=2, Hq=16, Hkv=2, ctx=32 * 150 + 5)     # V in mapped host memory
+    announce("hot admission from host-mapped V")
+    layer = hz.DeviceLayer(w, summaries="build", hot_mode="cold")
+    try:
+        q = hz.queries_device(w)
+        bufs = hz.StepBuffers(w)
+        hz.score(layer, q, bufs)
+        hz.topk(layer, bufs)
+        hz.attend(layer, q, bufs)
+        torch.cuda.synchronize()
+        out0, lse0 = bufs.out.cpu().numpy().copy(), bufs.lse.cpu().numpy().copy()
+        n_slots = layer.v_hot.shape[0]
+        slot_page = torch.from_numpy(np.array(layer.hot_pages, dtype=np.int32)).cuda()
+        if slot_page.numel() < n_slots:
+            slot_page = torch.cat([slot_page, torch.full((n_slots - slot_page.numel(),), -1, dtype=torch.int32,
+                                                          device="cuda")])
+        slot_stamp = torch.zeros(n_slots, dtype=torch.int32, device="cuda")
+        hot = layer.v_hot_slot.clone()
+        ws = torch.zeros(kv.hot_admit_workspace_size(n_slots) // 4, dtype=torch.int32, device="cuda")
+        kv.hot_admit(layer.L, layer.host_v.dev.value, layer.v_hot, hot, slot_page, slot_stamp, layer.bt,
+                     layer.seq_lens, bufs.sel, bufs.sel_count, 1, ws)
+        torch.cuda.synchronize()
+        layer.v_hot_slot = hot
+        layer.pages = layer._make_pages()
+        # every selected page is hot now (the step fits the buffer) ...
+        sel, cnt = bufs.sel.cpu().numpy(), bufs.sel_count.cpu().numpy()
+        U = oracle.selected_physical_pages(sel, cnt, layer.bt_np, w.Hkv, layer.seq_lens_np, w.P)
+        if U.size <= n_slots:
+            assert np.all(hot.cpu().numpy()[U] >= 0)
+        # ... and attention reads the same bits from the buffer
+        hz.attend(layer, q, bufs)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bufs.out.cpu().numpy(), out0)
+        np.testing.assert_array_equal(bufs.lse.cpu().numpy(), lse0)
+    finally:
+        layer.release()
