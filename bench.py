@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy (known bytes) for scaling counter readings")
+    ap.add_argument("--mem-kv", action="store_true",
+                    help="host-resident workloads: also time the variant with K in host memory too")
     ap.add_argument("--groups", type=int, default=1,
                     help="row groups per step, each on its own stream (1 = one chain for the batch)")
     return ap.parse_args()
@@ -132,8 +134,10 @@ def main():
     from quantized_kv_cache_summary_amd import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
-    if w.v_host or w.tier_fracs is not None:
-        raise SystemExit("bench.py times the resident native-tier workloads; see the tests for the others")
+    if w.v_host:
+        return mem_main(args, w)
+    if w.tier_fracs is not None:
+        raise SystemExit("bench.py times the native-tier workloads; the tiered one is covered by the tests")
     torch.cuda.set_device(0)
     # bytes one step touches: every summary record plus the selected K/V pages
     touched = w.rows * w.Np * ((1 + w.rank) * w.d * 2 + 4) + w.rows * w.k_of(w.Np) * w.P * w.d * 2 * 2
@@ -351,6 +355,145 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     for l in layers:
         l.release()
+    print(json.dumps(result), flush=True)
+
+
+def selected_pages(sel, sel_count, bt, seq_lens, P):
+    """Physical page of every valid selection entry of one step (one per
+    (row, page) read, so a page appears once per KV head that selected it)."""
+    import numpy as np
+    B, Hkv, k_max = sel.shape
+    npg = np.minimum(bt.shape[1], -(-seq_lens.astype(np.int64) // P))
+    idx = np.arange(k_max)[None, None, :]
+    ok = (idx < np.clip(sel_count, 0, k_max)[:, :, None]) & (sel >= 0) & (sel < npg[:, None, None])
+    b = np.broadcast_to(np.arange(B)[:, None, None], sel.shape)
+    return bt[b[ok], sel[ok]]
+
+
+def mem_main(args, w):
+    """The host-resident workload: V (and with --mem-kv K too) in pinned,
+    device-mapped host memory with an HBM hot buffer of a fixed share of the
+    pages.  One layer; each step uses a different query.  Timed: steps with the
+    hot buffer left as set up (the headline value), steps with LRU admission
+    after every step on a side stream (kv_hot_admit), and the same for mem-kv."""
+    import numpy as np
+    import torch
+    from quantized_kv_cache_summary_amd import harness as hz
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    nq = max(args.queries, 2)
+
+    def run(layer, admit):
+        qs = [hz.queries_device(w, 0, j) for j in range(nq)]
+        ms = hz.MemStep(layer, admit=admit)
+        for i in range(W):
+            ms(qs[i % nq])
+        ms.finish()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(K):
+            ms(qs[(W + i) % nq])
+        ms.finish()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms_step = a.elapsed_time(b) / K
+        # untimed pass: attention and admission per step, hot share of the pages read
+        att, adm, hit, n_sel, cold, copies = [], [], [], [], [], []
+        for i in range(min(K, 6)):
+            bufs = ms.bufs[ms.t & 1]
+            q = qs[(W + K + i) % nq]
+            hz.score(layer, q, bufs)
+            hz.topk(layer, bufs)
+            ms.finish()
+            torch.cuda.synchronize()
+            reads = selected_pages(bufs.sel.cpu().numpy(), bufs.sel_count.cpu().numpy(), layer.bt_np,
+                                   layer.seq_lens_np, w.P)
+            hot_map = layer.v_hot_slot.cpu().numpy()
+            U = np.unique(reads)
+            hit.append(float((hot_map[U] >= 0).mean()) if U.size else 0.0)
+            n_sel.append(int(U.size))
+            cold.append(int((hot_map[reads] < 0).sum()))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            hz.attend(layer, q, bufs)
+            e1.record(stream)
+            ms.t += 1
+            if admit:
+                ms.side.wait_stream(stream)
+                ms.admit_start.record(ms.side)
+                from quantized_kv_cache_summary_amd import kvsparse as kv
+                kv.hot_admit(layer.L, layer.host_v.dev.value, layer.v_hot, layer.v_hot_slot, ms.slot_page,
+                             ms.slot_stamp, layer.bt, layer.seq_lens, bufs.sel, bufs.sel_count, ms.t, ms.ws, ms.side,
+                             k16_ptr=layer.host_k.dev.value if layer.host_k is not None else None,
+                             k_hot=layer.k_hot)
+                ms.admitted.record(ms.side)
+            torch.cuda.synchronize()
+            att.append(e0.elapsed_time(e1) * 1e3)
+            if admit:
+                adm.append(ms.admit_start.elapsed_time(ms.admitted) * 1e3)
+                copies.append(int(ms.ws[0].item()))
+        sel_counts = ms.bufs[0].sel_count.cpu().numpy()
+        return {"ms_per_step": ms_step, "value": 1e3 / ms_step, "unit": "steps/s", "steps": K,
+                "attention_us": float(np.median(att)), "admission_us": float(np.median(adm)) if adm else None,
+                "pages_copied_per_step": float(np.mean(copies)) if copies else 0.0,
+                "hot_share_of_pages_read": float(np.mean(hit)), "distinct_pages_read": float(np.mean(n_sel)),
+                "host_bytes_read_by_attention": float(np.mean(cold)) * w.P * w.d * 2 *
+                (2 if layer.host_k is not None else 1),
+                "hot_slots": int(layer.v_hot.shape[0])}, sel_counts
+
+    t0 = time.time()
+    layer = hz.DeviceLayer(w, summaries="build", hot_mode="cold")
+    log(f"[bench] {w.name}: set-up {time.time() - t0:.1f}s")
+    static, sel_counts = run(layer, False)
+    log(f"[bench] static hot buffer: {static}")
+    admitted, _ = run(layer, True)
+    log(f"[bench] with admission: {admitted}")
+    layer.release()
+    memkv = None
+    if args.mem_kv:
+        t0 = time.time()
+        layer = hz.DeviceLayer(w, summaries="build", hot_mode="cold", host_k=True)
+        log(f"[bench] {w.name} mem-kv: set-up {time.time() - t0:.1f}s")
+        memkv = {"static": run(layer, False)[0], "admission": run(layer, True)[0]}
+        log(f"[bench] mem-kv: {memkv}")
+        layer.release()
+
+    summary_b, selected_b = algorithmic_bytes(w, sel_counts)
+    page_v = w.Hkv * w.P * w.d * 2
+    result = {
+        "metric": METRIC,
+        "value": static["value"],
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": static["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) keys/values with planted hot pages; no dataset)",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "page_size": w.P, "ctx": w.ctx, "rank": w.rank, "keep": w.keep,
+                   "hot_buffer_frac": w.hot_buffer_frac, "timing": "eager, one layer, HIP events",
+                   "value_pool": "pinned device-mapped host memory"},
+        "algorithmic_bytes_per_step": {"summaries": summary_b, "selected_kv": selected_b},
+        "host_link": {
+            "note": "V of selected pages not in the hot buffer is read over the host link by the attention "
+                    "kernel (one KV head's part per selecting row)",
+            "bytes_per_step": static["host_bytes_read_by_attention"],
+            "achieved_GBps": static["host_bytes_read_by_attention"] / (static["attention_us"] * 1e3),
+            "admission_copy_GBps": (admitted["pages_copied_per_step"] * page_v / (admitted["admission_us"] * 1e3)
+                                    if admitted["admission_us"] else None),
+        },
+        "static_hot_buffer": static,
+        "lru_admission": admitted,
+        "mem_kv": memkv,
+        "cpu_baseline": None,
+    }
     print(json.dumps(result), flush=True)
 
 

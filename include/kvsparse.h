@@ -107,7 +107,13 @@ typedef struct kv_layout {
  *     v_hot_slot[phys] >= 0, else from v16[slot]; v16 may then be pinned host
  *     memory mapped into the device address space (zero-copy reads over the
  *     host link).  AMASS page, section "What is in the box" item 2 (the DRAM
- *     value tier with a bounded resident hot buffer). */
+ *     value tier with a bounded resident hot buffer).
+ *   k_hot != NULL (needs v_hot_slot): the mem-kv variant (AMASS page, table
+ *     "Two variants, one algorithm": K and V both offloaded).  A hot slot holds
+ *     the page's K as well, K of page phys is read from k_hot[v_hot_slot[phys]]
+ *     ([hot][Hkv][P][d] 16-bit) when that slot is >= 0, else from k16[slot],
+ *     which may then be device-mapped host memory too.  Native pages only: a
+ *     packed tier's codes stay where kq/vq point. */
 typedef struct kv_pages {
   const void* k16;
   const void* v16;
@@ -118,6 +124,7 @@ typedef struct kv_pages {
   const uint32_t* page_entry;
   const void* v_hot;
   const int32_t* v_hot_slot;
+  const void* k_hot;
 } kv_pages;
 
 /* ---------------------------------------------------------------------------
@@ -306,15 +313,17 @@ int32_t kv_sparse_decode_attn_num_splits(const kv_layout* layout, int32_t B, int
  *      (slot_page[s] = p, v_hot_slot[p] = s, slot_stamp[s] = step) and p's V
  *      for every KV head, [Hkv][P][d] 16-bit, is copied from v16 (the pool,
  *      [n_phys][Hkv][P][d], device-mapped host memory or device memory) into
- *      v_hot ([n_slots][Hkv][P][d]).
+ *      v_hot ([n_slots][Hkv][P][d]); with k16 and k_hot given (the mem-kv
+ *      variant, both or neither) p's K is copied from k16 into k_hot the same
+ *      way.
  * State, device memory owned by the caller: v_hot_slot int32 [n_phys],
  * slot_page int32 [n_slots], slot_stamp uint32 [n_slots] (0 = never used).
  * Initialise them consistently (all -1 / 0 for an empty buffer).  step >= 1
  * and increasing across calls.  n_phys <= 2^19, n_slots <= 2^14.
  * ws/ws_bytes: kv_hot_admit_workspace_size(n_slots).
  * --------------------------------------------------------------------------- */
-int kv_hot_admit(const kv_layout* layout, const void* v16, void* v_hot, int32_t* v_hot_slot,
-                 int32_t n_phys, int32_t* slot_page, uint32_t* slot_stamp, int32_t n_slots,
+int kv_hot_admit(const kv_layout* layout, const void* v16, void* v_hot, const void* k16, void* k_hot,
+                 int32_t* v_hot_slot, int32_t n_phys, int32_t* slot_page, uint32_t* slot_stamp, int32_t n_slots,
                  const int32_t* block_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,
                  const int32_t* sel, const int32_t* sel_count, int32_t k_max, uint32_t step,
                  void* ws, size_t ws_bytes, void* stream);

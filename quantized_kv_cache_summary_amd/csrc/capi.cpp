@@ -78,6 +78,7 @@ int check_pages(const kv_layout* L, const kv_pages* pg) {
     }
   }
   if (pg->v_hot_slot && (!pg->v_hot || !aligned16(pg->v_hot))) return KV_ERR_INVALID_ARG;
+  if (pg->k_hot && (!pg->v_hot_slot || !aligned16(pg->k_hot))) return KV_ERR_INVALID_ARG;
   (void)L;
   return KV_OK;
 }
@@ -273,7 +274,8 @@ size_t kv_hot_admit_workspace_size(int32_t n_slots) {
   return n_slots > 0 ? kvs::hot_admit_workspace_bytes(n_slots) : 0;
 }
 
-int kv_hot_admit(const kv_layout* L, const void* v16, void* v_hot, int32_t* v_hot_slot, int32_t n_phys,
+int kv_hot_admit(const kv_layout* L, const void* v16, void* v_hot, const void* k16, void* k_hot,
+                 int32_t* v_hot_slot, int32_t n_phys,
                  int32_t* slot_page, uint32_t* slot_stamp, int32_t n_slots, const int32_t* block_table,
                  const int32_t* seq_lens, int32_t B, int32_t max_pages, const int32_t* sel,
                  const int32_t* sel_count, int32_t k_max, uint32_t step, void* ws, size_t ws_bytes,
@@ -284,10 +286,11 @@ int kv_hot_admit(const kv_layout* L, const void* v16, void* v_hot, int32_t* v_ho
   if (n_phys > kvs::kAdmitMaxPhys || n_slots > kvs::kAdmitMaxSlots) return KV_ERR_UNSUPPORTED;
   if (!v16 || !v_hot || !v_hot_slot || !slot_page || !slot_stamp) return KV_ERR_INVALID_ARG;
   if (!aligned16(v16) || !aligned16(v_hot)) return KV_ERR_INVALID_ARG;
+  if (!k16 != !k_hot || (k16 && (!aligned16(k16) || !aligned16(k_hot)))) return KV_ERR_INVALID_ARG;
   if (B > 0 && k_max > 0 && (!block_table || !seq_lens || !sel || !sel_count)) return KV_ERR_INVALID_ARG;
   if ((int64_t)B * L->num_kv_heads * k_max > 0x7FFFFFFF) return KV_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < kv_hot_admit_workspace_size(n_slots)) return KV_ERR_WORKSPACE;
-  return from_hip(kvs::launch_hot_admit(*L, v16, v_hot, v_hot_slot, n_phys, slot_page, slot_stamp, n_slots,
+  return from_hip(kvs::launch_hot_admit(*L, v16, v_hot, k16, k_hot, v_hot_slot, n_phys, slot_page, slot_stamp, n_slots,
                                         block_table, seq_lens, B, max_pages, sel, sel_count, k_max, step,
                                         (int32_t*)ws, (hipStream_t)stream));
 }

@@ -12,7 +12,8 @@
 //      slots stamped below the step), one per slot, paired in ascending slot
 //      order; with fewer such slots than pages, the lowest page ids win;
 //   3. an admitted slot drops its old page, takes the new one, is stamped, and
-//      the page's V (every KV head) is copied in from the pool.
+//      the page's V (every KV head) is copied in from the pool; with a K hot
+//      buffer (the mem-kv variant: K offloaded as well) its K too.
 //
 // One block plans the step: U as a bitmap in LDS (integer atomics), the misses
 // by an ordered compaction of the bitmap, the victim slots as the k largest of
@@ -162,21 +163,25 @@ __global__ __launch_bounds__(kAdmitThreads) void hot_admit_plan_kernel(
   });
 }
 
-// Copies V of the admitted pages (all KV heads, P x d 16-bit values each):
-// block i copies pair i of the plan; blocks past the plan's count exit.
+// Copies the admitted pages (all KV heads, P x d 16-bit values each): block
+// (i, 0) copies V of pair i, block (i, 1) its K; blocks past the plan's count exit.
 __global__ __launch_bounds__(256) void hot_admit_copy_kernel(const uint16_t* __restrict__ v16,
-                                                             uint16_t* __restrict__ v_hot, size_t page_elems,
+                                                             uint16_t* __restrict__ v_hot,
+                                                             const uint16_t* __restrict__ k16,
+                                                             uint16_t* __restrict__ k_hot, size_t page_elems,
                                                              const int32_t* __restrict__ ws) {
   const int i = blockIdx.x;
   if (i >= ws[0]) return;
   const int p = ws[1 + 2 * i], s = ws[2 + 2 * i];
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(v16 + (size_t)p * page_elems);
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(v_hot + (size_t)s * page_elems);
+  const bool is_k = blockIdx.y == 1;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>((is_k ? k16 : v16) + (size_t)p * page_elems);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>((is_k ? k_hot : v_hot) + (size_t)s * page_elems);
   const size_t n16 = page_elems / 8;
   for (size_t j = threadIdx.x; j < n16; j += 256) dst[j] = src[j];
 }
 
-hipError_t launch_hot_admit(const kv_layout& L, const void* v16, void* v_hot, int32_t* hot, int n_phys,
+hipError_t launch_hot_admit(const kv_layout& L, const void* v16, void* v_hot, const void* k16, void* k_hot,
+                            int32_t* hot, int n_phys,
                             int32_t* slot_page, uint32_t* slot_stamp, int n_slots, const int32_t* block_table,
                             const int32_t* seq_lens, int B, int max_pages, const int32_t* sel,
                             const int32_t* sel_count, int k_max, uint32_t step, int32_t* ws, hipStream_t st) {
@@ -190,8 +195,8 @@ hipError_t launch_hot_admit(const kv_layout& L, const void* v16, void* v_hot, in
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t page_elems = (size_t)L.num_kv_heads * L.page_size * L.head_dim;
-  hipLaunchKernelGGL(hot_admit_copy_kernel, dim3(n_slots), dim3(256), 0, st, (const uint16_t*)v16,
-                     (uint16_t*)v_hot, page_elems, ws);
+  hipLaunchKernelGGL(hot_admit_copy_kernel, dim3(n_slots, k_hot ? 2 : 1), dim3(256), 0, st, (const uint16_t*)v16,
+                     (uint16_t*)v_hot, (const uint16_t*)k16, (uint16_t*)k_hot, page_elems, ws);
   return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ constexpr int kAdmitMaxPhys = 1 << 19;
 constexpr int kAdmitMaxSlots = 1 << 14;
 inline size_t hot_admit_workspace_bytes(int n_slots) { return (size_t)(1 + 3 * n_slots) * sizeof(int32_t); }
 
-hipError_t launch_hot_admit(const kv_layout& L, const void* v16, void* v_hot, int32_t* hot, int n_phys,
+hipError_t launch_hot_admit(const kv_layout& L, const void* v16, void* v_hot, const void* k16, void* k_hot,
+                            int32_t* hot, int n_phys,
                             int32_t* slot_page, uint32_t* slot_stamp, int n_slots, const int32_t* block_table,
                             const int32_t* seq_lens, int B, int max_pages, const int32_t* sel,
                             const int32_t* sel_count, int k_max, uint32_t step, int32_t* ws, hipStream_t st);

@@ -44,6 +44,7 @@ struct PagesDev {
   const uint32_t* page_entry;
   const uint16_t* v_hot;
   const int32_t* v_hot_slot;
+  const uint16_t* k_hot;
 };
 
 // ---------------------------------------------------------------- packed decode
@@ -320,8 +321,9 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
           const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, jj);
           const int hot = __builtin_amdgcn_readlane(l_hot, jj);
           const size_t pr = (size_t)slot * Hkv + g;
-          const uint16_t* kb = pg.k16 + pr * page_elems;
-          const uint16_t* vb = hot >= 0 ? pg.v_hot + ((size_t)hot * Hkv + g) * page_elems : pg.v16 + pr * page_elems;
+          const size_t hr = ((size_t)hot * Hkv + g) * page_elems;
+          const uint16_t* kb = hot >= 0 && pg.k_hot ? pg.k_hot + hr : pg.k16 + pr * page_elems;
+          const uint16_t* vb = hot >= 0 ? pg.v_hot + hr : pg.v16 + pr * page_elems;
           load_native_chunk<D>(r[u], kb, vb, ci - jj * cpp, col, grp);
         }
       };
@@ -376,8 +378,9 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
         const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, jj);
         const int hot = __builtin_amdgcn_readlane(l_hot, jj);
         const size_t pr = (size_t)slot * Hkv + g;
-        const uint16_t* kbase = pg.k16 + pr * page_elems;
-        const uint16_t* vbase = hot >= 0 ? pg.v_hot + ((size_t)hot * Hkv + g) * page_elems : pg.v16 + pr * page_elems;
+        const size_t hr = ((size_t)hot * Hkv + g) * page_elems;
+        const uint16_t* kbase = hot >= 0 && pg.k_hot ? pg.k_hot + hr : pg.k16 + pr * page_elems;
+        const uint16_t* vbase = hot >= 0 ? pg.v_hot + hr : pg.v16 + pr * page_elems;
         for (int c = 0; c < cpp; ++c) {
           const int tok0 = p * P + c * 16;
           f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
@@ -593,6 +596,7 @@ static PagesDev to_dev(const kv_pages& pg) {
   d.page_entry = pg.page_entry;
   d.v_hot = (const uint16_t*)pg.v_hot;
   d.v_hot_slot = pg.v_hot_slot;
+  d.k_hot = (const uint16_t*)pg.k_hot;
   return d;
 }
 
@@ -638,9 +642,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(PagesDev pg, const int32_t
     float x[RUN];
     if (tier == KV_TIER_NATIVE) {
       const uint16_t* src = (kv == 0 ? pg.k16 : pg.v16) + prow * D;
-      if (kv == 1 && pg.v_hot_slot) {
+      if (pg.v_hot_slot && (kv == 1 || pg.k_hot)) {
         const int hs = pg.v_hot_slot[phys];
-        if (hs >= 0) src = pg.v_hot + (((size_t)hs * Hkv + g) * P + tk) * D;
+        if (hs >= 0) src = (kv == 0 ? pg.k_hot : pg.v_hot) + (((size_t)hs * Hkv + g) * P + tk) * D;
       }
       const u32x4_t w = ld16(src + run * RUN);
 #pragma unroll

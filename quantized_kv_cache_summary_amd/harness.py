@@ -61,16 +61,24 @@ class DeviceLayer:
     """K/V pools, block table, summaries (and tier pools / host V) of one layer."""
 
     def __init__(self, w: wl.Workload, layer=0, summaries="build", device="cuda", host_v=None,
-                 hot_mode="warm", seq_lens=None, threads=None):
+                 hot_mode="warm", seq_lens=None, threads=None, host_k=None):
         self.w, self.layer, self.device = w, layer, device
         self.L = layout_of(w)
         host_v = w.v_host if host_v is None else host_v
+        host_k = w.k_host if host_k is None else host_k
+        if host_k and (not host_v or w.tier_fracs is not None):
+            raise ValueError("a host-resident K pool needs a host-resident V pool and native pages only")
         shape = (w.n_phys, w.Hkv, w.P, w.d)
         self.bt_np = wl.block_table(w, layer)
         self.bt = torch.from_numpy(self.bt_np).to(device)
         self.seq_lens_np = wl.seq_lens(w) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
         self.seq_lens = torch.from_numpy(self.seq_lens_np).to(device)
-        kbits = np.empty(shape, dtype=np.uint16)
+        self.host_k = None
+        if host_k:
+            self.host_k = MappedHostBuffer(int(np.prod(shape)) * 2)
+            kbits = self.host_k.numpy(np.uint16, shape)
+        else:
+            kbits = np.empty(shape, dtype=np.uint16)
         self.host_v = None
         if host_v:
             self.host_v = MappedHostBuffer(int(np.prod(shape)) * 2)
@@ -78,7 +86,10 @@ class DeviceLayer:
         else:
             vbits = np.empty(shape, dtype=np.uint16)
         wl.fill_pools(w, layer, kbits, vbits, self.bt_np, threads=threads)
-        self.k16 = to_device16(kbits, w.dtype, device)
+        # the K pool as the kernels take it: a device tensor, or the device
+        # address of the mapped host pool
+        self.k16 = None if host_k else to_device16(kbits, w.dtype, device)
+        self.k_src = self.host_k.dev.value if host_k else self.k16
         del kbits
         self.v16 = None if host_v else to_device16(vbits, w.dtype, device)
         del vbits
@@ -113,7 +124,7 @@ class DeviceLayer:
         self.page_entry = None
         if w.tier_fracs is not None:
             self._pack_tiers()
-        self.v_hot = None
+        self.v_hot = self.k_hot = None
         self.v_hot_slot = None
         if host_v:
             self._init_hot_buffer(hot_mode)
@@ -128,7 +139,7 @@ class DeviceLayer:
     # summary of every logical page, over its valid tokens (0 -> empty record)
     def build_summaries(self, stream=None):
         entries, nv = self._all_entries()
-        kv.summary_build(self.L, self.k16, self.bt, entries, nv, self.summary, self.log_n, stream)
+        kv.summary_build(self.L, self.k_src, self.bt, entries, nv, self.summary, self.log_n, stream)
 
     def with_basis_summaries(self, stream=None):
         """The same layer (pools, block table, tiers, host V shared) scored from
@@ -141,7 +152,7 @@ class DeviceLayer:
         v.mu = torch.empty((w.B, w.Hkv, w.Np, w.d), dtype=torch.bfloat16, device=self.device)
         v.lam = torch.empty((w.B, w.Hkv, w.Np, w.rank), dtype=torch.float32, device=self.device)
         v.log_n = torch.empty_like(self.log_n)
-        v.host_v = None
+        v.host_v = v.host_k = None
         v.build_basis(stream)
         v.build_basis_summaries(stream)
         return v
@@ -158,7 +169,7 @@ class DeviceLayer:
         w = self.w
         nb = kv.basis_build_workspace_size(self.L, w.B, w.Np)
         ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device=self.device)
-        kv.basis_build(self.L, self.k16, self.bt, self.seq_lens, self.basis, ws, stream)
+        kv.basis_build(self.L, self.k_src, self.bt, self.seq_lens, self.basis, ws, stream)
         if stream is None:
             torch.cuda.current_stream().synchronize()
         del ws
@@ -166,7 +177,7 @@ class DeviceLayer:
     # shared-basis statistics of every logical page (0 valid tokens -> zeros)
     def build_basis_summaries(self, stream=None):
         entries, nv = self._all_entries()
-        kv.summary_build_basis(self.L, self.k16, self.bt, entries, nv, self.basis, self.mu, self.lam,
+        kv.summary_build_basis(self.L, self.k_src, self.bt, entries, nv, self.basis, self.mu, self.lam,
                                self.log_n, stream)
 
     def _pack_tiers(self):
@@ -201,6 +212,8 @@ class DeviceLayer:
         n_slots = max(1, int(round(w.hot_buffer_frac * w.n_phys)))
         self.n_hot = n_slots
         self.v_hot = torch.empty((n_slots, w.Hkv, w.P, w.d), dtype=TORCH16[w.dtype], device=self.device)
+        if self.host_k is not None:
+            self.k_hot = torch.empty_like(self.v_hot)
         self.set_hot_pages(np.zeros(0, np.int64) if sel_pages is None else sel_pages, fill_random=True)
 
     def set_hot_pages(self, must_include, fill_random=True):
@@ -212,6 +225,10 @@ class DeviceLayer:
         vh = self.host_v.numpy(np.uint16, (w.n_phys, w.Hkv, w.P, w.d))
         stage = torch.from_numpy(np.ascontiguousarray(vh[chosen]).view(np.int16)).view(TORCH16[w.dtype])
         self.v_hot[: len(chosen)].copy_(stage.to(self.device))
+        if self.host_k is not None:
+            kh = self.host_k.numpy(np.uint16, (w.n_phys, w.Hkv, w.P, w.d))
+            stage = torch.from_numpy(np.ascontiguousarray(kh[chosen]).view(np.int16)).view(TORCH16[w.dtype])
+            self.k_hot[: len(chosen)].copy_(stage.to(self.device))
         self.hot_pages = chosen
         self.pages = self._make_pages()
 
@@ -222,13 +239,17 @@ class DeviceLayer:
             return kv.make_pages(self.k16, v16, self.kq, self.vq, self.ksz, self.vsz, self.page_entry,
                                  self.v_hot, self.v_hot_slot, v16_ptr=v16_ptr)
         return kv.make_pages(self.k16, v16, page_entry=None, v_hot=self.v_hot, v_hot_slot=self.v_hot_slot,
-                             v16_ptr=v16_ptr)
+                             v16_ptr=v16_ptr, k_hot=self.k_hot,
+                             k16_ptr=self.host_k.dev.value if self.host_k is not None else None)
 
     def release(self):
-        if self.host_v is not None:
+        if self.host_v is not None or self.host_k is not None:
             torch.cuda.synchronize()
-            self.host_v.free()
-            self.host_v = None
+        for name in ("host_v", "host_k"):
+            buf = getattr(self, name)
+            if buf is not None:
+                buf.free()
+                setattr(self, name, None)
 
 
 # ------------------------------------------------------------------ step buffers
@@ -347,3 +368,60 @@ class SplitStep:
                                       v.out, v.lse, v.ws, self.num_splits, s)
         for s in self.streams:
             main.wait_stream(s)
+
+
+# ------------------------------------------------------------------ host-resident pool with admission
+
+class MemStep:
+    """Decode steps over a host-resident V (or K and V) pool with hot-buffer
+    admission after every step (kv_hot_admit).
+
+    Per step, on the caller's stream: score, top-k, then attention once the
+    previous step's admission has finished (the hot map and the buffer must be
+    consistent while attention reads them).  This step's admission then runs
+    on a side stream (default priority) and overlaps the next step's score and
+    top-k.  Two step buffers alternate, so the admission reads a selection the
+    next top-k does not overwrite.  With admit=False the hot buffer stays as
+    the layer set it up."""
+
+    def __init__(self, layer: DeviceLayer, admit=True):
+        w = layer.w
+        if layer.v_hot is None:
+            raise ValueError("MemStep needs a layer with a host-resident pool and a hot buffer")
+        self.layer, self.admit = layer, admit
+        self.bufs = [StepBuffers(w, layer.device), StepBuffers(w, layer.device)]
+        n_slots = layer.v_hot.shape[0]
+        sp = np.full(n_slots, -1, dtype=np.int32)
+        sp[: len(layer.hot_pages)] = np.asarray(layer.hot_pages, dtype=np.int32)
+        self.slot_page = torch.from_numpy(sp).to(layer.device)
+        self.slot_stamp = torch.zeros(n_slots, dtype=torch.int32, device=layer.device)
+        self.ws = torch.zeros(kv.hot_admit_workspace_size(n_slots) // 4, dtype=torch.int32, device=layer.device)
+        self.side = torch.cuda.Stream()
+        self.admitted = torch.cuda.Event(enable_timing=True)
+        self.admit_start = torch.cuda.Event(enable_timing=True)
+        self.t = 0
+
+    def __call__(self, q):
+        layer = self.layer
+        bufs = self.bufs[self.t & 1]
+        main = torch.cuda.current_stream()
+        score(layer, q, bufs)
+        topk(layer, bufs)
+        if self.t > 0 and self.admit:
+            main.wait_event(self.admitted)
+        attend(layer, q, bufs)
+        self.t += 1
+        if self.admit:
+            self.side.wait_stream(main)
+            self.admit_start.record(self.side)
+            kv.hot_admit(layer.L, layer.host_v.dev.value, layer.v_hot, layer.v_hot_slot, self.slot_page,
+                         self.slot_stamp, layer.bt, layer.seq_lens, bufs.sel, bufs.sel_count, self.t, self.ws,
+                         self.side, k16_ptr=layer.host_k.dev.value if layer.host_k is not None else None,
+                         k_hot=layer.k_hot)
+            self.admitted.record(self.side)
+        return bufs
+
+    def finish(self):
+        """Makes the caller's stream wait for the last admission."""
+        if self.admit and self.t > 0:
+            torch.cuda.current_stream().wait_event(self.admitted)

@@ -50,6 +50,7 @@ class KvPages(ctypes.Structure):
         ("kq", ctypes.c_void_p * 4), ("vq", ctypes.c_void_p * 4),
         ("ksz", ctypes.c_void_p * 4), ("vsz", ctypes.c_void_p * 4),
         ("page_entry", ctypes.c_void_p), ("v_hot", ctypes.c_void_p), ("v_hot_slot", ctypes.c_void_p),
+        ("k_hot", ctypes.c_void_p),
     ]
 
 
@@ -74,7 +75,7 @@ def lib():
             "kv_page_topk": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _I, _P, _P, _I, _P,
                                   _P, _SZ, _P]),
             "kv_page_topk_workspace_size": (_SZ, [_LP, _I, _I]),
-            "kv_hot_admit": (_I, [_LP, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, ctypes.c_uint32,
+            "kv_hot_admit": (_I, [_LP, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, ctypes.c_uint32,
                                   _P, _SZ, _P]),
             "kv_hot_admit_workspace_size": (_SZ, [_I]),
             "kv_page_topk_coverage": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P, _I, _P,
@@ -130,12 +131,12 @@ def _check(rc, fn):
 
 
 def make_pages(k16, v16, kq=None, vq=None, ksz=None, vsz=None, page_entry=None, v_hot=None,
-               v_hot_slot=None, v16_ptr=None):
+               v_hot_slot=None, v16_ptr=None, k_hot=None, k16_ptr=None):
     """KvPages struct; keeps the tensors alive on the returned object.
 
-    v16_ptr overrides v16's pointer (a device-mapped host address)."""
+    v16_ptr / k16_ptr override v16's / k16's pointer (a device-mapped host address)."""
     pg = KvPages()
-    pg.k16 = _p(k16)
+    pg.k16 = k16_ptr if k16_ptr is not None else _p(k16)
     pg.v16 = v16_ptr if v16_ptr is not None else _p(v16)
     for t in range(4):
         pg.kq[t] = _p(kq[t]) if kq else None
@@ -145,7 +146,8 @@ def make_pages(k16, v16, kq=None, vq=None, ksz=None, vsz=None, page_entry=None, 
     pg.page_entry = _p(page_entry)
     pg.v_hot = _p(v_hot)
     pg.v_hot_slot = _p(v_hot_slot)
-    pg._keep = (k16, v16, kq, vq, ksz, vsz, page_entry, v_hot, v_hot_slot)
+    pg.k_hot = _p(k_hot)
+    pg._keep = (k16, v16, kq, vq, ksz, vsz, page_entry, v_hot, v_hot_slot, k_hot)
     return pg
 
 
@@ -227,10 +229,12 @@ def hot_admit_workspace_size(n_slots):
 
 
 def hot_admit(L, v16_ptr, v_hot, v_hot_slot, slot_page, slot_stamp, block_table, seq_lens, sel, sel_count, step,
-              ws, stream=None):
-    """v16_ptr: device address (int) of the V pool, which may be device-mapped host memory."""
+              ws, stream=None, k16_ptr=None, k_hot=None):
+    """v16_ptr / k16_ptr: device addresses (int) of the V / K pools, which may be
+    device-mapped host memory; K is admitted only with k16_ptr and k_hot."""
     B, max_pages = block_table.shape
-    rc = lib().kv_hot_admit(ctypes.byref(L), ctypes.c_void_p(v16_ptr), _p(v_hot), _p(v_hot_slot),
+    rc = lib().kv_hot_admit(ctypes.byref(L), ctypes.c_void_p(v16_ptr), _p(v_hot),
+                            None if k16_ptr is None else ctypes.c_void_p(k16_ptr), _p(k_hot), _p(v_hot_slot),
                             int(v_hot_slot.shape[0]), _p(slot_page), _p(slot_stamp), int(slot_page.shape[0]),
                             _p(block_table), _p(seq_lens), int(B), int(max_pages), _p(sel), _p(sel_count),
                             int(sel.shape[-1]), int(step), _p(ws), ws.numel() * ws.element_size(),

@@ -55,6 +55,7 @@ class Workload:
     gmm_std: float = 0.0
     tier_fracs: tuple | None = None   # fractions per tier, most to least important
     v_host: bool = False          # V pool in pinned host memory, read through a mapping
+    k_host: bool = False          # K pool there too (mem-kv; needs v_host)
     hot_buffer_frac: float = 0.0  # HBM hot buffer for V, fraction of physical pages
 
     @property

@@ -132,6 +132,11 @@ def test_attention_validation_and_workspace():
     hot.v16 = FAKE
     hot.v_hot_slot = FAKE
     assert call(pages=hot) == kv.KV_ERR_INVALID_ARG                 # hot buffer missing
+    kh = kv.KvPages()
+    kh.k16 = FAKE
+    kh.v16 = FAKE
+    kh.k_hot = FAKE
+    assert call(pages=kh) == kv.KV_ERR_INVALID_ARG                  # K hot buffer without the slot map
 
 
 def test_pack_build_dequant_validation():
@@ -177,3 +182,28 @@ def test_shared_basis_validation():
     assert ps(lam=FAKE + 2) == kv.KV_ERR_INVALID_ARG
     assert ps(lam=None) == kv.KV_ERR_INVALID_ARG
     assert _score(_L(head_dim=96)) == kv.KV_ERR_UNSUPPORTED
+
+
+def test_hot_admit_validation_and_workspace():
+    L = _L()
+    f = kv.lib().kv_hot_admit
+    assert kv.hot_admit_workspace_size(100) == (1 + 3 * 100) * 4
+    assert kv.hot_admit_workspace_size(0) == 0
+
+    def call(v16=FAKE, v_hot=FAKE, k16=None, k_hot=None, hot=FAKE, n_phys=1000, n_slots=100, step=1,
+             ws=FAKE, ws_bytes=1 << 20, sel=FAKE, B=2):
+        return f(ctypes.byref(L), v16, v_hot, k16, k_hot, hot, n_phys, FAKE, FAKE, n_slots, FAKE, FAKE, B, 64,
+                 sel, FAKE, 12, step, ws, ws_bytes, None)
+
+    assert call(step=0) == kv.KV_ERR_INVALID_ARG                     # steps start at 1
+    assert call(n_slots=0) == kv.KV_ERR_INVALID_ARG
+    assert call(n_slots=(1 << 14) + 1) == kv.KV_ERR_UNSUPPORTED
+    assert call(n_phys=(1 << 19) + 1) == kv.KV_ERR_UNSUPPORTED
+    assert call(v16=None) == kv.KV_ERR_INVALID_ARG
+    assert call(v_hot=FAKE + 8) == kv.KV_ERR_INVALID_ARG
+    assert call(hot=None) == kv.KV_ERR_INVALID_ARG
+    assert call(k16=FAKE) == kv.KV_ERR_INVALID_ARG                   # K pool without a K hot buffer
+    assert call(k_hot=FAKE) == kv.KV_ERR_INVALID_ARG                 # and the reverse
+    assert call(sel=None) == kv.KV_ERR_INVALID_ARG
+    assert call(ws_bytes=(1 + 3 * 100) * 4 - 1) == kv.KV_ERR_WORKSPACE
+    assert call(ws=None) == kv.KV_ERR_WORKSPACE

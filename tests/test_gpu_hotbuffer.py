@@ -118,3 +118,58 @@ def test_admission_from_host_mapped_pool_keeps_attention(hz):
         np.testing.assert_array_equal(bufs.lse.cpu().numpy(), lse0)
     finally:
         layer.release()
+
+
+def test_mem_kv_pool_with_admission_matches_resident(hz):
+    """K and V both in device-mapped host memory (mem-kv) with a hot buffer for
+    each, driven step by step with admission on a side stream: every step's
+    selection and attention are bit-identical to the same layer held in HBM,
+    and every hot slot holds its page's K and V."""
+    from parity import assert_attn_close, check_selection
+    base = W["heavy70b_128k"].replace(B=2, Hq=16, Hkv=2, ctx=32 * 150 + 5)
+    announce("mem-kv pool (K and V host-mapped) against the resident layer")
+    res = hz.DeviceLayer(base.replace(v_host=False), summaries="build")
+    mem = hz.DeviceLayer(base.replace(k_host=True), summaries="build", hot_mode="cold")
+    try:
+        assert mem.k16 is None and mem.k_hot is not None
+        np.testing.assert_array_equal(mem.summary.view(torch.int16).cpu().numpy(),
+                                      res.summary.view(torch.int16).cpu().numpy())
+        rbufs = hz.StepBuffers(base)
+        ms = hz.MemStep(mem)
+        w = base
+        for t in range(6):
+            q = hz.queries_device(w, 0, t % 2)          # steps repeat, so later ones hit the buffer
+            hz.decode_step(res, q, rbufs)
+            mb = ms(q)
+            ms.finish()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(mb.sel_count.cpu().numpy(), rbufs.sel_count.cpu().numpy())
+            np.testing.assert_array_equal(mb.sel.cpu().numpy(), rbufs.sel.cpu().numpy())
+            np.testing.assert_array_equal(mb.out.cpu().numpy(), rbufs.out.cpu().numpy())
+            np.testing.assert_array_equal(mb.lse.cpu().numpy(), rbufs.lse.cpu().numpy())
+        # the buffer's contents follow its map, for K and V
+        kh = mem.host_k.numpy(np.uint16, (w.n_phys, w.Hkv, w.P, w.d))
+        vh = mem.host_v.numpy(np.uint16, (w.n_phys, w.Hkv, w.P, w.d))
+        k_hot = mem.k_hot.view(torch.int16).cpu().numpy().view(np.uint16)
+        v_hot = mem.v_hot.view(torch.int16).cpu().numpy().view(np.uint16)
+        slot_page = ms.slot_page.cpu().numpy()
+        hot = mem.v_hot_slot.cpu().numpy()
+        assert (slot_page >= 0).sum() == k_hot.shape[0]
+        for s, p in enumerate(slot_page):
+            assert hot[p] == s
+            np.testing.assert_array_equal(k_hot[s], kh[p])
+            np.testing.assert_array_equal(v_hot[s], vh[p])
+        # and the last step against the oracle on every row
+        sel, out, lse = mb.sel.cpu().numpy(), mb.out.cpu().numpy(), mb.lse.cpu().numpy()
+        for b in range(w.B):
+            for g in range(w.Hkv):
+                r = oracle.decode_row(wl.queries(w, 0, b, g, qidx=1).astype(np.float64),
+                                      wl.row_keys(w, 0, b, g), wl.row_values(w, 0, b, g), w.ctx, w.P, w.rank,
+                                      w.tau, w.keep, w.k_fixed)
+                k = r["k"]
+                check_selection(r["S"], k, sel[b, g, :k], rel=1e-3)
+                if set(sel[b, g, :k].tolist()) == set(r["sel"].tolist()):
+                    hs = slice(g * w.G, (g + 1) * w.G)
+                    assert_attn_close(out[b, hs], lse[b, hs], r["out"], r["lse"])
+    finally:
+        mem.release()
