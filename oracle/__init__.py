@@ -36,8 +36,9 @@ from .basis import (row_basis, row_covariance, store_basis, basis_page_stats, st
 from .select import group_aggregate, selection_count, select_pages, coverage_count
 from .attention import sparse_attention, dense_attention
 from .codec import (
-    BITS_OF_TIER, TIER_NATIVE, TIER_I8, TIER_I4, TIER_I2, TIER_B1,
-    encode_group_int, encode_group_1bit, encode_vector, decode_vector,
+    BITS_OF_TIER, TIER_NATIVE, TIER_I8, TIER_I4, TIER_I2, TIER_B1, TIER_FP8, FP8_MAX,
+    encode_group_int, encode_group_1bit, encode_group_fp8, e4m3_magnitudes, e4m3_value, round_e4m3,
+    encode_vector, decode_vector,
     pack_codes, unpack_codes,
 )
 from .hotbuffer import HotBuffer, selected_physical_pages
@@ -52,8 +53,9 @@ __all__ = [
     "page_score_basis",
     "group_aggregate", "selection_count", "select_pages", "coverage_count",
     "sparse_attention", "dense_attention",
-    "BITS_OF_TIER", "TIER_NATIVE", "TIER_I8", "TIER_I4", "TIER_I2", "TIER_B1",
-    "encode_group_int", "encode_group_1bit", "encode_vector", "decode_vector",
+    "BITS_OF_TIER", "TIER_NATIVE", "TIER_I8", "TIER_I4", "TIER_I2", "TIER_B1", "TIER_FP8", "FP8_MAX",
+    "encode_group_int", "encode_group_1bit", "encode_group_fp8", "e4m3_magnitudes", "e4m3_value",
+    "round_e4m3", "encode_vector", "decode_vector",
     "pack_codes", "unpack_codes",
     "HotBuffer", "selected_physical_pages",
     "decode_row",

@@ -29,18 +29,34 @@ Byte layout, LSB first in head-dim order: int8 one code per byte; int4 element
 element 8i+j in bit j.  A vector's d*b/8 code bytes are contiguous; the
 (s, z) pairs live in a separate array.
 
+FP8 tier (the cascade's first step below 16 bits, "gentle precision
+quantization" in the tier legend; the page names no format).  Reading: the
+OCP 8-bit float E4M3 in its finite variant (1 sign, 4 exponent bits with bias
+7, 3 mantissa bits; no infinities; exponent 15 with mantissa 7 is NaN, so the
+largest finite value is 448), one code per byte, with a symmetric per-group
+scale so that any 16-bit input range fits:
+    s = fp16(fp32(max |x|) / 448),  z = 0
+    c = 0 if s == 0 else E4M3(fp32(x / s))
+where E4M3(y) is the nearest finite E4M3 value to y, ties to the even code,
+|y| >= 448 saturating to 448, the sign taken from y's sign bit.  Decoder: the
+code's value times s plus z (exact in float64, returned as float32).
+
 Pinned in tests/test_oracle_codec.py: hand-packed bytes (0xA3, 0xE4, 0x8D), the
 int4 ramp 0..31 (s = fp16(31/15) = 2.06640625), exactly representable inputs
 mapping back to their codes, the per-group error bound, the 1-bit value set
-and sign, and pack/unpack identity.
+and sign, and pack/unpack identity.  FP8 in tests/test_oracle_fp8.py: the
+format's landmark codes, torch's float8_e4m3fn cast for in-range values, a
+brute-force nearest-value search over all 127 magnitudes, a hand-worked group
+(tests/golden/fp8_group.json), the relative error bound and saturation.
 """
 
 import numpy as np
 
 from .rounding import round_fp16_sat
 
-TIER_NATIVE, TIER_I8, TIER_I4, TIER_I2, TIER_B1 = 0, 1, 2, 3, 4
-BITS_OF_TIER = {TIER_I8: 8, TIER_I4: 4, TIER_I2: 2, TIER_B1: 1}
+TIER_NATIVE, TIER_I8, TIER_I4, TIER_I2, TIER_B1, TIER_FP8 = 0, 1, 2, 3, 4, 5
+BITS_OF_TIER = {TIER_I8: 8, TIER_I4: 4, TIER_I2: 2, TIER_B1: 1, TIER_FP8: 8}
+FP8_MAX = 448.0
 GROUP = 32
 
 
@@ -81,6 +97,47 @@ def encode_group_1bit(x):
     return c, s, z
 
 
+def e4m3_magnitudes():
+    """float64 values of the non-negative finite E4M3 codes 0..126 (ascending):
+    exponent field e = code >> 3, mantissa m = code & 7; e = 0 is subnormal,
+    m * 2^-9, otherwise 2^(e - 7) * (1 + m / 8)."""
+    code = np.arange(127)
+    e, m = code >> 3, code & 7
+    return np.where(e == 0, m * 2.0 ** -9, np.ldexp(1.0 + m / 8.0, e - 7))
+
+
+def e4m3_value(code):
+    """float64 value of E4M3 codes (bit 7 = sign); code 0x7F / 0xFF (NaN) never occurs."""
+    c = np.asarray(code, dtype=np.int64)
+    mag = e4m3_magnitudes()[c & 0x7F]
+    return np.where((c & 0x80) != 0, -mag, mag)
+
+
+def round_e4m3(y):
+    """float32 y -> E4M3 code (uint8): nearest finite magnitude, ties to the even
+    code, saturating at 448; sign bit copied from y."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y).astype(np.float64)
+    vals = e4m3_magnitudes()
+    hi = np.minimum(np.searchsorted(vals, a, side="left"), 126)   # first magnitude >= a (or the largest)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    mag = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return (mag | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def encode_group_fp8(x):
+    """x: float32 (..., 32).  Returns (codes uint8 (..., 32), s f32 (...), z f32 (...))."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)
+    s = _f16(amax / np.float32(FP8_MAX))
+    z = np.zeros_like(s)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = x / s[..., None]
+    c = round_e4m3(np.where((s == 0)[..., None], np.float32(0), y))
+    return c, s, z
+
+
 def pack_codes(codes, bits):
     """codes uint8 (..., d) -> bytes uint8 (..., d*bits/8), LSB first."""
     c = np.asarray(codes, dtype=np.uint8)
@@ -118,6 +175,8 @@ def encode_vector(x16, tier):
     bits = BITS_OF_TIER[tier]
     if tier == TIER_B1:
         c, s, z = encode_group_1bit(g)
+    elif tier == TIER_FP8:
+        c, s, z = encode_group_fp8(g)
     else:
         c, s, z = encode_group_int(g, bits)
     packed = pack_codes(c.reshape(x.shape), bits)
@@ -127,7 +186,8 @@ def encode_vector(x16, tier):
 def decode_vector(packed, scale_zero, tier, d):
     """Decode token vectors to float32 (..., d) (exact float64 value rounded once)."""
     bits = BITS_OF_TIER[tier]
-    c = unpack_codes(packed, bits, d).astype(np.float64)
+    c = unpack_codes(packed, bits, d)
+    c = e4m3_value(c) if tier == TIER_FP8 else c.astype(np.float64)
     sz = np.asarray(scale_zero, dtype=np.float64)
     c = c.reshape(c.shape[:-1] + (d // GROUP, GROUP))
     s = sz[..., 0][..., None]
