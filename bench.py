@@ -51,10 +51,30 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(w, sel_counts):
+TIER_BITS = {0: 16, 1: 8, 2: 4, 3: 2, 4: 1, 5: 8}
+
+
+def page_bytes(w, tier):
+    """K plus V bytes of one (row, page) in a tier: codes plus a 4-byte
+    (scale, zero) pair per 32-element group for the packed tiers."""
+    if tier == 0:
+        return 2 * w.P * w.d * 2
+    return 2 * w.P * (w.d * TIER_BITS[tier] // 8 + (w.d // 32) * 4)
+
+
+def algorithmic_bytes(w, sel_counts, sel=None, tiers=None):
+    """Summary bytes and selected K/V bytes of one step; with tiers (B, Np) the
+    selected pages are priced at their tier's size (sel gives the pages)."""
     rec = (1 + w.rank) * w.d * 2 + 4                       # bf16 record + float32 log n
     summary = w.rows * w.Np * rec
-    selected = int(sel_counts.sum()) * w.P * w.d * 2 * 2   # K and V, 16-bit
+    if tiers is None:
+        return summary, int(sel_counts.sum()) * page_bytes(w, 0)
+    selected = 0
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            pages = sel[b, g, :sel_counts[b, g]]
+            for t, n in zip(*__import__("numpy").unique(tiers[b, pages], return_counts=True)):
+                selected += int(n) * page_bytes(w, int(t))
     return summary, selected
 
 
@@ -136,11 +156,12 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if w.v_host:
         return mem_main(args, w)
-    if w.tier_fracs is not None:
-        raise SystemExit("bench.py times the native-tier workloads; the tiered one is covered by the tests")
+    tiers = wl.page_tiers(w)
     torch.cuda.set_device(0)
     # bytes one step touches: every summary record plus the selected K/V pages
-    touched = w.rows * w.Np * ((1 + w.rank) * w.d * 2 + 4) + w.rows * w.k_of(w.Np) * w.P * w.d * 2 * 2
+    avg_page = (page_bytes(w, 0) if tiers is None else
+                sum(f * page_bytes(w, t) for f, t in zip(w.tier_fracs, w.tier_order)))
+    touched = w.rows * w.Np * ((1 + w.rank) * w.d * 2 + 4) + w.rows * w.k_of(w.Np) * avg_page
     n_layers = args.layers or max(1, math.ceil(4 * 256e6 / touched))
     log(f"[bench] workload {w.name}: {n_layers} layers rotated, {touched / 1e6:.1f} MB touched per step, "
         f"{args.queries} queries")
@@ -251,7 +272,8 @@ def main():
     log(f"[bench] timed {timed_steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
     sel_counts = bufs[0].sel_count.cpu().numpy()
-    summary_b, selected_b = algorithmic_bytes(w, sel_counts)
+    summary_b, selected_b = algorithmic_bytes(w, sel_counts, bufs[0].sel.cpu().numpy(),
+                                              None if tiers is None else wl.page_tiers(w, 0))
     step_bytes = summary_b + selected_b
     score_avg_s = float(score_ms.mean()) / 1e3
     achieved = summary_b / score_avg_s / 1e9
@@ -292,7 +314,24 @@ def main():
             "bytes_per_launch": summary_b,
         },
     }
-    if not args.no_basis:
+    if tiers is not None:
+        # attention alone over the same shape with every page in one packed
+        # tier (same rotation, queries and selections): the decode cost per tier
+        uni = {}
+        for t in (1, 5):
+            ulayers = [hz.DeviceLayer(w.replace(tier_fracs=(1.0,), tier_order=(t,)), layer=i, summaries=None)
+                       for i in range(n_layers)]
+            us, _ = graph_avg_us(lambda li, q: hz.attend(ulayers[li], q, bufs[li]))
+            b_sel = int(sel_counts.sum()) * page_bytes(w, t)
+            uni[wl.TIER_NAMES[t]] = {"attention_avg_us": us, "selected_bytes": b_sel,
+                                     "achieved_GBps": b_sel / (us * 1e3)}
+            for l in ulayers:
+                l.release()
+            del ulayers
+            torch.cuda.empty_cache()
+        result["uniform_tier_attention"] = uni
+        log(f"[bench] attention with every page in one tier: {uni}")
+    if not args.no_basis and tiers is None:
         # the same layers scored from shared-basis summaries (row basis built
         # from each layer's keys, then per-page means and variances), same
         # rotation, queries, selection rule, attention and timing
@@ -336,6 +375,8 @@ def main():
     # coverage-mode selection (k per row from the mass prefix) on the headline
     # layers' scores: its kernel time and the k it picks, for context
     from quantized_kv_cache_summary_amd import kvsparse as kvs
+    if tiers is not None:
+        args.no_cpu_baseline = True
     cov_sel = [torch.empty((w.B, w.Hkv, w.Np), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
     cov_cnt = [torch.empty((w.B, w.Hkv), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
     for li in range(n_layers):

@@ -72,8 +72,10 @@ enum {
 
 enum { KV_F16 = 0, KV_BF16 = 1 };   /* the cache's native 16-bit dtype (also q's) */
 
-/* Page tiers (ARGUS tier legend).  NATIVE is the cache's own 16-bit dtype. */
-enum { KV_TIER_NATIVE = 0, KV_TIER_I8 = 1, KV_TIER_I4 = 2, KV_TIER_I2 = 3, KV_TIER_B1 = 4 };
+/* Page tiers (ARGUS tier legend).  NATIVE is the cache's own 16-bit dtype;
+ * FP8 is the 8-bit float E4M3 (OCP, finite variant). */
+enum { KV_TIER_NATIVE = 0, KV_TIER_I8 = 1, KV_TIER_I4 = 2, KV_TIER_I2 = 3, KV_TIER_B1 = 4, KV_TIER_FP8 = 5 };
+#define KV_NUM_PACKED_TIERS 5
 
 /* page_entry word: tier in bits 29..31, slot in bits 0..28. */
 #define KV_PAGE_ENTRY(tier, slot) ((((uint32_t)(tier)) << 29) | ((uint32_t)(slot) & 0x1FFFFFFFu))
@@ -96,12 +98,15 @@ typedef struct kv_layout {
  *   page_entry == NULL: every physical page is native and lives at
  *     k16/v16[phys] ([n_phys][Hkv][P][d] 16-bit).
  *   page_entry != NULL: page_entry[phys] = KV_PAGE_ENTRY(tier, slot); native
- *     pages live at k16/v16[slot]; a packed tier t (1..4, bits 8/4/2/1) keeps
+ *     pages live at k16/v16[slot]; a packed tier t (1..5, bits 8/4/2/1/8) keeps
  *     codes at kq[t-1]/vq[t-1][slot] ([slots][Hkv][P][d*bits/8] bytes, codes
  *     LSB-first in head-dim order) and one (scale, zero) float16 pair per
  *     32-element group at ksz[t-1]/vsz[t-1][slot] ([slots][Hkv][P][d/32][2]).
  *     A tier's K and V share the slot.  Decoding: int-b x = c*s + z rounded
- *     once to float32 (fused multiply-add); 1-bit x = z + s if c else z - s.
+ *     once to float32 (fused multiply-add); 1-bit x = z + s if c else z - s;
+ *     FP8 x = e4m3(c)*s + z (exact).  Every one of the five tiers' pointers
+ *     must be set when page_entry is (a tier with no pages may point to a
+ *     one-slot dummy).
  *   v_hot_slot != NULL: V of physical page phys is read from
  *     v_hot[v_hot_slot[phys]] ([hot][Hkv][P][d] 16-bit, device memory) when
  *     v_hot_slot[phys] >= 0, else from v16[slot]; v16 may then be pinned host
@@ -117,10 +122,10 @@ typedef struct kv_layout {
 typedef struct kv_pages {
   const void* k16;
   const void* v16;
-  const uint8_t* kq[4];
-  const uint8_t* vq[4];
-  const void* ksz[4];
-  const void* vsz[4];
+  const uint8_t* kq[KV_NUM_PACKED_TIERS];
+  const uint8_t* vq[KV_NUM_PACKED_TIERS];
+  const void* ksz[KV_NUM_PACKED_TIERS];
+  const void* vsz[KV_NUM_PACKED_TIERS];
   const uint32_t* page_entry;
   const void* v_hot;
   const int32_t* v_hot_slot;
@@ -341,8 +346,9 @@ int kv_dequant_tier(const kv_layout* layout, const kv_pages* pages_desc, const i
                     int32_t n, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------
- * kv_pack_tier -- encode 16-bit pages into packed tier `tier` (1..4; ARGUS tier
- * legend: INT8, INT4 2-way, INT2 4-way, 1-bit 8-way sign-packed).
+ * kv_pack_tier -- encode 16-bit pages into packed tier `tier` (1..5; ARGUS tier
+ * legend and "Visual Architecture": INT8, INT4 2-way, INT2 4-way, 1-bit 8-way
+ * sign-packed, FP8).
  * Per token vector, per group of 32 consecutive head-dim elements, x the
  * float32 value of the 16-bit input, every step an IEEE float32 operation
  * rounded to nearest even, no fused multiply-add:
@@ -350,6 +356,10 @@ int kv_dequant_tier(const kv_layout* layout, const kv_pages* pages_desc, const i
  *          c = 0 if s == 0 else clamp(rint(f32(x - z) / s), 0, 2^b - 1)
  *   1-bit: z = f16(T(x) / 32), s = f16(T(|x - z|) / 32), c = (x >= z),
  *          T the pairwise tree sum (level by level, pairs (2i, 2i+1))
+ *   FP8:   s = f16(f32(max |x|) / 448), z = 0,
+ *          c = 0 if s == 0 else E4M3(f32(x / s)), one code per byte, where
+ *          E4M3(y) is the nearest finite E4M3 value (ties to the even code,
+ *          |y| >= 448 saturating to 448, sign bit copied from y)
  *   f16() rounds to nearest even and saturates at +-65504.
  * Source page src_pages[i] of src16 ([*][Hkv][P][d]) goes to slot dst_slots[i]
  * of codes ([slots][Hkv][P][d*bits/8]) and scale_zero ([slots][Hkv][P][d/32][2]

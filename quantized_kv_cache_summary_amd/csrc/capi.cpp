@@ -70,7 +70,7 @@ int check_pages(const kv_layout* L, const kv_pages* pg) {
   if (!pg->k16 || !pg->v16) return KV_ERR_INVALID_ARG;
   if (!aligned16(pg->k16) || !aligned16(pg->v16)) return KV_ERR_INVALID_ARG;
   if (pg->page_entry) {
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < KV_NUM_PACKED_TIERS; ++t) {
       if (!pg->kq[t] || !pg->vq[t] || !pg->ksz[t] || !pg->vsz[t]) return KV_ERR_INVALID_ARG;
       if (!aligned16(pg->kq[t]) || !aligned16(pg->vq[t])) return KV_ERR_INVALID_ARG;
       if ((reinterpret_cast<uintptr_t>(pg->ksz[t]) & 3u) || (reinterpret_cast<uintptr_t>(pg->vsz[t]) & 3u))
@@ -312,7 +312,7 @@ int kv_pack_tier(const kv_layout* L, const void* src16, const int32_t* src_pages
                  void* stream) {
   int rc = check_layout(L);
   if (rc) return rc;
-  if (tier < KV_TIER_I8 || tier > KV_TIER_B1) return KV_ERR_UNSUPPORTED;
+  if (tier < KV_TIER_I8 || tier > KV_TIER_FP8) return KV_ERR_UNSUPPORTED;
   if (n < 0) return KV_ERR_INVALID_ARG;
   if (n == 0) return KV_OK;
   if (!src16 || !codes || !scale_zero) return KV_ERR_INVALID_ARG;

@@ -11,6 +11,9 @@
 //   1-bit: z = f16(T(x) / 32), s = f16(T(|x - z|) / 32), c = (x >= z)
 //          with T the pairwise tree sum, level by level, pairs (2i, 2i+1)
 //   f16(): round to nearest even, saturating at +-65504.
+//   FP8 (the cascade's first step below 16 bits, "gentle precision" in the
+//   tier legend; format read as OCP E4M3, finite variant): s = f16(max|x| /
+//   448), z = 0, c = 0 if s == 0 else e4m3(f32(x / s)), one code per byte.
 // Codes are packed LSB first in head-dim order; (s, z) are stored as a float16
 // pair per group.  One thread encodes one group.
 
@@ -28,11 +31,31 @@ __device__ __forceinline__ uint16_t f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// float32 -> E4M3 code: nearest finite value, ties to the even code, |y| >= 448
+// saturating to 448 (0x7E), the sign bit copied from y.  Below 2^-6 the codes
+// are the subnormal multiples of 2^-9 (|y| * 512 is exact, then rounded to an
+// integer half to even); above, the float32 pattern is rounded half to even at
+// the 3rd mantissa bit and the exponent rebiased from 127 to 7.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t mag;
+  if (a >= 0x43E00000u) {            // 448
+    mag = 0x7Eu;
+  } else if (a < 0x3C800000u) {      // 2^-6
+    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.f);
+  } else {
+    mag = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sign | mag;
+}
+
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pack_tier_kernel(const uint16_t* __restrict__ src16,
                                                         const int32_t* __restrict__ src_pages,
                                                         const int32_t* __restrict__ dst_slots, int n,
-                                                        int Hkv, int P, int bits,
+                                                        int Hkv, int P, int bits, bool fp8,
                                                         uint8_t* __restrict__ codes,
                                                         uint16_t* __restrict__ scale_zero) {
   constexpr int NG = D / 32;
@@ -77,6 +100,14 @@ __global__ __launch_bounds__(256) void pack_tier_kernel(const uint16_t* __restri
       s = f16_sat(t[0] / 32.f);
 #pragma unroll
       for (int j = 0; j < 32; ++j) c[j] = x[j] >= z ? 1u : 0u;
+    } else if (fp8) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
+      s = f16_sat(amax / 448.f);
+      z = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) c[j] = s != 0.f ? f32_to_e4m3(x[j] / s) : 0u;
     } else {
       const float qmax = (float)((1 << bits) - 1);
       float mn = x[0], mx = x[0];
@@ -109,19 +140,20 @@ __global__ __launch_bounds__(256) void pack_tier_kernel(const uint16_t* __restri
 hipError_t launch_pack_tier(const kv_layout& L, const void* src16, const int32_t* src_pages, int n,
                             int tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
                             hipStream_t st) {
-  static const int kBits[5] = {16, 8, 4, 2, 1};
+  static const int kBits[6] = {16, 8, 4, 2, 1, 8};
   const int bits = kBits[tier];
+  const bool fp8 = tier == KV_TIER_FP8;
   const size_t total = (size_t)n * L.num_kv_heads * L.page_size * (L.head_dim / 32);
   const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
   const uint16_t* s = (const uint16_t*)src16;
   uint16_t* sz = (uint16_t*)scale_zero;
   const bool f16 = L.kv_dtype == KV_F16;
   if (L.head_dim == 64) {
-    if (f16) hipLaunchKernelGGL((pack_tier_kernel<64, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, codes, sz);
-    else hipLaunchKernelGGL((pack_tier_kernel<64, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, codes, sz);
+    if (f16) hipLaunchKernelGGL((pack_tier_kernel<64, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, fp8, codes, sz);
+    else hipLaunchKernelGGL((pack_tier_kernel<64, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, fp8, codes, sz);
   } else {
-    if (f16) hipLaunchKernelGGL((pack_tier_kernel<128, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, codes, sz);
-    else hipLaunchKernelGGL((pack_tier_kernel<128, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, codes, sz);
+    if (f16) hipLaunchKernelGGL((pack_tier_kernel<128, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, fp8, codes, sz);
+    else hipLaunchKernelGGL((pack_tier_kernel<128, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, fp8, codes, sz);
   }
   return hipGetLastError();
 }

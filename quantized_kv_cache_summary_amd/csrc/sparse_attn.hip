@@ -37,10 +37,10 @@ constexpr int kBatch = 2;   // 16-token chunks per load batch; two batches are i
 struct PagesDev {
   const uint16_t* k16;
   const uint16_t* v16;
-  const uint8_t* kq[4];
-  const uint8_t* vq[4];
-  const uint16_t* ksz[4];
-  const uint16_t* vsz[4];
+  const uint8_t* kq[KV_NUM_PACKED_TIERS];
+  const uint8_t* vq[KV_NUM_PACKED_TIERS];
+  const uint16_t* ksz[KV_NUM_PACKED_TIERS];
+  const uint16_t* vsz[KV_NUM_PACKED_TIERS];
   const uint32_t* page_entry;
   const uint16_t* v_hot;
   const int32_t* v_hot_slot;
@@ -88,6 +88,35 @@ __device__ __forceinline__ void decode_run(const uint8_t* codes, const uint16_t*
   } else {
 #pragma unroll
     for (int e = 0; e < EL; ++e) x[e] = __builtin_fmaf((float)code_at<BITS>(w, sh, e), s, z);
+  }
+}
+
+// Decodes EL FP8 (E4M3) codes, one byte each, starting at e0 of token row
+// `tokrow`: x = e4m3(c) * s + z, exact (a 4-bit by 11-bit significand product)
+// before the float32 rounding; the hardware's E4M3 conversion gives e4m3(c).
+template <int D, int EL>
+__device__ __forceinline__ void decode_fp8(const uint8_t* codes, const uint16_t* sz, size_t tokrow, int e0,
+                                           float* x) {
+  static_assert(EL == 4 || EL == 8, "runs of 4 or 8 codes");
+  uint32_t w[EL / 4];
+  const uint8_t* p = codes + tokrow * D + e0;
+  if constexpr (EL == 8) {
+    const u32x2_t t = *reinterpret_cast<const u32x2_t*>(p);
+    w[0] = t[0];
+    w[1] = t[1];
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+  const uint32_t szw = *reinterpret_cast<const uint32_t*>(sz + (tokrow * (D / 32) + e0 / 32) * 2);
+  const float s = f16_bits_to_f32(szw & 0xFFFFu), z = f16_bits_to_f32(szw >> 16);
+#pragma unroll
+  for (int i = 0; i < EL / 4; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    x[4 * i + 0] = __builtin_fmaf(lo[0], s, z);
+    x[4 * i + 1] = __builtin_fmaf(lo[1], s, z);
+    x[4 * i + 2] = __builtin_fmaf(hi[0], s, z);
+    x[4 * i + 3] = __builtin_fmaf(hi[1], s, z);
   }
 }
 
@@ -402,6 +431,7 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
                 case KV_TIER_I8: decode_run<D, 8, 8>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
                 case KV_TIER_I4: decode_run<D, 8, 4>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
                 case KV_TIER_I2: decode_run<D, 8, 2>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
+                case KV_TIER_FP8: decode_fp8<D, 8>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
                 default: decode_run<D, 8, 1>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
               }
               u32x4_t ah, al;
@@ -440,6 +470,7 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
                 case KV_TIER_I8: decode_run<D, EV, 8>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
                 case KV_TIER_I4: decode_run<D, EV, 4>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
                 case KV_TIER_I2: decode_run<D, EV, 2>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
+                case KV_TIER_FP8: decode_fp8<D, EV>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
                 default: decode_run<D, EV, 1>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
               }
               if (!valid) {
@@ -587,7 +618,7 @@ static PagesDev to_dev(const kv_pages& pg) {
   PagesDev d;
   d.k16 = (const uint16_t*)pg.k16;
   d.v16 = (const uint16_t*)pg.v16;
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < KV_NUM_PACKED_TIERS; ++t) {
     d.kq[t] = pg.kq[t];
     d.vq[t] = pg.vq[t];
     d.ksz[t] = (const uint16_t*)pg.ksz[t];
@@ -657,6 +688,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(PagesDev pg, const int32_t
         case KV_TIER_I8: decode_run<D, RUN, 8>(codes, sz, prow, run * RUN, x); break;
         case KV_TIER_I4: decode_run<D, RUN, 4>(codes, sz, prow, run * RUN, x); break;
         case KV_TIER_I2: decode_run<D, RUN, 2>(codes, sz, prow, run * RUN, x); break;
+        case KV_TIER_FP8: decode_fp8<D, RUN>(codes, sz, prow, run * RUN, x); break;
         default: decode_run<D, RUN, 1>(codes, sz, prow, run * RUN, x); break;
       }
     }

@@ -188,7 +188,7 @@ class DeviceLayer:
         self.tier_phys = tier_phys
         entry = np.zeros(w.n_phys, dtype=np.uint32)
         self.kq, self.vq, self.ksz, self.vsz = [], [], [], []
-        for t in range(1, 5):
+        for t in range(1, kv.NUM_PACKED_TIERS + 1):
             phys = np.nonzero(tier_phys == t)[0].astype(np.int32)
             n = max(1, phys.size)
             bits = kv.TIER_BITS[t]

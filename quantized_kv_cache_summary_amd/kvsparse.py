@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvsparse
 
 KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_HIP = 0, -1, -2, -3, -4
 KV_F16, KV_BF16 = 0, 1
-KV_TIER_NATIVE, KV_TIER_I8, KV_TIER_I4, KV_TIER_I2, KV_TIER_B1 = range(5)
-TIER_BITS = {KV_TIER_I8: 8, KV_TIER_I4: 4, KV_TIER_I2: 2, KV_TIER_B1: 1}
+KV_TIER_NATIVE, KV_TIER_I8, KV_TIER_I4, KV_TIER_I2, KV_TIER_B1, KV_TIER_FP8 = range(6)
+NUM_PACKED_TIERS = 5
+TIER_BITS = {KV_TIER_I8: 8, KV_TIER_I4: 4, KV_TIER_I2: 2, KV_TIER_B1: 1, KV_TIER_FP8: 8}
 
 # every entry point declared in include/kvsparse.h
 SYMBOLS = (
@@ -47,8 +48,8 @@ class KvLayout(ctypes.Structure):
 class KvPages(ctypes.Structure):
     _fields_ = [
         ("k16", ctypes.c_void_p), ("v16", ctypes.c_void_p),
-        ("kq", ctypes.c_void_p * 4), ("vq", ctypes.c_void_p * 4),
-        ("ksz", ctypes.c_void_p * 4), ("vsz", ctypes.c_void_p * 4),
+        ("kq", ctypes.c_void_p * NUM_PACKED_TIERS), ("vq", ctypes.c_void_p * NUM_PACKED_TIERS),
+        ("ksz", ctypes.c_void_p * NUM_PACKED_TIERS), ("vsz", ctypes.c_void_p * NUM_PACKED_TIERS),
         ("page_entry", ctypes.c_void_p), ("v_hot", ctypes.c_void_p), ("v_hot_slot", ctypes.c_void_p),
         ("k_hot", ctypes.c_void_p),
     ]
@@ -138,7 +139,7 @@ def make_pages(k16, v16, kq=None, vq=None, ksz=None, vsz=None, page_entry=None, 
     pg = KvPages()
     pg.k16 = k16_ptr if k16_ptr is not None else _p(k16)
     pg.v16 = v16_ptr if v16_ptr is not None else _p(v16)
-    for t in range(4):
+    for t in range(NUM_PACKED_TIERS):
         pg.kq[t] = _p(kq[t]) if kq else None
         pg.vq[t] = _p(vq[t]) if vq else None
         pg.ksz[t] = _p(ksz[t]) if ksz else None

@@ -29,7 +29,7 @@ SEED = 2026
 
 T_Q, T_K, T_V, T_HOT, T_TABLE, T_TIER, T_SEL, T_SUMMARY, T_CENTERS, T_HOTBUF, T_BASIS = range(11)
 
-TIER_NAMES = ("native", "int8", "int4", "int2", "1bit")
+TIER_NAMES = ("native", "int8", "int4", "int2", "1bit", "fp8")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -54,6 +54,7 @@ class Workload:
     gmm_centers: int = 0
     gmm_std: float = 0.0
     tier_fracs: tuple | None = None   # fractions per tier, most to least important
+    tier_order: tuple = (0, 1, 2, 3, 4)   # tier id of each fraction (5 = fp8)
     v_host: bool = False          # V pool in pinned host memory, read through a mapping
     k_host: bool = False          # K pool there too (mem-kv; needs v_host)
     hot_buffer_frac: float = 0.0  # HBM hot buffer for V, fraction of physical pages
@@ -100,6 +101,11 @@ WORKLOADS = {
                  tier_fracs=(0.05, 0.15, 0.30, 0.40, 0.10)),
         Workload("qwen3b_128k", 3, B=16, Hq=16, Hkv=2, d=128, P=16, ctx=131072, rank=4, keep=0.05,
                  k_fixed=0, dtype="bf16", keys="gmm", gmm_centers=64, gmm_std=0.5),
+        # the tiered shape with the cascade's FP8 step added (native, fp8, int8,
+        # int4, int2, 1-bit)
+        Workload("tiers_fp8_64k", 5, B=4, Hq=32, Hkv=8, d=128, P=16, ctx=65536, rank=4, keep=0.10,
+                 k_fixed=0, dtype="bf16", keys="hot", hot_frac=0.02, sink=True, plant_scale=2.5,
+                 tier_fracs=(0.05, 0.10, 0.15, 0.25, 0.35, 0.10), tier_order=(0, 5, 1, 2, 3, 4)),
         Workload("heavy70b_128k", 4, B=32, Hq=64, Hkv=8, d=128, P=32, ctx=131072, rank=4, keep=0.10,
                  k_fixed=0, dtype="bf16", keys="hot", hot_frac=0.01, plant_scale=2.5,
                  v_host=True, hot_buffer_frac=0.10),
@@ -220,8 +226,8 @@ def page_tiers(w: Workload, layer: int = 0):
         imp = rng_for(w, layer, b, 0, T_TIER).random(w.Np)
         order = np.argsort(-imp, kind="stable")
         lo = 0
-        for t, hi in enumerate(bounds):
-            out[b, order[lo:hi]] = t
+        for i, hi in enumerate(bounds):
+            out[b, order[lo:hi]] = w.tier_order[i]
             lo = hi
     return out
 

@@ -143,7 +143,8 @@ def test_pack_build_dequant_validation():
     L = _L()
     lib = kv.lib()
     assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 4, 0, FAKE, FAKE, None, None) == kv.KV_ERR_UNSUPPORTED
-    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 4, 5, FAKE, FAKE, None, None) == kv.KV_ERR_UNSUPPORTED
+    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 4, 6, FAKE, FAKE, None, None) == kv.KV_ERR_UNSUPPORTED
+    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 0, kv.KV_TIER_FP8, FAKE, FAKE, None, None) == kv.KV_OK
     assert lib.kv_pack_tier(ctypes.byref(L), None, None, 4, 1, FAKE, FAKE, None, None) == kv.KV_ERR_INVALID_ARG
     assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 0, 1, FAKE, FAKE, None, None) == kv.KV_OK
     sb = lib.kv_summary_build

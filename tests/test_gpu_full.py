@@ -59,7 +59,7 @@ def _score_select_check(w, layer, bufs, rows):
         check_selection(S_ref, k, bufs.sel[b, g, :k].cpu().numpy())
 
 
-@pytest.mark.parametrize("name", ["llama8b_32k", "tiers_64k", "qwen3b_128k"])
+@pytest.mark.parametrize("name", ["llama8b_32k", "tiers_64k", "tiers_fp8_64k", "qwen3b_128k"])
 def test_full_size_score_select_and_attention(hz, name):
     w = W[name]
     announce(f"full size {name}: score/select on synthetic summaries")
@@ -113,7 +113,7 @@ def _e2e_check(w, layer, bufs, rows, band=1e-3):
     assert compared >= 1
 
 
-@pytest.mark.parametrize("name", ["llama8b_32k", "qwen3b_128k", "tiers_64k"])
+@pytest.mark.parametrize("name", ["llama8b_32k", "qwen3b_128k", "tiers_64k", "tiers_fp8_64k"])
 def test_full_size_end_to_end(hz, name):
     w = W[name]
     announce(f"full size {name}: end to end with GPU-built summaries")

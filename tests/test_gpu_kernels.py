@@ -404,18 +404,20 @@ def test_summary_builder_invariants(hz, name):
 
 # ---------------------------------------------------------------- codec
 
-@pytest.mark.parametrize("shape", ["bf16_d128", "f16_d64"])
+@pytest.mark.parametrize("shape", ["bf16_d128", "f16_d64", "fp8_bf16_d128", "fp8_f16_d64"])
 def test_pack_and_dequant_bit_exact(hz, shape):
     from quantized_kv_cache_summary_amd import kvsparse as kv
-    if shape == "bf16_d128":
-        w = W["tiers_64k"].replace(B=2, ctx=16 * 96)
+    base = W["tiers_fp8_64k"] if shape.startswith("fp8") else W["tiers_64k"]
+    if shape.endswith("bf16_d128"):
+        w = base.replace(B=2, ctx=16 * 96)
     else:
-        w = W["tiers_64k"].replace(B=2, ctx=16 * 96, d=64, Hq=8, Hkv=2, dtype="f16", rank=2)
+        w = base.replace(B=2, ctx=16 * 96, d=64, Hq=8, Hkv=2, dtype="f16", rank=2)
     announce(f"codec {shape}")
     layer = hz.DeviceLayer(w, summaries=None)
     k_all = layer.k16.view(torch.int16).cpu().numpy().view(np.uint16)
     v_all = layer.v16.view(torch.int16).cpu().numpy().view(np.uint16)
-    for t in range(1, 5):
+    present = sorted(set(w.tier_order) - {0})
+    for t in present:
         phys = np.nonzero(layer.tier_phys == t)[0]
         assert phys.size > 0
         for src, codes, sz in ((k_all, layer.kq[t - 1], layer.ksz[t - 1]), (v_all, layer.vq[t - 1], layer.vsz[t - 1])):
@@ -431,7 +433,7 @@ def test_pack_and_dequant_bit_exact(hz, shape):
     kv.dequant_tier(layer.L, layer.pages, ids, out)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
-    for t in range(0, 5):
+    for t in [0] + present:
         phys = np.nonzero(layer.tier_phys == t)[0]
         for kvi, src in ((0, k_all), (1, v_all)):
             x = wl.bits_to_f32(src[phys], w.dtype)
@@ -443,9 +445,67 @@ def test_pack_and_dequant_bit_exact(hz, shape):
             np.testing.assert_array_equal(out[phys, kvi], ref)
 
 
-def test_tiered_attention_parity(hz):
-    w = W["tiers_64k"].replace(B=2, ctx=16 * 300)
-    announce("tiered attention")
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fp8_every_code_ties_and_saturation(hz, dtype):
+    """Crafted groups through kv_pack_tier and kv_dequant_tier: every finite
+    E4M3 code (groups with max |x| = 448, so s = 1), the midpoints between
+    neighbouring codes (ties to even), values past 448 after a rounded-down
+    scale (saturation), signed zeros, and an all-zero group; codes, scales and
+    decoded values bit-exact against the oracle."""
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    mags = oracle.e4m3_magnitudes()
+    vals = np.concatenate([mags, -mags, (mags[:-1] + mags[1:]) / 2, -(mags[:-1] + mags[1:]) / 2, [-0.0]])
+    groups = []
+    for i in range(0, vals.size, 31):
+        g = np.zeros(32)
+        g[0] = 448.0
+        chunk = vals[i:i + 31]
+        g[1:1 + chunk.size] = chunk
+        groups.append(g)
+    g = np.zeros(32)
+    g[:4] = [449.0, -449.0, 1.0, 300.0] if dtype == "f16" else [450.0, -450.0, 1.0, 300.0]
+    groups.append(g)
+    groups.append(np.zeros(32))
+    d, P, Hkv = 128, 16, 1
+    n_el = len(groups) * 32
+    n_pages = -(-n_el // (P * d))
+    x = np.zeros(n_pages * P * d)
+    x[:n_el] = np.concatenate(groups)
+    x32 = x.astype(np.float32)
+    bits = wl.to_bits(x32, dtype)
+    assert np.array_equal(wl.bits_to_f32(bits, dtype), x32)          # every crafted value is exact
+    L = kv.layout(4, Hkv, d, P, 4, dtype)
+    src = torch.from_numpy(bits.view(np.int16).reshape(n_pages, Hkv, P, d)).cuda()
+    codes = torch.zeros((n_pages, Hkv, P, d), dtype=torch.uint8, device="cuda")
+    sz = torch.zeros((n_pages, Hkv, P, d // 32, 2), dtype=torch.float16, device="cuda")
+    announce(f"fp8 crafted groups {dtype}: {len(groups)} groups in {n_pages} pages")
+    kv.pack_tier(L, src, n_pages, kv.KV_TIER_FP8, codes, sz)
+    torch.cuda.synchronize()
+    ref_c, ref_sz = oracle.encode_vector(x32.reshape(n_pages, Hkv, P, d), oracle.TIER_FP8)
+    np.testing.assert_array_equal(codes.cpu().numpy(), ref_c)
+    np.testing.assert_array_equal(sz.float().cpu().numpy(), ref_sz)
+    assert set(range(256)) - set(np.unique(ref_c).tolist()) == {0x7F, 0xFF}   # every finite code occurs
+    # decode through a page table with every page in the FP8 tier
+    dummy8 = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    dummysz = torch.zeros(8, dtype=torch.float16, device="cuda")
+    kq = [dummy8] * 4 + [codes]
+    ksz = [dummysz] * 4 + [sz]
+    entry = torch.from_numpy(((np.uint32(kv.KV_TIER_FP8) << np.uint32(29)) |
+                              np.arange(n_pages, dtype=np.uint32)).view(np.int32)).cuda()
+    pages = kv.make_pages(src, src, kq, kq, ksz, ksz, entry)
+    out = torch.empty((n_pages, 2, Hkv, P, d), dtype=torch.float32, device="cuda")
+    kv.dequant_tier(L, pages, torch.arange(n_pages, dtype=torch.int32, device="cuda"), out)
+    torch.cuda.synchronize()
+    ref = oracle.decode_vector(ref_c, ref_sz, oracle.TIER_FP8, d)
+    got = out.cpu().numpy()
+    for kvi in (0, 1):
+        np.testing.assert_array_equal(got[:, kvi].view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["tiers_64k", "tiers_fp8_64k"])
+def test_tiered_attention_parity(hz, name):
+    w = W[name].replace(B=2, ctx=16 * 300)
+    announce(f"tiered attention {name}")
     layer = hz.DeviceLayer(w, summaries=None)
     q = hz.queries_device(w)
     k = w.k_of(w.Np)
