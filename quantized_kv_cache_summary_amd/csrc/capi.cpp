@@ -50,7 +50,7 @@ int topk_bound(int max_pages, float keep, int k_fixed) {
 int auto_splits(int rows, int k_max, bool tiered) {
   if (rows <= 0) return 1;
   const int waves = 4;
-  const int target = tiered ? 768 : 256;
+  const int target = tiered ? 512 : 256;
   int s = (target + rows - 1) / rows;
   int cap = k_max / (2 * waves);
   if (cap < 1) cap = 1;

@@ -24,6 +24,8 @@
 // cross blocks through device-coherent stores and loads: a release fence
 // would write back the whole L2 and costs far more than the merge.
 
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -117,6 +119,69 @@ __device__ __forceinline__ void decode_fp8(const uint8_t* codes, const uint16_t*
     x[4 * i + 1] = __builtin_fmaf(lo[1], s, z);
     x[4 * i + 2] = __builtin_fmaf(hi[0], s, z);
     x[4 * i + 3] = __builtin_fmaf(hi[1], s, z);
+  }
+}
+
+template <int T>
+struct TierTag {
+  static constexpr int value = T;
+};
+
+template <int T>
+constexpr int tier_bits() {
+  return T == KV_TIER_I4 ? 4 : T == KV_TIER_I2 ? 2 : T == KV_TIER_B1 ? 1 : 8;
+}
+
+// Raw code words of one 16-token chunk of a page in packed tier T as the
+// attention lanes read it: per MFMA k-step the codes of the lane's 8 key
+// elements and their group's (scale, zero) word; per value slot j the codes of
+// the lane's D/16 value elements and their (scale, zero) word.
+template <int D, int T>
+struct TierChunk {
+  static constexpr int BITS = tier_bits<T>();
+  static constexpr int KW = (8 * BITS + 31) / 32;
+  static constexpr int VW = ((D / 16) * BITS + 31) / 32;
+  uint32_t k[D / 32][KW];
+  uint32_t ksz[D / 32];
+  uint32_t v[4][VW];
+  uint32_t vsz[4];
+};
+
+// Requests the codes of EL elements from e0 of token row `tokrow` of packed
+// tier T and the group's (scale, zero) word.
+template <int D, int EL, int T>
+__device__ __forceinline__ void tier_load(const uint8_t* codes, const uint16_t* sz, size_t tokrow, int e0,
+                                          uint32_t* w, uint32_t& szw) {
+  constexpr int BITS = tier_bits<T>();
+  szw = *reinterpret_cast<const uint32_t*>(sz + (tokrow * (D / 32) + e0 / 32) * 2);
+  int sh;
+  load_code_words<EL, BITS>(codes + tokrow * (D * BITS / 8), e0, w, sh);
+}
+
+// Decodes what tier_load requested: int-b x = c*s + z (one FMA), 1-bit
+// x = z +- s, FP8 x = e4m3(c)*s + z.
+template <int EL, int T>
+__device__ __forceinline__ void tier_decode(const uint32_t* w, uint32_t szw, int e0, float* x) {
+  constexpr int BITS = tier_bits<T>();
+  const float s = f16_bits_to_f32(szw & 0xFFFFu), z = f16_bits_to_f32(szw >> 16);
+  const int sh = (e0 * BITS) & 7;
+  if constexpr (T == KV_TIER_FP8) {
+#pragma unroll
+    for (int i = 0; i < EL / 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+      x[4 * i + 0] = __builtin_fmaf(lo[0], s, z);
+      x[4 * i + 1] = __builtin_fmaf(lo[1], s, z);
+      x[4 * i + 2] = __builtin_fmaf(hi[0], s, z);
+      x[4 * i + 3] = __builtin_fmaf(hi[1], s, z);
+    }
+  } else if constexpr (T == KV_TIER_B1) {
+    const float zp = z + s, zm = z - s;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) x[e] = code_at<1>(w, sh, e) ? zp : zm;
+  } else {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) x[e] = __builtin_fmaf((float)code_at<BITS>(w, sh, e), s, z);
   }
 }
 
@@ -306,31 +371,31 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
   const int cpp = P / 16;   // 16-token chunks per page
   float (*pt)[16] = ptile[wave];
 
-  for (int j0 = 0; j0 < n_mine; j0 += 64) {
-    const int nb = n_mine - j0 < 64 ? n_mine - j0 : 64;
-    // this wave's pages, one per lane: logical page, slot, hot-buffer slot
-    int l_p = -1, l_hot = -1;
-    uint32_t l_tier = 0, l_slot = 0;
-    if (lane < nb) {
-      const int p = srow[beg + wave + kAttnWaves * (j0 + lane)];
-      if (p >= 0 && p < Np) {
-        l_p = p;
-        const int phys = bt[p];
-        l_slot = (uint32_t)phys;
-        if constexpr (TIERED) {
-          if (pg.page_entry) {
-            const uint32_t e = pg.page_entry[phys];
-            l_tier = e >> 29;
-            l_slot = e & 0x1FFFFFFFu;
+  if constexpr (!TIERED) {
+    for (int j0 = 0; j0 < n_mine; j0 += 64) {
+      const int nb = n_mine - j0 < 64 ? n_mine - j0 : 64;
+      // this wave's pages, one per lane: logical page, slot, hot-buffer slot
+      int l_p = -1, l_hot = -1;
+      uint32_t l_tier = 0, l_slot = 0;
+      if (lane < nb) {
+        const int p = srow[beg + wave + kAttnWaves * (j0 + lane)];
+        if (p >= 0 && p < Np) {
+          l_p = p;
+          const int phys = bt[p];
+          l_slot = (uint32_t)phys;
+          if constexpr (TIERED) {
+            if (pg.page_entry) {
+              const uint32_t e = pg.page_entry[phys];
+              l_tier = e >> 29;
+              l_slot = e & 0x1FFFFFFFu;
+            }
           }
+          if (pg.v_hot_slot) l_hot = pg.v_hot_slot[phys];
         }
-        if (pg.v_hot_slot) l_hot = pg.v_hot_slot[phys];
       }
-    }
-    const unsigned long long valid = __ballot(l_p >= 0);
-    if (valid == 0) continue;
+      const unsigned long long valid = __ballot(l_p >= 0);
+      if (valid == 0) continue;
 
-    if constexpr (!TIERED) {
       // skipped entries read the first valid page of the list instead (and are
       // masked), so every load of a batch is unconditional straight-line code
       const int first = __ffsll((long long)valid) - 1;
@@ -342,7 +407,7 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
       // issue the loads of chunks [cb, cb + NB) into r (the last chunk is
       // re-read past the end; those extra chunks are never computed)
       auto issue = [&](ChunkRaw<D> (&r)[kBatch], int (&pp)[kBatch], int cb) {
-#pragma unroll
+  #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int ci = cb + u < nch ? cb + u : nch - 1;
           const int jj = ci / cpp;
@@ -357,27 +422,27 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
         }
       };
       auto compute = [&](const ChunkRaw<D> (&r)[kBatch], const int (&pp)[kBatch], int cb) {
-#pragma unroll
+  #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           if (cb + u >= nch) break;
           const int ci = cb + u;
           const int c = ci - (ci / cpp) * cpp;
           const int p = pp[u];
           f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+  #pragma unroll
           for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(r[u].k[s], qop[s], zacc);
           const int tok0 = p * P + c * 16;
           softmax_chunk<D, GM>(st, zacc, tok0, L, p >= 0, scale_log2, pt, grp, col);
           // values of tokens that do not exist (past seq_len, skipped entries)
           // are zeroed: their probability is 0 but the memory may hold NaN
           const bool full = p >= 0 && tok0 + 16 <= L;
-#pragma unroll
+  #pragma unroll
           for (int j = 0; j < 4; ++j) {
             float v[EV];
             unpack_v<F16, EV>(r[u].v[j], v);
             if (!full) {
               const uint32_t vk = (p >= 0 && tok0 + 4 * j + grp < L) ? 0xFFFFFFFFu : 0u;
-#pragma unroll
+  #pragma unroll
               for (int e = 0; e < EV; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) & vk);
             }
             pv_accumulate<D, GM>(st, v, pt, 4 * j + grp);
@@ -398,42 +463,84 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
           compute(rb, pb, cb + kBatch);
         }
       }
-    } else {
-      // tiered pages: decode in registers, one chunk at a time
-      for (int jj = 0; jj < nb; ++jj) {
-        const int p = __builtin_amdgcn_readlane(l_p, jj);
-        if (p < 0) continue;
-        const uint32_t tier = (uint32_t)__builtin_amdgcn_readlane((int)l_tier, jj);
-        const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, jj);
-        const int hot = __builtin_amdgcn_readlane(l_hot, jj);
-        const size_t pr = (size_t)slot * Hkv + g;
-        const size_t hr = ((size_t)hot * Hkv + g) * page_elems;
-        const uint16_t* kbase = hot >= 0 && pg.k_hot ? pg.k_hot + hr : pg.k16 + pr * page_elems;
-        const uint16_t* vbase = hot >= 0 ? pg.v_hot + hr : pg.v16 + pr * page_elems;
-        for (int c = 0; c < cpp; ++c) {
+    }
+  } else {
+    // Tiered pages: the wave's pages in batches of 64 (one per lane), each
+    // batch taken tier by tier so that every loop below has one load shape.
+    for (int j0 = 0; j0 < n_mine; j0 += 64) {
+      const int nb = n_mine - j0 < 64 ? n_mine - j0 : 64;
+      int l_p = -1, l_hot = -1;
+      uint32_t l_tier = 7, l_slot = 0;   // 7: not a valid entry
+      if (lane < nb) {
+        const int p = srow[beg + wave + kAttnWaves * (j0 + lane)];
+        if (p >= 0 && p < Np) {
+          l_p = p;
+          const int phys = bt[p];
+          l_slot = (uint32_t)phys;
+          l_tier = KV_TIER_NATIVE;
+          if (pg.page_entry) {
+            const uint32_t e = pg.page_entry[phys];
+            l_tier = e >> 29;
+            l_slot = e & 0x1FFFFFFFu;
+          }
+          if (pg.v_hot_slot) l_hot = pg.v_hot_slot[phys];
+        }
+      }
+      auto run_tier = [&](auto tc) {
+        constexpr int T = decltype(tc)::value;
+        using Raw = typename std::conditional<T == KV_TIER_NATIVE, ChunkRaw<D>, TierChunk<D, T>>::type;
+        const unsigned long long mask = __ballot(l_p >= 0 && l_tier == (uint32_t)T);
+        if (mask == 0) return;
+        const int nu = __popcll(mask) * cpp;
+        // units in list order; past the last one the iterator repeats it (a
+        // request whose result is never computed), so every load below is
+        // unconditional and the wait counts do not depend on the path
+        unsigned long long it = mask;
+        int it_c = 0, last_lane = __ffsll((long long)mask) - 1, last_c = 0;
+        auto next = [&](int& lane_out, int& c_out) {
+          if (it == 0) {
+            lane_out = last_lane;
+            c_out = last_c;
+            return;
+          }
+          lane_out = last_lane = __ffsll((long long)it) - 1;
+          c_out = last_c = it_c;
+          if (++it_c == cpp) {
+            it_c = 0;
+            it &= it - 1;
+          }
+        };
+        auto issue = [&](Raw& r, int jj, int c) {
+          const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, jj);
+          const size_t pr = (size_t)slot * Hkv + g;
+          if constexpr (T == KV_TIER_NATIVE) {
+            const int hot = __builtin_amdgcn_readlane(l_hot, jj);
+            const size_t hr = ((size_t)hot * Hkv + g) * page_elems;
+            const uint16_t* kbase = hot >= 0 && pg.k_hot ? pg.k_hot + hr : pg.k16 + pr * page_elems;
+            const uint16_t* vbase = hot >= 0 ? pg.v_hot + hr : pg.v16 + pr * page_elems;
+            load_native_chunk<D>(r, kbase, vbase, c, col, grp);
+          } else {
+            const size_t tok = pr * P + c * 16;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+              tier_load<D, 8, T>(pg.kq[T - 1], pg.ksz[T - 1], tok + col, 32 * s + 8 * grp, r.k[s], r.ksz[s]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              tier_load<D, EV, T>(pg.vq[T - 1], pg.vsz[T - 1], tok + 4 * j + grp, col * EV, r.v[j], r.vsz[j]);
+          }
+        };
+        auto compute = [&](const Raw& r, int jj, int c) {
+          const int p = __builtin_amdgcn_readlane(l_p, jj);
           const int tok0 = p * P + c * 16;
           f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
-          if (tier == KV_TIER_NATIVE) {
-            const uint16_t* kp = kbase + (size_t)(c * 16 + col) * D + 8 * grp;
-            u32x4_t a[KS];
+          if constexpr (T == KV_TIER_NATIVE) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) a[s] = ld16(kp + 32 * s);
-#pragma unroll
-            for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(a[s], qop[s], zacc);
+            for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(r.k[s], qop[s], zacc);
           } else {
-            // decode the elements this lane feeds at each k-step, [32s + 8grp, +8)
-            const size_t tokrow = pr * P + c * 16 + col;
-            const int t = (int)tier - 1;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
               float x[8];
-              switch (tier) {
-                case KV_TIER_I8: decode_run<D, 8, 8>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
-                case KV_TIER_I4: decode_run<D, 8, 4>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
-                case KV_TIER_I2: decode_run<D, 8, 2>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
-                case KV_TIER_FP8: decode_fp8<D, 8>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
-                default: decode_run<D, 8, 1>(pg.kq[t], pg.ksz[t], tokrow, 32 * s + 8 * grp, x); break;
-              }
+              tier_decode<8, T>(r.k[s], r.ksz[s], 32 * s + 8 * grp, x);
               u32x4_t ah, al;
 #pragma unroll
               for (int w = 0; w < 4; ++w) {
@@ -447,42 +554,46 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
             }
           }
           softmax_chunk<D, GM>(st, zacc, tok0, L, true, scale_log2, pt, grp, col);
+          const bool full = tok0 + 16 <= L;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int tk = 4 * j + grp;
-            const bool valid = tok0 + tk < L;
             float v[EV];
-            if (tier == KV_TIER_NATIVE) {
-              const uint16_t* vp = vbase + (size_t)(c * 16 + tk) * D + col * EV;
-              u32x4_t r = u32x4_t{0, 0, 0, 0};
-              if (valid) {
-                if constexpr (EV == 8) r = ld16(vp);
-                else {
-                  const u32x2_t t2 = *reinterpret_cast<const u32x2_t*>(vp);
-                  r = u32x4_t{t2[0], t2[1], 0, 0};
-                }
-              }
-              unpack_v<F16, EV>(r, v);
-            } else {
-              const size_t tokrow = pr * P + c * 16 + tk;
-              const int t = (int)tier - 1;
-              switch (tier) {
-                case KV_TIER_I8: decode_run<D, EV, 8>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
-                case KV_TIER_I4: decode_run<D, EV, 4>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
-                case KV_TIER_I2: decode_run<D, EV, 2>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
-                case KV_TIER_FP8: decode_fp8<D, EV>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
-                default: decode_run<D, EV, 1>(pg.vq[t], pg.vsz[t], tokrow, col * EV, v); break;
-              }
-              if (!valid) {
+            if constexpr (T == KV_TIER_NATIVE) unpack_v<F16, EV>(r.v[j], v);
+            else tier_decode<EV, T>(r.v[j], r.vsz[j], col * EV, v);
+            // values of tokens past seq_len are zeroed: probability 0, memory may hold NaN
+            if (!full) {
+              const uint32_t vk = tok0 + tk < L ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-                for (int e = 0; e < EV; ++e) v[e] = 0.f;
-              }
+              for (int e = 0; e < EV; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) & vk);
             }
             pv_accumulate<D, GM>(st, v, pt, tk);
           }
           wave_lds_sync();
+        };
+        Raw ra, rb;
+        int ja, ca, jb, cb;
+        next(ja, ca);
+        issue(ra, ja, ca);
+        int u = 0;
+        for (; u + 2 <= nu; u += 2) {
+          next(jb, cb);
+          issue(rb, jb, cb);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(ra, ja, ca);
+          next(ja, ca);
+          issue(ra, ja, ca);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(rb, jb, cb);
         }
-      }
+        if (u < nu) compute(ra, ja, ca);
+      };
+      run_tier(TierTag<KV_TIER_NATIVE>{});
+      run_tier(TierTag<KV_TIER_FP8>{});
+      run_tier(TierTag<KV_TIER_I8>{});
+      run_tier(TierTag<KV_TIER_I4>{});
+      run_tier(TierTag<KV_TIER_I2>{});
+      run_tier(TierTag<KV_TIER_B1>{});
     }
   }
 

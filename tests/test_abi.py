@@ -111,8 +111,8 @@ def test_attention_validation_and_workspace():
                  FAKE, FAKE, 164, splits, FAKE, FAKE, ws, ws_bytes, None)
 
     s = kv.attn_num_splits(L, 8, 164)                  # native pages: one block per CU
-    st = kv.attn_num_splits(L, 8, 164, tiered=True)    # packed tiers: three blocks per CU
-    assert (s, st) == (4, 12)
+    st = kv.attn_num_splits(L, 8, 164, tiered=True)    # packed tiers: two blocks per CU
+    assert (s, st) == (4, 8)
     assert kv.attn_num_splits(L, 8, 16) == 2           # at least two pages per wave
     need = kv.attn_workspace_size(L, 8, 164, s)
     assert need == 64 * s * 4 * 130 * 4 + 64 * 4       # partials + one counter per row
