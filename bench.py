@@ -240,6 +240,7 @@ def main():
 
     # ---- timed region: K steps (row groups overlapped on streams), replayed
     #      from a HIP graph that holds one pass over the rotated layers
+    per_replay = None
     if args.eager:
         timed_steps = K
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -261,14 +262,16 @@ def main():
         torch.cuda.synchronize()
         reps = max(1, K // n_cap)
         timed_steps = reps * n_cap
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # one event per replay boundary (events only, no synchronisation inside)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
+        ev[0].record(stream)
+        for r in range(reps):
             g.replay()
-        b.record(stream)
+            ev[r + 1].record(stream)
         torch.cuda.synchronize()
-        ms_per_step = a.elapsed_time(b) / timed_steps
+        ms_per_step = ev[0].elapsed_time(ev[-1]) / timed_steps
+        per_replay = np.array([ev[r].elapsed_time(ev[r + 1]) / n_cap for r in range(reps)])
     log(f"[bench] timed {timed_steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
     sel_counts = bufs[0].sel_count.cpu().numpy()
@@ -301,6 +304,10 @@ def main():
         "pct_hbm_peak": 100.0 * step_bytes / (best_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": {"summaries": summary_b, "selected_kv": selected_b},
         "eager_single_chain_ms_per_step": eager_ms,
+        "step_ms_distribution": None if per_replay is None else {
+            "over": f"{len(per_replay)} graph replays of {n_cap} steps each",
+            "median": float(np.median(per_replay)), "p10": float(np.percentile(per_replay, 10)),
+            "p90": float(np.percentile(per_replay, 90))},
         "kernel_avg_us": {"page_score": score_us, "page_topk": topk_us, "sparse_decode_attn": attend_us},
         "roofline": {
             "kernel": "page_score_kernel",
@@ -372,6 +379,25 @@ def main():
             "note": "same layers, queries and attention; summaries = shared row basis + per-page mean "
                     "and variances (not the headline's per-page directions)",
         }
+    # dense line for context: the same attention kernel over every page of
+    # every row (k = Np, no score and no selection)
+    if tiers is None:
+        dsel = torch.arange(w.Np, dtype=torch.int32, device="cuda").repeat(w.B, w.Hkv, 1).contiguous()
+        dcnt = torch.full((w.B, w.Hkv), w.Np, dtype=torch.int32, device="cuda")
+        dout = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+        dlse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+        dws = torch.zeros(max(1, kv.attn_workspace_size(layers[0].L, w.B, w.Np) // 4), dtype=torch.float32,
+                          device="cuda")
+        dense_us, _ = graph_avg_us(lambda li, q: kv.sparse_decode_attn(layers[li].L, q, layers[li].pages,
+                                                                       layers[li].bt, layers[li].seq_lens, dsel,
+                                                                       dcnt, dout, dlse, dws))
+        dense_b = w.rows * w.Np * page_bytes(w, 0)
+        result["dense_attention"] = {"avg_launch_us": dense_us, "kv_bytes": dense_b,
+                                     "achieved_GBps": dense_b / (dense_us * 1e3),
+                                     "note": "every page of every row through kv_sparse_decode_attn; context "
+                                             "only, not the path"}
+        log(f"[bench] dense attention (k = Np): {dense_us:.1f} us, {dense_b / (dense_us * 1e3):.0f} GB/s")
+        del dsel, dws
     # coverage-mode selection (k per row from the mass prefix) on the headline
     # layers' scores: its kernel time and the k it picks, for context
     from quantized_kv_cache_summary_amd import kvsparse as kvs
@@ -409,6 +435,19 @@ def selected_pages(sel, sel_count, bt, seq_lens, P):
     ok = (idx < np.clip(sel_count, 0, k_max)[:, :, None]) & (sel >= 0) & (sel < npg[:, None, None])
     b = np.broadcast_to(np.arange(B)[:, None, None], sel.shape)
     return bt[b[ok], sel[ok]]
+
+
+HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction, nominal
+
+
+def combined_bound(summary_b, selected_b, run):
+    """The step's bound when V of cold pages crosses the host link: the larger
+    of (HBM bytes / 8 TB/s) and (host-link bytes / the link's nominal rate)."""
+    host_b = run["host_bytes_read_by_attention"]
+    hbm_b = summary_b + selected_b - host_b
+    t = max(hbm_b / (HBM_PEAK_GBS * 1e9), host_b / (HOST_LINK_GBS * 1e9))
+    return {"hbm_bytes": hbm_b, "host_bytes": host_b, "bound_ms": t * 1e3,
+            "frac": t * 1e3 / run["ms_per_step"]}
 
 
 def mem_main(args, w):
@@ -529,7 +568,9 @@ def mem_main(args, w):
             "achieved_GBps": static["host_bytes_read_by_attention"] / (static["attention_us"] * 1e3),
             "admission_copy_GBps": (admitted["pages_copied_per_step"] * page_v / (admitted["admission_us"] * 1e3)
                                     if admitted["admission_us"] else None),
+            "link_peak_GBps": HOST_LINK_GBS,
         },
+        "combined_bound": combined_bound(summary_b, selected_b, static),
         "static_hot_buffer": static,
         "lru_admission": admitted,
         "mem_kv": memkv,
