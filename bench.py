@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-basis", action="store_true",
                     help="skip the shared-basis summary variant (reported beside the headline)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the context lines (dense attention, coverage-mode top-k), e.g. under a profiler")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy (known bytes) for scaling counter readings")
     ap.add_argument("--mem-kv", action="store_true",
@@ -321,7 +323,7 @@ def main():
             "bytes_per_launch": summary_b,
         },
     }
-    if tiers is not None:
+    if tiers is not None and not args.no_extras:
         # attention alone over the same shape with every page in one packed
         # tier (same rotation, queries and selections): the decode cost per tier
         uni = {}
@@ -381,7 +383,7 @@ def main():
         }
     # dense line for context: the same attention kernel over every page of
     # every row (k = Np, no score and no selection)
-    if tiers is None:
+    if tiers is None and not args.no_extras:
         dsel = torch.arange(w.Np, dtype=torch.int32, device="cuda").repeat(w.B, w.Hkv, 1).contiguous()
         dcnt = torch.full((w.B, w.Hkv), w.Np, dtype=torch.int32, device="cuda")
         dout = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
@@ -403,20 +405,21 @@ def main():
     from quantized_kv_cache_summary_amd import kvsparse as kvs
     if tiers is not None:
         args.no_cpu_baseline = True
-    cov_sel = [torch.empty((w.B, w.Hkv, w.Np), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
-    cov_cnt = [torch.empty((w.B, w.Hkv), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
-    for li in range(n_layers):
-        hz.score(layers[li], qs[li][0], bufs[li])
-    cov = {}
-    for c in (0.5, 0.95):
-        us, _ = graph_avg_us(lambda li, q: kvs.page_topk_coverage(layers[li].L, bufs[li].head_scores,
-                                                                  bufs[li].lse_partial, layers[li].seq_lens, w.Np,
-                                                                  c, cov_sel[li], cov_cnt[li]))
-        kk = cov_cnt[0].cpu().numpy()
-        cov[str(c)] = {"avg_launch_us": us, "k_mean": float(kk.mean()), "k_min": int(kk.min()),
-                       "k_max": int(kk.max())}
-    result["coverage_topk"] = cov
-    log(f"[bench] coverage-mode top-k: {cov}")
+    if not args.no_extras:
+        cov_sel = [torch.empty((w.B, w.Hkv, w.Np), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+        cov_cnt = [torch.empty((w.B, w.Hkv), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+        for li in range(n_layers):
+            hz.score(layers[li], qs[li][0], bufs[li])
+        cov = {}
+        for c in (0.5, 0.95):
+            us, _ = graph_avg_us(lambda li, q: kvs.page_topk_coverage(layers[li].L, bufs[li].head_scores,
+                                                                      bufs[li].lse_partial, layers[li].seq_lens, w.Np,
+                                                                      c, cov_sel[li], cov_cnt[li]))
+            kk = cov_cnt[0].cpu().numpy()
+            cov[str(c)] = {"avg_launch_us": us, "k_mean": float(kk.mean()), "k_min": int(kk.min()),
+                           "k_max": int(kk.max())}
+        result["coverage_topk"] = cov
+        log(f"[bench] coverage-mode top-k: {cov}")
     if not args.no_cpu_baseline:
         log("[bench] oracle baseline on the host ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
