@@ -42,6 +42,8 @@ from .codec import (
     pack_codes, unpack_codes,
 )
 from .hotbuffer import HotBuffer, selected_physical_pages
+from .cascade import (TIER_OF_LEVEL, LEVEL_OF_TIER, page_importance, rank_pages, desired_levels, plan_row,
+                      retier_vectors)
 from .pipeline import decode_row
 
 __all__ = [
@@ -58,5 +60,7 @@ __all__ = [
     "round_e4m3", "encode_vector", "decode_vector",
     "pack_codes", "unpack_codes",
     "HotBuffer", "selected_physical_pages",
+    "TIER_OF_LEVEL", "LEVEL_OF_TIER", "page_importance", "rank_pages", "desired_levels", "plan_row",
+    "retier_vectors",
     "decode_row",
 ]
