@@ -369,6 +369,43 @@ int kv_pack_tier(const kv_layout* layout, const void* src16, const int32_t* src_
                  int32_t tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
                  void* stream);
 
+/* ---------------------------------------------------------------------------
+ * kv_tier_plan -- which pages move one step down the compression cascade
+ * (ARGUS page, "The One-Minute Explanation" and "Visual Architecture": 16-bit
+ * for critical and recent pages, then FP8 -> int8 -> int4 -> int2 -> 1-bit as
+ * pages cool; per-tier page budgets from its configuration).  Levels: 0
+ * native, 1 FP8, 2 int8, 3 int4, 4 int2, 5 1-bit.  For every sequence b, over
+ * its valid pages p < Np_b:
+ *   importance i_p = max over KV heads g of page_S[b][g][p] (the group-mean
+ *   page mass kv_page_topk writes; NaN counts as -inf);
+ *   rank: the first n_force_first and last n_force_last pages first (by
+ *   index), then i descending, page index ascending;
+ *   desired level d_p = the smallest l <= 4 with rank < caps[0] + .. + caps[l],
+ *   else 5 (caps: host array of 5 page budgets, >= 0);
+ *   a page with d_p above its current level (from page_entry through
+ *   block_table) moves down one level; no page moves up.
+ * page_S float32 [B][Hkv][max_pages]; moves int32 [B][max_pages][2] receives
+ * per sequence, in page order, (physical page, new tier id); move_count int32
+ * [B].  max_pages <= 15360.
+ * --------------------------------------------------------------------------- */
+int kv_tier_plan(const kv_layout* layout, const float* page_S, const int32_t* seq_lens, int32_t B,
+                 int32_t max_pages, const int32_t* block_table, const uint32_t* page_entry, const int32_t* caps,
+                 int32_t n_force_first, int32_t n_force_last, int32_t* moves, int32_t* move_count, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_tier_demote -- carry out a tier plan: every listed page's K and V (all KV
+ * heads and tokens) is decoded from its current tier (the attention kernel's
+ * decoding) and encoded into the new tier with kv_pack_tier's encoder, applied
+ * to the decoded float32 values; the codes and (scale, zero) pairs go to slot
+ * `phys` of the new tier's pools, which must therefore hold at least n_phys
+ * slots, and page_entry[phys] becomes KV_PAGE_ENTRY(new tier, phys).
+ * pages_desc: the pools (written: the tier pools named by the moves) with
+ * pages_desc->page_entry == page_entry.  moves / move_count as kv_tier_plan
+ * leaves them (device memory).  Pages of a move list are distinct.
+ * --------------------------------------------------------------------------- */
+int kv_tier_demote(const kv_layout* layout, const kv_pages* pages_desc, uint32_t* page_entry, int32_t B,
+                   int32_t max_pages, const int32_t* moves, const int32_t* move_count, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kv_status_string(int status);
 

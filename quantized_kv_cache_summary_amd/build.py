@@ -28,6 +28,7 @@ SOURCES = {
     "basis_build.hip": [],
     "score_basis.hip": [],
     "hot_admit.hip": [],
+    "tier_plan.hip": [],
     "codec.hip": ["-ffp-contract=off"],
 }
 

@@ -307,6 +307,37 @@ int kv_dequant_tier(const kv_layout* L, const kv_pages* pg, const int32_t* pages
   return from_hip(kvs::launch_dequant_tier(*L, *pg, pages, n, out, (hipStream_t)stream));
 }
 
+int kv_tier_plan(const kv_layout* L, const float* page_S, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                 const int32_t* block_table, const uint32_t* page_entry, const int32_t* caps,
+                 int32_t n_force_first, int32_t n_force_last, int32_t* moves, int32_t* move_count, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0 || n_force_first < 0 || n_force_last < 0 || !caps) return KV_ERR_INVALID_ARG;
+  if (max_pages > kvs::kMaxTopkPages) return KV_ERR_UNSUPPORTED;
+  if (B == 0 || max_pages == 0) return KV_OK;
+  if (!page_S || !seq_lens || !block_table || !page_entry || !moves || !move_count) return KV_ERR_INVALID_ARG;
+  int32_t c[5];
+  for (int l = 0; l < 5; ++l) {
+    if (caps[l] < 0) return KV_ERR_INVALID_ARG;
+    c[l] = caps[l] < max_pages ? caps[l] : max_pages;
+  }
+  return from_hip(kvs::launch_tier_plan(*L, page_S, seq_lens, B, max_pages, block_table, page_entry, c,
+                                        n_force_first, n_force_last, moves, move_count, (hipStream_t)stream));
+}
+
+int kv_tier_demote(const kv_layout* L, const kv_pages* pg, uint32_t* page_entry, int32_t B, int32_t max_pages,
+                   const int32_t* moves, const int32_t* move_count, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
+  if (B == 0 || max_pages == 0) return KV_OK;
+  rc = check_pages(L, pg);
+  if (rc) return rc;
+  if (!page_entry || pg->page_entry != page_entry || !moves || !move_count) return KV_ERR_INVALID_ARG;
+  return from_hip(kvs::launch_tier_demote(*L, *pg, page_entry, B, max_pages, moves, move_count,
+                                          (hipStream_t)stream));
+}
+
 int kv_pack_tier(const kv_layout* L, const void* src16, const int32_t* src_pages, int32_t n,
                  int32_t tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
                  void* stream) {

@@ -19,6 +19,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "tiers.h"
 
 namespace kvs {
 
@@ -51,14 +52,82 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return sign | mag;
 }
 
+// Bits per code of a packed tier.
+__device__ __forceinline__ int tier_code_bits(int tier) {
+  return tier == KV_TIER_I4 ? 4 : tier == KV_TIER_I2 ? 2 : tier == KV_TIER_B1 ? 1 : 8;
+}
+
+// Encodes one 32-element group of float32 values into packed tier `tier`.
+__device__ __forceinline__ void encode_group(const float (&x)[32], int tier, uint32_t (&c)[32], float& s, float& z) {
+  if (tier == KV_TIER_B1) {
+    float t[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t[j] = x[2 * j] + x[2 * j + 1];
+#pragma unroll
+    for (int len = 8; len >= 1; len >>= 1)
+#pragma unroll
+      for (int j = 0; j < len; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+    z = f16_sat(t[0] / 32.f);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t[j] = fabsf(x[2 * j] - z) + fabsf(x[2 * j + 1] - z);
+#pragma unroll
+    for (int len = 8; len >= 1; len >>= 1)
+#pragma unroll
+      for (int j = 0; j < len; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+    s = f16_sat(t[0] / 32.f);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j] = x[j] >= z ? 1u : 0u;
+  } else if (tier == KV_TIER_FP8) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    s = f16_sat(amax / 448.f);
+    z = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j] = s != 0.f ? f32_to_e4m3(x[j] / s) : 0u;
+  } else {
+    const int bits = tier_code_bits(tier);
+    const float qmax = (float)((1 << bits) - 1);
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
+    s = f16_sat((mx - mn) / qmax);
+    z = f16_sat(mn);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      float cj = 0.f;
+      if (s != 0.f) cj = fminf(fmaxf(__builtin_rintf((x[j] - z) / s), 0.f), qmax);
+      c[j] = (uint32_t)cj;
+    }
+  }
+}
+
+// Writes one encoded group: its codes (LSB first) into token row `row` of a
+// code pool ([slots][Hkv][P][D*bits/8]) and its (scale, zero) pair.
+template <int D>
+__device__ __forceinline__ void store_group(uint8_t* codes, uint16_t* scale_zero, size_t row, int grp, int bits,
+                                            const uint32_t (&c)[32], float s, float z) {
+  uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * (D * bits / 8) + grp * 4 * bits);
+  const int per_word = 32 / bits;
+  for (int wdx = 0; wdx < bits; ++wdx) {
+    uint32_t word = 0;
+    for (int j = 0; j < per_word; ++j) word |= c[wdx * per_word + j] << (j * bits);
+    dst[wdx] = word;
+  }
+  uint16_t* szp = scale_zero + (row * (D / 32) + grp) * 2;
+  szp[0] = f16_bits(s);
+  szp[1] = f16_bits(z);
+}
+
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void pack_tier_kernel(const uint16_t* __restrict__ src16,
                                                         const int32_t* __restrict__ src_pages,
                                                         const int32_t* __restrict__ dst_slots, int n,
-                                                        int Hkv, int P, int bits, bool fp8,
+                                                        int Hkv, int P, int tier,
                                                         uint8_t* __restrict__ codes,
                                                         uint16_t* __restrict__ scale_zero) {
   constexpr int NG = D / 32;
+  const int bits = tier_code_bits(tier);
   const size_t total = (size_t)n * Hkv * P * NG;
   for (size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x; id < total;
        id += (size_t)gridDim.x * blockDim.x) {
@@ -82,78 +151,132 @@ __global__ __launch_bounds__(256) void pack_tier_kernel(const uint16_t* __restri
     }
     uint32_t c[32];
     float s, z;
-    if (bits == 1) {
-      float t[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) t[j] = x[2 * j] + x[2 * j + 1];
-#pragma unroll
-      for (int len = 8; len >= 1; len >>= 1)
-#pragma unroll
-        for (int j = 0; j < len; ++j) t[j] = t[2 * j] + t[2 * j + 1];
-      z = f16_sat(t[0] / 32.f);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) t[j] = fabsf(x[2 * j] - z) + fabsf(x[2 * j + 1] - z);
-#pragma unroll
-      for (int len = 8; len >= 1; len >>= 1)
-#pragma unroll
-        for (int j = 0; j < len; ++j) t[j] = t[2 * j] + t[2 * j + 1];
-      s = f16_sat(t[0] / 32.f);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) c[j] = x[j] >= z ? 1u : 0u;
-    } else if (fp8) {
-      float amax = 0.f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
-      s = f16_sat(amax / 448.f);
-      z = 0.f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) c[j] = s != 0.f ? f32_to_e4m3(x[j] / s) : 0u;
-    } else {
-      const float qmax = (float)((1 << bits) - 1);
-      float mn = x[0], mx = x[0];
-#pragma unroll
-      for (int j = 1; j < 32; ++j) { mn = fminf(mn, x[j]); mx = fmaxf(mx, x[j]); }
-      s = f16_sat((mx - mn) / qmax);
-      z = f16_sat(mn);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        float cj = 0.f;
-        if (s != 0.f) cj = fminf(fmaxf(__builtin_rintf((x[j] - z) / s), 0.f), qmax);
-        c[j] = (uint32_t)cj;
-      }
-    }
-    // pack: 32 codes of `bits` bits -> bits 32-bit words, LSB first
-    const size_t row = ((size_t)ds * Hkv + g) * P + tk;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * (D * bits / 8) + grp * 4 * bits);
-    const int per_word = 32 / bits;
-    for (int wdx = 0; wdx < bits; ++wdx) {
-      uint32_t word = 0;
-      for (int j = 0; j < per_word; ++j) word |= c[wdx * per_word + j] << (j * bits);
-      dst[wdx] = word;
-    }
-    uint16_t* szp = scale_zero + (row * NG + grp) * 2;
-    szp[0] = f16_bits(s);
-    szp[1] = f16_bits(z);
+    encode_group(x, tier, c, s, z);
+    store_group<D>(codes, scale_zero, ((size_t)ds * Hkv + g) * P + tk, grp, bits, c, s, z);
   }
 }
 
 hipError_t launch_pack_tier(const kv_layout& L, const void* src16, const int32_t* src_pages, int n,
                             int tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
                             hipStream_t st) {
-  static const int kBits[6] = {16, 8, 4, 2, 1, 8};
-  const int bits = kBits[tier];
-  const bool fp8 = tier == KV_TIER_FP8;
   const size_t total = (size_t)n * L.num_kv_heads * L.page_size * (L.head_dim / 32);
   const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
   const uint16_t* s = (const uint16_t*)src16;
   uint16_t* sz = (uint16_t*)scale_zero;
   const bool f16 = L.kv_dtype == KV_F16;
   if (L.head_dim == 64) {
-    if (f16) hipLaunchKernelGGL((pack_tier_kernel<64, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, fp8, codes, sz);
-    else hipLaunchKernelGGL((pack_tier_kernel<64, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, fp8, codes, sz);
+    if (f16) hipLaunchKernelGGL((pack_tier_kernel<64, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz);
+    else hipLaunchKernelGGL((pack_tier_kernel<64, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz);
   } else {
-    if (f16) hipLaunchKernelGGL((pack_tier_kernel<128, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, fp8, codes, sz);
-    else hipLaunchKernelGGL((pack_tier_kernel<128, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, bits, fp8, codes, sz);
+    if (f16) hipLaunchKernelGGL((pack_tier_kernel<128, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz);
+    else hipLaunchKernelGGL((pack_tier_kernel<128, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- demotion
+
+// Re-encodes the pages a tier plan moves (ARGUS, "Visual Architecture": the
+// compression cascade).  Block (i, b) takes move i of sequence b: every
+// 32-element group of the page's K and V (all KV heads and tokens) is decoded
+// from its current tier (page_entry) and encoded into the new one at slot
+// phys, then the page's entry is switched.  Blocks past a row's move count
+// exit.
+struct TierPools {
+  const uint16_t* k16;
+  const uint16_t* v16;
+  uint8_t* kq[KV_NUM_PACKED_TIERS];
+  uint8_t* vq[KV_NUM_PACKED_TIERS];
+  uint16_t* ksz[KV_NUM_PACKED_TIERS];
+  uint16_t* vsz[KV_NUM_PACKED_TIERS];
+};
+
+template <int D, bool F16>
+__device__ __forceinline__ void decode_group_any(const TierPools& tp, int kv, uint32_t tier, size_t row, int grp,
+                                                 float (&x)[32]) {
+  if (tier == KV_TIER_NATIVE) {
+    const uint16_t* xs = (kv == 0 ? tp.k16 : tp.v16) + row * D + grp * 32;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u32x4_t w = ld16(xs + 8 * v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * v + 2 * j] = lo16<F16>(w[j]);
+        x[8 * v + 2 * j + 1] = hi16<F16>(w[j]);
+      }
+    }
+    return;
+  }
+  const int t = (int)tier - 1;
+  const uint8_t* codes = kv == 0 ? tp.kq[t] : tp.vq[t];
+  const uint16_t* sz = kv == 0 ? tp.ksz[t] : tp.vsz[t];
+  switch (tier) {
+    case KV_TIER_I8: decode_run<D, 32, 8>(codes, sz, row, grp * 32, x); break;
+    case KV_TIER_I4: decode_run<D, 32, 4>(codes, sz, row, grp * 32, x); break;
+    case KV_TIER_I2: decode_run<D, 32, 2>(codes, sz, row, grp * 32, x); break;
+    case KV_TIER_FP8:
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float y[8];
+        decode_fp8<D, 8>(codes, sz, row, grp * 32 + 8 * j, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * j + e] = y[e];
+      }
+      break;
+    default: decode_run<D, 32, 1>(codes, sz, row, grp * 32, x); break;
+  }
+}
+
+template <int D, bool F16>
+__global__ __launch_bounds__(256) void tier_demote_kernel(TierPools tp, uint32_t* __restrict__ page_entry, int Hkv,
+                                                          int P, int max_pages, const int32_t* __restrict__ moves,
+                                                          const int32_t* __restrict__ move_count) {
+  constexpr int NG = D / 32;
+  const int i = blockIdx.x, b = blockIdx.y;
+  if (i >= move_count[b]) return;
+  const int32_t* mv = moves + ((size_t)b * max_pages + i) * 2;
+  const int phys = mv[0], nt = mv[1];
+  const uint32_t e = page_entry[phys];
+  const uint32_t ot = e >> 29, oslot = e & 0x1FFFFFFFu;
+  const int bits = tier_code_bits(nt);
+  const int groups = 2 * Hkv * P * NG;
+  for (int id = threadIdx.x; id < groups; id += 256) {
+    int r = id;
+    const int grp = r % NG; r /= NG;
+    const int tk = r % P; r /= P;
+    const int g = r % Hkv; r /= Hkv;
+    const int kv = r;
+    float x[32];
+    decode_group_any<D, F16>(tp, kv, ot, ((size_t)oslot * Hkv + g) * P + tk, grp, x);
+    uint32_t c[32];
+    float s, z;
+    encode_group(x, nt, c, s, z);
+    store_group<D>(kv == 0 ? tp.kq[nt - 1] : tp.vq[nt - 1], kv == 0 ? tp.ksz[nt - 1] : tp.vsz[nt - 1],
+                   ((size_t)phys * Hkv + g) * P + tk, grp, bits, c, s, z);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) page_entry[phys] = ((uint32_t)nt << 29) | (uint32_t)phys;
+}
+
+hipError_t launch_tier_demote(const kv_layout& L, const kv_pages& pg, uint32_t* page_entry, int B, int max_pages,
+                              const int32_t* moves, const int32_t* move_count, hipStream_t st) {
+  TierPools tp;
+  tp.k16 = (const uint16_t*)pg.k16;
+  tp.v16 = (const uint16_t*)pg.v16;
+  for (int t = 0; t < KV_NUM_PACKED_TIERS; ++t) {
+    tp.kq[t] = const_cast<uint8_t*>(pg.kq[t]);
+    tp.vq[t] = const_cast<uint8_t*>(pg.vq[t]);
+    tp.ksz[t] = (uint16_t*)const_cast<void*>(pg.ksz[t]);
+    tp.vsz[t] = (uint16_t*)const_cast<void*>(pg.vsz[t]);
+  }
+  const dim3 grid(max_pages, B);
+  const bool f16 = L.kv_dtype == KV_F16;
+  if (L.head_dim == 64) {
+    if (f16) hipLaunchKernelGGL((tier_demote_kernel<64, true>), grid, dim3(256), 0, st, tp, page_entry, L.num_kv_heads, L.page_size, max_pages, moves, move_count);
+    else hipLaunchKernelGGL((tier_demote_kernel<64, false>), grid, dim3(256), 0, st, tp, page_entry, L.num_kv_heads, L.page_size, max_pages, moves, move_count);
+  } else {
+    if (f16) hipLaunchKernelGGL((tier_demote_kernel<128, true>), grid, dim3(256), 0, st, tp, page_entry, L.num_kv_heads, L.page_size, max_pages, moves, move_count);
+    else hipLaunchKernelGGL((tier_demote_kernel<128, false>), grid, dim3(256), 0, st, tp, page_entry, L.num_kv_heads, L.page_size, max_pages, moves, move_count);
   }
   return hipGetLastError();
 }

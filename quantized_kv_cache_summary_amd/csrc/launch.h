@@ -84,6 +84,14 @@ hipError_t launch_sparse_attn(const kv_layout& L, const void* q, const kv_pages&
 hipError_t launch_dequant_tier(const kv_layout& L, const kv_pages& pg, const int32_t* pages, int n,
                                float* out, hipStream_t st);
 
+hipError_t launch_tier_plan(const kv_layout& L, const float* page_S, const int32_t* seq_lens, int B,
+                            int max_pages, const int32_t* block_table, const uint32_t* page_entry,
+                            const int32_t* caps, int n_force_first, int n_force_last, int32_t* moves,
+                            int32_t* move_count, hipStream_t st);
+
+hipError_t launch_tier_demote(const kv_layout& L, const kv_pages& pg, uint32_t* page_entry, int B, int max_pages,
+                              const int32_t* moves, const int32_t* move_count, hipStream_t st);
+
 hipError_t launch_pack_tier(const kv_layout& L, const void* src16, const int32_t* src_pages, int n,
                             int tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
                             hipStream_t st);

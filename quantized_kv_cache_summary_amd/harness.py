@@ -61,7 +61,7 @@ class DeviceLayer:
     """K/V pools, block table, summaries (and tier pools / host V) of one layer."""
 
     def __init__(self, w: wl.Workload, layer=0, summaries="build", device="cuda", host_v=None,
-                 hot_mode="warm", seq_lens=None, threads=None, host_k=None):
+                 hot_mode="warm", seq_lens=None, threads=None, host_k=None, tier_slots="compact"):
         self.w, self.layer, self.device = w, layer, device
         self.L = layout_of(w)
         host_v = w.v_host if host_v is None else host_v
@@ -123,7 +123,7 @@ class DeviceLayer:
         self.tiers = None
         self.page_entry = None
         if w.tier_fracs is not None:
-            self._pack_tiers()
+            self._pack_tiers(tier_slots)
         self.v_hot = self.k_hot = None
         self.v_hot_slot = None
         if host_v:
@@ -180,7 +180,11 @@ class DeviceLayer:
         kv.summary_build_basis(self.L, self.k_src, self.bt, entries, nv, self.basis, self.mu, self.lam,
                                self.log_n, stream)
 
-    def _pack_tiers(self):
+    def _pack_tiers(self, tier_slots="compact"):
+        """Packs every page into its tier.  tier_slots "compact": a tier's pool
+        holds only its pages; "phys": every tier pool has a slot per physical
+        page and a page sits at slot = its physical id (what tier demotion
+        writes to)."""
         w = self.w
         tiers_logical = wl.page_tiers(w, self.layer)              # (B, Np)
         tier_phys = np.zeros(w.n_phys, dtype=np.int64)
@@ -188,9 +192,10 @@ class DeviceLayer:
         self.tier_phys = tier_phys
         entry = np.zeros(w.n_phys, dtype=np.uint32)
         self.kq, self.vq, self.ksz, self.vsz = [], [], [], []
+        full = tier_slots == "phys"
         for t in range(1, kv.NUM_PACKED_TIERS + 1):
             phys = np.nonzero(tier_phys == t)[0].astype(np.int32)
-            n = max(1, phys.size)
+            n = w.n_phys if full else max(1, phys.size)
             bits = kv.TIER_BITS[t]
             kc = torch.zeros((n, w.Hkv, w.P, w.d * bits // 8), dtype=torch.uint8, device=self.device)
             vc = torch.zeros_like(kc)
@@ -198,9 +203,11 @@ class DeviceLayer:
             vs = torch.zeros_like(ks)
             if phys.size:
                 src = torch.from_numpy(phys).to(self.device)
-                kv.pack_tier(self.L, self.k16, phys.size, t, kc, ks, src_pages=src)
-                kv.pack_tier(self.L, self.v16, phys.size, t, vc, vs, src_pages=src)
-                entry[phys] = (np.uint32(t) << np.uint32(29)) | np.arange(phys.size, dtype=np.uint32)
+                slots = phys if full else np.arange(phys.size, dtype=np.int32)
+                dst = torch.from_numpy(slots).to(self.device) if full else None
+                kv.pack_tier(self.L, self.k16, phys.size, t, kc, ks, src_pages=src, dst_slots=dst)
+                kv.pack_tier(self.L, self.v16, phys.size, t, vc, vs, src_pages=src, dst_slots=dst)
+                entry[phys] = (np.uint32(t) << np.uint32(29)) | slots.astype(np.uint32)
             self.kq.append(kc); self.vq.append(vc); self.ksz.append(ks); self.vsz.append(vs)
         native = np.nonzero(tier_phys == 0)[0]
         entry[native] = native.astype(np.uint32)                  # native slot = physical page

@@ -27,7 +27,7 @@ SYMBOLS = (
     "kv_page_topk_workspace_size", "kv_sparse_decode_attn", "kv_sparse_decode_attn_workspace_size",
     "kv_sparse_decode_attn_num_splits", "kv_dequant_tier", "kv_pack_tier", "kv_status_string",
     "kv_basis_build", "kv_basis_build_workspace_size", "kv_summary_build_basis", "kv_page_score_basis",
-    "kv_page_topk_coverage", "kv_hot_admit", "kv_hot_admit_workspace_size",
+    "kv_page_topk_coverage", "kv_hot_admit", "kv_hot_admit_workspace_size", "kv_tier_plan", "kv_tier_demote",
 )
 
 
@@ -79,6 +79,8 @@ def lib():
             "kv_hot_admit": (_I, [_LP, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, ctypes.c_uint32,
                                   _P, _SZ, _P]),
             "kv_hot_admit_workspace_size": (_SZ, [_I]),
+            "kv_tier_plan": (_I, [_LP, _P, _P, _I, _I, _P, _P, ctypes.POINTER(ctypes.c_int32), _I, _I, _P, _P, _P]),
+            "kv_tier_demote": (_I, [_LP, ctypes.POINTER(KvPages), _P, _I, _I, _P, _P, _P]),
             "kv_page_topk_coverage": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P, _I, _P,
                                            _P, _SZ, _P]),
             "kv_sparse_decode_attn": (_I, [_LP, _P, _PP, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _P,
@@ -241,6 +243,24 @@ def hot_admit(L, v16_ptr, v_hot, v_hot_slot, slot_page, slot_stamp, block_table,
                             int(sel.shape[-1]), int(step), _p(ws), ws.numel() * ws.element_size(),
                             _stream(stream))
     _check(rc, "kv_hot_admit")
+
+
+def tier_plan(L, page_S, seq_lens, block_table, page_entry, caps, moves, move_count, n_force_first=0,
+              n_force_last=0, stream=None):
+    """caps: 5 page budgets (native, FP8, int8, int4, int2)."""
+    B, max_pages = block_table.shape
+    c = (ctypes.c_int32 * 5)(*[int(x) for x in caps])
+    rc = lib().kv_tier_plan(ctypes.byref(L), _p(page_S), _p(seq_lens), int(B), int(max_pages), _p(block_table),
+                            _p(page_entry), c, int(n_force_first), int(n_force_last), _p(moves), _p(move_count),
+                            _stream(stream))
+    _check(rc, "kv_tier_plan")
+
+
+def tier_demote(L, pages, page_entry, block_table, moves, move_count, stream=None):
+    B, max_pages = block_table.shape
+    rc = lib().kv_tier_demote(ctypes.byref(L), ctypes.byref(pages), _p(page_entry), int(B), int(max_pages),
+                              _p(moves), _p(move_count), _stream(stream))
+    _check(rc, "kv_tier_demote")
 
 
 def attn_num_splits(L, B, k_max, tiered=False):

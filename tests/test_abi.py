@@ -208,3 +208,36 @@ def test_hot_admit_validation_and_workspace():
     assert call(sel=None) == kv.KV_ERR_INVALID_ARG
     assert call(ws_bytes=(1 + 3 * 100) * 4 - 1) == kv.KV_ERR_WORKSPACE
     assert call(ws=None) == kv.KV_ERR_WORKSPACE
+
+
+def test_tier_plan_and_demote_validation():
+    L = _L()
+    lib = kv.lib()
+    ok = (ctypes.c_int32 * 5)(1, 1, 1, 1, 1)
+    bad = (ctypes.c_int32 * 5)(1, -1, 1, 1, 1)
+
+    def plan(caps=ok, B=2, mp=64, S=FAKE, ff=0):
+        return lib.kv_tier_plan(ctypes.byref(L), S, FAKE, B, mp, FAKE, FAKE, caps, ff, 0, FAKE, FAKE, None)
+
+    assert plan(caps=None) == kv.KV_ERR_INVALID_ARG
+    assert plan(caps=bad) == kv.KV_ERR_INVALID_ARG
+    assert plan(ff=-1) == kv.KV_ERR_INVALID_ARG
+    assert plan(mp=20000) == kv.KV_ERR_UNSUPPORTED
+    assert plan(S=None) == kv.KV_ERR_INVALID_ARG
+    assert plan(B=0) == kv.KV_OK
+    pg = kv.KvPages()
+    pg.k16 = FAKE
+    pg.v16 = FAKE
+    pg.page_entry = FAKE
+    for t in range(kv.NUM_PACKED_TIERS):
+        pg.kq[t] = pg.vq[t] = pg.ksz[t] = pg.vsz[t] = FAKE
+
+    def demote(entry=FAKE, pages=pg, B=2):
+        return lib.kv_tier_demote(ctypes.byref(L), ctypes.byref(pages) if pages is not None else None, entry, B, 64,
+                                  FAKE, FAKE, None)
+
+    assert demote(entry=FAKE + 16) == kv.KV_ERR_INVALID_ARG        # not the pools' own page_entry
+    assert demote(pages=None) == kv.KV_ERR_INVALID_ARG
+    assert demote(B=0) == kv.KV_OK
+    pg.kq[2] = None
+    assert demote() == kv.KV_ERR_INVALID_ARG                        # a tier pool missing

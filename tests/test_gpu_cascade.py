@@ -1,0 +1,185 @@
+"""GPU parity of the tier demotion along the compression cascade
+(kv_tier_plan, kv_tier_demote) against the oracle's reading: plans are exact
+(integers), re-encoded codes and scales are bit-exact, attention over the
+demoted pages matches the oracle, and repeated calls converge to the budgets."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import assert_attn_close
+from quantized_kv_cache_summary_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+W = wl.WORKLOADS
+TIERS = (0, 5, 1, 2, 3, 4)
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def kv():
+    from quantized_kv_cache_summary_amd import kvsparse
+    return kvsparse
+
+
+@pytest.fixture(scope="module")
+def hz():
+    from quantized_kv_cache_summary_amd import harness
+    return harness
+
+
+def _expected_moves(S, seq_lens, bt, entry, P, caps, ff, fl):
+    out = []
+    for b in range(bt.shape[0]):
+        npg = min(bt.shape[1], -(-int(seq_lens[b]) // P)) if seq_lens[b] > 0 else 0
+        if npg == 0:
+            out.append([])
+            continue
+        phys = bt[b, :npg]
+        cur = (entry[phys] >> 29).astype(np.int64)
+        new = oracle.plan_row(oracle.page_importance(S[b, :, :npg]), cur, caps, ff, fl)
+        out.append([(int(phys[p]), int(new[p])) for p in range(npg) if new[p] != cur[p]])
+    return out
+
+
+@pytest.mark.parametrize("max_pages,caps,ff,fl", [(300, (3, 7, 0, 20, 50), 1, 2), (1500, (40, 100, 200, 300, 400), 0, 1),
+                                                  (64, (0, 0, 0, 0, 0), 0, 0), (64, (500, 0, 0, 0, 0), 2, 0)])
+def test_plan_matches_oracle(kv, max_pages, caps, ff, fl):
+    announce(f"tier plan max_pages={max_pages} caps={caps}")
+    rng = np.random.default_rng(max_pages + sum(caps))
+    B, Hkv, P = 3, 2, 16
+    L = kv.layout(8, Hkv, 64, P, 2, "f16")
+    seq_lens = np.array([max_pages * P, (max_pages // 2) * P + 5, 0], dtype=np.int32)
+    n_phys = B * max_pages
+    bt = rng.permutation(n_phys).astype(np.int32).reshape(B, max_pages)
+    tiers = rng.choice(TIERS, n_phys, p=[0.4, 0.2, 0.2, 0.1, 0.05, 0.05]).astype(np.uint32)
+    entry = (tiers << np.uint32(29)) | np.arange(n_phys, dtype=np.uint32)
+    S = rng.standard_normal((B, Hkv, max_pages)).astype(np.float32)
+    S[rng.random(S.shape) < 0.3] = 0.25                          # ties across pages and heads
+    S[rng.random(S.shape) < 0.05] = np.nan
+    S[1, :, :5] = np.nan                                        # pages with no finite score
+    moves = torch.full((B, max_pages, 2), -7, dtype=torch.int32, device="cuda")
+    count = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    kv.tier_plan(L, torch.from_numpy(S).cuda(), torch.from_numpy(seq_lens).cuda(), torch.from_numpy(bt).cuda(),
+                 torch.from_numpy(entry.view(np.int32)).cuda(), caps, moves, count, ff, fl)
+    torch.cuda.synchronize()
+    want = _expected_moves(S, seq_lens, bt, entry, P, caps, ff, fl)
+    got_c, got_m = count.cpu().numpy(), moves.cpu().numpy()
+    for b in range(B):
+        assert got_c[b] == len(want[b]), (b, got_c[b], len(want[b]))
+        assert [tuple(x) for x in got_m[b, :got_c[b]].tolist()] == want[b], b
+
+
+def _chain_pages(x16_rows, tiers_before, tiers_after, seq_len, P, bt_row):
+    """Row values as attention sees them: each page encoded in its tier before
+    the call and, if it moved, re-encoded from those decoded values."""
+    x = np.array(x16_rows[:seq_len], dtype=np.float32)
+    out = x.astype(np.float64)
+    d = x.shape[1]
+    for p in range(-(-seq_len // P)):
+        lo, hi = p * P, min((p + 1) * P, seq_len)
+        t0, t1 = int(tiers_before[bt_row[p]]), int(tiers_after[bt_row[p]])
+        v = x[lo:hi]
+        if t0 != 0:
+            c, sz = oracle.encode_vector(v, t0)
+            v = oracle.decode_vector(c, sz, t0, d)
+        if t1 != t0:
+            c, sz = oracle.retier_vectors(v, t0, t1, d)
+            v = oracle.decode_vector(c, sz, t1, d)
+        out[lo:hi] = v
+    return out
+
+
+def test_demote_codes_and_attention(hz, kv):
+    w = W["tiers_fp8_64k"].replace(B=2, ctx=16 * 300 + 7)
+    announce("tier demotion on a tiered layer with a slot per physical page")
+    layer = hz.DeviceLayer(w, summaries="build", tier_slots="phys")
+    q = hz.queries_device(w)
+    bufs = hz.StepBuffers(w, with_S=True)
+    hz.score(layer, q, bufs)
+    hz.topk(layer, bufs)
+    caps = (10, 10, 20, 20, 30)
+    moves = torch.empty((w.B, w.Np, 2), dtype=torch.int32, device="cuda")
+    count = torch.empty((w.B,), dtype=torch.int32, device="cuda")
+    kv.tier_plan(layer.L, bufs.page_S, layer.seq_lens, layer.bt, layer.page_entry, caps, moves, count, 1, 1)
+    torch.cuda.synchronize()
+    before = layer.page_entry.cpu().numpy().view(np.uint32).copy()
+    S = bufs.page_S.cpu().numpy()
+    want = _expected_moves(S, layer.seq_lens_np, layer.bt_np, before, w.P, caps, 1, 1)
+    cnt, mv = count.cpu().numpy(), moves.cpu().numpy()
+    for b in range(w.B):
+        assert [tuple(x) for x in mv[b, :cnt[b]].tolist()] == want[b]
+    assert cnt.sum() > 0
+    kv.tier_demote(layer.L, layer.pages, layer.page_entry, layer.bt, moves, count)
+    torch.cuda.synchronize()
+    after = layer.page_entry.cpu().numpy().view(np.uint32)
+    t_before, t_after = before >> 29, after >> 29
+    moved = {p: t for b in range(w.B) for p, t in want[b]}
+    for p in range(w.n_phys):
+        if p in moved:
+            assert after[p] == (np.uint32(moved[p]) << np.uint32(29)) | np.uint32(p)
+        else:
+            assert after[p] == before[p]
+    # re-encoded codes and scales, K and V, against the oracle's chain
+    k_all = layer.k16.view(torch.int16).cpu().numpy().view(np.uint16)
+    v_all = layer.v16.view(torch.int16).cpu().numpy().view(np.uint16)
+    pools = {t: [(layer.kq[t - 1].cpu().numpy(), layer.ksz[t - 1].float().cpu().numpy()),
+                 (layer.vq[t - 1].cpu().numpy(), layer.vsz[t - 1].float().cpu().numpy())] for t in range(1, 6)}
+    checked = 0
+    for p, nt in list(moved.items())[:200]:
+        ot = int(t_before[p])
+        for kvi, src in ((0, k_all), (1, v_all)):
+            x = wl.bits_to_f32(src[p], w.dtype)                # (Hkv, P, d)
+            if ot != 0:
+                c, sz = oracle.encode_vector(x, ot)
+                x = oracle.decode_vector(c, sz, ot, w.d)
+            c2, sz2 = oracle.retier_vectors(x, ot, nt, w.d)
+            codes, szp = pools[nt][kvi]
+            np.testing.assert_array_equal(codes[p], c2)
+            np.testing.assert_array_equal(szp[p], sz2)
+            checked += 1
+    assert checked > 0
+    # attention through the demoted pages
+    sel_np, cnt_np = wl.synthetic_selection(w, w.k_of(w.Np))
+    hz.attend(layer, q, bufs, sel=torch.from_numpy(sel_np).cuda(), sel_count=torch.from_numpy(cnt_np).cuda())
+    torch.cuda.synchronize()
+    out, lse = bufs.out.cpu().numpy(), bufs.lse.cpu().numpy()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            K = _chain_pages(wl.row_keys(w, 0, b, g), t_before, t_after, w.ctx, w.P, layer.bt_np[b])
+            V = _chain_pages(wl.row_values(w, 0, b, g), t_before, t_after, w.ctx, w.P, layer.bt_np[b])
+            qr = wl.queries(w, 0, b, g).astype(np.float64)
+            o_ref, l_ref = oracle.sparse_attention(qr, K, V, w.ctx, w.P, sel_np[b, g], w.tau)
+            hs = slice(g * w.G, (g + 1) * w.G)
+            assert_attn_close(out[b, hs], lse[b, hs], o_ref, l_ref)
+
+
+def test_repeated_calls_reach_the_budgets(hz, kv):
+    w = W["tiers_64k"].replace(B=2, ctx=16 * 200, tier_fracs=(1.0,), tier_order=(0,))
+    announce("tier demotion: repeated calls from an all-native pool")
+    layer = hz.DeviceLayer(w, summaries="build", tier_slots="phys")
+    q = hz.queries_device(w)
+    bufs = hz.StepBuffers(w, with_S=True)
+    hz.score(layer, q, bufs)
+    hz.topk(layer, bufs)
+    caps = (7, 11, 13, 17, 19)
+    moves = torch.empty((w.B, w.Np, 2), dtype=torch.int32, device="cuda")
+    count = torch.empty((w.B,), dtype=torch.int32, device="cuda")
+    n_moves = []
+    for _ in range(6):
+        kv.tier_plan(layer.L, bufs.page_S, layer.seq_lens, layer.bt, layer.page_entry, caps, moves, count)
+        kv.tier_demote(layer.L, layer.pages, layer.page_entry, layer.bt, moves, count)
+        n_moves.append(int(count.sum().item()))
+    torch.cuda.synchronize()
+    assert n_moves[-1] == 0 and n_moves[0] == w.B * (w.Np - caps[0])
+    tiers = layer.page_entry.cpu().numpy().view(np.uint32) >> 29
+    for b in range(w.B):
+        lv = np.array([oracle.LEVEL_OF_TIER[int(t)] for t in tiers[layer.bt_np[b]]])
+        for lvl in range(5):
+            assert np.sum(lv == lvl) == caps[lvl]
+        assert np.sum(lv == 5) == w.Np - sum(caps)
