@@ -340,6 +340,48 @@ def main():
             torch.cuda.empty_cache()
         result["uniform_tier_attention"] = uni
         log(f"[bench] attention with every page in one tier: {uni}")
+        # tier demotion along the cascade on layer 0's scores: budgets at half
+        # of the workload's mix, so many pages step down in one call
+        clayer = hz.DeviceLayer(w, layer=0, summaries=None, tier_slots="phys")
+        hz.score(layers[0], qs[0][0], bufs[0])
+        cb = hz.StepBuffers(w, with_S=True)
+        cb.head_scores.copy_(bufs[0].head_scores)
+        cb.lse_partial.copy_(bufs[0].lse_partial)
+        hz.topk(layers[0], cb)
+        level_frac = {t: f for f, t in zip(w.tier_fracs, w.tier_order)}
+        caps = [int(0.5 * level_frac.get(t, 0.0) * w.Np) for t in (0, 5, 1, 2, 3)]
+        moves = torch.empty((w.B, w.Np, 2), dtype=torch.int32, device="cuda")
+        mcount = torch.empty((w.B,), dtype=torch.int32, device="cuda")
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        # an untimed plan first (it writes only the move list): first-launch costs
+        kv.tier_plan(clayer.L, cb.page_S, clayer.seq_lens, clayer.bt, clayer.page_entry, caps, moves, mcount, 1, 1)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        kv.tier_plan(clayer.L, cb.page_S, clayer.seq_lens, clayer.bt, clayer.page_entry, caps, moves, mcount, 1, 1)
+        e1.record(stream)
+        entry0 = clayer.page_entry.clone()
+        torch.cuda.synchronize()
+        e1b = torch.cuda.Event(enable_timing=True)
+        e1b.record(stream)
+        kv.tier_demote(clayer.L, clayer.pages, clayer.page_entry, clayer.bt, moves, mcount)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        mv = moves.cpu().numpy()
+        cnt = mcount.cpu().numpy()
+        old_t = (entry0.cpu().numpy().view(np.uint32) >> 29)
+        moved_b = 0
+        for b in range(w.B):
+            for phys, nt in mv[b, :cnt[b]]:
+                moved_b += page_bytes(w, int(old_t[phys])) * w.Hkv + page_bytes(w, int(nt)) * w.Hkv
+        plan_us, demote_us = e0.elapsed_time(e1) * 1e3, e1b.elapsed_time(e2) * 1e3
+        result["tier_demotion"] = {
+            "caps": caps, "pages_moved": int(cnt.sum()), "plan_us": plan_us, "demote_us": demote_us,
+            "demote_bytes": moved_b, "demote_GBps": moved_b / (demote_us * 1e3) if demote_us > 0 else None,
+            "note": "one plan (after an untimed one) and one demotion call, eager, on layer 0's scores; "
+                    "bytes = K+V read in the old tier plus written in the new one"}
+        log(f"[bench] tier demotion: {result['tier_demotion']}")
+        clayer.release()
+        del clayer
     if not args.no_basis and tiers is None:
         # the same layers scored from shared-basis summaries (row basis built
         # from each layer's keys, then per-page means and variances), same
