@@ -11,7 +11,7 @@ namespace kvs {
 
 // Pages of 16 logical pages per MFMA tile; a score block covers this many pages.
 constexpr int kScorePagesPerBlock = 64;
-constexpr int kTopkThreads = 512;        // selector block; rows longer than kTopkWideFrom pages get twice this
+constexpr int kTopkThreads = 512;        // selector block; rows of kTopkWideFrom pages or more get twice this
 constexpr int kTopkWideFrom = 4096;
 constexpr int kMaxTopkPages = 15360;   // keys in LDS stay under 64 KB
 constexpr int kMaxSplits = 256;

@@ -68,7 +68,7 @@ hipError_t launch_page_topk(const kv_layout& L, const float* head_scores, const 
                      head_scores, lse_partial, seq_lens, L.num_kv_heads, G, L.page_size, max_pages,     \
                      score_tiles(max_pages), keep, k_fixed, coverage, n_force_first, n_force_last, sel, \
                      sel_count, k_max, page_S)
-  const bool wide = max_pages > kTopkWideFrom;
+  const bool wide = max_pages >= kTopkWideFrom;
   if (G <= 4) { if (wide) KVS_TOPK(4, 2 * kTopkThreads); else KVS_TOPK(4, kTopkThreads); }
   else if (G <= 8) { if (wide) KVS_TOPK(8, 2 * kTopkThreads); else KVS_TOPK(8, kTopkThreads); }
   else { if (wide) KVS_TOPK(16, 2 * kTopkThreads); else KVS_TOPK(16, kTopkThreads); }

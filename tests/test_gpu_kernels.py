@@ -154,7 +154,7 @@ def _expected_selection(S, Np, k):
 def test_selection_branches_exact(G, max_pages):
     """Selection on crafted head scores, checked bit-exactly against an
     exhaustive sort of the kernel's own float32 S (the order is unique given S).
-    Rows over 4096 pages take the selector's wide-block variant."""
+    Rows of 4096 pages or more take the selector's wide-block variant."""
     from quantized_kv_cache_summary_amd import kvsparse as kv
     announce(f"crafted selection G={G} max_pages={max_pages}")
     rng = np.random.default_rng(17 + G)
