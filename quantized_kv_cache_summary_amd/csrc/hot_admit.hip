@@ -50,40 +50,60 @@ __global__ __launch_bounds__(kAdmitThreads) void hot_admit_plan_kernel(
   if (tid < 256) sh.hist[0][tid] = 0;
   __syncthreads();
 
-  // 1. U: every valid selection entry, through the block table
+  // 1. U: every valid selection entry, through the block table; a thread
+  //    takes kBatch entries at a time so their loads are in flight together
+  constexpr int kBatch = 16;
   const size_t n_entries = (size_t)B * Hkv * k_max;
-  for (size_t e = tid; e < n_entries; e += NT) {
-    const int row = (int)(e / k_max), i = (int)(e - (size_t)row * k_max);
-    int cnt = sel_count[row];
-    cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
-    if (i >= cnt) continue;
-    const int b = row / Hkv;
-    const int L = seq_lens[b];
-    int Np = L > 0 ? (L + P - 1) / P : 0;
-    Np = Np < max_pages ? Np : max_pages;
-    const int p = sel[e];
-    if (p < 0 || p >= Np) continue;
-    const int phys = block_table[(size_t)b * max_pages + p];
-    if (phys < 0 || phys >= n_phys) continue;
-    atomicOr(&bits[phys >> 5], 1u << (phys & 31));
+  for (size_t e0 = tid; e0 < n_entries; e0 += (size_t)NT * kBatch) {
+    int p[kBatch], b[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const size_t e = e0 + (size_t)j * NT;
+      p[j] = -1;
+      b[j] = 0;
+      if (e < n_entries) {
+        const int row = (int)(e / k_max), i = (int)(e - (size_t)row * k_max);
+        int cnt = sel_count[row];
+        cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
+        b[j] = row / Hkv;
+        if (i < cnt) p[j] = sel[e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int L = seq_lens[b[j]];
+      int Np = L > 0 ? (L + P - 1) / P : 0;
+      Np = Np < max_pages ? Np : max_pages;
+      p[j] = p[j] >= 0 && p[j] < Np ? block_table[(size_t)b[j] * max_pages + p[j]] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (p[j] >= 0 && p[j] < n_phys) atomicOr(&bits[p[j] >> 5], 1u << (p[j] & 31));
   }
   __syncthreads();
 
-  // 2. hits get the step's stamp; misses are counted per word, then listed
-  //    ascending (each thread owns a contiguous run of words)
+  // 2. hits get the step's stamp; each word of the bitmap is replaced by its
+  //    misses (the hot-map loads of a word are in flight together), then the
+  //    misses are listed ascending (each thread owns a contiguous run of words)
   const int chunk = (n_words + NT - 1) / NT;
   const int w0 = tid * chunk, w1 = w0 + chunk < n_words ? w0 + chunk : n_words;
   int my_miss = 0;
   for (int w = w0; w < w1; ++w) {
-    uint32_t m = bits[w];
-    while (m) {
-      const int bit = __ffs((int)m) - 1;
-      m &= m - 1u;
-      const int p = (w << 5) + bit;
-      const int s = hot[p];
-      if (s >= 0 && s < n_slots) slot_stamp[s] = step;
-      else ++my_miss;
+    const uint32_t m = bits[w];
+    if (m == 0u) continue;
+    int hs[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) hs[j] = (m >> j) & 1u ? hot[(w << 5) + j] : 0;
+    uint32_t miss = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (!((m >> j) & 1u)) continue;
+      const int sl = hs[j];
+      if (sl >= 0 && sl < n_slots) slot_stamp[sl] = step;
+      else miss |= 1u << j;
     }
+    bits[w] = miss;
+    my_miss += __popc(miss);
   }
   // exclusive scan of the miss counts over the block
   const int incl = wave_incl_sum(my_miss);
@@ -102,9 +122,7 @@ __global__ __launch_bounds__(kAdmitThreads) void hot_admit_plan_kernel(
     while (m && pos < n_slots) {
       const int bit = __ffs((int)m) - 1;
       m &= m - 1u;
-      const int p = (w << 5) + bit;
-      const int s = hot[p];
-      if (!(s >= 0 && s < n_slots)) miss[pos++] = p;
+      miss[pos++] = (w << 5) + bit;
     }
   }
   __syncthreads();   // hit stamps and the miss list are visible to the block
