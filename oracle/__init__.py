@@ -42,6 +42,7 @@ from .codec import (
     pack_codes, unpack_codes,
 )
 from .hotbuffer import HotBuffer, selected_physical_pages
+from .lowrank import row_mean, store_mean, key_coords, row_lowrank, page_score_lowrank
 from .cascade import (TIER_OF_LEVEL, LEVEL_OF_TIER, page_importance, rank_pages, desired_levels, plan_row,
                       retier_vectors)
 from .pipeline import decode_row
@@ -60,6 +61,7 @@ __all__ = [
     "round_e4m3", "encode_vector", "decode_vector",
     "pack_codes", "unpack_codes",
     "HotBuffer", "selected_physical_pages",
+    "row_mean", "store_mean", "key_coords", "row_lowrank", "page_score_lowrank",
     "TIER_OF_LEVEL", "LEVEL_OF_TIER", "page_importance", "rank_pages", "desired_levels", "plan_row",
     "retier_vectors",
     "decode_row",
