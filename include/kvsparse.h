@@ -191,9 +191,10 @@ size_t kv_page_score_partial_size(const kv_layout* layout, int32_t B, int32_t ma
  * basis: float32 [B][Hkv][R][d].  Eigenvectors inside a degenerate eigenspace
  * are arbitrary.  A row with no tokens gets the first R unit vectors.
  * ws/ws_bytes: kv_basis_build_workspace_size() (no state kept between calls).
- * --------------------------------------------------------------------------- */
+ * --------------------------------------------------------------------------- * mean (optional, may be NULL): float32 [B][Hkv][d] receives the row mean of
+ * the same keys (the r8 low-rank score's centre). */
 int kv_basis_build(const kv_layout* layout, const void* k16, const int32_t* block_table,
-                   const int32_t* seq_lens, int32_t B, int32_t max_pages, float* basis,
+                   const int32_t* seq_lens, int32_t B, int32_t max_pages, float* basis, float* mean,
                    void* ws, size_t ws_bytes, void* stream);
 
 size_t kv_basis_build_workspace_size(const kv_layout* layout, int32_t B, int32_t max_pages);
@@ -220,6 +221,32 @@ int kv_summary_build_basis(const kv_layout* layout, const void* k16, const int32
 int kv_page_score_basis(const kv_layout* layout, const void* q, const void* mu, const float* lam,
                         const float* basis, const float* log_n, const int32_t* seq_lens, int32_t B,
                         int32_t max_pages, float* head_scores, float* lse_partial, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * r8 low-rank score (AMASS page, "Quickstart": the r8 low-rank fallback score;
+ * "Headline results": r8 keeps per-key low-rank state).  layout->rank is the
+ * basis rank r (the pages' r8: 8).  Per (sequence, KV head) row: the basis
+ * u_1..u_r and mean m from kv_basis_build (with this rank); per key the
+ * coordinates c_tj = bfloat16(u_j . (k_t - m)) (round to nearest even).
+ *
+ * kv_lowrank_coords -- coordinates of appended pages: for every entry i,
+ * (b, p) = (entries[2i], entries[2i+1]), and KV head g, the first n_valid[i]
+ * tokens of the page (through block_table, as kv_summary_build); later
+ * tokens of the page get 0.  basis float32 [B][Hkv][r][d], mean float32
+ * [B][Hkv][d]; coords bfloat16 [B][Hkv][max_pages][P][r] in LOGICAL page
+ * order.  Entries must be distinct within a call. */
+int kv_lowrank_coords(const kv_layout* layout, const void* k16, const int32_t* block_table, int32_t max_pages,
+                      const int32_t* entries, const int32_t* n_valid, int32_t n, const float* basis,
+                      const float* mean, void* coords, void* stream);
+
+/* kv_page_score_lowrank -- for every page and query head h of the row's group
+ *   s[b][g][h][p] = tau q_h.m + log sum_{t < n_p} exp(tau sum_j (q_h.u_j) c_tj)
+ * over the page's n_p valid tokens (-inf for n_p = 0); outputs exactly as
+ * kv_page_score, so kv_page_topk follows unchanged.  coords (layout above)
+ * and q must be 16-byte aligned. */
+int kv_page_score_lowrank(const kv_layout* layout, const void* q, const void* coords, const float* mean,
+                          const float* basis, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                          float* head_scores, float* lse_partial, void* stream);
 
 /* ---------------------------------------------------------------------------
  * kv_page_topk -- per row, select k pages (AMASS page, "Quickstart": budget,

@@ -29,6 +29,7 @@ SOURCES = {
     "score_basis.hip": [],
     "hot_admit.hip": [],
     "tier_plan.hip": [],
+    "score_lowrank.hip": [],
     "codec.hip": ["-ffp-contract=off"],
 }
 

@@ -127,7 +127,8 @@ __global__ __launch_bounds__((D / 8) * (D / 8)) void basis_cov_kernel(
 template <int D>
 __global__ __launch_bounds__((D / 8) * (D / 8)) void basis_eigen_kernel(const float* __restrict__ part,
                                                                           int n_chunks, int R,
-                                                                          float* __restrict__ basis) {
+                                                                          float* __restrict__ basis,
+                                                                          float* __restrict__ mean_out) {
   constexpr int NB = D / 8;
   constexpr int NT = NB * NB;
   constexpr int HALF = D / 2;
@@ -172,6 +173,8 @@ __global__ __launch_bounds__((D / 8) * (D / 8)) void basis_eigen_kernel(const fl
     n = tot;
     __syncthreads();
   }
+  if (mean_out)
+    for (int e = tid; e < D; e += NT) mean_out[(size_t)row * D + e] = mean[e];
   const float inv_n = n > 0.f ? 1.f / n : 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -337,8 +340,8 @@ __global__ __launch_bounds__(64) void summary_basis_kernel(
 }
 
 hipError_t launch_basis_build(const kv_layout& L, const void* k16, const int32_t* block_table,
-                              const int32_t* seq_lens, int B, int max_pages, float* basis, float* part,
-                              hipStream_t st) {
+                              const int32_t* seq_lens, int B, int max_pages, float* basis, float* mean,
+                              float* part, hipStream_t st) {
   const int rows = B * L.num_kv_heads;
   const int n_chunks = basis_chunks(max_pages);
   const dim3 gc(n_chunks, rows);
@@ -353,9 +356,9 @@ hipError_t launch_basis_build(const kv_layout& L, const void* k16, const int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (L.head_dim == 64)
-    hipLaunchKernelGGL((basis_eigen_kernel<64>), dim3(rows), dim3(64), 0, st, part, n_chunks, L.rank, basis);
+    hipLaunchKernelGGL((basis_eigen_kernel<64>), dim3(rows), dim3(64), 0, st, part, n_chunks, L.rank, basis, mean);
   else
-    hipLaunchKernelGGL((basis_eigen_kernel<128>), dim3(rows), dim3(256), 0, st, part, n_chunks, L.rank, basis);
+    hipLaunchKernelGGL((basis_eigen_kernel<128>), dim3(rows), dim3(256), 0, st, part, n_chunks, L.rank, basis, mean);
   return hipGetLastError();
 }
 

@@ -139,7 +139,8 @@ size_t kv_basis_build_workspace_size(const kv_layout* L, int32_t B, int32_t max_
 }
 
 int kv_basis_build(const kv_layout* L, const void* k16, const int32_t* block_table, const int32_t* seq_lens,
-                   int32_t B, int32_t max_pages, float* basis, void* ws, size_t ws_bytes, void* stream) {
+                   int32_t B, int32_t max_pages, float* basis, float* mean, void* ws, size_t ws_bytes,
+                   void* stream) {
   int rc = check_layout(L);
   if (rc) return rc;
   if (B < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
@@ -149,7 +150,7 @@ int kv_basis_build(const kv_layout* L, const void* k16, const int32_t* block_tab
   if ((int64_t)B * L->num_kv_heads > 65535) return KV_ERR_UNSUPPORTED;
   if ((int64_t)max_pages * L->page_size > 0x3FFFFFFF) return KV_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < kv_basis_build_workspace_size(L, B, max_pages)) return KV_ERR_WORKSPACE;
-  return from_hip(kvs::launch_basis_build(*L, k16, block_table, seq_lens, B, max_pages, basis, (float*)ws,
+  return from_hip(kvs::launch_basis_build(*L, k16, block_table, seq_lens, B, max_pages, basis, mean, (float*)ws,
                                           (hipStream_t)stream));
 }
 
@@ -183,6 +184,35 @@ int kv_page_score_basis(const kv_layout* L, const void* q, const void* mu, const
   if ((int64_t)B * L->num_kv_heads > 65535) return KV_ERR_UNSUPPORTED;
   return from_hip(kvs::launch_page_score_basis(*L, q, mu, lam, basis, log_n, seq_lens, B, max_pages,
                                                scale_of(L), head_scores, lse_partial, (hipStream_t)stream));
+}
+
+int kv_lowrank_coords(const kv_layout* L, const void* k16, const int32_t* block_table, int32_t max_pages,
+                      const int32_t* entries, const int32_t* n_valid, int32_t n, const float* basis,
+                      const float* mean, void* coords, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (n < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
+  if (n == 0) return KV_OK;
+  if (max_pages == 0 || !k16 || !block_table || !entries || !n_valid || !basis || !mean || !coords)
+    return KV_ERR_INVALID_ARG;
+  if (!aligned16(k16)) return KV_ERR_INVALID_ARG;
+  if (n > 0x7FFFFFFF / 2) return KV_ERR_UNSUPPORTED;
+  return from_hip(kvs::launch_lowrank_coords(*L, k16, block_table, max_pages, entries, n_valid, n, basis, mean,
+                                             coords, (hipStream_t)stream));
+}
+
+int kv_page_score_lowrank(const kv_layout* L, const void* q, const void* coords, const float* mean,
+                          const float* basis, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                          float* head_scores, float* lse_partial, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0) return KV_ERR_INVALID_ARG;
+  if (B == 0 || max_pages == 0) return KV_OK;
+  if (!q || !coords || !mean || !basis || !seq_lens || !head_scores || !lse_partial) return KV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(coords)) return KV_ERR_INVALID_ARG;
+  if ((int64_t)B * L->num_kv_heads > 65535) return KV_ERR_UNSUPPORTED;
+  return from_hip(kvs::launch_page_score_lowrank(*L, q, coords, mean, basis, seq_lens, B, max_pages, scale_of(L),
+                                                 head_scores, lse_partial, (hipStream_t)stream));
 }
 
 size_t kv_page_topk_workspace_size(const kv_layout* L, int32_t B, int32_t max_pages) {

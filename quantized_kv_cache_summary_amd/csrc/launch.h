@@ -37,8 +37,16 @@ inline size_t basis_workspace_bytes(int rows, int max_pages, int d) {
 }
 
 hipError_t launch_basis_build(const kv_layout& L, const void* k16, const int32_t* block_table,
-                              const int32_t* seq_lens, int B, int max_pages, float* basis, float* part,
-                              hipStream_t st);
+                              const int32_t* seq_lens, int B, int max_pages, float* basis, float* mean,
+                              float* part, hipStream_t st);
+
+hipError_t launch_lowrank_coords(const kv_layout& L, const void* k16, const int32_t* block_table, int max_pages,
+                                 const int32_t* entries, const int32_t* n_valid, int n, const float* basis,
+                                 const float* mean, void* coords, hipStream_t st);
+
+hipError_t launch_page_score_lowrank(const kv_layout& L, const void* q, const void* coords, const float* mean,
+                                     const float* basis, const int32_t* seq_lens, int B, int max_pages,
+                                     float tau, float* head_scores, float* lse_partial, hipStream_t st);
 
 hipError_t launch_summary_build_basis(const kv_layout& L, const void* k16, const int32_t* block_table,
                                       int max_pages, const int32_t* entries, const int32_t* n_valid, int n,

@@ -97,6 +97,7 @@ class DeviceLayer:
         # directions ("build", "synthetic") or a shared row basis with per-page
         # means and variances ("basis_build", "basis_synthetic")
         self.summary = self.basis = self.mu = self.lam = None
+        self.coords = self.lr_basis = self.lr_mean = None
         self.log_n = torch.empty((w.B, w.Np), dtype=torch.float32, device=device)
         if summaries in ("build", "synthetic"):
             self.summary = torch.empty((w.B, w.Hkv, w.Np, (1 + w.rank) * w.d), dtype=torch.bfloat16,
@@ -111,7 +112,16 @@ class DeviceLayer:
             rec, n_valid = wl.synthetic_summary(w, layer)
             self.summary.copy_(to_device16(rec.reshape(w.B, w.Hkv, w.Np, -1), "bf16", device))
             self.log_n.copy_(torch.from_numpy(np.log(n_valid.astype(np.float64)).astype(np.float32)))
-        elif summaries == "basis_build":
+        elif summaries in ("lowrank_build", "lowrank_synthetic"):
+            self._alloc_lowrank()
+            if summaries == "lowrank_build":
+                self.build_lowrank()
+            else:
+                U, m, cbits = wl.synthetic_lowrank(w, layer, seq_lens_=self.seq_lens_np)
+                self.lr_basis.copy_(torch.from_numpy(U))
+                self.lr_mean.copy_(torch.from_numpy(m))
+                self.coords.copy_(to_device16(cbits, "bf16", device))
+        if summaries == "basis_build":
             self.build_basis()
             self.build_basis_summaries()
         elif summaries == "basis_synthetic":
@@ -155,6 +165,37 @@ class DeviceLayer:
         v.host_v = v.host_k = None
         v.build_basis(stream)
         v.build_basis_summaries(stream)
+        return v
+
+    # r8 low-rank state: row basis (rank 8) and mean, per-key coordinates
+    def _alloc_lowrank(self, rank=8):
+        w = self.w
+        self.L_lr = layout_of(w.replace(rank=rank))
+        self.lr_basis = torch.empty((w.B, w.Hkv, rank, w.d), dtype=torch.float32, device=self.device)
+        self.lr_mean = torch.empty((w.B, w.Hkv, w.d), dtype=torch.float32, device=self.device)
+        self.coords = torch.zeros((w.B, w.Hkv, w.Np, w.P, rank), dtype=torch.bfloat16, device=self.device)
+
+    def build_lowrank(self, stream=None):
+        w = self.w
+        nb = kv.basis_build_workspace_size(self.L_lr, w.B, w.Np)
+        ws = torch.empty(max(1, nb // 4), dtype=torch.float32, device=self.device)
+        kv.basis_build(self.L_lr, self.k_src, self.bt, self.seq_lens, self.lr_basis, ws, stream, mean=self.lr_mean)
+        entries, nv = self._all_entries()
+        kv.lowrank_coords(self.L_lr, self.k_src, self.bt, entries, nv, self.lr_basis, self.lr_mean, self.coords,
+                          stream)
+        if stream is None:
+            torch.cuda.current_stream().synchronize()
+        del ws
+
+    def with_lowrank_summaries(self, stream=None):
+        """The same layer scored with the r8 low-rank score built from its keys;
+        release() the original only."""
+        import copy
+        v = copy.copy(self)
+        v.summary = v.basis = v.mu = v.lam = None
+        v.host_v = v.host_k = None
+        v._alloc_lowrank()
+        v.build_lowrank(stream)
         return v
 
     def _all_entries(self):
@@ -284,7 +325,10 @@ def queries_device(w: wl.Workload, layer=0, qidx=0, device="cuda"):
 
 
 def score(layer: DeviceLayer, q, bufs: StepBuffers, stream=None):
-    if layer.basis is not None:
+    if layer.coords is not None:
+        kv.page_score_lowrank(layer.L_lr, q, layer.coords, layer.lr_mean, layer.lr_basis, layer.seq_lens,
+                              bufs.head_scores, bufs.lse_partial, stream)
+    elif layer.basis is not None:
         kv.page_score_basis(layer.L, q, layer.mu, layer.lam, layer.basis, layer.log_n, layer.seq_lens,
                             bufs.head_scores, bufs.lse_partial, stream)
     else:

@@ -28,6 +28,7 @@ SYMBOLS = (
     "kv_sparse_decode_attn_num_splits", "kv_dequant_tier", "kv_pack_tier", "kv_status_string",
     "kv_basis_build", "kv_basis_build_workspace_size", "kv_summary_build_basis", "kv_page_score_basis",
     "kv_page_topk_coverage", "kv_hot_admit", "kv_hot_admit_workspace_size", "kv_tier_plan", "kv_tier_demote",
+    "kv_lowrank_coords", "kv_page_score_lowrank",
 )
 
 
@@ -90,7 +91,9 @@ def lib():
             "kv_dequant_tier": (_I, [_LP, _PP, _P, _I, _P, _P]),
             "kv_pack_tier": (_I, [_LP, _P, _P, _I, _I, _P, _P, _P, _P]),
             "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-            "kv_basis_build": (_I, [_LP, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+            "kv_basis_build": (_I, [_LP, _P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
+            "kv_lowrank_coords": (_I, [_LP, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P]),
+            "kv_page_score_lowrank": (_I, [_LP, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
             "kv_basis_build_workspace_size": (_SZ, [_LP, _I, _I]),
             "kv_summary_build_basis": (_I, [_LP, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
             "kv_page_score_basis": (_I, [_LP, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
@@ -166,10 +169,10 @@ def basis_build_workspace_size(L, B, max_pages):
     return int(lib().kv_basis_build_workspace_size(ctypes.byref(L), int(B), int(max_pages)))
 
 
-def basis_build(L, k16, block_table, seq_lens, basis, ws, stream=None):
+def basis_build(L, k16, block_table, seq_lens, basis, ws, stream=None, mean=None):
     B, max_pages = block_table.shape
     rc = lib().kv_basis_build(ctypes.byref(L), _p(k16), _p(block_table), _p(seq_lens), int(B), int(max_pages),
-                              _p(basis), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+                              _p(basis), _p(mean), _p(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "kv_basis_build")
 
 
@@ -243,6 +246,20 @@ def hot_admit(L, v16_ptr, v_hot, v_hot_slot, slot_page, slot_stamp, block_table,
                             int(sel.shape[-1]), int(step), _p(ws), ws.numel() * ws.element_size(),
                             _stream(stream))
     _check(rc, "kv_hot_admit")
+
+
+def lowrank_coords(L, k16, block_table, entries, n_valid, basis, mean, coords, stream=None):
+    max_pages = block_table.shape[1]
+    rc = lib().kv_lowrank_coords(ctypes.byref(L), _p(k16), _p(block_table), int(max_pages), _p(entries),
+                                 _p(n_valid), int(n_valid.numel()), _p(basis), _p(mean), _p(coords), _stream(stream))
+    _check(rc, "kv_lowrank_coords")
+
+
+def page_score_lowrank(L, q, coords, mean, basis, seq_lens, head_scores, lse_partial, stream=None):
+    B, max_pages = head_scores.shape[0], head_scores.shape[-1]
+    rc = lib().kv_page_score_lowrank(ctypes.byref(L), _p(q), _p(coords), _p(mean), _p(basis), _p(seq_lens),
+                                     int(B), int(max_pages), _p(head_scores), _p(lse_partial), _stream(stream))
+    _check(rc, "kv_page_score_lowrank")
 
 
 def tier_plan(L, page_S, seq_lens, block_table, page_entry, caps, moves, move_count, n_force_first=0,

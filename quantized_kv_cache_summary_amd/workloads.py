@@ -27,7 +27,7 @@ import numpy as np
 
 SEED = 2026
 
-T_Q, T_K, T_V, T_HOT, T_TABLE, T_TIER, T_SEL, T_SUMMARY, T_CENTERS, T_HOTBUF, T_BASIS = range(11)
+T_Q, T_K, T_V, T_HOT, T_TABLE, T_TIER, T_SEL, T_SUMMARY, T_CENTERS, T_HOTBUF, T_BASIS, T_LOWRANK = range(12)
 
 TIER_NAMES = ("native", "int8", "int4", "int2", "1bit", "fp8")
 
@@ -308,6 +308,33 @@ def synthetic_basis_summary(w: Workload, layer: int = 0, lam_scale=(3.0, 2.0, 1.
     lam = (rng.chisquare(w.P, (w.B, w.Hkv, w.Np, w.rank)).astype(np.float32) / np.float32(w.P)) * scale
     n_valid = np.full((w.B, w.Np), w.P, dtype=np.int32)
     return basis, bf16_bits(mu), lam.astype(np.float32), n_valid
+
+
+def synthetic_lowrank(w: Workload, layer: int = 0, rank: int = 8, seq_lens_=None):
+    """Random stored low-rank (r8) state, for score/select tests.
+
+    Returns (basis float32 [B, Hkv, rank, d] with orthonormal rows before
+    rounding, mean float32 [B, Hkv, d], coords uint16 bf16 bits
+    [B, Hkv, Np, P, rank]; tokens past a row's length hold 0).  Coordinates are
+    N(0, 1) scaled by 1.5 / sqrt(j + 1) along direction j; planted pages get
+    their first coordinate raised by 2, so they carry more mass."""
+    rng = rng_for(w, layer, 0, 0, T_LOWRANK)
+    lens = seq_lens(w) if seq_lens_ is None else np.asarray(seq_lens_)
+    basis = np.empty((w.B, w.Hkv, rank, w.d), dtype=np.float32)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            Q, _ = np.linalg.qr(rng.standard_normal((w.d, rank)))
+            basis[b, g] = Q.T.astype(np.float32)
+    mean = (0.3 * rng.standard_normal((w.B, w.Hkv, w.d))).astype(np.float32)
+    scale = (1.5 / np.sqrt(np.arange(1, rank + 1))).astype(np.float32)
+    c = rng.standard_normal((w.B, w.Hkv, w.Np, w.P, rank)).astype(np.float32) * scale
+    for b in range(w.B):
+        hp = hot_pages(w, layer, b)
+        if hp.size:
+            c[b][:, hp, :, 0] += np.float32(2.0)
+        tok = np.arange(w.Np * w.P).reshape(w.Np, w.P)
+        c[b][:, tok >= lens[b]] = 0.0
+    return basis, mean, bf16_bits(c)
 
 
 # ---------------------------------------------------------------- whole pools

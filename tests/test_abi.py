@@ -164,12 +164,12 @@ def test_shared_basis_validation():
     need = kv.basis_build_workspace_size(L, 2, 300)
     assert need == 16 * 2 * (1 + 128 + 128 * 128) * 4           # rows x 256-page chunks x statistics
     bb = lambda **o: lib.kv_basis_build(ctypes.byref(L), o.get("k", FAKE), FAKE, FAKE, 2, 300,
-                                        o.get("basis", FAKE), o.get("ws", FAKE), o.get("wsb", need), None)
+                                        o.get("basis", FAKE), None, o.get("ws", FAKE), o.get("wsb", need), None)
     assert bb(wsb=need - 1) == kv.KV_ERR_WORKSPACE
     assert bb(ws=None) == kv.KV_ERR_WORKSPACE
     assert bb(basis=None) == kv.KV_ERR_INVALID_ARG
     assert bb(k=FAKE + 2) == kv.KV_ERR_INVALID_ARG
-    assert lib.kv_basis_build(ctypes.byref(L), FAKE, FAKE, FAKE, 0, 300, FAKE, None, 0, None) == kv.KV_OK
+    assert lib.kv_basis_build(ctypes.byref(L), FAKE, FAKE, FAKE, 0, 300, FAKE, None, None, 0, None) == kv.KV_OK
     sb = lambda **o: lib.kv_summary_build_basis(ctypes.byref(L), FAKE, FAKE, 300, FAKE, FAKE, o.get("n", 4),
                                                 o.get("basis", FAKE), o.get("mu", FAKE), FAKE, FAKE, None)
     assert sb(basis=None) == kv.KV_ERR_INVALID_ARG
@@ -241,3 +241,22 @@ def test_tier_plan_and_demote_validation():
     assert demote(B=0) == kv.KV_OK
     pg.kq[2] = None
     assert demote() == kv.KV_ERR_INVALID_ARG                        # a tier pool missing
+
+
+def test_lowrank_validation():
+    L = _L(rank=8)
+    lib = kv.lib()
+    co = lambda **o: lib.kv_lowrank_coords(ctypes.byref(L), o.get("k", FAKE), FAKE, 300, FAKE, FAKE, o.get("n", 4),
+                                           o.get("basis", FAKE), o.get("mean", FAKE), o.get("coords", FAKE), None)
+    assert co(n=-1) == kv.KV_ERR_INVALID_ARG
+    assert co(n=0) == kv.KV_OK
+    assert co(mean=None) == kv.KV_ERR_INVALID_ARG
+    assert co(coords=None) == kv.KV_ERR_INVALID_ARG
+    assert co(k=FAKE + 2) == kv.KV_ERR_INVALID_ARG
+    sc = lambda **o: lib.kv_page_score_lowrank(ctypes.byref(L), o.get("q", FAKE), o.get("coords", FAKE),
+                                               FAKE, FAKE, FAKE, o.get("B", 2), 300, FAKE, FAKE, None)
+    assert sc(coords=FAKE + 8) == kv.KV_ERR_INVALID_ARG
+    assert sc(q=None) == kv.KV_ERR_INVALID_ARG
+    assert sc(B=0) == kv.KV_OK
+    assert lib.kv_page_score_lowrank(ctypes.byref(_L(rank=3)), FAKE, FAKE, FAKE, FAKE, FAKE, 2, 300, FAKE, FAKE,
+                                     None) == kv.KV_ERR_UNSUPPORTED
