@@ -423,6 +423,48 @@ def main():
             "note": "same layers, queries and attention; summaries = shared row basis + per-page mean "
                     "and variances (not the headline's per-page directions)",
         }
+    if not args.no_basis and tiers is None:
+        # the r8 low-rank score (per-key coordinates in a rank-8 row basis) on
+        # the same layers: the alternative selector, same selection and attention
+        t0 = time.time()
+        rlayers = [l.with_lowrank_summaries() for l in layers]
+        torch.cuda.synchronize()
+        log(f"[bench] r8 state built in {time.time() - t0:.1f}s")
+        rsteps = [hz.SplitStep(rlayers[i], bufs[i], 1) for i in range(n_layers)]
+        for i in range(args.warmup):
+            hz.decode_step(rlayers[i % n_layers], qs[i % n_layers][(i // n_layers) % args.queries], bufs[i % n_layers])
+        n_cap = n_layers * min(args.queries, 4)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(n_cap):
+                hz.decode_step(rlayers[i % n_layers], qs[i % n_layers][(i // n_layers) % args.queries],
+                               bufs[i % n_layers])
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        reps = max(1, K // n_cap)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            gr.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        r_ms = a.elapsed_time(b) / (reps * n_cap)
+        rscore_us, _ = graph_avg_us(lambda li, q: hz.score(rlayers[li], q, bufs[li]))
+        coord_b = w.rows * w.Np * w.P * 8 * 2 + w.rows * (8 + 1) * w.d * 4
+        rsel = bufs[0].sel_count.cpu().numpy()
+        _, rselb = algorithmic_bytes(w, rsel)
+        log(f"[bench] r8 step {r_ms * 1e3:.1f} us, score {rscore_us:.2f} us")
+        result["lowrank_r8"] = {
+            "value": 1e3 / r_ms, "unit": "steps/s", "ms_per_step": r_ms, "steps": reps * n_cap,
+            "algorithmic_bytes_per_step": {"coordinates": coord_b, "selected_kv": rselb},
+            "effective_GBps": (coord_b + rselb) / (r_ms / 1e3) / 1e9,
+            "score_kernel": {"avg_launch_us": rscore_us, "achieved_GBps": coord_b / (rscore_us * 1e3),
+                             "frac": coord_b / (rscore_us * 1e3) / HBM_PEAK_GBS},
+            "note": "same layers, queries, selection rule and attention; pages scored by the exact log-mass of "
+                    "their keys' rank-8 approximations (an alternative selector, not the headline's)",
+        }
+        del rsteps
     # dense line for context: the same attention kernel over every page of
     # every row (k = Np, no score and no selection)
     if tiers is None and not args.no_extras:

@@ -8,11 +8,13 @@
 //
 // Score kernel: a block covers 64 pages of one row (the quad score's tiles,
 // so the selector reads the same partials).  The block first forms
-// tau q_h.u_j and tau q_h.m for its heads from the row basis and mean staged
-// in LDS; then each wave takes 16 pages, four lanes per page, each lane P/4
-// consecutive tokens whose coordinates are contiguous (a wave reads 16 whole
-// pages, one contiguous span); the four lanes' (max, sum exp) are merged with
-// lane exchanges.
+// tau q_h.u_j and tau q_h.m for its heads from the query, row basis and mean
+// staged in LDS (one wave per product, lanes over the head dim).  Then each
+// wave takes 16 pages, four lanes per page, each lane P/4 consecutive tokens
+// whose coordinates are contiguous (a wave reads 16 whole pages, one
+// contiguous span); the four lanes share the page's maximum and sum their
+// exponentials through DPP quad permutes, and the per-head tile partials are
+// DPP wave reductions.
 
 #include "device.h"
 #include "launch.h"
@@ -21,6 +23,14 @@ namespace kvs {
 
 constexpr int kLrPages = kScorePagesPerBlock;   // pages per block
 constexpr int kLrWaves = kLrPages / 16;
+
+// lane exchanges within groups of four lanes (DPP quad permutes, no LDS)
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+}
 
 // coordinates of appended pages: one 64-thread block per (entry, KV head)
 template <int D, int R, bool F16>
@@ -103,25 +113,41 @@ __global__ __launch_bounds__(64 * kLrWaves) void page_score_lowrank_kernel(
     }
   }
 
-  for (int e = tid; e < (R + 1) * D; e += NT) {
-    const int j = e / D, x = e - j * D;
-    sv[j][x] = j < R ? basis[((size_t)row * R + j) * D + x] : mean[(size_t)row * D + x];
+  __shared__ float sq[GM][D];              // the group's query heads
+  const int Hq = Hkv * G;
+  // every staging load is requested before any is stored
+  constexpr int NSV = ((R + 1) * D + NT - 1) / NT, NSQ = (GM * D + NT - 1) / NT;
+  float tv[NSV];
+  uint16_t tq[NSQ];
+#pragma unroll
+  for (int i = 0; i < NSV; ++i) {
+    const int e = tid + i * NT, j = e / D, x = e - j * D;
+    tv[i] = e >= (R + 1) * D ? 0.f : (j < R ? basis[((size_t)row * R + j) * D + x] : mean[(size_t)row * D + x]);
+  }
+#pragma unroll
+  for (int i = 0; i < NSQ; ++i) {
+    const int e = tid + i * NT, h = e / D, x = e - h * D;
+    tq[i] = h < G ? q[((size_t)b * Hq + (size_t)g * G + h) * D + x] : (uint16_t)0;
+  }
+#pragma unroll
+  for (int i = 0; i < NSV; ++i) {
+    const int e = tid + i * NT;
+    if (e < (R + 1) * D) sv[e / D][e % D] = tv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NSQ; ++i) {
+    const int e = tid + i * NT;
+    if (e / D < G) sq[e / D][e % D] = h16_to_f32<F16>(tq[i]);
   }
   __syncthreads();
-  const int Hq = Hkv * G;
-  for (int o = tid; o < G * (R + 1); o += NT) {
+  // tau q_h.u_j and tau q_h.m: one wave per product, lanes over the head dim
+  for (int o = wave; o < G * (R + 1); o += kLrWaves) {
     const int h = o / (R + 1), j = o - h * (R + 1);
-    const uint16_t* qp = q + ((size_t)b * Hq + (size_t)g * G + h) * D;
-    float acc = 0.f;
-    for (int e = 0; e < D; e += 8) {
-      const u32x4_t w = ld16(qp + e);
+    float part = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc = __builtin_fmaf(lo16<F16>(w[k]), sv[j][e + 2 * k], acc);
-        acc = __builtin_fmaf(hi16<F16>(w[k]), sv[j][e + 2 * k + 1], acc);
-      }
-    }
-    qv[h][j] = tau * acc;
+    for (int e = lane; e < D; e += 64) part = __builtin_fmaf(sq[h][e], sv[j][e], part);
+    part = wave_sum_f32(part);
+    if (lane == 0) qv[h][j] = tau * part;
   }
   __syncthreads();
 
@@ -130,11 +156,10 @@ __global__ __launch_bounds__(64 * kLrWaves) void page_score_lowrank_kernel(
   Np = Np < max_pages ? Np : max_pages;
   int n = p < Np ? L - p * P : 0;
   n = n > P ? P : n;
-  float tm[GM], ts[GM];
+  float sc[GM];
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
-    tm[h] = -INFINITY;
-    ts[h] = 0.f;
+    sc[h] = -INFINITY;
     if (h >= G) continue;
     float z[8];
     float zm = -INFINITY;
@@ -152,32 +177,28 @@ __global__ __launch_bounds__(64 * kLrWaves) void page_score_lowrank_kernel(
         zm = fmaxf(zm, a);
       }
     }
+    // the page's four lanes share one maximum, then sum their exponentials
+    zm = fmaxf(zm, quad_xor1(zm));
+    zm = fmaxf(zm, quad_xor2(zm));
     float zs = 0.f;
     if (zm != -INFINITY) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
-        if (t < tpl) zs += z[t] == -INFINITY ? 0.f : __expf(z[t] - zm);
+        if (t < tpl && z[t] != -INFINITY) zs += __expf(z[t] - zm);
     }
-    // the page's four lanes, in a fixed order
-    float m2 = __shfl_xor(zm, 1), s2 = __shfl_xor(zs, 1);
-    lse_merge(zm, zs, m2, s2);
-    m2 = __shfl_xor(zm, 2);
-    s2 = __shfl_xor(zs, 2);
-    lse_merge(zm, zs, m2, s2);
-    const float s = zm == -INFINITY ? -INFINITY : qv[h][R] + zm + __logf(zs);
-    if (quarter == (h & 3) && p < max_pages) head_scores[((size_t)row * G + h) * max_pages + p] = s;
-    if (s != -INFINITY) { tm[h] = s; ts[h] = 1.f; }
+    zs += quad_xor1(zs);
+    zs += quad_xor2(zs);
+    sc[h] = zm == -INFINITY ? -INFINITY : qv[h][R] + zm + __logf(zs);
+    if (quarter == (h & 3) && p < max_pages) head_scores[((size_t)row * G + h) * max_pages + p] = sc[h];
   }
-  // per head (max, sum exp) over the block's pages: the wave's 16 pages, then
-  // the waves in order
+  // per head (max, sum exp) over the block's pages: the wave's 16 pages (one
+  // lane of each), then the waves in order
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
-#pragma unroll
-    for (int x = 4; x < 64; x <<= 1) {
-      const float m2 = __shfl_xor(tm[h], x), s2 = __shfl_xor(ts[h], x);
-      lse_merge(tm[h], ts[h], m2, s2);
-    }
-    if (lane == 0) { red_m[wave][h] = tm[h]; red_s[wave][h] = ts[h]; }
+    if (h >= G) continue;
+    const float M = wave_max_f32(sc[h]);
+    const float S = wave_sum_f32(quarter == 0 && sc[h] != -INFINITY ? __expf(sc[h] - M) : 0.f);
+    if (lane == 0) { red_m[wave][h] = M; red_s[wave][h] = S; }
   }
   __syncthreads();
   if (tid < G) {
