@@ -21,8 +21,10 @@
 
 namespace kvs {
 
-constexpr int kLrPages = kScorePagesPerBlock;   // pages per block
+constexpr int kLrTiles = 4;                                   // score tiles per block
+constexpr int kLrPages = kLrTiles * kScorePagesPerBlock;     // pages per block
 constexpr int kLrWaves = kLrPages / 16;
+constexpr int kLrTileWaves = kScorePagesPerBlock / 16;   // waves per score tile
 
 // lane exchanges within groups of four lanes (DPP quad permutes, no LDS)
 __device__ __forceinline__ float quad_xor1(float x) {
@@ -201,13 +203,19 @@ __global__ __launch_bounds__(64 * kLrWaves) void page_score_lowrank_kernel(
     if (lane == 0) { red_m[wave][h] = M; red_s[wave][h] = S; }
   }
   __syncthreads();
-  if (tid < G) {
-    float m = red_m[0][tid], s = red_s[0][tid];
+  // one partial per 64-page score tile: waves [tile * kLrTileWaves, +kLrTileWaves)
+  if (tid < kLrTiles * G) {
+    const int h = tid % G, part = tid / G;
+    const int tile = blockIdx.x * kLrTiles + part;
+    const int w0 = part * kLrTileWaves;
+    float m = red_m[w0][h], s = red_s[w0][h];
 #pragma unroll
-    for (int w = 1; w < kLrWaves; ++w) lse_merge(m, s, red_m[w][tid], red_s[w][tid]);
-    float* dst = lse_partial + (((size_t)row * n_tiles + blockIdx.x) * G + tid) * 2;
-    dst[0] = m;
-    dst[1] = s;
+    for (int w = 1; w < kLrTileWaves; ++w) lse_merge(m, s, red_m[w0 + w][h], red_s[w0 + w][h]);
+    if (tile < n_tiles) {
+      float* dst = lse_partial + (((size_t)row * n_tiles + tile) * G + h) * 2;
+      dst[0] = m;
+      dst[1] = s;
+    }
   }
 }
 
@@ -217,7 +225,7 @@ static hipError_t launch_lr_score(const kv_layout& L, const void* q, const void*
                                   float* hs, float* lp, hipStream_t st) {
   const int G = L.num_q_heads / L.num_kv_heads;
   const int n_tiles = score_tiles(max_pages);
-  const dim3 grid(n_tiles, B * L.num_kv_heads);
+  const dim3 grid((n_tiles + kLrTiles - 1) / kLrTiles, B * L.num_kv_heads);
 #define KVS_LR(GM_) hipLaunchKernelGGL((page_score_lowrank_kernel<D, R, GM_, F16>), grid, dim3(64 * kLrWaves), 0, st, \
                        (const uint16_t*)q, (const uint16_t*)coords, mean, basis, sl, L.num_kv_heads, G, L.page_size,   \
                        max_pages, n_tiles, tau, hs, lp)
