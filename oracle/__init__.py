@@ -38,7 +38,7 @@ from .attention import sparse_attention, dense_attention
 from .codec import (
     BITS_OF_TIER, TIER_NATIVE, TIER_I8, TIER_I4, TIER_I2, TIER_B1, TIER_FP8, FP8_MAX,
     encode_group_int, encode_group_1bit, encode_group_fp8, e4m3_magnitudes, e4m3_value, round_e4m3,
-    encode_vector, decode_vector,
+    encode_vector, decode_vector, outlier_words, apply_outliers,
     pack_codes, unpack_codes,
 )
 from .hotbuffer import HotBuffer, selected_physical_pages
@@ -58,7 +58,7 @@ __all__ = [
     "sparse_attention", "dense_attention",
     "BITS_OF_TIER", "TIER_NATIVE", "TIER_I8", "TIER_I4", "TIER_I2", "TIER_B1", "TIER_FP8", "FP8_MAX",
     "encode_group_int", "encode_group_1bit", "encode_group_fp8", "e4m3_magnitudes", "e4m3_value",
-    "round_e4m3", "encode_vector", "decode_vector",
+    "round_e4m3", "encode_vector", "decode_vector", "outlier_words", "apply_outliers",
     "pack_codes", "unpack_codes",
     "HotBuffer", "selected_physical_pages",
     "row_mean", "store_mean", "key_coords", "row_lowrank", "page_score_lowrank",

@@ -41,6 +41,14 @@ where E4M3(y) is the nearest finite E4M3 value to y, ties to the even code,
 |y| >= 448 saturating to 448, the sign taken from y's sign bit.  Decoder: the
 code's value times s plus z (exact in float64, returned as float32).
 
+1-bit outlier side table (the tier legend: the 1-bit tier is sign-packed
+"with FP16 outlier preservation"; count and format unstated).  Reading: per
+32-element group, after the 1-bit encoding above (s and z unchanged), the
+element e* with the largest fp32(|x_e - z|) (ties: lowest index) is kept as
+v = fp16(x_e*) (round to nearest even, saturating), in one 32-bit side-table
+word per group: e* in bits 0..4, the float16 bits of v in bits 16..31.  The
+decoder returns v at e* and z +- s elsewhere.
+
 Pinned in tests/test_oracle_codec.py: hand-packed bytes (0xA3, 0xE4, 0x8D), the
 int4 ramp 0..31 (s = fp16(31/15) = 2.06640625), exactly representable inputs
 mapping back to their codes, the per-group error bound, the 1-bit value set
@@ -138,6 +146,26 @@ def encode_group_fp8(x):
     return c, s, z
 
 
+def outlier_words(x, z):
+    """Side-table words of 1-bit groups: x float32 (..., 32), z (...) their zeros."""
+    x = np.asarray(x, dtype=np.float32)
+    dev = np.abs(x - np.asarray(z, dtype=np.float32)[..., None])      # float32 steps
+    idx = np.argmax(dev, axis=-1)                                     # first maximum
+    v = np.take_along_axis(x, idx[..., None], axis=-1)[..., 0]
+    bits = round_fp16_sat(v).astype(np.float16).view(np.uint16).astype(np.uint32)
+    return (idx.astype(np.uint32) | (bits << np.uint32(16))).astype(np.uint32)
+
+
+def apply_outliers(xh, words):
+    """Decoded 1-bit groups xh float32 (..., 32) with their side-table words applied."""
+    xh = np.array(xh, dtype=np.float32)
+    w = np.asarray(words, dtype=np.uint32)
+    idx = (w & np.uint32(31)).astype(np.int64)
+    v = (w >> np.uint32(16)).astype(np.uint16).view(np.float16).astype(np.float32)
+    np.put_along_axis(xh, idx[..., None], v[..., None], axis=-1)
+    return xh
+
+
 def pack_codes(codes, bits):
     """codes uint8 (..., d) -> bytes uint8 (..., d*bits/8), LSB first."""
     c = np.asarray(codes, dtype=np.uint8)
@@ -163,11 +191,13 @@ def unpack_codes(packed, bits, d):
     return out
 
 
-def encode_vector(x16, tier):
+def encode_vector(x16, tier, outliers=False):
     """Encode token vectors.
 
     x16: float32 (..., d) holding exact 16-bit values, d a multiple of 32.
-    Returns (packed bytes (..., d*bits/8), scale_zero float32 (..., d/32, 2)).
+    Returns (packed bytes (..., d*bits/8), scale_zero float32 (..., d/32, 2)),
+    and for the 1-bit tier with outliers=True also the side-table words
+    (..., d/32) uint32.
     """
     x = np.asarray(x16, dtype=np.float32)
     d = x.shape[-1]
@@ -180,11 +210,14 @@ def encode_vector(x16, tier):
     else:
         c, s, z = encode_group_int(g, bits)
     packed = pack_codes(c.reshape(x.shape), bits)
+    if outliers and tier == TIER_B1:
+        return packed, np.stack([s, z], axis=-1), outlier_words(g, z)
     return packed, np.stack([s, z], axis=-1)
 
 
-def decode_vector(packed, scale_zero, tier, d):
-    """Decode token vectors to float32 (..., d) (exact float64 value rounded once)."""
+def decode_vector(packed, scale_zero, tier, d, outlier=None):
+    """Decode token vectors to float32 (..., d) (exact float64 value rounded once);
+    outlier: the 1-bit tier's side-table words (..., d/32), applied if given."""
     bits = BITS_OF_TIER[tier]
     c = unpack_codes(packed, bits, d)
     c = e4m3_value(c) if tier == TIER_FP8 else c.astype(np.float64)
@@ -196,4 +229,7 @@ def decode_vector(packed, scale_zero, tier, d):
         xh = z + (2.0 * c - 1.0) * s
     else:
         xh = c * s + z
-    return xh.reshape(xh.shape[:-2] + (d,)).astype(np.float32)
+    xh = xh.astype(np.float32)
+    if outlier is not None and tier == TIER_B1:
+        xh = apply_outliers(xh, outlier)
+    return xh.reshape(xh.shape[:-2] + (d,))
