@@ -327,13 +327,13 @@ def main():
         # attention alone over the same shape with every page in one packed
         # tier (same rotation, queries and selections): the decode cost per tier
         uni = {}
-        for t in (1, 5):
-            ulayers = [hz.DeviceLayer(w.replace(tier_fracs=(1.0,), tier_order=(t,)), layer=i, summaries=None)
-                       for i in range(n_layers)]
+        for t, outl in ((1, False), (5, False), (4, False), (4, True)):
+            ulayers = [hz.DeviceLayer(w.replace(tier_fracs=(1.0,), tier_order=(t,)), layer=i, summaries=None,
+                                      b1_outliers=outl) for i in range(n_layers)]
             us, _ = graph_avg_us(lambda li, q: hz.attend(ulayers[li], q, bufs[li]))
-            b_sel = int(sel_counts.sum()) * page_bytes(w, t)
-            uni[wl.TIER_NAMES[t]] = {"attention_avg_us": us, "selected_bytes": b_sel,
-                                     "achieved_GBps": b_sel / (us * 1e3)}
+            b_sel = int(sel_counts.sum()) * (page_bytes(w, t) + (2 * w.P * (w.d // 32) * 4 if outl else 0))
+            uni[wl.TIER_NAMES[t] + ("_outliers" if outl else "")] = {
+                "attention_avg_us": us, "selected_bytes": b_sel, "achieved_GBps": b_sel / (us * 1e3)}
             for l in ulayers:
                 l.release()
             del ulayers

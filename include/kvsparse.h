@@ -118,7 +118,12 @@ typedef struct kv_layout {
  *     the page's K as well, K of page phys is read from k_hot[v_hot_slot[phys]]
  *     ([hot][Hkv][P][d] 16-bit) when that slot is >= 0, else from k16[slot],
  *     which may then be device-mapped host memory too.  Native pages only: a
- *     packed tier's codes stay where kq/vq point. */
+ *     packed tier's codes stay where kq/vq point.
+ *   kout/vout != NULL (both or neither, with page_entry): the 1-bit tier's
+ *     outlier side tables for K and V, uint32 [slots][Hkv][P][d/32] as
+ *     kv_pack_tier writes them; a 1-bit group then decodes its kept element
+ *     from the table (ARGUS tier legend: 1-bit "with FP16 outlier
+ *     preservation"). */
 typedef struct kv_pages {
   const void* k16;
   const void* v16;
@@ -130,6 +135,8 @@ typedef struct kv_pages {
   const void* v_hot;
   const int32_t* v_hot_slot;
   const void* k_hot;
+  const uint32_t* kout;
+  const uint32_t* vout;
 } kv_pages;
 
 /* ---------------------------------------------------------------------------
@@ -391,9 +398,13 @@ int kv_dequant_tier(const kv_layout* layout, const kv_pages* pages_desc, const i
  * Source page src_pages[i] of src16 ([*][Hkv][P][d]) goes to slot dst_slots[i]
  * of codes ([slots][Hkv][P][d*bits/8]) and scale_zero ([slots][Hkv][P][d/32][2]
  * float16, scale first).  NULL src_pages / dst_slots mean i.
+ * outliers (1-bit tier only, may be NULL): uint32 [slots][Hkv][P][d/32]; per
+ * group, the element e* farthest from z (fp32 |x - z|, lowest index on ties)
+ * is kept: word = e* | (float16 bits of x_e*, round to nearest even,
+ * saturating) << 16.  Must be NULL for the other tiers.
  * --------------------------------------------------------------------------- */
 int kv_pack_tier(const kv_layout* layout, const void* src16, const int32_t* src_pages, int32_t n,
-                 int32_t tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
+                 int32_t tier, uint8_t* codes, void* scale_zero, uint32_t* outliers, const int32_t* dst_slots,
                  void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -425,7 +436,8 @@ int kv_tier_plan(const kv_layout* layout, const float* page_S, const int32_t* se
  * decoding) and encoded into the new tier with kv_pack_tier's encoder, applied
  * to the decoded float32 values; the codes and (scale, zero) pairs go to slot
  * `phys` of the new tier's pools, which must therefore hold at least n_phys
- * slots, and page_entry[phys] becomes KV_PAGE_ENTRY(new tier, phys).
+ * slots, and page_entry[phys] becomes KV_PAGE_ENTRY(new tier, phys).  With
+ * kout/vout set, pages entering the 1-bit tier get their outlier words too.
  * pages_desc: the pools (written: the tier pools named by the moves) with
  * pages_desc->page_entry == page_entry.  moves / move_count as kv_tier_plan
  * leaves them (device memory).  Pages of a move list are distinct.

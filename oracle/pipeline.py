@@ -55,8 +55,9 @@ def build_row_basis_summaries(keys, seq_len, page_size, rank, basis=None):
     return U, mu, lam, log_n
 
 
-def reconstruct_tiers(x, seq_len, page_size, page_tiers):
-    """Encode and decode every token vector of the non-native pages (float64 out)."""
+def reconstruct_tiers(x, seq_len, page_size, page_tiers, b1_outliers=False):
+    """Encode and decode every token vector of the non-native pages (float64 out);
+    with b1_outliers the 1-bit pages keep their outlier side-table elements."""
     x = np.array(x, dtype=np.float64)
     if page_tiers is None:
         return x
@@ -65,8 +66,8 @@ def reconstruct_tiers(x, seq_len, page_size, page_tiers):
         if tier == TIER_NATIVE:
             continue
         lo, hi = p * page_size, min((p + 1) * page_size, seq_len)
-        packed, sz = encode_vector(x[lo:hi].astype(np.float32), int(tier))
-        x[lo:hi] = decode_vector(packed, sz, int(tier), d)
+        enc = encode_vector(x[lo:hi].astype(np.float32), int(tier), outliers=b1_outliers)
+        x[lo:hi] = decode_vector(enc[0], enc[1], int(tier), d, outlier=enc[2] if len(enc) > 2 else None)
     return x
 
 

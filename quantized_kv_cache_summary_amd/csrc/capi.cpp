@@ -79,6 +79,8 @@ int check_pages(const kv_layout* L, const kv_pages* pg) {
   }
   if (pg->v_hot_slot && (!pg->v_hot || !aligned16(pg->v_hot))) return KV_ERR_INVALID_ARG;
   if (pg->k_hot && (!pg->v_hot_slot || !aligned16(pg->k_hot))) return KV_ERR_INVALID_ARG;
+  if (!pg->kout != !pg->vout) return KV_ERR_INVALID_ARG;
+  if (pg->kout && !pg->page_entry) return KV_ERR_INVALID_ARG;
   (void)L;
   return KV_OK;
 }
@@ -369,18 +371,19 @@ int kv_tier_demote(const kv_layout* L, const kv_pages* pg, uint32_t* page_entry,
 }
 
 int kv_pack_tier(const kv_layout* L, const void* src16, const int32_t* src_pages, int32_t n,
-                 int32_t tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
+                 int32_t tier, uint8_t* codes, void* scale_zero, uint32_t* outliers, const int32_t* dst_slots,
                  void* stream) {
   int rc = check_layout(L);
   if (rc) return rc;
   if (tier < KV_TIER_I8 || tier > KV_TIER_FP8) return KV_ERR_UNSUPPORTED;
+  if (outliers && tier != KV_TIER_B1) return KV_ERR_INVALID_ARG;
   if (n < 0) return KV_ERR_INVALID_ARG;
   if (n == 0) return KV_OK;
   if (!src16 || !codes || !scale_zero) return KV_ERR_INVALID_ARG;
   if (!aligned16(src16) || (reinterpret_cast<uintptr_t>(codes) & 3u) ||
       (reinterpret_cast<uintptr_t>(scale_zero) & 3u))
     return KV_ERR_INVALID_ARG;
-  return from_hip(kvs::launch_pack_tier(*L, src16, src_pages, n, tier, codes, scale_zero, dst_slots,
+  return from_hip(kvs::launch_pack_tier(*L, src16, src_pages, n, tier, codes, scale_zero, outliers, dst_slots,
                                         (hipStream_t)stream));
 }
 

@@ -102,6 +102,22 @@ __device__ __forceinline__ void encode_group(const float (&x)[32], int tier, uin
   }
 }
 
+// The 1-bit tier's side-table word of a group: the element farthest from z
+// (float32 |x - z|, lowest index on ties) with its float16 value.
+__device__ __forceinline__ uint32_t outlier_word(const float (&x)[32], float z) {
+  int idx = 0;
+  float best = fabsf(x[0] - z);
+#pragma unroll
+  for (int j = 1; j < 32; ++j) {
+    const float dv = fabsf(x[j] - z);
+    if (dv > best) { best = dv; idx = j; }
+  }
+  float v = x[0];
+#pragma unroll
+  for (int j = 1; j < 32; ++j) v = j == idx ? x[j] : v;
+  return (uint32_t)idx | ((uint32_t)f16_bits(f16_sat(v)) << 16);
+}
+
 // Writes one encoded group: its codes (LSB first) into token row `row` of a
 // code pool ([slots][Hkv][P][D*bits/8]) and its (scale, zero) pair.
 template <int D>
@@ -125,7 +141,8 @@ __global__ __launch_bounds__(256) void pack_tier_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ dst_slots, int n,
                                                         int Hkv, int P, int tier,
                                                         uint8_t* __restrict__ codes,
-                                                        uint16_t* __restrict__ scale_zero) {
+                                                        uint16_t* __restrict__ scale_zero,
+                                                        uint32_t* __restrict__ outliers) {
   constexpr int NG = D / 32;
   const int bits = tier_code_bits(tier);
   const size_t total = (size_t)n * Hkv * P * NG;
@@ -152,24 +169,26 @@ __global__ __launch_bounds__(256) void pack_tier_kernel(const uint16_t* __restri
     uint32_t c[32];
     float s, z;
     encode_group(x, tier, c, s, z);
-    store_group<D>(codes, scale_zero, ((size_t)ds * Hkv + g) * P + tk, grp, bits, c, s, z);
+    const size_t row = ((size_t)ds * Hkv + g) * P + tk;
+    store_group<D>(codes, scale_zero, row, grp, bits, c, s, z);
+    if (outliers) outliers[row * NG + grp] = outlier_word(x, z);
   }
 }
 
 hipError_t launch_pack_tier(const kv_layout& L, const void* src16, const int32_t* src_pages, int n,
-                            int tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
-                            hipStream_t st) {
+                            int tier, uint8_t* codes, void* scale_zero, uint32_t* outliers,
+                            const int32_t* dst_slots, hipStream_t st) {
   const size_t total = (size_t)n * L.num_kv_heads * L.page_size * (L.head_dim / 32);
   const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
   const uint16_t* s = (const uint16_t*)src16;
   uint16_t* sz = (uint16_t*)scale_zero;
   const bool f16 = L.kv_dtype == KV_F16;
   if (L.head_dim == 64) {
-    if (f16) hipLaunchKernelGGL((pack_tier_kernel<64, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz);
-    else hipLaunchKernelGGL((pack_tier_kernel<64, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz);
+    if (f16) hipLaunchKernelGGL((pack_tier_kernel<64, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz, outliers);
+    else hipLaunchKernelGGL((pack_tier_kernel<64, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz, outliers);
   } else {
-    if (f16) hipLaunchKernelGGL((pack_tier_kernel<128, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz);
-    else hipLaunchKernelGGL((pack_tier_kernel<128, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz);
+    if (f16) hipLaunchKernelGGL((pack_tier_kernel<128, true>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz, outliers);
+    else hipLaunchKernelGGL((pack_tier_kernel<128, false>), dim3(blocks), dim3(256), 0, st, s, src_pages, dst_slots, n, L.num_kv_heads, L.page_size, tier, codes, sz, outliers);
   }
   return hipGetLastError();
 }
@@ -189,6 +208,8 @@ struct TierPools {
   uint8_t* vq[KV_NUM_PACKED_TIERS];
   uint16_t* ksz[KV_NUM_PACKED_TIERS];
   uint16_t* vsz[KV_NUM_PACKED_TIERS];
+  uint32_t* kout;
+  uint32_t* vout;
 };
 
 template <int D, bool F16>
@@ -251,8 +272,10 @@ __global__ __launch_bounds__(256) void tier_demote_kernel(TierPools tp, uint32_t
     uint32_t c[32];
     float s, z;
     encode_group(x, nt, c, s, z);
-    store_group<D>(kv == 0 ? tp.kq[nt - 1] : tp.vq[nt - 1], kv == 0 ? tp.ksz[nt - 1] : tp.vsz[nt - 1],
-                   ((size_t)phys * Hkv + g) * P + tk, grp, bits, c, s, z);
+    const size_t nrow = ((size_t)phys * Hkv + g) * P + tk;
+    store_group<D>(kv == 0 ? tp.kq[nt - 1] : tp.vq[nt - 1], kv == 0 ? tp.ksz[nt - 1] : tp.vsz[nt - 1], nrow, grp,
+                   bits, c, s, z);
+    if (nt == KV_TIER_B1 && tp.kout) (kv == 0 ? tp.kout : tp.vout)[nrow * NG + grp] = outlier_word(x, z);
   }
   __syncthreads();
   if (threadIdx.x == 0) page_entry[phys] = ((uint32_t)nt << 29) | (uint32_t)phys;
@@ -269,6 +292,8 @@ hipError_t launch_tier_demote(const kv_layout& L, const kv_pages& pg, uint32_t* 
     tp.ksz[t] = (uint16_t*)const_cast<void*>(pg.ksz[t]);
     tp.vsz[t] = (uint16_t*)const_cast<void*>(pg.vsz[t]);
   }
+  tp.kout = const_cast<uint32_t*>(pg.kout);
+  tp.vout = const_cast<uint32_t*>(pg.vout);
   const dim3 grid(max_pages, B);
   const bool f16 = L.kv_dtype == KV_F16;
   if (L.head_dim == 64) {

@@ -101,7 +101,7 @@ hipError_t launch_tier_demote(const kv_layout& L, const kv_pages& pg, uint32_t* 
                               const int32_t* moves, const int32_t* move_count, hipStream_t st);
 
 hipError_t launch_pack_tier(const kv_layout& L, const void* src16, const int32_t* src_pages, int n,
-                            int tier, uint8_t* codes, void* scale_zero, const int32_t* dst_slots,
-                            hipStream_t st);
+                            int tier, uint8_t* codes, void* scale_zero, uint32_t* outliers,
+                            const int32_t* dst_slots, hipStream_t st);
 
 }  // namespace kvs

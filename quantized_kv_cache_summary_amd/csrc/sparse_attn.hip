@@ -48,6 +48,8 @@ struct PagesDev {
   const uint16_t* v_hot;
   const int32_t* v_hot_slot;
   const uint16_t* k_hot;
+  const uint32_t* kout;
+  const uint32_t* vout;
 };
 
 template <int T>
@@ -73,6 +75,8 @@ struct TierChunk {
   uint32_t ksz[D / 32];
   uint32_t v[4][VW];
   uint32_t vsz[4];
+  uint32_t ko[D / 32];   // 1-bit outlier words, when the pools have side tables
+  uint32_t vo[4];
 };
 
 // Requests the codes of EL elements from e0 of token row `tokrow` of packed
@@ -455,6 +459,14 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               tier_load<D, EV, T>(pg.vq[T - 1], pg.vsz[T - 1], tok + 4 * j + grp, col * EV, r.v[j], r.vsz[j]);
+            if constexpr (T == KV_TIER_B1) {
+              if (pg.kout) {
+#pragma unroll
+                for (int s = 0; s < KS; ++s) r.ko[s] = pg.kout[(tok + col) * (D / 32) + s];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) r.vo[j] = pg.vout[(tok + 4 * j + grp) * (D / 32) + (col * EV) / 32];
+              }
+            }
           }
         };
         auto compute = [&](const Raw& r, int jj, int c) {
@@ -469,6 +481,8 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
             for (int s = 0; s < KS; ++s) {
               float x[8];
               tier_decode<8, T>(r.k[s], r.ksz[s], 32 * s + 8 * grp, x);
+              if constexpr (T == KV_TIER_B1)
+                if (pg.kout) apply_outlier<8>(x, 32 * s + 8 * grp, r.ko[s]);
               u32x4_t ah, al;
 #pragma unroll
               for (int w = 0; w < 4; ++w) {
@@ -488,7 +502,11 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
             const int tk = 4 * j + grp;
             float v[EV];
             if constexpr (T == KV_TIER_NATIVE) unpack_v<F16, EV>(r.v[j], v);
-            else tier_decode<EV, T>(r.v[j], r.vsz[j], col * EV, v);
+            else {
+              tier_decode<EV, T>(r.v[j], r.vsz[j], col * EV, v);
+              if constexpr (T == KV_TIER_B1)
+                if (pg.vout) apply_outlier<EV>(v, col * EV, r.vo[j]);
+            }
             // values of tokens past seq_len are zeroed: probability 0, memory may hold NaN
             if (!full) {
               const uint32_t vk = tok0 + tk < L ? 0xFFFFFFFFu : 0u;
@@ -667,6 +685,8 @@ static PagesDev to_dev(const kv_pages& pg) {
   d.v_hot = (const uint16_t*)pg.v_hot;
   d.v_hot_slot = pg.v_hot_slot;
   d.k_hot = (const uint16_t*)pg.k_hot;
+  d.kout = pg.kout;
+  d.vout = pg.vout;
   return d;
 }
 
@@ -728,7 +748,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(PagesDev pg, const int32_t
         case KV_TIER_I4: decode_run<D, RUN, 4>(codes, sz, prow, run * RUN, x); break;
         case KV_TIER_I2: decode_run<D, RUN, 2>(codes, sz, prow, run * RUN, x); break;
         case KV_TIER_FP8: decode_fp8<D, RUN>(codes, sz, prow, run * RUN, x); break;
-        default: decode_run<D, RUN, 1>(codes, sz, prow, run * RUN, x); break;
+        default:
+          decode_run<D, RUN, 1>(codes, sz, prow, run * RUN, x);
+          if (pg.kout) apply_outlier<RUN>(x, run * RUN, (kv == 0 ? pg.kout : pg.vout)[prow * (D / 32) + run * RUN / 32]);
+          break;
       }
     }
     float* dst = out + ((((size_t)i * 2 + kv) * Hkv + g) * P + tk) * D + run * RUN;

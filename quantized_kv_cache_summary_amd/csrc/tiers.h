@@ -81,4 +81,15 @@ __device__ __forceinline__ void decode_fp8(const uint8_t* codes, const uint16_t*
   }
 }
 
+// The 1-bit tier's outlier side table: replaces, in a decoded run
+// [e0, e0 + EL) of one 32-element group, the element the group's word keeps
+// (index in bits 0..4, float16 value in bits 16..31).
+template <int EL>
+__device__ __forceinline__ void apply_outlier(float* x, int e0, uint32_t word) {
+  const int idx = (int)(word & 31u) - (e0 & 31);
+  const float v = f16_bits_to_f32(word >> 16);
+#pragma unroll
+  for (int e = 0; e < EL; ++e) x[e] = e == idx ? v : x[e];
+}
+
 }  // namespace kvs

@@ -61,7 +61,8 @@ class DeviceLayer:
     """K/V pools, block table, summaries (and tier pools / host V) of one layer."""
 
     def __init__(self, w: wl.Workload, layer=0, summaries="build", device="cuda", host_v=None,
-                 hot_mode="warm", seq_lens=None, threads=None, host_k=None, tier_slots="compact"):
+                 hot_mode="warm", seq_lens=None, threads=None, host_k=None, tier_slots="compact",
+                 b1_outliers=False):
         self.w, self.layer, self.device = w, layer, device
         self.L = layout_of(w)
         host_v = w.v_host if host_v is None else host_v
@@ -132,8 +133,9 @@ class DeviceLayer:
             self.log_n.copy_(torch.from_numpy(np.log(n_valid.astype(np.float64)).astype(np.float32)))
         self.tiers = None
         self.page_entry = None
+        self.kout = self.vout = None
         if w.tier_fracs is not None:
-            self._pack_tiers(tier_slots)
+            self._pack_tiers(tier_slots, b1_outliers)
         self.v_hot = self.k_hot = None
         self.v_hot_slot = None
         if host_v:
@@ -221,11 +223,11 @@ class DeviceLayer:
         kv.summary_build_basis(self.L, self.k_src, self.bt, entries, nv, self.basis, self.mu, self.lam,
                                self.log_n, stream)
 
-    def _pack_tiers(self, tier_slots="compact"):
+    def _pack_tiers(self, tier_slots="compact", b1_outliers=False):
         """Packs every page into its tier.  tier_slots "compact": a tier's pool
         holds only its pages; "phys": every tier pool has a slot per physical
         page and a page sits at slot = its physical id (what tier demotion
-        writes to)."""
+        writes to).  b1_outliers: the 1-bit tier keeps outlier side tables."""
         w = self.w
         tiers_logical = wl.page_tiers(w, self.layer)              # (B, Np)
         tier_phys = np.zeros(w.n_phys, dtype=np.int64)
@@ -242,12 +244,17 @@ class DeviceLayer:
             vc = torch.zeros_like(kc)
             ks = torch.zeros((n, w.Hkv, w.P, w.d // 32, 2), dtype=torch.float16, device=self.device)
             vs = torch.zeros_like(ks)
+            ko = vo = None
+            if b1_outliers and t == kv.KV_TIER_B1:
+                ko = torch.zeros((n, w.Hkv, w.P, w.d // 32), dtype=torch.int32, device=self.device)
+                vo = torch.zeros_like(ko)
+                self.kout, self.vout = ko, vo
             if phys.size:
                 src = torch.from_numpy(phys).to(self.device)
                 slots = phys if full else np.arange(phys.size, dtype=np.int32)
                 dst = torch.from_numpy(slots).to(self.device) if full else None
-                kv.pack_tier(self.L, self.k16, phys.size, t, kc, ks, src_pages=src, dst_slots=dst)
-                kv.pack_tier(self.L, self.v16, phys.size, t, vc, vs, src_pages=src, dst_slots=dst)
+                kv.pack_tier(self.L, self.k16, phys.size, t, kc, ks, src_pages=src, dst_slots=dst, outliers=ko)
+                kv.pack_tier(self.L, self.v16, phys.size, t, vc, vs, src_pages=src, dst_slots=dst, outliers=vo)
                 entry[phys] = (np.uint32(t) << np.uint32(29)) | slots.astype(np.uint32)
             self.kq.append(kc); self.vq.append(vc); self.ksz.append(ks); self.vsz.append(vs)
         native = np.nonzero(tier_phys == 0)[0]
@@ -285,7 +292,7 @@ class DeviceLayer:
         v16_ptr = self.host_v.dev.value if self.host_v is not None else None
         if self.page_entry is not None:
             return kv.make_pages(self.k16, v16, self.kq, self.vq, self.ksz, self.vsz, self.page_entry,
-                                 self.v_hot, self.v_hot_slot, v16_ptr=v16_ptr)
+                                 self.v_hot, self.v_hot_slot, v16_ptr=v16_ptr, kout=self.kout, vout=self.vout)
         return kv.make_pages(self.k16, v16, page_entry=None, v_hot=self.v_hot, v_hot_slot=self.v_hot_slot,
                              v16_ptr=v16_ptr, k_hot=self.k_hot,
                              k16_ptr=self.host_k.dev.value if self.host_k is not None else None)

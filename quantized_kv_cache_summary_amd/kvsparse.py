@@ -53,6 +53,7 @@ class KvPages(ctypes.Structure):
         ("ksz", ctypes.c_void_p * NUM_PACKED_TIERS), ("vsz", ctypes.c_void_p * NUM_PACKED_TIERS),
         ("page_entry", ctypes.c_void_p), ("v_hot", ctypes.c_void_p), ("v_hot_slot", ctypes.c_void_p),
         ("k_hot", ctypes.c_void_p),
+        ("kout", ctypes.c_void_p), ("vout", ctypes.c_void_p),
     ]
 
 
@@ -89,7 +90,7 @@ def lib():
             "kv_sparse_decode_attn_workspace_size": (_SZ, [_LP, _I, _I, _I]),
             "kv_sparse_decode_attn_num_splits": (_I, [_LP, _I, _I, _I]),
             "kv_dequant_tier": (_I, [_LP, _PP, _P, _I, _P, _P]),
-            "kv_pack_tier": (_I, [_LP, _P, _P, _I, _I, _P, _P, _P, _P]),
+            "kv_pack_tier": (_I, [_LP, _P, _P, _I, _I, _P, _P, _P, _P, _P]),
             "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "kv_basis_build": (_I, [_LP, _P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
             "kv_lowrank_coords": (_I, [_LP, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P]),
@@ -137,7 +138,7 @@ def _check(rc, fn):
 
 
 def make_pages(k16, v16, kq=None, vq=None, ksz=None, vsz=None, page_entry=None, v_hot=None,
-               v_hot_slot=None, v16_ptr=None, k_hot=None, k16_ptr=None):
+               v_hot_slot=None, v16_ptr=None, k_hot=None, k16_ptr=None, kout=None, vout=None):
     """KvPages struct; keeps the tensors alive on the returned object.
 
     v16_ptr / k16_ptr override v16's / k16's pointer (a device-mapped host address)."""
@@ -153,7 +154,9 @@ def make_pages(k16, v16, kq=None, vq=None, ksz=None, vsz=None, page_entry=None, 
     pg.v_hot = _p(v_hot)
     pg.v_hot_slot = _p(v_hot_slot)
     pg.k_hot = _p(k_hot)
-    pg._keep = (k16, v16, kq, vq, ksz, vsz, page_entry, v_hot, v_hot_slot, k_hot)
+    pg.kout = _p(kout)
+    pg.vout = _p(vout)
+    pg._keep = (k16, v16, kq, vq, ksz, vsz, page_entry, v_hot, v_hot_slot, k_hot, kout, vout)
     return pg
 
 
@@ -307,7 +310,7 @@ def dequant_tier(L, pages, page_ids, out, stream=None):
     _check(rc, "kv_dequant_tier")
 
 
-def pack_tier(L, src16, n, tier, codes, scale_zero, src_pages=None, dst_slots=None, stream=None):
+def pack_tier(L, src16, n, tier, codes, scale_zero, src_pages=None, dst_slots=None, stream=None, outliers=None):
     rc = lib().kv_pack_tier(ctypes.byref(L), _p(src16), _p(src_pages), int(n), int(tier), _p(codes),
-                            _p(scale_zero), _p(dst_slots), _stream(stream))
+                            _p(scale_zero), _p(outliers), _p(dst_slots), _stream(stream))
     _check(rc, "kv_pack_tier")

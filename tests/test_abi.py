@@ -137,16 +137,26 @@ def test_attention_validation_and_workspace():
     kh.v16 = FAKE
     kh.k_hot = FAKE
     assert call(pages=kh) == kv.KV_ERR_INVALID_ARG                  # K hot buffer without the slot map
+    ko = kv.KvPages()
+    ko.k16 = FAKE
+    ko.v16 = FAKE
+    ko.page_entry = FAKE
+    for t in range(kv.NUM_PACKED_TIERS):
+        ko.kq[t] = ko.vq[t] = ko.ksz[t] = ko.vsz[t] = FAKE
+    ko.kout = FAKE
+    assert call(pages=ko) == kv.KV_ERR_INVALID_ARG                  # K outlier table without V's
 
 
 def test_pack_build_dequant_validation():
     L = _L()
     lib = kv.lib()
-    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 4, 0, FAKE, FAKE, None, None) == kv.KV_ERR_UNSUPPORTED
-    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 4, 6, FAKE, FAKE, None, None) == kv.KV_ERR_UNSUPPORTED
-    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 0, kv.KV_TIER_FP8, FAKE, FAKE, None, None) == kv.KV_OK
-    assert lib.kv_pack_tier(ctypes.byref(L), None, None, 4, 1, FAKE, FAKE, None, None) == kv.KV_ERR_INVALID_ARG
-    assert lib.kv_pack_tier(ctypes.byref(L), FAKE, None, 0, 1, FAKE, FAKE, None, None) == kv.KV_OK
+    pt = lib.kv_pack_tier
+    assert pt(ctypes.byref(L), FAKE, None, 4, 0, FAKE, FAKE, None, None, None) == kv.KV_ERR_UNSUPPORTED
+    assert pt(ctypes.byref(L), FAKE, None, 4, 6, FAKE, FAKE, None, None, None) == kv.KV_ERR_UNSUPPORTED
+    assert pt(ctypes.byref(L), FAKE, None, 0, kv.KV_TIER_FP8, FAKE, FAKE, None, None, None) == kv.KV_OK
+    assert pt(ctypes.byref(L), None, None, 4, 1, FAKE, FAKE, None, None, None) == kv.KV_ERR_INVALID_ARG
+    assert pt(ctypes.byref(L), FAKE, None, 0, 1, FAKE, FAKE, None, None, None) == kv.KV_OK
+    assert pt(ctypes.byref(L), FAKE, None, 4, kv.KV_TIER_I8, FAKE, FAKE, FAKE, None, None) == kv.KV_ERR_INVALID_ARG
     sb = lib.kv_summary_build
     assert sb(ctypes.byref(L), FAKE, FAKE, 8, FAKE, FAKE, -1, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG
     assert sb(ctypes.byref(L), FAKE + 4, FAKE, 8, FAKE, FAKE, 3, FAKE, FAKE, None) == kv.KV_ERR_INVALID_ARG

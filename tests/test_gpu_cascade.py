@@ -75,9 +75,10 @@ def test_plan_matches_oracle(kv, max_pages, caps, ff, fl):
         assert [tuple(x) for x in got_m[b, :got_c[b]].tolist()] == want[b], b
 
 
-def _chain_pages(x16_rows, tiers_before, tiers_after, seq_len, P, bt_row):
+def _chain_pages(x16_rows, tiers_before, tiers_after, seq_len, P, bt_row, outl=False):
     """Row values as attention sees them: each page encoded in its tier before
-    the call and, if it moved, re-encoded from those decoded values."""
+    the call and, if it moved, re-encoded from those decoded values (1-bit
+    pages with their outlier elements when outl)."""
     x = np.array(x16_rows[:seq_len], dtype=np.float32)
     out = x.astype(np.float64)
     d = x.shape[1]
@@ -86,11 +87,12 @@ def _chain_pages(x16_rows, tiers_before, tiers_after, seq_len, P, bt_row):
         t0, t1 = int(tiers_before[bt_row[p]]), int(tiers_after[bt_row[p]])
         v = x[lo:hi]
         if t0 != 0:
-            c, sz = oracle.encode_vector(v, t0)
-            v = oracle.decode_vector(c, sz, t0, d)
+            enc = oracle.encode_vector(v, t0, outliers=outl)
+            v = oracle.decode_vector(enc[0], enc[1], t0, d, outlier=enc[2] if len(enc) > 2 else None)
         if t1 != t0:
             c, sz = oracle.retier_vectors(v, t0, t1, d)
-            v = oracle.decode_vector(c, sz, t1, d)
+            words = oracle.outlier_words(v.reshape(v.shape[0], -1, 32), sz[..., 1]) if outl and t1 == 4 else None
+            v = oracle.decode_vector(c, sz, t1, d, outlier=words)
         out[lo:hi] = v
     return out
 
@@ -98,7 +100,7 @@ def _chain_pages(x16_rows, tiers_before, tiers_after, seq_len, P, bt_row):
 def test_demote_codes_and_attention(hz, kv):
     w = W["tiers_fp8_64k"].replace(B=2, ctx=16 * 300 + 7)
     announce("tier demotion on a tiered layer with a slot per physical page")
-    layer = hz.DeviceLayer(w, summaries="build", tier_slots="phys")
+    layer = hz.DeviceLayer(w, summaries="build", tier_slots="phys", b1_outliers=True)
     q = hz.queries_device(w)
     bufs = hz.StepBuffers(w, with_S=True)
     hz.score(layer, q, bufs)
@@ -131,7 +133,8 @@ def test_demote_codes_and_attention(hz, kv):
     pools = {t: [(layer.kq[t - 1].cpu().numpy(), layer.ksz[t - 1].float().cpu().numpy()),
                  (layer.vq[t - 1].cpu().numpy(), layer.vsz[t - 1].float().cpu().numpy())] for t in range(1, 6)}
     checked = 0
-    for p, nt in list(moved.items())[:200]:
+    checked_b1 = [0]
+    for p, nt in sorted(moved.items(), key=lambda kv_: -int(kv_[1] == 4))[:200]:
         ot = int(t_before[p])
         for kvi, src in ((0, k_all), (1, v_all)):
             x = wl.bits_to_f32(src[p], w.dtype)                # (Hkv, P, d)
@@ -142,8 +145,13 @@ def test_demote_codes_and_attention(hz, kv):
             codes, szp = pools[nt][kvi]
             np.testing.assert_array_equal(codes[p], c2)
             np.testing.assert_array_equal(szp[p], sz2)
+            if nt == 4:                                         # into the 1-bit tier: its outlier words
+                table = (layer.kout if kvi == 0 else layer.vout)[p].cpu().numpy().view(np.uint32)
+                np.testing.assert_array_equal(table, oracle.outlier_words(x.reshape(w.Hkv, w.P, -1, 32),
+                                                                          sz2[..., 1]))
+                checked_b1[0] += 1
             checked += 1
-    assert checked > 0
+    assert checked > 0 and checked_b1[0] > 0
     # attention through the demoted pages
     sel_np, cnt_np = wl.synthetic_selection(w, w.k_of(w.Np))
     hz.attend(layer, q, bufs, sel=torch.from_numpy(sel_np).cuda(), sel_count=torch.from_numpy(cnt_np).cuda())
@@ -151,8 +159,8 @@ def test_demote_codes_and_attention(hz, kv):
     out, lse = bufs.out.cpu().numpy(), bufs.lse.cpu().numpy()
     for b in range(w.B):
         for g in range(w.Hkv):
-            K = _chain_pages(wl.row_keys(w, 0, b, g), t_before, t_after, w.ctx, w.P, layer.bt_np[b])
-            V = _chain_pages(wl.row_values(w, 0, b, g), t_before, t_after, w.ctx, w.P, layer.bt_np[b])
+            K = _chain_pages(wl.row_keys(w, 0, b, g), t_before, t_after, w.ctx, w.P, layer.bt_np[b], outl=True)
+            V = _chain_pages(wl.row_values(w, 0, b, g), t_before, t_after, w.ctx, w.P, layer.bt_np[b], outl=True)
             qr = wl.queries(w, 0, b, g).astype(np.float64)
             o_ref, l_ref = oracle.sparse_attention(qr, K, V, w.ctx, w.P, sel_np[b, g], w.tau)
             hs = slice(g * w.G, (g + 1) * w.G)

@@ -404,7 +404,8 @@ def test_summary_builder_invariants(hz, name):
 
 # ---------------------------------------------------------------- codec
 
-@pytest.mark.parametrize("shape", ["bf16_d128", "f16_d64", "fp8_bf16_d128", "fp8_f16_d64"])
+@pytest.mark.parametrize("shape", ["bf16_d128", "f16_d64", "fp8_bf16_d128", "fp8_f16_d64", "out_bf16_d128",
+                                   "out_f16_d64"])
 def test_pack_and_dequant_bit_exact(hz, shape):
     from quantized_kv_cache_summary_amd import kvsparse as kv
     base = W["tiers_fp8_64k"] if shape.startswith("fp8") else W["tiers_64k"]
@@ -412,8 +413,9 @@ def test_pack_and_dequant_bit_exact(hz, shape):
         w = base.replace(B=2, ctx=16 * 96)
     else:
         w = base.replace(B=2, ctx=16 * 96, d=64, Hq=8, Hkv=2, dtype="f16", rank=2)
+    outl = shape.startswith("out")
     announce(f"codec {shape}")
-    layer = hz.DeviceLayer(w, summaries=None)
+    layer = hz.DeviceLayer(w, summaries=None, b1_outliers=outl)
     k_all = layer.k16.view(torch.int16).cpu().numpy().view(np.uint16)
     v_all = layer.v16.view(torch.int16).cpu().numpy().view(np.uint16)
     present = sorted(set(w.tier_order) - {0})
@@ -427,6 +429,11 @@ def test_pack_and_dequant_bit_exact(hz, shape):
             got_sz = sz[: phys.size].float().cpu().numpy()
             np.testing.assert_array_equal(got_codes, ref_codes)
             np.testing.assert_array_equal(got_sz, ref_sz)
+        if outl and t == kv.KV_TIER_B1:
+            for src, table in ((k_all, layer.kout), (v_all, layer.vout)):
+                x = wl.bits_to_f32(src[phys], w.dtype)
+                ref_words = oracle.encode_vector(x, t, outliers=True)[2]
+                np.testing.assert_array_equal(table[: phys.size].cpu().numpy().view(np.uint32), ref_words)
     # standalone decode of every page through page_entry
     ids = torch.arange(w.n_phys, dtype=torch.int32).cuda()
     out = torch.empty((w.n_phys, 2, w.Hkv, w.P, w.d), dtype=torch.float32).cuda()
@@ -440,8 +447,8 @@ def test_pack_and_dequant_bit_exact(hz, shape):
             if t == 0:
                 ref = x
             else:
-                c, sz = oracle.encode_vector(x, t)
-                ref = oracle.decode_vector(c, sz, t, w.d)
+                enc = oracle.encode_vector(x, t, outliers=outl)
+                ref = oracle.decode_vector(enc[0], enc[1], t, w.d, outlier=enc[2] if len(enc) > 2 else None)
             np.testing.assert_array_equal(out[phys, kvi], ref)
 
 
@@ -502,11 +509,11 @@ def test_fp8_every_code_ties_and_saturation(hz, dtype):
         np.testing.assert_array_equal(got[:, kvi].view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("name", ["tiers_64k", "tiers_fp8_64k"])
-def test_tiered_attention_parity(hz, name):
+@pytest.mark.parametrize("name,outl", [("tiers_64k", False), ("tiers_fp8_64k", False), ("tiers_64k", True)])
+def test_tiered_attention_parity(hz, name, outl):
     w = W[name].replace(B=2, ctx=16 * 300)
-    announce(f"tiered attention {name}")
-    layer = hz.DeviceLayer(w, summaries=None)
+    announce(f"tiered attention {name} outliers={outl}")
+    layer = hz.DeviceLayer(w, summaries=None, b1_outliers=outl)
     q = hz.queries_device(w)
     k = w.k_of(w.Np)
     sel_np, cnt_np = wl.synthetic_selection(w, k)
@@ -517,8 +524,8 @@ def test_tiered_attention_parity(hz, name):
     tiers = wl.page_tiers(w)
     for b in range(w.B):
         for g in range(w.Hkv):
-            K = reconstruct_tiers(wl.row_keys(w, 0, b, g), w.ctx, w.P, tiers[b])
-            V = reconstruct_tiers(wl.row_values(w, 0, b, g), w.ctx, w.P, tiers[b])
+            K = reconstruct_tiers(wl.row_keys(w, 0, b, g), w.ctx, w.P, tiers[b], b1_outliers=outl)
+            V = reconstruct_tiers(wl.row_values(w, 0, b, g), w.ctx, w.P, tiers[b], b1_outliers=outl)
             o_ref, l_ref = oracle.sparse_attention(_q_ref(w, b, g), K, V, w.ctx, w.P, sel_np[b, g], w.tau)
             hs = slice(g * w.G, (g + 1) * w.G)
             assert_attn_close(out[b, hs], lse[b, hs], o_ref, l_ref)
