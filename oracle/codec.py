@@ -56,6 +56,8 @@ and sign, and pack/unpack identity.  FP8 in tests/test_oracle_fp8.py: the
 format's landmark codes, torch's float8_e4m3fn cast for in-range values, a
 brute-force nearest-value search over all 127 magnitudes, a hand-worked group
 (tests/golden/fp8_group.json), the relative error bound and saturation.
+Outlier words in tests/test_oracle_outlier.py: a hand-worked group, ties,
+exactness of the kept element, the rest of the group unchanged, saturation.
 """
 
 import numpy as np
