@@ -48,6 +48,10 @@ def parse():
                     help="also run a 512 MiB device copy (known bytes) for scaling counter readings")
     ap.add_argument("--mem-kv", action="store_true",
                     help="host-resident workloads: also time the variant with K in host memory too")
+    ap.add_argument("--two-kernel", action="store_true",
+                    help="time the step as separate top-k and attention launches (default: the fused call "
+                         "where it is the faster step)")
+    ap.add_argument("--splits", type=int, default=0, help="attention splits per row (0 = the library's choice)")
     ap.add_argument("--groups", type=int, default=1,
                     help="row groups per step, each on its own stream (1 = one chain for the batch)")
     return ap.parse_args()
@@ -170,8 +174,10 @@ def main():
     t0 = time.time()
     layers = [hz.DeviceLayer(w, layer=i, summaries="build") for i in range(n_layers)]
     qs = [[hz.queries_device(w, i, j) for j in range(args.queries)] for i in range(n_layers)]
-    bufs = [hz.StepBuffers(w) for _ in range(n_layers)]
-    steps_split = [hz.SplitStep(layers[i], bufs[i], args.groups) for i in range(n_layers)]
+    bufs = [hz.StepBuffers(w, num_splits=args.splits) for _ in range(n_layers)]
+    fused = not args.two_kernel and args.groups == 1 and hz.fused_preferred(layers[0], bufs[0])
+    steps_split = [hz.SplitStep(layers[i], bufs[i], args.groups, num_splits=args.splits, fused=fused)
+                   for i in range(n_layers)]
     torch.cuda.synchronize()
     log(f"[bench] set-up {time.time() - t0:.1f}s (generation, upload, summary build)")
 
@@ -236,9 +242,11 @@ def main():
     score_us, n_score = graph_avg_us(lambda li, q: hz.score(layers[li], q, bufs[li]))
     topk_us, _ = graph_avg_us(lambda li, q: hz.topk(layers[li], bufs[li]))
     attend_us, _ = graph_avg_us(lambda li, q: hz.attend(layers[li], q, bufs[li]))
+    fused_us = graph_avg_us(lambda li, q: hz.topk_attend(layers[li], q, bufs[li]))[0] if fused else None
     score_ms = np.array([score_us / 1e3])
     log(f"[bench] eager single chain: {eager_ms * 1e3:.1f} us/step; per launch: score {score_us:.2f} us "
-        f"({n_score} graph-replayed launches), top-k {topk_us:.2f} us, attention {attend_us:.2f} us")
+        f"({n_score} graph-replayed launches), top-k {topk_us:.2f} us, attention {attend_us:.2f} us"
+        + (f", fused top-k + attention {fused_us:.2f} us" if fused else ""))
 
     # ---- timed region: K steps (row groups overlapped on streams), replayed
     #      from a HIP graph that holds one pass over the rotated layers
@@ -274,7 +282,29 @@ def main():
         torch.cuda.synchronize()
         ms_per_step = ev[0].elapsed_time(ev[-1]) / timed_steps
         per_replay = np.array([ev[r].elapsed_time(ev[r + 1]) / n_cap for r in range(reps)])
-    log(f"[bench] timed {timed_steps} steps: {ms_per_step * 1e3:.1f} us/step")
+    log(f"[bench] timed {timed_steps} steps: {ms_per_step * 1e3:.1f} us/step"
+        + (" (top-k and attention fused)" if fused else ""))
+    two_kernel = None
+    if fused and not args.eager:
+        # the same steps with separate top-k and attention launches, for comparison
+        two = [hz.SplitStep(layers[i], bufs[i], 1, num_splits=args.splits) for i in range(n_layers)]
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            for i in range(n_cap):
+                two[i % n_layers](qs[i % n_layers][(i // n_layers) % args.queries])
+        for _ in range(3):
+            g2.replay()
+        torch.cuda.synchronize()
+        t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0e.record(stream)
+        for _ in range(reps):
+            g2.replay()
+        t1e.record(stream)
+        torch.cuda.synchronize()
+        two_ms = t0e.elapsed_time(t1e) / (reps * n_cap)
+        two_kernel = {"ms_per_step": two_ms, "value": 1e3 / two_ms, "unit": "steps/s",
+                      "note": "score, then kv_page_topk and kv_sparse_decode_attn as separate launches"}
+        log(f"[bench] same steps with separate top-k and attention launches: {two_ms * 1e3:.1f} us/step")
 
     sel_counts = bufs[0].sel_count.cpu().numpy()
     summary_b, selected_b = algorithmic_bytes(w, sel_counts, bufs[0].sel.cpu().numpy(),
@@ -300,6 +330,7 @@ def main():
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
             "page_size": w.P, "ctx": w.ctx, "rank": w.rank, "keep": w.keep, "k_per_row": int(sel_counts.max()),
             "rotated_layers": n_layers, "row_groups_on_streams": args.groups,
+            "topk_attention": "fused (kv_topk_sparse_decode_attn)" if fused else "separate launches",
             "timing": "eager" if args.eager else "hip graph replay",
         },
         "effective_GBps": step_bytes / (best_ms / 1e3) / 1e9,
@@ -310,7 +341,9 @@ def main():
             "over": f"{len(per_replay)} graph replays of {n_cap} steps each",
             "median": float(np.median(per_replay)), "p10": float(np.percentile(per_replay, 10)),
             "p90": float(np.percentile(per_replay, 90))},
-        "kernel_avg_us": {"page_score": score_us, "page_topk": topk_us, "sparse_decode_attn": attend_us},
+        "kernel_avg_us": {"page_score": score_us, "page_topk": topk_us, "sparse_decode_attn": attend_us,
+                          **({"topk_sparse_decode_attn": fused_us} if fused else {})},
+        "two_kernel_step": two_kernel,
         "roofline": {
             "kernel": "page_score_kernel",
             "bound": "hbm",

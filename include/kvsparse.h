@@ -4,6 +4,7 @@
  *
  * One decode step for one layer is
  *     kv_page_score  -> kv_page_topk  -> kv_sparse_decode_attn
+ * (the last two also fused as kv_topk_sparse_decode_attn)
  * and, when a page is appended, kv_summary_build (and kv_pack_tier for pages
  * stored in a packed low-bit tier).  With shared-basis summaries the score is
  * kv_page_score_basis, the basis comes from kv_basis_build at prefill and the
@@ -332,6 +333,37 @@ size_t kv_sparse_decode_attn_workspace_size(const kv_layout* layout, int32_t B, 
  * for a pool with packed tiers (pages->page_entry set), 0 for native pages. */
 int32_t kv_sparse_decode_attn_num_splits(const kv_layout* layout, int32_t B, int32_t k_max,
                                          int32_t tiered);
+
+/* ---------------------------------------------------------------------------
+ * kv_topk_sparse_decode_attn -- the selector and the sparse attention of one
+ * step in one launch (AMASS page, "Benchmarking": the top-B and decode stages
+ * of a step, here without the selection's round trip through memory).  With
+ * coverage < 0 the selection is kv_page_topk's (keep_frac, k_fixed); with
+ * coverage >= 0 it is kv_page_topk_coverage's (keep_frac and k_fixed ignored,
+ * k_max the cap).  Every block of a row selects the row's pages itself and
+ * attends over its split's share of them; sel, sel_count and page_S
+ * (optional, may be NULL) are written exactly as the selector call writes
+ * them, and out and lse are bit-identical to kv_sparse_decode_attn over that
+ * selection with the same num_splits (0 picks the same automatic count).
+ * Arguments and their rules are the union of the two calls'; ws/ws_bytes:
+ * kv_sparse_decode_attn_workspace_size() for the split count, with the same
+ * zeroed counters and the same rule against overlapping calls.  Returns
+ * KV_ERR_UNSUPPORTED when the row's keys and a split's share of the selection
+ * do not fit one block's LDS (max_pages 2048 at d = 128 always fits); then the
+ * two calls do the same work.  coverage may not be NaN or infinite.
+ * --------------------------------------------------------------------------- */
+int kv_topk_sparse_decode_attn(const kv_layout* layout, const void* q, const kv_pages* pages,
+                               const int32_t* block_table, const int32_t* seq_lens, int32_t B,
+                               int32_t max_pages, const float* head_scores, const float* lse_partial,
+                               float keep_frac, int32_t k_fixed, float coverage, int32_t n_force_first,
+                               int32_t n_force_last, int32_t* sel, int32_t* sel_count, int32_t k_max,
+                               float* page_S, int32_t num_splits, float* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* 1 when kv_topk_sparse_decode_attn supports this shape with num_splits (> 0,
+ * the count it will use) splits per row, else 0. */
+int32_t kv_topk_sparse_decode_attn_supported(const kv_layout* layout, int32_t max_pages, int32_t k_max,
+                                             int32_t num_splits);
 
 /* ---------------------------------------------------------------------------
  * kv_hot_admit -- hot-buffer admission for a host-resident V pool (AMASS page,

@@ -302,6 +302,52 @@ int kv_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages* pg,
                                           (hipStream_t)stream));
 }
 
+int32_t kv_topk_sparse_decode_attn_supported(const kv_layout* L, int32_t max_pages, int32_t k_max,
+                                             int32_t num_splits) {
+  if (check_layout(L) || max_pages < 0 || k_max < 0 || num_splits <= 0 || num_splits > kvs::kMaxSplits) return 0;
+  if (max_pages > kvs::kMaxTopkPages) return 0;
+  return kvs::topk_attn_dyn_lds_bytes(*L, max_pages, k_max, num_splits) <= kvs::kTopkAttnMaxLds ? 1 : 0;
+}
+
+int kv_topk_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages* pg,
+                               const int32_t* block_table, const int32_t* seq_lens, int32_t B,
+                               int32_t max_pages, const float* head_scores, const float* lse_partial,
+                               float keep_frac, int32_t k_fixed, float coverage, int32_t n_force_first,
+                               int32_t n_force_last, int32_t* sel, int32_t* sel_count, int32_t k_max,
+                               float* page_S, int32_t num_splits, float* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0 || k_max < 0 || k_fixed < 0 || n_force_first < 0 || n_force_last < 0 ||
+      num_splits < 0)
+    return KV_ERR_INVALID_ARG;
+  if (coverage != coverage || std::isinf(coverage)) return KV_ERR_INVALID_ARG;
+  const bool cov = coverage >= 0.f;
+  if (!cov && (!(keep_frac >= 0.f) || !std::isfinite(keep_frac))) return KV_ERR_INVALID_ARG;
+  if (cov && k_max < 1) return KV_ERR_INVALID_ARG;
+  if (num_splits > kvs::kMaxSplits) return KV_ERR_UNSUPPORTED;
+  if (B == 0) return KV_OK;
+  if (max_pages > kvs::kMaxTopkPages) return KV_ERR_UNSUPPORTED;
+  if (!q || !block_table || !seq_lens || !sel_count || !out || !lse) return KV_ERR_INVALID_ARG;
+  if (k_max > 0 && !sel) return KV_ERR_INVALID_ARG;
+  if (max_pages > 0 && (!head_scores || !lse_partial)) return KV_ERR_INVALID_ARG;
+  if (!cov && k_max < topk_bound(max_pages, keep_frac, k_fixed)) return KV_ERR_INVALID_ARG;
+  if (!aligned16(q)) return KV_ERR_INVALID_ARG;
+  rc = check_pages(L, pg);
+  if (rc) return rc;
+  const int rows = B * L->num_kv_heads;
+  if ((int64_t)rows > 65535) return KV_ERR_UNSUPPORTED;
+  const int s = num_splits > 0 ? num_splits : auto_splits(rows, k_max, pg->page_entry != nullptr);
+  if (kvs::topk_attn_dyn_lds_bytes(*L, max_pages, k_max, s) > kvs::kTopkAttnMaxLds) return KV_ERR_UNSUPPORTED;
+  const size_t need = kv_sparse_decode_attn_workspace_size(L, B, k_max, s);
+  if (!ws || ws_bytes < need) return KV_ERR_WORKSPACE;
+  return from_hip(kvs::launch_topk_sparse_attn(*L, q, *pg, block_table, seq_lens, B, max_pages, head_scores,
+                                               lse_partial, cov ? 0.f : keep_frac, cov ? 0 : k_fixed,
+                                               cov ? coverage : -1.f, n_force_first, n_force_last, sel,
+                                               sel_count, k_max, page_S, s, scale_of(L), out, lse, (float*)ws,
+                                               (hipStream_t)stream));
+}
+
 size_t kv_hot_admit_workspace_size(int32_t n_slots) {
   return n_slots > 0 ? kvs::hot_admit_workspace_bytes(n_slots) : 0;
 }

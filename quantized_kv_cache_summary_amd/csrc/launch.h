@@ -89,6 +89,20 @@ hipError_t launch_sparse_attn(const kv_layout& L, const void* q, const kv_pages&
                               int n_splits, float tau, float* out, float* lse, float* partials,
                               hipStream_t st);
 
+// Fused selector + attention: every block of a row selects the row's pages
+// (as launch_page_topk) and attends over its split's slice of them.  Dynamic
+// LDS: the slice, then the selector's state and the row's keys, reused by the
+// attention afterwards.  Kept under 64 KB (the fused call refuses larger).
+size_t topk_attn_dyn_lds_bytes(const kv_layout& L, int max_pages, int k_max, int n_splits);
+constexpr size_t kTopkAttnMaxLds = 64 * 1024 - 64;
+
+hipError_t launch_topk_sparse_attn(const kv_layout& L, const void* q, const kv_pages& pg,
+                                   const int32_t* block_table, const int32_t* seq_lens, int B, int max_pages,
+                                   const float* head_scores, const float* lse_partial, float keep, int k_fixed,
+                                   float coverage, int n_force_first, int n_force_last, int32_t* sel,
+                                   int32_t* sel_count, int k_max, float* page_S, int n_splits, float tau,
+                                   float* out, float* lse, float* partials, hipStream_t st);
+
 hipError_t launch_dequant_tier(const kv_layout& L, const kv_pages& pg, const int32_t* pages, int n,
                                float* out, hipStream_t st);
 

@@ -20,7 +20,13 @@
 //     probabilities reach it through a 1 KB per-wave LDS tile; acc[head][d/16]
 //     accumulates in float32 FMAs.
 // The four waves merge in LDS; the last block of a row to finish (a counter per
-// row in the workspace) merges the row's splits into out and lse.  Partials
+// row in the workspace) merges the row's splits into out and lse.
+// With SEL the kernel also selects the pages: every block of a row runs the
+// row's exact top-k (select.h) on the head scores in LDS and keeps the slice of
+// the ascending page list its split owns, so the list never makes a round trip
+// through memory and no selector launch sits between score and attention.  The
+// selection is the separate selector's bit for bit, and the pages are dealt to
+// the waves as in the plain kernel, so out and lse are too.  Partials
 // cross blocks through device-coherent stores and loads: a release fence
 // would write back the whole L2 and costs far more than the merge.
 
@@ -28,13 +34,35 @@
 
 #include "device.h"
 #include "launch.h"
+#include "select.h"
 #include "tiers.h"
 
 namespace kvs {
 
-// waves per block: enough that a CU holds four waves per SIMD with few splits
-template <int GM>
-constexpr int attn_waves() { return 4; }
+// Waves per block: four (one per SIMD), which also read the pages.  The fused
+// selector kernel has eight for up to four query heads per KV head (more would
+// spill registers at two waves per SIMD), so that the latency-bound selection
+// runs with two waves per SIMD; only the first four then read pages (a second
+// wave per SIMD finishes its pages well after the first and the block's merge
+// would wait for it).
+template <int GM, bool SEL>
+constexpr int attn_waves() { return SEL && GM <= 4 ? 8 : 4; }
+constexpr int kStreamWaves = 4;
+
+// The attention's LDS: per-wave probability tiles and the wave merge.
+template <int W, int GM, int D>
+struct AttnLds {
+  float ptile[W][16][16];   // [wave][token][head]
+  float wm[W][16], wl[W][16];
+  float wacc[W][GM][D];
+};
+
+// Fused kernel's dynamic LDS, in 32-bit words: the split's share of the
+// selection, then (16-byte aligned) the selector's state and the row's keys,
+// whose space the attention's LDS reuses once the selection is done.
+__host__ __device__ inline int sel_slice_words(int k_max, int n_splits) {
+  return ((k_max + n_splits - 1) / n_splits + 1 + 3) & ~3;
+}
 constexpr int kBatch = 2;   // 16-token chunks per load batch; two batches are in flight
 
 struct PagesDev {
@@ -50,6 +78,19 @@ struct PagesDev {
   const uint16_t* k_hot;
   const uint32_t* kout;
   const uint32_t* vout;
+};
+
+// Selector inputs and outputs of the fused kernel (unused without SEL).
+struct SelArgs {
+  const float* head_scores;   // [rows][G][max_pages]
+  const float* lse_partial;   // [rows][n_tiles][G][2]
+  float keep;
+  int k_fixed;
+  float coverage;             // < 0: budget mode (keep / k_fixed)
+  int n_force_first, n_force_last, n_tiles;
+  int32_t* sel;               // [rows][k_max], written by split 0
+  int32_t* sel_count;         // [rows], written by split 0
+  float* page_S;              // optional [rows][max_pages], written by split 0
 };
 
 template <int T>
@@ -242,22 +283,36 @@ __device__ __forceinline__ void load_native_chunk(ChunkRaw<D>& r, const uint16_t
   }
 }
 
-template <int D, int GM, bool F16, bool TIERED>
-__global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
+template <int D, int GM, bool F16, bool TIERED, bool SEL>
+__global__ __launch_bounds__((64 * attn_waves<GM, SEL>())) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, PagesDev pg, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int Hkv, int G, int P, int max_pages,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int k_max, int n_splits,
     float scale_log2, float* __restrict__ partials, unsigned* __restrict__ counters,
-    float* __restrict__ out, float* __restrict__ lse) {
+    float* __restrict__ out, float* __restrict__ lse, SelArgs sa) {
   constexpr int KS = D / 32;     // MFMA k-steps
   constexpr int EK = D / 4;      // key elements per lane
   constexpr int EV = D / 16;     // value elements per lane
-  constexpr int kAttnWaves = attn_waves<GM>();
+  constexpr int kAttnWaves = attn_waves<GM, SEL>();
   constexpr int kThreads = 64 * kAttnWaves;
+  using ALds = AttnLds<kStreamWaves, GM, D>;
+  using SLds = SelectLds<kThreads>;
 
-  __shared__ float ptile[kAttnWaves][16][16];       // [wave][token][head]
-  __shared__ float wm[kAttnWaves][16], wl[kAttnWaves][16];
-  __shared__ float wacc[kAttnWaves][GM][D];
+  __shared__ typename std::conditional<SEL, char, ALds>::type al_static;
+  extern __shared__ __align__(16) uint32_t sel_lds[];   // SEL only
+  ALds* al;
+  SLds* sshp = nullptr;
+  uint32_t* keys = nullptr;
+  int32_t* mine = nullptr;
+  if constexpr (SEL) {
+    const int off = sel_slice_words(k_max, n_splits);
+    mine = reinterpret_cast<int32_t*>(sel_lds);
+    al = reinterpret_cast<ALds*>(sel_lds + off);
+    sshp = reinterpret_cast<SLds*>(sel_lds + off);
+    keys = sel_lds + off + sizeof(SLds) / sizeof(uint32_t);
+  } else {
+    al = &al_static;
+  }
 
   const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / Hkv, g = row - b * Hkv;
@@ -268,11 +323,20 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
   const int L = seq_lens[b];
   int Np = L > 0 ? (L + P - 1) / P : 0;
   Np = Np < max_pages ? Np : max_pages;
-  int cnt = sel_count[row];
-  cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
-  const int beg = (int)(((long long)split * cnt) / n_splits);
-  const int end = (int)(((long long)(split + 1) * cnt) / n_splits);
-  const int n_mine = end - beg > wave ? (end - beg - wave + kAttnWaves - 1) / kAttnWaves : 0;
+  int cnt;
+  const float* hs_row = nullptr;
+  SelectLoads<kThreads, GM> sld;
+  if constexpr (SEL) {
+    // head scores in flight before anything else is known
+    hs_row = sa.head_scores + (size_t)row * G * max_pages;
+    if (max_pages > 0)
+      select_issue<kThreads, GM>(sld, hs_row, sa.lse_partial + (size_t)row * sa.n_tiles * G * 2, G, max_pages,
+                                 sa.n_tiles);
+    cnt = sa.coverage >= 0.f ? (Np > 0 ? 1 : 0) : selection_count(Np, sa.keep, sa.k_fixed);
+  } else {
+    cnt = sel_count[row];
+    cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
+  }
 
   // B operand: query head `col`, at k-step s the elements [32s + 8grp, +8)
   // (the same assignment as the key rows); heads past G are zero.
@@ -289,6 +353,47 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
     }
   }
 
+  // SEL: the row's selection (identical in every block of the row); split 0
+  // publishes it, every block keeps its own slice in LDS
+  if constexpr (SEL) {
+    SLds& ssh = *sshp;
+    const bool writer = split == 0;
+    const bool cov = sa.coverage >= 0.f;
+    SelectStats sst{};
+    if (cnt > 0) {
+      sst = select_keys<kThreads, GM>(ssh, keys, sld, hs_row, G, max_pages, sa.n_tiles, Np, sa.n_force_first,
+                                      sa.n_force_last,
+                                      writer && sa.page_S ? sa.page_S + (size_t)row * max_pages : nullptr, cov);
+      if (cov) {
+        cnt = select_coverage_k<kThreads>(ssh, keys, Np, sst, sa.coverage, k_max);
+        __syncthreads();             // every wave is done with the histograms
+        if (threadIdx.x < 256) ssh.hist[0][threadIdx.x] = 0;
+        __syncthreads();
+      }
+    }
+    int32_t* sout = sa.sel + (size_t)row * k_max;
+    if (writer) {
+      for (int i = cnt + (int)threadIdx.x; i < k_max; i += kThreads) sout[i] = -1;
+      if (threadIdx.x == 0) sa.sel_count[row] = cnt;
+    }
+    if (cnt > 0) {
+      const int lo = (int)(((long long)split * cnt) / n_splits);
+      const int hi = (int)(((long long)(split + 1) * cnt) / n_splits);
+      uint32_t T;
+      int take;
+      select_kth<kThreads>(ssh, keys, Np, sst, cnt, T, take);
+      select_compact<kThreads>(ssh, keys, Np, T, take, [&](int p, int pos) {
+        if (writer && pos < cnt) sout[pos] = p;
+        if (pos >= lo && pos < hi) mine[pos - lo] = p;
+      });
+    }
+    __syncthreads();
+  }
+  const int beg = (int)(((long long)split * cnt) / n_splits);
+  const int end = (int)(((long long)(split + 1) * cnt) / n_splits);
+  const int n_mine =
+      wave < kStreamWaves && end - beg > wave ? (end - beg - wave + kStreamWaves - 1) / kStreamWaves : 0;
+
   AttnState<D, GM> st;
   st.m_run = -INFINITY;
   st.l_run = 0.f;
@@ -297,11 +402,11 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
 #pragma unroll
     for (int e = 0; e < EV; ++e) st.acc[h][e] = 0.f;
 
-  const int32_t* srow = sel + (size_t)row * k_max;
+  const int32_t* srow = SEL ? nullptr : sel + (size_t)row * k_max;
   const int32_t* bt = block_table + (size_t)b * max_pages;
   const size_t page_elems = (size_t)P * D;
   const int cpp = P / 16;   // 16-token chunks per page
-  float (*pt)[16] = ptile[wave];
+  float (*pt)[16] = al->ptile[wave < kStreamWaves ? wave : 0];   // used by streaming waves only
 
   if constexpr (!TIERED) {
     for (int j0 = 0; j0 < n_mine; j0 += 64) {
@@ -310,7 +415,8 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
       int l_p = -1, l_hot = -1;
       uint32_t l_tier = 0, l_slot = 0;
       if (lane < nb) {
-        const int p = srow[beg + wave + kAttnWaves * (j0 + lane)];
+        const int li = wave + kStreamWaves * (j0 + lane);
+        const int p = SEL ? mine[li] : srow[beg + li];
         if (p >= 0 && p < Np) {
           l_p = p;
           const int phys = bt[p];
@@ -404,7 +510,8 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
       int l_p = -1, l_hot = -1;
       uint32_t l_tier = 7, l_slot = 0;   // 7: not a valid entry
       if (lane < nb) {
-        const int p = srow[beg + wave + kAttnWaves * (j0 + lane)];
+        const int li = wave + kStreamWaves * (j0 + lane);
+        const int p = SEL ? mine[li] : srow[beg + li];
         if (p >= 0 && p < Np) {
           l_p = p;
           const int phys = bt[p];
@@ -556,12 +663,12 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
       a += __shfl_xor(a, 32);
       st.acc[h][e] = a;
     }
-  if (lane < 16) { wm[wave][lane] = st.m_run; wl[wave][lane] = l_run; }
-  if (grp == 0) {
+  if (wave < kStreamWaves && lane < 16) { al->wm[wave][lane] = st.m_run; al->wl[wave][lane] = l_run; }
+  if (wave < kStreamWaves && grp == 0) {
 #pragma unroll
     for (int h = 0; h < GM; ++h)
 #pragma unroll
-      for (int e = 0; e < EV; ++e) wacc[wave][h][col * EV + e] = st.acc[h][e];
+      for (int e = 0; e < EV; ++e) al->wacc[wave][h][col * EV + e] = st.acc[h][e];
   }
   __syncthreads();
 
@@ -571,14 +678,14 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
     const int h = idx / D, e = idx - h * D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = nan_max(M, wm[w][h]);
+    for (int w = 0; w < kStreamWaves; ++w) M = nan_max(M, al->wm[w][h]);
     float a = 0.f, l = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float f = exp2f(wm[w][h] - M);
-        a += wacc[w][h][e] * f;
-        l += wl[w][h] * f;
+      for (int w = 0; w < kStreamWaves; ++w) {
+        const float f = exp2f(al->wm[w][h] - M);
+        a += al->wacc[w][h][e] * f;
+        l += al->wl[w][h] * f;
       }
     }
     // device-coherent stores (written through to the chip's coherence point),
@@ -637,38 +744,56 @@ __global__ __launch_bounds__(64 * attn_waves<GM>()) void sparse_attn_kernel(
   if (threadIdx.x == 0) __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int GM, bool F16, bool TIERED>
-static hipError_t launch_attn_t(const kv_layout& L, const void* q, const PagesDev& pd,
-                                const int32_t* bt, const int32_t* sl, int B, int max_pages,
-                                const int32_t* sel, const int32_t* cnt, int k_max, int n_splits,
-                                float tau, float* out, float* lse, float* partials, hipStream_t st) {
+// Arguments shared by every instantiation's launch.
+struct AttnLaunch {
+  const void* q;
+  PagesDev pd;
+  const int32_t* bt;
+  const int32_t* sl;
+  int B, max_pages;
+  const int32_t* sel;
+  const int32_t* cnt;
+  int k_max, n_splits;
+  float tau;
+  float* out;
+  float* lse;
+  float* partials;
+  SelArgs sa;
+  size_t dyn_lds;
+};
+
+template <int D, int GM, bool F16, bool TIERED, bool SEL>
+static hipError_t launch_attn_t(const kv_layout& L, const AttnLaunch& a, hipStream_t st) {
   const int G = L.num_q_heads / L.num_kv_heads;
-  const int rows = B * L.num_kv_heads;
-  unsigned* counters = reinterpret_cast<unsigned*>(partials + attn_partial_floats(rows, n_splits, G, D));
-  hipLaunchKernelGGL((sparse_attn_kernel<D, GM, F16, TIERED>), dim3(n_splits, rows), dim3(64 * attn_waves<GM>()), 0, st,
-                     (const uint16_t*)q, pd, bt, sl, L.num_kv_heads, G, L.page_size, max_pages, sel, cnt,
-                     k_max, n_splits, tau * kLog2e, partials, counters, out, lse);
+  const int rows = a.B * L.num_kv_heads;
+  unsigned* counters = reinterpret_cast<unsigned*>(a.partials + attn_partial_floats(rows, a.n_splits, G, D));
+  hipLaunchKernelGGL((sparse_attn_kernel<D, GM, F16, TIERED, SEL>), dim3(a.n_splits, rows),
+                     dim3(64 * attn_waves<GM, SEL>()), a.dyn_lds, st, (const uint16_t*)a.q, a.pd, a.bt, a.sl,
+                     L.num_kv_heads, G, L.page_size, a.max_pages, a.sel, a.cnt, a.k_max, a.n_splits,
+                     a.tau * kLog2e, a.partials, counters, a.out, a.lse, a.sa);
   return hipGetLastError();
 }
 
-template <int D, bool F16, bool TIERED>
-static hipError_t launch_attn_g(const kv_layout& L, const void* q, const PagesDev& pd,
-                                const int32_t* bt, const int32_t* sl, int B, int max_pages,
-                                const int32_t* sel, const int32_t* cnt, int k_max, int n_splits,
-                                float tau, float* out, float* lse, float* partials, hipStream_t st) {
+template <int D, bool F16, bool TIERED, bool SEL>
+static hipError_t launch_attn_g(const kv_layout& L, const AttnLaunch& a, hipStream_t st) {
   const int G = L.num_q_heads / L.num_kv_heads;
-  if (G <= 4) return launch_attn_t<D, 4, F16, TIERED>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
-  if (G <= 8) return launch_attn_t<D, 8, F16, TIERED>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
-  return launch_attn_t<D, 16, F16, TIERED>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
+  if (G <= 4) return launch_attn_t<D, 4, F16, TIERED, SEL>(L, a, st);
+  if (G <= 8) return launch_attn_t<D, 8, F16, TIERED, SEL>(L, a, st);
+  return launch_attn_t<D, 16, F16, TIERED, SEL>(L, a, st);
 }
 
-template <int D, bool F16>
-static hipError_t launch_attn_d(const kv_layout& L, const void* q, const PagesDev& pd, bool tiered,
-                                const int32_t* bt, const int32_t* sl, int B, int max_pages,
-                                const int32_t* sel, const int32_t* cnt, int k_max, int n_splits,
-                                float tau, float* out, float* lse, float* partials, hipStream_t st) {
-  if (tiered) return launch_attn_g<D, F16, true>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
-  return launch_attn_g<D, F16, false>(L, q, pd, bt, sl, B, max_pages, sel, cnt, k_max, n_splits, tau, out, lse, partials, st);
+template <bool SEL>
+static hipError_t launch_attn_any(const kv_layout& L, const AttnLaunch& a, bool tiered, hipStream_t st) {
+  const bool f16 = L.kv_dtype == KV_F16;
+#define KVS_ATTN(D_, F16_)                                                              \
+  return tiered ? launch_attn_g<D_, F16_, true, SEL>(L, a, st) : launch_attn_g<D_, F16_, false, SEL>(L, a, st)
+  if (L.head_dim == 64) {
+    if (f16) KVS_ATTN(64, true);
+    KVS_ATTN(64, false);
+  }
+  if (f16) KVS_ATTN(128, true);
+  KVS_ATTN(128, false);
+#undef KVS_ATTN
 }
 
 static PagesDev to_dev(const kv_pages& pg) {
@@ -695,14 +820,39 @@ hipError_t launch_sparse_attn(const kv_layout& L, const void* q, const kv_pages&
                               int max_pages, const int32_t* sel, const int32_t* sel_count, int k_max,
                               int n_splits, float tau, float* out, float* lse, float* partials,
                               hipStream_t st) {
-  const PagesDev pd = to_dev(pg);
-  const bool tiered = pg.page_entry != nullptr;
-  const bool f16 = L.kv_dtype == KV_F16;
+  AttnLaunch a{q, to_dev(pg), block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits,
+               tau, out, lse, partials, SelArgs{}, 0};
+  return launch_attn_any<false>(L, a, pg.page_entry != nullptr, st);
+}
+
+template <int D, int GM>
+static size_t sel_dyn_bytes(int max_pages, int k_max, int n_splits) {
+  constexpr int W = attn_waves<GM, true>();
+  const size_t sel = sizeof(SelectLds<64 * W>) + (size_t)(max_pages > 0 ? max_pages : 1) * sizeof(uint32_t);
+  const size_t att = sizeof(AttnLds<kStreamWaves, GM, D>);
+  return (size_t)sel_slice_words(k_max, n_splits) * sizeof(uint32_t) + (sel > att ? sel : att);
+}
+
+size_t topk_attn_dyn_lds_bytes(const kv_layout& L, int max_pages, int k_max, int n_splits) {
+  const int G = L.num_q_heads / L.num_kv_heads;
   if (L.head_dim == 64)
-    return f16 ? launch_attn_d<64, true>(L, q, pd, tiered, block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits, tau, out, lse, partials, st)
-               : launch_attn_d<64, false>(L, q, pd, tiered, block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits, tau, out, lse, partials, st);
-  return f16 ? launch_attn_d<128, true>(L, q, pd, tiered, block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits, tau, out, lse, partials, st)
-             : launch_attn_d<128, false>(L, q, pd, tiered, block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits, tau, out, lse, partials, st);
+    return G <= 4 ? sel_dyn_bytes<64, 4>(max_pages, k_max, n_splits)
+                  : (G <= 8 ? sel_dyn_bytes<64, 8>(max_pages, k_max, n_splits) : sel_dyn_bytes<64, 16>(max_pages, k_max, n_splits));
+  return G <= 4 ? sel_dyn_bytes<128, 4>(max_pages, k_max, n_splits)
+                : (G <= 8 ? sel_dyn_bytes<128, 8>(max_pages, k_max, n_splits) : sel_dyn_bytes<128, 16>(max_pages, k_max, n_splits));
+}
+
+hipError_t launch_topk_sparse_attn(const kv_layout& L, const void* q, const kv_pages& pg,
+                                   const int32_t* block_table, const int32_t* seq_lens, int B, int max_pages,
+                                   const float* head_scores, const float* lse_partial, float keep, int k_fixed,
+                                   float coverage, int n_force_first, int n_force_last, int32_t* sel,
+                                   int32_t* sel_count, int k_max, float* page_S, int n_splits, float tau,
+                                   float* out, float* lse, float* partials, hipStream_t st) {
+  SelArgs sa{head_scores, lse_partial, keep, k_fixed, coverage, n_force_first, n_force_last,
+             score_tiles(max_pages), sel, sel_count, page_S};
+  AttnLaunch a{q, to_dev(pg), block_table, seq_lens, B, max_pages, nullptr, nullptr, k_max, n_splits,
+               tau, out, lse, partials, sa, topk_attn_dyn_lds_bytes(L, max_pages, k_max, n_splits)};
+  return launch_attn_any<true>(L, a, pg.page_entry != nullptr, st);
 }
 
 // ---------------------------------------------------------------- standalone decode

@@ -355,11 +355,41 @@ def attend(layer: DeviceLayer, q, bufs: StepBuffers, sel=None, sel_count=None, s
                           bufs.out, bufs.lse, bufs.ws, bufs.num_splits, stream)
 
 
-def decode_step(layer: DeviceLayer, q, bufs: StepBuffers, stream=None):
-    """score -> top-k -> sparse attention for one layer of the whole batch."""
+def fused_supported(layer: DeviceLayer, bufs: StepBuffers):
+    w = layer.w
+    s = bufs.num_splits or kv.attn_num_splits(layer.L, w.B, bufs.sel.shape[-1], layer.page_entry is not None)
+    return kv.topk_attn_supported(layer.L, w.Np, bufs.sel.shape[-1], s)
+
+
+def fused_preferred(layer: DeviceLayer, bufs: StepBuffers):
+    """Where the fused top-k + attention call is the faster step: native pages,
+    up to four query heads per KV head (eight-wave blocks) and rows under 4096
+    pages.  Packed tiers want two blocks per CU, and long rows or wider groups
+    select too slowly inside one block; there the separate launches win."""
+    w = layer.w
+    return (layer.page_entry is None and w.G <= 4 and w.Np < 4096 and fused_supported(layer, bufs))
+
+
+def topk_attend(layer: DeviceLayer, q, bufs: StepBuffers, n_force_first=0, n_force_last=0, coverage=-1.0,
+                stream=None):
+    """top-k and sparse attention in one launch (the same results as topk + attend)."""
+    w = layer.w
+    kv.topk_sparse_decode_attn(layer.L, q, layer.pages, layer.bt, layer.seq_lens, bufs.head_scores,
+                               bufs.lse_partial, bufs.sel, bufs.sel_count, bufs.out, bufs.lse, bufs.ws,
+                               keep_frac=w.keep, k_fixed=w.k_fixed, coverage=coverage,
+                               n_force_first=n_force_first, n_force_last=n_force_last, page_S=bufs.page_S,
+                               num_splits=bufs.num_splits, stream=stream)
+
+
+def decode_step(layer: DeviceLayer, q, bufs: StepBuffers, stream=None, fused=False):
+    """score -> top-k -> sparse attention for one layer of the whole batch
+    (fused: top-k and attention in one launch)."""
     score(layer, q, bufs, stream)
-    topk(layer, bufs, stream=stream)
-    attend(layer, q, bufs, stream=stream)
+    if fused:
+        topk_attend(layer, q, bufs, stream=stream)
+    else:
+        topk(layer, bufs, stream=stream)
+        attend(layer, q, bufs, stream=stream)
 
 
 # ------------------------------------------------------------------ overlapped row groups
@@ -377,9 +407,10 @@ class SplitStep:
     pointers offset to that group's sequences (no library change).  All
     streams keep the default priority."""
 
-    def __init__(self, layer: DeviceLayer, bufs: StepBuffers, n_groups=2, num_splits=0):
+    def __init__(self, layer: DeviceLayer, bufs: StepBuffers, n_groups=2, num_splits=0, fused=False):
         w = layer.w
         self.layer, self.bufs = layer, bufs
+        self.fused = fused
         n_groups = max(1, min(n_groups, w.B))
         edges = [round(i * w.B / n_groups) for i in range(n_groups + 1)]
         self.streams = [torch.cuda.Stream() for _ in range(n_groups)]
@@ -420,6 +451,12 @@ class SplitStep:
                                         v.lse_partial, s)
                 else:
                     kv.page_score(layer.L, qg, v.summary, v.log_n, v.seq_lens, v.head_scores, v.lse_partial, s)
+                if self.fused:
+                    kv.topk_sparse_decode_attn(layer.L, qg, layer.pages, v.bt, v.seq_lens, v.head_scores,
+                                               v.lse_partial, v.sel, v.sel_count, v.out, v.lse, v.ws,
+                                               keep_frac=w.keep, k_fixed=w.k_fixed, page_S=v.page_S,
+                                               num_splits=self.num_splits, stream=s)
+                    continue
                 kv.page_topk(layer.L, v.head_scores, v.lse_partial, v.seq_lens, w.Np, w.keep, w.k_fixed,
                              v.sel, v.sel_count, 0, 0, v.page_S, None, s)
                 kv.sparse_decode_attn(layer.L, qg, layer.pages, v.bt, v.seq_lens, v.sel, v.sel_count,

@@ -28,7 +28,8 @@ SYMBOLS = (
     "kv_sparse_decode_attn_num_splits", "kv_dequant_tier", "kv_pack_tier", "kv_status_string",
     "kv_basis_build", "kv_basis_build_workspace_size", "kv_summary_build_basis", "kv_page_score_basis",
     "kv_page_topk_coverage", "kv_hot_admit", "kv_hot_admit_workspace_size", "kv_tier_plan", "kv_tier_demote",
-    "kv_lowrank_coords", "kv_page_score_lowrank",
+    "kv_lowrank_coords", "kv_page_score_lowrank", "kv_topk_sparse_decode_attn",
+    "kv_topk_sparse_decode_attn_supported",
 )
 
 
@@ -88,6 +89,10 @@ def lib():
             "kv_sparse_decode_attn": (_I, [_LP, _P, _PP, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _P,
                                            _SZ, _P]),
             "kv_sparse_decode_attn_workspace_size": (_SZ, [_LP, _I, _I, _I]),
+            "kv_topk_sparse_decode_attn": (_I, [_LP, _P, _PP, _P, _P, _I, _I, _P, _P, ctypes.c_float, _I,
+                                                ctypes.c_float, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _SZ,
+                                                _P]),
+            "kv_topk_sparse_decode_attn_supported": (_I, [_LP, _I, _I, _I]),
             "kv_sparse_decode_attn_num_splits": (_I, [_LP, _I, _I, _I]),
             "kv_dequant_tier": (_I, [_LP, _PP, _P, _I, _P, _P]),
             "kv_pack_tier": (_I, [_LP, _P, _P, _I, _I, _P, _P, _P, _P, _P]),
@@ -302,6 +307,26 @@ def sparse_decode_attn(L, q, pages, block_table, seq_lens, sel, sel_count, out, 
                                      0 if ws is None else ws.numel() * ws.element_size(),
                                      _stream(stream))
     _check(rc, "kv_sparse_decode_attn")
+
+
+def topk_attn_supported(L, max_pages, k_max, num_splits):
+    return bool(lib().kv_topk_sparse_decode_attn_supported(ctypes.byref(L), int(max_pages), int(k_max),
+                                                           int(num_splits)))
+
+
+def topk_sparse_decode_attn(L, q, pages, block_table, seq_lens, head_scores, lse_partial, sel, sel_count,
+                            out, lse, ws, keep_frac=0.0, k_fixed=0, coverage=-1.0, n_force_first=0,
+                            n_force_last=0, page_S=None, num_splits=0, stream=None):
+    """Selector and sparse attention in one launch; coverage < 0 selects by
+    keep_frac / k_fixed, coverage >= 0 by mass coverage (sel's row length is the cap)."""
+    B, max_pages = block_table.shape
+    k_max = sel.shape[-1]
+    rc = lib().kv_topk_sparse_decode_attn(
+        ctypes.byref(L), _p(q), ctypes.byref(pages), _p(block_table), _p(seq_lens), int(B), int(max_pages),
+        _p(head_scores), _p(lse_partial), float(keep_frac), int(k_fixed), float(coverage), int(n_force_first),
+        int(n_force_last), _p(sel), _p(sel_count), int(k_max), _p(page_S), int(num_splits), _p(out), _p(lse),
+        _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "kv_topk_sparse_decode_attn")
 
 
 def dequant_tier(L, pages, page_ids, out, stream=None):

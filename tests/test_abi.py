@@ -147,6 +147,43 @@ def test_attention_validation_and_workspace():
     assert call(pages=ko) == kv.KV_ERR_INVALID_ARG                  # K outlier table without V's
 
 
+def test_fused_topk_attention_validation():
+    L = _L()
+    pg = kv.KvPages()
+    pg.k16 = FAKE
+    pg.v16 = FAKE
+    f = kv.lib().kv_topk_sparse_decode_attn
+    s = kv.attn_num_splits(L, 8, 164)
+    need = kv.attn_workspace_size(L, 8, 164, s)
+
+    def call(L=L, pages=pg, max_pages=2048, keep=0.08, k_fixed=0, coverage=-1.0, k_max=164, sel=FAKE,
+             hs=FAKE, splits=0, ws=FAKE, ws_bytes=need, q=FAKE):
+        return f(ctypes.byref(L), q, ctypes.byref(pages) if pages is not None else None, FAKE, FAKE, 8,
+                 max_pages, hs, FAKE, keep, k_fixed, coverage, 0, 0, sel, FAKE, k_max, None, splits, FAKE,
+                 FAKE, ws, ws_bytes, None)
+
+    assert call(ws_bytes=need - 1) == kv.KV_ERR_WORKSPACE
+    assert call(ws=None) == kv.KV_ERR_WORKSPACE
+    assert call(k_max=163) == kv.KV_ERR_INVALID_ARG                 # ceil(0.08 * 2048) = 164
+    assert call(keep=float("nan")) == kv.KV_ERR_INVALID_ARG
+    assert call(coverage=float("nan")) == kv.KV_ERR_INVALID_ARG
+    assert call(coverage=float("inf")) == kv.KV_ERR_INVALID_ARG
+    assert call(coverage=0.9, k_max=0, sel=None) == kv.KV_ERR_INVALID_ARG
+    assert call(sel=None) == kv.KV_ERR_INVALID_ARG
+    assert call(hs=None) == kv.KV_ERR_INVALID_ARG
+    assert call(pages=None) == kv.KV_ERR_INVALID_ARG
+    assert call(q=FAKE + 8) == kv.KV_ERR_INVALID_ARG
+    assert call(splits=300) == kv.KV_ERR_UNSUPPORTED
+    assert call(max_pages=15361, k_max=15361) == kv.KV_ERR_UNSUPPORTED
+    # the row's keys and a split's share of the selection must fit one block's LDS
+    assert kv.topk_attn_supported(L, 2048, 164, s)
+    assert kv.topk_attn_supported(_L(num_q_heads=128), 2048, 2048, 1)
+    assert not kv.topk_attn_supported(L, 15360, 15360, 1)
+    assert call(max_pages=15360, k_max=15360, keep=1.0, splits=1,
+                ws_bytes=kv.attn_workspace_size(L, 8, 15360, 1)) == kv.KV_ERR_UNSUPPORTED
+    assert not kv.topk_attn_supported(L, 2048, 164, 0)
+
+
 def test_pack_build_dequant_validation():
     L = _L()
     lib = kv.lib()
