@@ -189,6 +189,9 @@ __device__ SelectStats select_keys(SelectLds<NT>& sh, uint32_t* keys, SelectLoad
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
   int npos = 0, nneg = 0;
   unsigned long long fmass = 0ull;
+  // Straight-line per page (selects, no branches): head slots past G enter as
+  // -inf, whose exp is an exact +0 at the end of the sum, so S is the same as
+  // over the G heads alone; NaN and all -inf rows are patched in afterwards.
   for (int r0 = 0; r0 < Np; r0 += NT * U) {
     const bool more = r0 + NT * U < Np;
     float nx[U][GM];
@@ -196,40 +199,35 @@ __device__ SelectStats select_keys(SelectLds<NT>& sh, uint32_t* keys, SelectLoad
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = r0 + tid + u * NT;
-      if (p >= Np) break;
+      const bool live = p < Np;
       float x[GM];
       float M = -INFINITY;
       bool nan = false;
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-          x[h] = ld.v[u][h] - Lr[h];
-          nan |= x[h] != x[h];
-          M = fmaxf(M, x[h]);
-        }
+        x[h] = h < G ? ld.v[u][h] - Lr[h] : -INFINITY;
+        nan |= x[h] != x[h];
+        M = fmaxf(M, x[h]);
       }
-      float S;
-      if (nan) S = __int_as_float(0x7FC00000);
-      else if (M == -INFINITY) S = -INFINITY;
-      else {
-        float sum = 0.f;
+      float sum = 0.f;
 #pragma unroll
-        for (int h = 0; h < GM; ++h) if (h < G) sum += __expf(x[h] - M);
-        S = M + __logf(sum) - logG;
-      }
-      if (p < n_force_first || p >= Np - n_force_last) {
-        if (with_mass) fmass += mass_fixed(S);
-        S = INFINITY;
-      }
+      for (int h = 0; h < GM; ++h) sum += __expf(x[h] - M);
+      float S = M + __logf(sum) - logG;
+      S = M == -INFINITY ? -INFINITY : S;
+      S = nan ? __int_as_float(0x7FC00000) : S;
+      const bool forced = p < n_force_first || p >= Np - n_force_last;
+      if (with_mass && live && forced) fmass += mass_fixed(S);
+      S = forced ? INFINITY : S;
       const uint32_t key = order_key(S);
-      keys[p] = key;
-      if (finite_key(key)) {
-        kmax = key > kmax ? key : kmax;
-        kmin = key < kmin ? key : kmin;
+      if (live) {
+        keys[p] = key;
+        if (page_S_row) page_S_row[p] = S;
       }
-      npos += key == kKeyPosInf;
-      nneg += key == kKeyNegInf;
-      if (page_S_row) page_S_row[p] = S;
+      const bool fin = live && finite_key(key);
+      kmax = fin && key > kmax ? key : kmax;
+      kmin = fin && key < kmin ? key : kmin;
+      npos += live && key == kKeyPosInf;
+      nneg += live && key == kKeyNegInf;
     }
     if (more) {
 #pragma unroll
@@ -241,9 +239,8 @@ __device__ SelectStats select_keys(SelectLds<NT>& sh, uint32_t* keys, SelectLoad
   if (with_mass && fmass) atomicAdd(&sh.forced_mass, fmass);
   kmax = wave_max_u32(kmax);
   kmin = wave_min_u32(kmin);
-  npos = wave_sum_i32(npos);
-  nneg = wave_sum_i32(nneg);
-  if (lane == 0) { sh.wmax[wave] = kmax; sh.wmin[wave] = kmin; sh.wpos[wave] = npos; sh.wneg[wave] = nneg; }
+  const int pn = wave_sum_i32((npos << 16) | nneg);   // both counts < 2^15: one packed sum
+  if (lane == 0) { sh.wmax[wave] = kmax; sh.wmin[wave] = kmin; sh.wpos[wave] = pn >> 16; sh.wneg[wave] = pn & 0xFFFF; }
   __syncthreads();
   SelectStats st;
   st.kmax = sh.wmax[0];
