@@ -423,7 +423,7 @@ def main():
         blayers = [l.with_basis_summaries() for l in layers]
         torch.cuda.synchronize()
         log(f"[bench] shared-basis summaries built in {time.time() - t0:.1f}s")
-        bsteps = [hz.SplitStep(blayers[i], bufs[i], 1) for i in range(n_layers)]
+        bsteps = [hz.SplitStep(blayers[i], bufs[i], 1, fused=fused) for i in range(n_layers)]
         n_cap = n_layers * min(args.queries, 4)
         for i in range(args.warmup):
             bsteps[i % n_layers](qs[i % n_layers][(i // n_layers) % args.queries])
@@ -453,8 +453,9 @@ def main():
             "algorithmic_bytes_per_step": {"summaries": bsum, "selected_kv": bselb},
             "score_kernel": {"avg_launch_us": bscore_us, "achieved_GBps": bsum / (bscore_us * 1e3),
                              "frac": bsum / (bscore_us * 1e3) / HBM_PEAK_GBS},
-            "note": "same layers, queries and attention; summaries = shared row basis + per-page mean "
-                    "and variances (not the headline's per-page directions)",
+            "note": "same layers, queries, selection and attention (fused as in the headline step); "
+                    "summaries = shared row basis + per-page mean and variances (not the headline's "
+                    "per-page directions)",
         }
     if not args.no_basis and tiers is None:
         # the r8 low-rank score (per-key coordinates in a rank-8 row basis) on
@@ -463,15 +464,15 @@ def main():
         rlayers = [l.with_lowrank_summaries() for l in layers]
         torch.cuda.synchronize()
         log(f"[bench] r8 state built in {time.time() - t0:.1f}s")
-        rsteps = [hz.SplitStep(rlayers[i], bufs[i], 1) for i in range(n_layers)]
         for i in range(args.warmup):
-            hz.decode_step(rlayers[i % n_layers], qs[i % n_layers][(i // n_layers) % args.queries], bufs[i % n_layers])
+            hz.decode_step(rlayers[i % n_layers], qs[i % n_layers][(i // n_layers) % args.queries], bufs[i % n_layers],
+                           fused=fused)
         n_cap = n_layers * min(args.queries, 4)
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr):
             for i in range(n_cap):
                 hz.decode_step(rlayers[i % n_layers], qs[i % n_layers][(i // n_layers) % args.queries],
-                               bufs[i % n_layers])
+                               bufs[i % n_layers], fused=fused)
         for _ in range(3):
             gr.replay()
         torch.cuda.synchronize()
@@ -494,10 +495,10 @@ def main():
             "effective_GBps": (coord_b + rselb) / (r_ms / 1e3) / 1e9,
             "score_kernel": {"avg_launch_us": rscore_us, "achieved_GBps": coord_b / (rscore_us * 1e3),
                              "frac": coord_b / (rscore_us * 1e3) / HBM_PEAK_GBS},
-            "note": "same layers, queries, selection rule and attention; pages scored by the exact log-mass of "
-                    "their keys' rank-8 approximations (an alternative selector, not the headline's)",
+            "note": "same layers, queries, selection rule and attention (fused as in the headline step); pages "
+                    "scored by the exact log-mass of their keys' rank-8 approximations (an alternative "
+                    "selector, not the headline's)",
         }
-        del rsteps
     # dense line for context: the same attention kernel over every page of
     # every row (k = Np, no score and no selection)
     if tiers is None and not args.no_extras:
