@@ -176,6 +176,11 @@ def main():
     qs = [[hz.queries_device(w, i, j) for j in range(args.queries)] for i in range(n_layers)]
     bufs = [hz.StepBuffers(w, num_splits=args.splits) for _ in range(n_layers)]
     fused = not args.two_kernel and args.groups == 1 and hz.fused_preferred(layers[0], bufs[0])
+    # the headline step is one library call (kv_sparse_decode_step), which takes
+    # the fused or the separate schedule by the same rule as fused_preferred
+    whole = not args.two_kernel and args.groups == 1 and hz.step_supported(layers[0], bufs[0])
+    if whole:
+        assert kv.step_fused(layers[0].L, layers[0].pages, w.B, w.Np, bufs[0].sel.shape[-1], args.splits) == fused
     steps_split = [hz.SplitStep(layers[i], bufs[i], args.groups, num_splits=args.splits, fused=fused)
                    for i in range(n_layers)]
     torch.cuda.synchronize()
@@ -186,7 +191,10 @@ def main():
     def step(i):
         li = i % n_layers
         q = qs[li][(i // n_layers) % args.queries]
-        steps_split[li](q)
+        if whole:
+            hz.whole_step(layers[li], q, bufs[li])
+        else:
+            steps_split[li](q)
 
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -330,6 +338,7 @@ def main():
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
             "page_size": w.P, "ctx": w.ctx, "rank": w.rank, "keep": w.keep, "k_per_row": int(sel_counts.max()),
             "rotated_layers": n_layers, "row_groups_on_streams": args.groups,
+            "step_call": "kv_sparse_decode_step" if whole else "separate calls",
             "topk_attention": "fused (kv_topk_sparse_decode_attn)" if fused else "separate launches",
             "timing": "eager" if args.eager else "hip graph replay",
         },

@@ -366,6 +366,48 @@ int32_t kv_topk_sparse_decode_attn_supported(const kv_layout* layout, int32_t ma
                                              int32_t num_splits);
 
 /* ---------------------------------------------------------------------------
+ * kv_sparse_decode_step -- a whole decode step of one layer in one call
+ * (AMASS page, "Benchmarking": the score, top-B and decode stages of a step):
+ * kv_page_score, then either kv_topk_sparse_decode_attn (one launch) or
+ * kv_page_topk / kv_page_topk_coverage followed by kv_sparse_decode_attn,
+ * whichever is the faster schedule for the shape on MI355X (the fused launch
+ * for native pages, at most four query heads per KV head and rows under 4096
+ * pages; kv_sparse_decode_step_fused says which a call will use).  All
+ * launches go to `stream`.  Outputs are bit-identical to kv_page_score
+ * followed by kv_topk_sparse_decode_attn with the same arguments (which equal
+ * the separate selector and attention calls'): head_scores and lse_partial
+ * (shapes and sizes as kv_page_score's), sel, sel_count, page_S (optional,
+ * may be NULL), out, lse.  coverage < 0 selects by keep_frac / k_fixed,
+ * coverage >= 0 by mass coverage with k_max as the cap (as
+ * kv_topk_sparse_decode_attn).  Every argument follows those calls' rules; in
+ * addition 1 <= max_pages <= 15360.  ws/ws_bytes:
+ * kv_sparse_decode_step_workspace_size(), which is kv_sparse_decode_attn's
+ * workspace for the split count, with the same zeroed counters and the same
+ * rule against overlapping calls.
+ * --------------------------------------------------------------------------- */
+int kv_sparse_decode_step(const kv_layout* layout, const void* q, const void* summary, const float* log_n,
+                          const kv_pages* pages, const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t B, int32_t max_pages, float keep_frac, int32_t k_fixed, float coverage,
+                          int32_t n_force_first, int32_t n_force_last, float* head_scores, float* lse_partial,
+                          int32_t* sel, int32_t* sel_count, int32_t k_max, float* page_S, int32_t num_splits,
+                          float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace for kv_sparse_decode_step: kv_sparse_decode_attn's for
+ * the same arguments; 0 for invalid arguments. */
+size_t kv_sparse_decode_step_workspace_size(const kv_layout* layout, int32_t B, int32_t k_max,
+                                            int32_t num_splits);
+
+/* 1 when kv_sparse_decode_step supports this layout and shape, else 0. */
+int32_t kv_sparse_decode_step_supported(const kv_layout* layout, int32_t B, int32_t max_pages, int32_t k_max,
+                                        int32_t num_splits);
+
+/* 1 when kv_sparse_decode_step uses the fused selector + attention launch
+ * for these arguments, 0 when it uses the separate selector and attention
+ * launches (or the shape is not supported). */
+int32_t kv_sparse_decode_step_fused(const kv_layout* layout, const kv_pages* pages, int32_t B, int32_t max_pages,
+                                    int32_t k_max, int32_t num_splits);
+
+/* ---------------------------------------------------------------------------
  * kv_hot_admit -- hot-buffer admission for a host-resident V pool (AMASS page,
  * "What is in the box" item 2 and the AMASS-mem variant: V in pinned,
  * device-mapped host memory, a bounded resident hot buffer plus a staging

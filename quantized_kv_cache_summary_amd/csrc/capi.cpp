@@ -348,6 +348,79 @@ int kv_topk_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages
                                                (hipStream_t)stream));
 }
 
+size_t kv_sparse_decode_step_workspace_size(const kv_layout* L, int32_t B, int32_t k_max, int32_t num_splits) {
+  return kv_sparse_decode_attn_workspace_size(L, B, k_max, num_splits);
+}
+
+int32_t kv_sparse_decode_step_supported(const kv_layout* L, int32_t B, int32_t max_pages, int32_t k_max,
+                                        int32_t num_splits) {
+  if (check_layout(L) || B < 0 || max_pages < 1 || k_max < 0 || num_splits < 0 || num_splits > kvs::kMaxSplits)
+    return 0;
+  return max_pages <= kvs::kMaxTopkPages ? 1 : 0;
+}
+
+int32_t kv_sparse_decode_step_fused(const kv_layout* L, const kv_pages* pages, int32_t B, int32_t max_pages,
+                                    int32_t k_max, int32_t num_splits) {
+  if (!kv_sparse_decode_step_supported(L, B, max_pages, k_max, num_splits) || !pages) return 0;
+  // measured: the fused selector + attention wins for native pages, up to four
+  // query heads per KV head (eight-wave blocks) and rows under 4096 pages;
+  // packed tiers want two attention blocks per CU, and longer rows or wider
+  // groups select too slowly inside one block
+  if (pages->page_entry || L->num_q_heads / L->num_kv_heads > 4 || max_pages >= kvs::kTopkWideFrom) return 0;
+  const int s = num_splits > 0 ? num_splits : auto_splits(B * L->num_kv_heads, k_max, false);
+  return kvs::topk_attn_dyn_lds_bytes(*L, max_pages, k_max, s) <= kvs::kTopkAttnMaxLds ? 1 : 0;
+}
+
+int kv_sparse_decode_step(const kv_layout* L, const void* q, const void* summary, const float* log_n,
+                          const kv_pages* pg, const int32_t* block_table, const int32_t* seq_lens, int32_t B,
+                          int32_t max_pages, float keep_frac, int32_t k_fixed, float coverage,
+                          int32_t n_force_first, int32_t n_force_last, float* head_scores, float* lse_partial,
+                          int32_t* sel, int32_t* sel_count, int32_t k_max, float* page_S, int32_t num_splits,
+                          float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layout(L);
+  if (rc) return rc;
+  if (B < 0 || max_pages < 0 || k_max < 0 || k_fixed < 0 || n_force_first < 0 || n_force_last < 0 ||
+      num_splits < 0)
+    return KV_ERR_INVALID_ARG;
+  if (coverage != coverage || std::isinf(coverage)) return KV_ERR_INVALID_ARG;
+  const bool cov = coverage >= 0.f;
+  if (!cov && (!(keep_frac >= 0.f) || !std::isfinite(keep_frac))) return KV_ERR_INVALID_ARG;
+  if (cov && k_max < 1) return KV_ERR_INVALID_ARG;
+  if (num_splits > kvs::kMaxSplits) return KV_ERR_UNSUPPORTED;
+  if (B == 0) return KV_OK;
+  if (max_pages == 0) return KV_ERR_INVALID_ARG;
+  if (max_pages > kvs::kMaxTopkPages) return KV_ERR_UNSUPPORTED;
+  if (!q || !summary || !log_n || !block_table || !seq_lens || !head_scores || !lse_partial || !sel_count ||
+      !out || !lse)
+    return KV_ERR_INVALID_ARG;
+  if (k_max > 0 && !sel) return KV_ERR_INVALID_ARG;
+  if (!cov && k_max < topk_bound(max_pages, keep_frac, k_fixed)) return KV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(summary)) return KV_ERR_INVALID_ARG;
+  rc = check_pages(L, pg);
+  if (rc) return rc;
+  const int rows = B * L->num_kv_heads;
+  if ((int64_t)rows > 65535) return KV_ERR_UNSUPPORTED;
+  const bool tiered = pg->page_entry != nullptr;
+  const int s = num_splits > 0 ? num_splits : auto_splits(rows, k_max, tiered);
+  if (!ws || ws_bytes < kv_sparse_decode_attn_workspace_size(L, B, k_max, s)) return KV_ERR_WORKSPACE;
+  const hipStream_t st = (hipStream_t)stream;
+  const float tau = scale_of(L);
+  const float kf = cov ? 0.f : keep_frac, cv = cov ? coverage : -1.f;
+  const int kx = cov ? 0 : k_fixed;
+  rc = from_hip(kvs::launch_page_score(*L, q, summary, log_n, seq_lens, B, max_pages, tau, head_scores,
+                                       lse_partial, st));
+  if (rc) return rc;
+  if (kv_sparse_decode_step_fused(L, pg, B, max_pages, k_max, s))
+    return from_hip(kvs::launch_topk_sparse_attn(*L, q, *pg, block_table, seq_lens, B, max_pages, head_scores,
+                                                 lse_partial, kf, kx, cv, n_force_first, n_force_last, sel,
+                                                 sel_count, k_max, page_S, s, tau, out, lse, (float*)ws, st));
+  rc = from_hip(kvs::launch_page_topk(*L, head_scores, lse_partial, seq_lens, B, max_pages, kf, kx, cv,
+                                      n_force_first, n_force_last, sel, sel_count, k_max, page_S, st));
+  if (rc) return rc;
+  return from_hip(kvs::launch_sparse_attn(*L, q, *pg, block_table, seq_lens, B, max_pages, sel, sel_count, k_max,
+                                          s, tau, out, lse, (float*)ws, st));
+}
+
 size_t kv_hot_admit_workspace_size(int32_t n_slots) {
   return n_slots > 0 ? kvs::hot_admit_workspace_bytes(n_slots) : 0;
 }

@@ -30,258 +30,10 @@
 // cross blocks through device-coherent stores and loads: a release fence
 // would write back the whole L2 and costs far more than the merge.
 
-#include <type_traits>
-
-#include "device.h"
-#include "launch.h"
+#include "attn_split.h"
 #include "select.h"
-#include "tiers.h"
 
 namespace kvs {
-
-// Waves per block: four (one per SIMD), which also read the pages.  The fused
-// selector kernel has eight for up to four query heads per KV head (more would
-// spill registers at two waves per SIMD), so that the latency-bound selection
-// runs with two waves per SIMD; only the first four then read pages (a second
-// wave per SIMD finishes its pages well after the first and the block's merge
-// would wait for it).
-template <int GM, bool SEL>
-constexpr int attn_waves() { return SEL && GM <= 4 ? 8 : 4; }
-constexpr int kStreamWaves = 4;
-
-// The attention's LDS: per-wave probability tiles and the wave merge.
-template <int W, int GM, int D>
-struct AttnLds {
-  float ptile[W][16][16];   // [wave][token][head]
-  float wm[W][16], wl[W][16];
-  float wacc[W][GM][D];
-};
-
-// Fused kernel's dynamic LDS, in 32-bit words: the split's share of the
-// selection, then (16-byte aligned) the selector's state and the row's keys,
-// whose space the attention's LDS reuses once the selection is done.
-__host__ __device__ inline int sel_slice_words(int k_max, int n_splits) {
-  return ((k_max + n_splits - 1) / n_splits + 1 + 3) & ~3;
-}
-constexpr int kBatch = 2;   // 16-token chunks per load batch; two batches are in flight
-
-struct PagesDev {
-  const uint16_t* k16;
-  const uint16_t* v16;
-  const uint8_t* kq[KV_NUM_PACKED_TIERS];
-  const uint8_t* vq[KV_NUM_PACKED_TIERS];
-  const uint16_t* ksz[KV_NUM_PACKED_TIERS];
-  const uint16_t* vsz[KV_NUM_PACKED_TIERS];
-  const uint32_t* page_entry;
-  const uint16_t* v_hot;
-  const int32_t* v_hot_slot;
-  const uint16_t* k_hot;
-  const uint32_t* kout;
-  const uint32_t* vout;
-};
-
-// Selector inputs and outputs of the fused kernel (unused without SEL).
-struct SelArgs {
-  const float* head_scores;   // [rows][G][max_pages]
-  const float* lse_partial;   // [rows][n_tiles][G][2]
-  float keep;
-  int k_fixed;
-  float coverage;             // < 0: budget mode (keep / k_fixed)
-  int n_force_first, n_force_last, n_tiles;
-  int32_t* sel;               // [rows][k_max], written by split 0
-  int32_t* sel_count;         // [rows], written by split 0
-  float* page_S;              // optional [rows][max_pages], written by split 0
-};
-
-template <int T>
-struct TierTag {
-  static constexpr int value = T;
-};
-
-template <int T>
-constexpr int tier_bits() {
-  return T == KV_TIER_I4 ? 4 : T == KV_TIER_I2 ? 2 : T == KV_TIER_B1 ? 1 : 8;
-}
-
-// Raw code words of one 16-token chunk of a page in packed tier T as the
-// attention lanes read it: per MFMA k-step the codes of the lane's 8 key
-// elements and their group's (scale, zero) word; per value slot j the codes of
-// the lane's D/16 value elements and their (scale, zero) word.
-template <int D, int T>
-struct TierChunk {
-  static constexpr int BITS = tier_bits<T>();
-  static constexpr int KW = (8 * BITS + 31) / 32;
-  static constexpr int VW = ((D / 16) * BITS + 31) / 32;
-  uint32_t k[D / 32][KW];
-  uint32_t ksz[D / 32];
-  uint32_t v[4][VW];
-  uint32_t vsz[4];
-  uint32_t ko[D / 32];   // 1-bit outlier words, when the pools have side tables
-  uint32_t vo[4];
-};
-
-// Requests the codes of EL elements from e0 of token row `tokrow` of packed
-// tier T and the group's (scale, zero) word.
-template <int D, int EL, int T>
-__device__ __forceinline__ void tier_load(const uint8_t* codes, const uint16_t* sz, size_t tokrow, int e0,
-                                          uint32_t* w, uint32_t& szw) {
-  constexpr int BITS = tier_bits<T>();
-  szw = *reinterpret_cast<const uint32_t*>(sz + (tokrow * (D / 32) + e0 / 32) * 2);
-  int sh;
-  load_code_words<EL, BITS>(codes + tokrow * (D * BITS / 8), e0, w, sh);
-}
-
-// Decodes what tier_load requested: int-b x = c*s + z (one FMA), 1-bit
-// x = z +- s, FP8 x = e4m3(c)*s + z.
-template <int EL, int T>
-__device__ __forceinline__ void tier_decode(const uint32_t* w, uint32_t szw, int e0, float* x) {
-  constexpr int BITS = tier_bits<T>();
-  const float s = f16_bits_to_f32(szw & 0xFFFFu), z = f16_bits_to_f32(szw >> 16);
-  const int sh = (e0 * BITS) & 7;
-  if constexpr (T == KV_TIER_FP8) {
-#pragma unroll
-    for (int i = 0; i < EL / 4; ++i) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
-      x[4 * i + 0] = __builtin_fmaf(lo[0], s, z);
-      x[4 * i + 1] = __builtin_fmaf(lo[1], s, z);
-      x[4 * i + 2] = __builtin_fmaf(hi[0], s, z);
-      x[4 * i + 3] = __builtin_fmaf(hi[1], s, z);
-    }
-  } else if constexpr (T == KV_TIER_B1) {
-    const float zp = z + s, zm = z - s;
-#pragma unroll
-    for (int e = 0; e < EL; ++e) x[e] = code_at<1>(w, sh, e) ? zp : zm;
-  } else {
-#pragma unroll
-    for (int e = 0; e < EL; ++e) x[e] = __builtin_fmaf((float)code_at<BITS>(w, sh, e), s, z);
-  }
-}
-
-// Exact split of float32 values into a 16-bit hi part and a 16-bit lo part.
-template <bool F16>
-__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  if constexpr (F16) {
-    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-    const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-    hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-  } else {
-    const uint32_t u0 = __float_as_uint(x0) & 0xFFFF0000u, u1 = __float_as_uint(x1) & 0xFFFF0000u;
-    hi = (u0 >> 16) | u1;
-    const uint32_t r0 = __float_as_uint(x0 - __uint_as_float(u0)), r1 = __float_as_uint(x1 - __uint_as_float(u1));
-    lo = (r0 >> 16) | (r1 & 0xFFFF0000u);
-  }
-}
-
-// ---------------------------------------------------------------- the kernel
-
-// Per-wave attention state: running max (per head, shared by the four lane
-// groups), this lane's partial softmax sum, and acc[head][d/16] of the
-// token slot / element chunk this lane owns.
-template <int D, int GM>
-struct AttnState {
-  static constexpr int EV = D / 16;
-  float m_run;
-  float l_run;
-  float acc[GM][EV];
-};
-
-// Softmax update for one 16-token chunk given its raw logits (head col,
-// tokens 4*grp + i); writes the probabilities to the wave's LDS tile.
-template <int D, int GM>
-__device__ __forceinline__ void softmax_chunk(AttnState<D, GM>& st, const f32x4_t& zacc, int tok0, int L,
-                                              bool page_ok, float scale_log2, float (*ptile)[16],
-                                              int grp, int col) {
-  constexpr int EV = D / 16;
-  constexpr float kRescale = 8.0f;
-  float z[4];
-  float cm = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tpos = tok0 + 4 * grp + i;
-    z[i] = (page_ok && tpos < L) ? zacc[i] * scale_log2 : -INFINITY;
-    cm = nan_max(cm, z[i]);
-  }
-  cm = nan_max(cm, __shfl_xor(cm, 16));
-  cm = nan_max(cm, __shfl_xor(cm, 32));
-  // a NaN logit (NaN query) makes the running max NaN, so the head's output
-  // and lse come out NaN instead of being dropped
-  const float m_new = nan_max(st.m_run, cm);
-  const bool need = (m_new > st.m_run + kRescale) || (m_new != m_new && st.m_run == st.m_run);
-  if (__ballot(need)) {
-    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
-    if (m_new != -INFINITY) st.m_run = m_new;
-    st.l_run *= alpha;
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      const float ah = readlane_f(alpha, h);
-#pragma unroll
-      for (int e = 0; e < EV; ++e) st.acc[h][e] *= ah;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float pz = (st.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[i] - st.m_run);
-    st.l_run += pz;
-    ptile[4 * grp + i][col] = pz;
-  }
-  wave_lds_sync();
-}
-
-// acc[h][:] += p[h][token] * v for one token slot of the chunk.
-template <int D, int GM>
-__device__ __forceinline__ void pv_accumulate(AttnState<D, GM>& st, const float* v, const float (*ptile)[16], int tk) {
-  constexpr int EV = D / 16;
-  float pv[GM];
-#pragma unroll
-  for (int h4 = 0; h4 < GM; h4 += 4) {
-    const float4 t4 = *reinterpret_cast<const float4*>(&ptile[tk][h4]);
-    pv[h4] = t4.x; pv[h4 + 1] = t4.y; pv[h4 + 2] = t4.z; pv[h4 + 3] = t4.w;
-  }
-#pragma unroll
-  for (int h = 0; h < GM; ++h)
-#pragma unroll
-    for (int e = 0; e < EV; ++e) st.acc[h][e] = __builtin_fmaf(pv[h], v[e], st.acc[h][e]);
-}
-
-template <bool F16, int EV>
-__device__ __forceinline__ void unpack_v(const u32x4_t& r, float* v) {
-  if constexpr (EV == 8) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) { v[2 * w] = lo16<F16>(r[w]); v[2 * w + 1] = hi16<F16>(r[w]); }
-  } else {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) { v[2 * w] = lo16<F16>(r[w]); v[2 * w + 1] = hi16<F16>(r[w]); }
-  }
-}
-
-// Raw loads of one 16-token chunk of a native page: K rows for the MFMA (key
-// row `col`, 64 contiguous bytes per k-step), V rows for the PV lanes (token
-// 4j + grp, 16 contiguous bytes per lane).
-template <int D>
-struct ChunkRaw {
-  u32x4_t k[D / 32];
-  u32x4_t v[4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_native_chunk(ChunkRaw<D>& r, const uint16_t* kbase, const uint16_t* vbase,
-                                                  int c, int col, int grp) {
-  constexpr int KS = D / 32, EV = D / 16;
-  const uint16_t* kp = kbase + (size_t)(c * 16 + col) * D + 8 * grp;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) r.k[s] = ld16(kp + 32 * s);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint16_t* vp = vbase + (size_t)(c * 16 + 4 * j + grp) * D + col * EV;
-    if constexpr (EV == 8) r.v[j] = ld16(vp);
-    else {
-      const u32x2_t t = *reinterpret_cast<const u32x2_t*>(vp);
-      r.v[j] = u32x4_t{t[0], t[1], 0, 0};
-    }
-  }
-}
 
 template <int D, int GM, bool F16, bool TIERED, bool SEL>
 __global__ __launch_bounds__((64 * attn_waves<GM, SEL>())) void sparse_attn_kernel(
@@ -389,359 +141,9 @@ __global__ __launch_bounds__((64 * attn_waves<GM, SEL>())) void sparse_attn_kern
     }
     __syncthreads();
   }
-  const int beg = (int)(((long long)split * cnt) / n_splits);
-  const int end = (int)(((long long)(split + 1) * cnt) / n_splits);
-  const int n_mine =
-      wave < kStreamWaves && end - beg > wave ? (end - beg - wave + kStreamWaves - 1) / kStreamWaves : 0;
-
-  AttnState<D, GM> st;
-  st.m_run = -INFINITY;
-  st.l_run = 0.f;
-#pragma unroll
-  for (int h = 0; h < GM; ++h)
-#pragma unroll
-    for (int e = 0; e < EV; ++e) st.acc[h][e] = 0.f;
-
-  const int32_t* srow = SEL ? nullptr : sel + (size_t)row * k_max;
-  const int32_t* bt = block_table + (size_t)b * max_pages;
-  const size_t page_elems = (size_t)P * D;
-  const int cpp = P / 16;   // 16-token chunks per page
-  float (*pt)[16] = al->ptile[wave < kStreamWaves ? wave : 0];   // used by streaming waves only
-
-  if constexpr (!TIERED) {
-    for (int j0 = 0; j0 < n_mine; j0 += 64) {
-      const int nb = n_mine - j0 < 64 ? n_mine - j0 : 64;
-      // this wave's pages, one per lane: logical page, slot, hot-buffer slot
-      int l_p = -1, l_hot = -1;
-      uint32_t l_tier = 0, l_slot = 0;
-      if (lane < nb) {
-        const int li = wave + kStreamWaves * (j0 + lane);
-        const int p = SEL ? mine[li] : srow[beg + li];
-        if (p >= 0 && p < Np) {
-          l_p = p;
-          const int phys = bt[p];
-          l_slot = (uint32_t)phys;
-          if constexpr (TIERED) {
-            if (pg.page_entry) {
-              const uint32_t e = pg.page_entry[phys];
-              l_tier = e >> 29;
-              l_slot = e & 0x1FFFFFFFu;
-            }
-          }
-          if (pg.v_hot_slot) l_hot = pg.v_hot_slot[phys];
-        }
-      }
-      const unsigned long long valid = __ballot(l_p >= 0);
-      if (valid == 0) continue;
-
-      // skipped entries read the first valid page of the list instead (and are
-      // masked), so every load of a batch is unconditional straight-line code
-      const int first = __ffsll((long long)valid) - 1;
-      if (l_p < 0) {
-        l_slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, first);
-        l_hot = __builtin_amdgcn_readlane(l_hot, first);
-      }
-      const int nch = nb * cpp;
-      // issue the loads of chunks [cb, cb + NB) into r (the last chunk is
-      // re-read past the end; those extra chunks are never computed)
-      auto issue = [&](ChunkRaw<D> (&r)[kBatch], int (&pp)[kBatch], int cb) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int ci = cb + u < nch ? cb + u : nch - 1;
-          const int jj = ci / cpp;
-          pp[u] = __builtin_amdgcn_readlane(l_p, jj);
-          const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, jj);
-          const int hot = __builtin_amdgcn_readlane(l_hot, jj);
-          const size_t pr = (size_t)slot * Hkv + g;
-          const size_t hr = ((size_t)hot * Hkv + g) * page_elems;
-          const uint16_t* kb = hot >= 0 && pg.k_hot ? pg.k_hot + hr : pg.k16 + pr * page_elems;
-          const uint16_t* vb = hot >= 0 ? pg.v_hot + hr : pg.v16 + pr * page_elems;
-          load_native_chunk<D>(r[u], kb, vb, ci - jj * cpp, col, grp);
-        }
-      };
-      auto compute = [&](const ChunkRaw<D> (&r)[kBatch], const int (&pp)[kBatch], int cb) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (cb + u >= nch) break;
-          const int ci = cb + u;
-          const int c = ci - (ci / cpp) * cpp;
-          const int p = pp[u];
-          f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(r[u].k[s], qop[s], zacc);
-          const int tok0 = p * P + c * 16;
-          softmax_chunk<D, GM>(st, zacc, tok0, L, p >= 0, scale_log2, pt, grp, col);
-          // values of tokens that do not exist (past seq_len, skipped entries)
-          // are zeroed: their probability is 0 but the memory may hold NaN
-          const bool full = p >= 0 && tok0 + 16 <= L;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float v[EV];
-            unpack_v<F16, EV>(r[u].v[j], v);
-            if (!full) {
-              const uint32_t vk = (p >= 0 && tok0 + 4 * j + grp < L) ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-              for (int e = 0; e < EV; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) & vk);
-            }
-            pv_accumulate<D, GM>(st, v, pt, 4 * j + grp);
-          }
-          wave_lds_sync();
-        }
-      };
-      ChunkRaw<D> ra[kBatch], rb[kBatch];
-      int pa[kBatch], pb[kBatch];
-      issue(ra, pa, 0);
-      for (int cb = 0; cb < nch; cb += 2 * kBatch) {
-        if (cb + kBatch < nch) issue(rb, pb, cb + kBatch);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(ra, pa, cb);
-        if (cb + kBatch < nch) {
-          if (cb + 2 * kBatch < nch) issue(ra, pa, cb + 2 * kBatch);
-          __builtin_amdgcn_sched_barrier(0);
-          compute(rb, pb, cb + kBatch);
-        }
-      }
-    }
-  } else {
-    // Tiered pages: the wave's pages in batches of 64 (one per lane), each
-    // batch taken tier by tier so that every loop below has one load shape.
-    for (int j0 = 0; j0 < n_mine; j0 += 64) {
-      const int nb = n_mine - j0 < 64 ? n_mine - j0 : 64;
-      int l_p = -1, l_hot = -1;
-      uint32_t l_tier = 7, l_slot = 0;   // 7: not a valid entry
-      if (lane < nb) {
-        const int li = wave + kStreamWaves * (j0 + lane);
-        const int p = SEL ? mine[li] : srow[beg + li];
-        if (p >= 0 && p < Np) {
-          l_p = p;
-          const int phys = bt[p];
-          l_slot = (uint32_t)phys;
-          l_tier = KV_TIER_NATIVE;
-          if (pg.page_entry) {
-            const uint32_t e = pg.page_entry[phys];
-            l_tier = e >> 29;
-            l_slot = e & 0x1FFFFFFFu;
-          }
-          if (pg.v_hot_slot) l_hot = pg.v_hot_slot[phys];
-        }
-      }
-      auto run_tier = [&](auto tc) {
-        constexpr int T = decltype(tc)::value;
-        using Raw = typename std::conditional<T == KV_TIER_NATIVE, ChunkRaw<D>, TierChunk<D, T>>::type;
-        const unsigned long long mask = __ballot(l_p >= 0 && l_tier == (uint32_t)T);
-        if (mask == 0) return;
-        const int nu = __popcll(mask) * cpp;
-        // units in list order; past the last one the iterator repeats it (a
-        // request whose result is never computed), so every load below is
-        // unconditional and the wait counts do not depend on the path
-        unsigned long long it = mask;
-        int it_c = 0, last_lane = __ffsll((long long)mask) - 1, last_c = 0;
-        auto next = [&](int& lane_out, int& c_out) {
-          if (it == 0) {
-            lane_out = last_lane;
-            c_out = last_c;
-            return;
-          }
-          lane_out = last_lane = __ffsll((long long)it) - 1;
-          c_out = last_c = it_c;
-          if (++it_c == cpp) {
-            it_c = 0;
-            it &= it - 1;
-          }
-        };
-        auto issue = [&](Raw& r, int jj, int c) {
-          const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, jj);
-          const size_t pr = (size_t)slot * Hkv + g;
-          if constexpr (T == KV_TIER_NATIVE) {
-            const int hot = __builtin_amdgcn_readlane(l_hot, jj);
-            const size_t hr = ((size_t)hot * Hkv + g) * page_elems;
-            const uint16_t* kbase = hot >= 0 && pg.k_hot ? pg.k_hot + hr : pg.k16 + pr * page_elems;
-            const uint16_t* vbase = hot >= 0 ? pg.v_hot + hr : pg.v16 + pr * page_elems;
-            load_native_chunk<D>(r, kbase, vbase, c, col, grp);
-          } else {
-            const size_t tok = pr * P + c * 16;
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-              tier_load<D, 8, T>(pg.kq[T - 1], pg.ksz[T - 1], tok + col, 32 * s + 8 * grp, r.k[s], r.ksz[s]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              tier_load<D, EV, T>(pg.vq[T - 1], pg.vsz[T - 1], tok + 4 * j + grp, col * EV, r.v[j], r.vsz[j]);
-            if constexpr (T == KV_TIER_B1) {
-              if (pg.kout) {
-#pragma unroll
-                for (int s = 0; s < KS; ++s) r.ko[s] = pg.kout[(tok + col) * (D / 32) + s];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) r.vo[j] = pg.vout[(tok + 4 * j + grp) * (D / 32) + (col * EV) / 32];
-              }
-            }
-          }
-        };
-        auto compute = [&](const Raw& r, int jj, int c) {
-          const int p = __builtin_amdgcn_readlane(l_p, jj);
-          const int tok0 = p * P + c * 16;
-          f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (T == KV_TIER_NATIVE) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(r.k[s], qop[s], zacc);
-          } else {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-              float x[8];
-              tier_decode<8, T>(r.k[s], r.ksz[s], 32 * s + 8 * grp, x);
-              if constexpr (T == KV_TIER_B1)
-                if (pg.kout) apply_outlier<8>(x, 32 * s + 8 * grp, r.ko[s]);
-              u32x4_t ah, al;
-#pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                uint32_t hw, lw;
-                split_pair<F16>(x[2 * w], x[2 * w + 1], hw, lw);
-                ah[w] = hw;
-                al[w] = lw;
-              }
-              zacc = mfma16<F16>(ah, qop[s], zacc);
-              zacc = mfma16<F16>(al, qop[s], zacc);
-            }
-          }
-          softmax_chunk<D, GM>(st, zacc, tok0, L, true, scale_log2, pt, grp, col);
-          const bool full = tok0 + 16 <= L;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int tk = 4 * j + grp;
-            float v[EV];
-            if constexpr (T == KV_TIER_NATIVE) unpack_v<F16, EV>(r.v[j], v);
-            else {
-              tier_decode<EV, T>(r.v[j], r.vsz[j], col * EV, v);
-              if constexpr (T == KV_TIER_B1)
-                if (pg.vout) apply_outlier<EV>(v, col * EV, r.vo[j]);
-            }
-            // values of tokens past seq_len are zeroed: probability 0, memory may hold NaN
-            if (!full) {
-              const uint32_t vk = tok0 + tk < L ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-              for (int e = 0; e < EV; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) & vk);
-            }
-            pv_accumulate<D, GM>(st, v, pt, tk);
-          }
-          wave_lds_sync();
-        };
-        Raw ra, rb;
-        int ja, ca, jb, cb;
-        next(ja, ca);
-        issue(ra, ja, ca);
-        int u = 0;
-        for (; u + 2 <= nu; u += 2) {
-          next(jb, cb);
-          issue(rb, jb, cb);
-          __builtin_amdgcn_sched_barrier(0);
-          compute(ra, ja, ca);
-          next(ja, ca);
-          issue(ra, ja, ca);
-          __builtin_amdgcn_sched_barrier(0);
-          compute(rb, jb, cb);
-        }
-        if (u < nu) compute(ra, ja, ca);
-      };
-      run_tier(TierTag<KV_TIER_NATIVE>{});
-      run_tier(TierTag<KV_TIER_FP8>{});
-      run_tier(TierTag<KV_TIER_I8>{});
-      run_tier(TierTag<KV_TIER_I4>{});
-      run_tier(TierTag<KV_TIER_I2>{});
-      run_tier(TierTag<KV_TIER_B1>{});
-    }
-  }
-
-  // ---- wave totals: l over lane groups, acc over token slots
-  float l_run = st.l_run;
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-#pragma unroll
-  for (int h = 0; h < GM; ++h)
-#pragma unroll
-    for (int e = 0; e < EV; ++e) {
-      float a = st.acc[h][e];
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      st.acc[h][e] = a;
-    }
-  if (wave < kStreamWaves && lane < 16) { al->wm[wave][lane] = st.m_run; al->wl[wave][lane] = l_run; }
-  if (wave < kStreamWaves && grp == 0) {
-#pragma unroll
-    for (int h = 0; h < GM; ++h)
-#pragma unroll
-      for (int e = 0; e < EV; ++e) al->wacc[wave][h][col * EV + e] = st.acc[h][e];
-  }
-  __syncthreads();
-
-  // ---- merge the waves (fixed order) and write this split's partial
-  float* dst = partials + ((size_t)row * n_splits + split) * G * (D + 2);
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D, e = idx - h * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kStreamWaves; ++w) M = nan_max(M, al->wm[w][h]);
-    float a = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kStreamWaves; ++w) {
-        const float f = exp2f(al->wm[w][h] - M);
-        a += al->wacc[w][h][e] * f;
-        l += al->wl[w][h] * f;
-      }
-    }
-    // device-coherent stores (written through to the chip's coherence point),
-    // so another block may read them after the counter below says so
-    __hip_atomic_store(dst + (size_t)h * (D + 2) + e, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (e == 0) {
-      __hip_atomic_store(dst + (size_t)h * (D + 2) + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(dst + (size_t)h * (D + 2) + D + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-
-  // ---- the last split of the row to finish merges all splits in split order.
-  // Every partial store above has completed before the count is raised, and
-  // the merging block reads partials with device-coherent loads; no cache
-  // write-back fence is needed because nothing else crosses blocks.
-  __shared__ int is_last;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    is_last = __hip_atomic_fetch_add(&counters[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (unsigned)(n_splits - 1);
-  __syncthreads();
-  if (!is_last) return;
-  const float* src = partials + (size_t)row * n_splits * G * (D + 2);
-  const size_t stride = (size_t)G * (D + 2);
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D, e = idx - h * D;
-    const float* sh = src + (size_t)h * (D + 2);
-    constexpr int U = 8;
-    float M = -INFINITY, a = 0.f, l = 0.f;
-    for (int s0 = 0; s0 < n_splits; s0 += U) {
-      float av[U], mv[U], lv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int si = s0 + u < n_splits ? s0 + u : n_splits - 1;
-        av[u] = __hip_atomic_load(sh + si * stride + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        mv[u] = __hip_atomic_load(sh + si * stride + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lv[u] = __hip_atomic_load(sh + si * stride + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (s0 + u >= n_splits) break;
-        const float Mn = nan_max(M, mv[u]);
-        if (Mn == -INFINITY) continue;
-        const float fo = exp2f(M - Mn), fn = exp2f(mv[u] - Mn);
-        a = a * fo + av[u] * fn;
-        l = l * fo + lv[u] * fn;
-        M = Mn;
-      }
-    }
-    const size_t hq = (size_t)b * Hkv * G + (size_t)g * G + h;
-    const bool empty = l == 0.f;
-    out[hq * D + e] = empty ? 0.f : a / l;
-    if (e == 0) lse[hq] = empty ? -INFINITY : (M + log2f(l)) * kLn2;
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  attend_split<D, GM, F16, TIERED, SEL, kThreads>(pg, block_table, Hkv, G, P, max_pages, row, split, n_splits, cnt,
+                                                 SEL ? mine : sel + (size_t)row * k_max, L, Np, qop,
+                                                 scale_log2, partials, counters, nullptr, out, lse, al);
 }
 
 // Arguments shared by every instantiation's launch.
@@ -794,25 +196,6 @@ static hipError_t launch_attn_any(const kv_layout& L, const AttnLaunch& a, bool 
   if (f16) KVS_ATTN(128, true);
   KVS_ATTN(128, false);
 #undef KVS_ATTN
-}
-
-static PagesDev to_dev(const kv_pages& pg) {
-  PagesDev d;
-  d.k16 = (const uint16_t*)pg.k16;
-  d.v16 = (const uint16_t*)pg.v16;
-  for (int t = 0; t < KV_NUM_PACKED_TIERS; ++t) {
-    d.kq[t] = pg.kq[t];
-    d.vq[t] = pg.vq[t];
-    d.ksz[t] = (const uint16_t*)pg.ksz[t];
-    d.vsz[t] = (const uint16_t*)pg.vsz[t];
-  }
-  d.page_entry = pg.page_entry;
-  d.v_hot = (const uint16_t*)pg.v_hot;
-  d.v_hot_slot = pg.v_hot_slot;
-  d.k_hot = (const uint16_t*)pg.k_hot;
-  d.kout = pg.kout;
-  d.vout = pg.vout;
-  return d;
 }
 
 hipError_t launch_sparse_attn(const kv_layout& L, const void* q, const kv_pages& pg,

@@ -381,9 +381,30 @@ def topk_attend(layer: DeviceLayer, q, bufs: StepBuffers, n_force_first=0, n_for
                                num_splits=bufs.num_splits, stream=stream)
 
 
+def step_supported(layer: DeviceLayer, bufs: StepBuffers):
+    """Whether kv_sparse_decode_step takes this layer (quad summaries)."""
+    w = layer.w
+    return (layer.summary is not None and layer.coords is None and layer.basis is None and
+            kv.step_supported(layer.L, w.B, w.Np, bufs.sel.shape[-1], bufs.num_splits))
+
+
+def whole_step(layer: DeviceLayer, q, bufs: StepBuffers, n_force_first=0, n_force_last=0, coverage=-1.0,
+               stream=None):
+    """score, top-k and sparse attention in one library call (kv_sparse_decode_step)."""
+    w = layer.w
+    kv.sparse_decode_step(layer.L, q, layer.summary, layer.log_n, layer.pages, layer.bt, layer.seq_lens,
+                          bufs.head_scores, bufs.lse_partial, bufs.sel, bufs.sel_count, bufs.out, bufs.lse,
+                          bufs.ws, keep_frac=w.keep, k_fixed=w.k_fixed, coverage=coverage,
+                          n_force_first=n_force_first, n_force_last=n_force_last, page_S=bufs.page_S,
+                          num_splits=bufs.num_splits, stream=stream)
+
+
 def decode_step(layer: DeviceLayer, q, bufs: StepBuffers, stream=None, fused=False):
     """score -> top-k -> sparse attention for one layer of the whole batch
-    (fused: top-k and attention in one launch)."""
+    (fused: top-k and attention in one launch; "step": kv_sparse_decode_step)."""
+    if fused == "step":
+        whole_step(layer, q, bufs, stream=stream)
+        return
     score(layer, q, bufs, stream)
     if fused:
         topk_attend(layer, q, bufs, stream=stream)

@@ -18,7 +18,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 PROFILES = os.path.join(ROOT, "profiles")
-SCORE_SOURCES = ("page_score.hip", "device.h", "launch.h")
+SCORE_SOURCES = ("page_score.hip", "score_tile.h", "device.h", "launch.h")
 COPY_BYTES = 3 * (512 << 20)
 
 

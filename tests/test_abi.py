@@ -184,6 +184,52 @@ def test_fused_topk_attention_validation():
     assert not kv.topk_attn_supported(L, 2048, 164, 0)
 
 
+def test_decode_step_validation():
+    L = _L()
+    pg = kv.KvPages()
+    pg.k16 = FAKE
+    pg.v16 = FAKE
+    f = kv.lib().kv_sparse_decode_step
+    s = kv.attn_num_splits(L, 8, 164)
+    need = kv.step_workspace_size(L, 8, 164)
+    assert need == kv.attn_workspace_size(L, 8, 164, 0)
+    assert kv.step_workspace_size(L, 0, 164) == 0
+
+    def call(L=L, pages=pg, B=8, max_pages=2048, keep=0.08, k_fixed=0, coverage=-1.0, k_max=164, sel=FAKE,
+             summary=FAKE, splits=0, ws=FAKE, ws_bytes=need, q=FAKE, hs=FAKE):
+        return f(ctypes.byref(L), q, summary, FAKE, ctypes.byref(pages) if pages is not None else None, FAKE,
+                 FAKE, B, max_pages, keep, k_fixed, coverage, 0, 0, hs, FAKE, sel, FAKE, k_max, None, splits,
+                 FAKE, FAKE, ws, ws_bytes, None)
+
+    assert call(B=0) == kv.KV_OK
+    assert call(ws_bytes=kv.attn_workspace_size(L, 8, 164, s) - 1) == kv.KV_ERR_WORKSPACE
+    assert call(ws=None) == kv.KV_ERR_WORKSPACE
+    assert call(max_pages=0) == kv.KV_ERR_INVALID_ARG
+    assert call(k_max=163) == kv.KV_ERR_INVALID_ARG                 # ceil(0.08 * 2048) = 164
+    assert call(keep=float("nan")) == kv.KV_ERR_INVALID_ARG
+    assert call(coverage=float("inf")) == kv.KV_ERR_INVALID_ARG
+    assert call(sel=None) == kv.KV_ERR_INVALID_ARG
+    assert call(summary=None) == kv.KV_ERR_INVALID_ARG
+    assert call(hs=None) == kv.KV_ERR_INVALID_ARG
+    assert call(summary=FAKE + 8) == kv.KV_ERR_INVALID_ARG
+    assert call(pages=None) == kv.KV_ERR_INVALID_ARG
+    assert call(splits=300) == kv.KV_ERR_UNSUPPORTED
+    assert call(max_pages=15361, k_max=15361) == kv.KV_ERR_UNSUPPORTED
+    assert kv.step_supported(L, 8, 2048, 164)
+    assert kv.step_supported(_L(num_q_heads=64), 8, 8192, 410)
+    assert not kv.step_supported(L, 8, 15361, 15361, 1)
+    assert not kv.step_supported(L, 8, 0, 1)
+    # the fused launch where it measured faster: native pages, G <= 4, rows under 4096 pages
+    assert kv.step_fused(L, pg, 8, 2048, 164)
+    assert not kv.step_fused(L, pg, 8, 4096, 410)
+    assert not kv.step_fused(_L(num_q_heads=64), pg, 8, 2048, 164)
+    tiered = kv.KvPages()
+    tiered.k16 = tiered.v16 = tiered.page_entry = FAKE
+    for t in range(kv.NUM_PACKED_TIERS):
+        tiered.kq[t] = tiered.vq[t] = tiered.ksz[t] = tiered.vsz[t] = FAKE
+    assert not kv.step_fused(L, tiered, 4, 4096, 410)
+
+
 def test_pack_build_dequant_validation():
     L = _L()
     lib = kv.lib()
