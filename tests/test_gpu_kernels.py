@@ -150,11 +150,12 @@ def _expected_selection(S, Np, k):
     return np.sort(order[:k])
 
 
-@pytest.mark.parametrize("G,max_pages", [(4, 600), (8, 600), (16, 600), (4, 5000), (16, 5000)])
+@pytest.mark.parametrize("G,max_pages", [(4, 600), (8, 600), (16, 600), (4, 5000), (16, 5000), (4, 15360)])
 def test_selection_branches_exact(G, max_pages):
     """Selection on crafted head scores, checked bit-exactly against an
     exhaustive sort of the kernel's own float32 S (the order is unique given S).
-    Rows of 4096 pages or more take the selector's wide-block variant."""
+    Rows of 4096 pages or more take the selector's wide-block variant; 15360
+    pages is the longest row the selector takes (its keys fill 60 KB of LDS)."""
     from quantized_kv_cache_summary_amd import kvsparse as kv
     announce(f"crafted selection G={G} max_pages={max_pages}")
     rng = np.random.default_rng(17 + G)
@@ -193,7 +194,7 @@ def _coverage_bounds(S, Np, cov, cap, nff, nfl, delta):
     return lo, hi
 
 
-@pytest.mark.parametrize("G,max_pages", [(4, 600), (8, 600), (4, 5000)])
+@pytest.mark.parametrize("G,max_pages", [(4, 600), (8, 600), (4, 5000), (8, 15360)])
 def test_coverage_selection_crafted(G, max_pages):
     """Coverage mode on crafted head scores: k within the counts for coverages
     +-1e-6 around the asked one, computed from the kernel's own float32 S
