@@ -125,6 +125,22 @@ def test_full_size_end_to_end(hz, name):
     _e2e_check(w, layer, bufs, sample_rows(w))
 
 
+@pytest.mark.timeout(600)
+def test_heavy_in_hbm_whole_step(hz):
+    """The 70B-shaped workload with K and V resident in HBM through the
+    whole-step call, as the benchmark times it beside the host-mapped pool:
+    sampled rows against the oracle's decode."""
+    w = W["heavy70b_128k"]
+    announce("heavy70b_128k with V in HBM: kv_sparse_decode_step")
+    layer = hz.DeviceLayer(w, summaries="build", host_v=False)
+    q = hz.queries_device(w)
+    bufs = hz.StepBuffers(w)
+    assert hz.step_supported(layer, bufs)
+    hz.whole_step(layer, q, bufs)
+    torch.cuda.synchronize()
+    _e2e_check(w, layer, bufs, sample_rows(w))
+
+
 def test_heavy_host_mapped_values(hz):
     w = W["heavy70b_128k"]
     announce("heavy70b_128k: K in HBM, V in pinned host memory; building summaries")
