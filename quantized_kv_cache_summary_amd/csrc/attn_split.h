@@ -325,7 +325,7 @@ __device__ __forceinline__ void attend_split(const PagesDev& pg, const int32_t* 
       const int nb = n_mine - j0 < 64 ? n_mine - j0 : 64;
       // this wave's pages, one per lane: logical page, slot, hot-buffer slot
       int l_p = -1, l_hot = -1;
-      uint32_t l_tier = 0, l_slot = 0;
+      uint32_t l_slot = 0;
       if (lane < nb) {
         const int li = wave + kStreamWaves * (j0 + lane);
         const int p = LDS_LIST ? list[li] : list[beg + li];
@@ -333,13 +333,6 @@ __device__ __forceinline__ void attend_split(const PagesDev& pg, const int32_t* 
           l_p = p;
           const int phys = bt[p];
           l_slot = (uint32_t)phys;
-          if constexpr (TIERED) {
-            if (pg.page_entry) {
-              const uint32_t e = pg.page_entry[phys];
-              l_tier = e >> 29;
-              l_slot = e & 0x1FFFFFFFu;
-            }
-          }
           if (pg.v_hot_slot) l_hot = pg.v_hot_slot[phys];
         }
       }

@@ -43,8 +43,6 @@ __global__ __launch_bounds__((64 * attn_waves<GM, SEL>())) void sparse_attn_kern
     float scale_log2, float* __restrict__ partials, unsigned* __restrict__ counters,
     float* __restrict__ out, float* __restrict__ lse, SelArgs sa) {
   constexpr int KS = D / 32;     // MFMA k-steps
-  constexpr int EK = D / 4;      // key elements per lane
-  constexpr int EV = D / 16;     // value elements per lane
   constexpr int kAttnWaves = attn_waves<GM, SEL>();
   constexpr int kThreads = 64 * kAttnWaves;
   using ALds = AttnLds<kStreamWaves, GM, D>;
@@ -69,7 +67,6 @@ __global__ __launch_bounds__((64 * attn_waves<GM, SEL>())) void sparse_attn_kern
   const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / Hkv, g = row - b * Hkv;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int col = lane & 15, grp = lane >> 4;
 
   const int L = seq_lens[b];
