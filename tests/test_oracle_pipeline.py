@@ -61,3 +61,28 @@ def test_tier_assignment_fractions():
     for b in range(w.B):
         counts = np.bincount(t[b], minlength=5)
         assert list(counts) == [50, 150, 300, 400, 100]
+
+
+def test_worked_step_closed_forms():
+    """A whole step on a hand-worked row (tests/golden/worked_step.json):
+    degenerate and one-token pages give exact scores, so the normalisers,
+    group scores, the top-k set for k = 1, 2, 3 and every attention output are
+    closed forms in e, derived by hand from the definitions."""
+    import json
+    import os
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_step.json")))
+    q = np.array(fx["q"])
+    keys, values = np.array(fx["keys"]), np.array(fx["values"])
+    s_ref = np.array(fx["s_hat"])
+    for case in fx["cases"]:
+        r = decode_row(q, keys, values, fx["seq_len"], fx["page_size"], fx["rank"], fx["tau"],
+                       k_fixed=case["k_fixed"])
+        # log n is stored in float32 (log 2 to 2e-9), everything else is exact
+        np.testing.assert_allclose(r["s_hat"], s_ref, rtol=0, atol=1e-7)
+        np.testing.assert_allclose(r["S"], fx["S"], rtol=0, atol=1e-7)
+        assert r["k"] == case["k_fixed"]
+        assert r["sel"].tolist() == case["sel"]
+        np.testing.assert_allclose(r["out"], case["out"], rtol=0, atol=1e-7)
+        np.testing.assert_allclose(r["lse"], case["lse"], rtol=0, atol=1e-7)
+    # with every page selected the attention's lse is the score's normaliser L_h
+    np.testing.assert_allclose(fx["cases"][2]["lse"], fx["L"], rtol=0, atol=1e-12)
