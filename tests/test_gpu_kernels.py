@@ -586,3 +586,60 @@ def test_nan_query_ranks_as_minus_inf(hz):
     out = bufs.out.cpu().numpy()
     assert np.isnan(out[0, 0]).all()
     assert not np.isnan(out[0, w.G:]).any()
+
+
+def test_out_of_range_device_values():
+    """Values read from device memory are not checked on the host; the calls
+    clamp or skip them as documented.  A sequence length past max_pages * P
+    gives the same step as the full length (bit for bit), a negative one the
+    same as an empty row; selection entries outside [0, Np) are skipped and a
+    count above k_max is clamped (attention within float32 rounding of the
+    call on the valid entries alone: the dealing of pages to waves changes)."""
+    from quantized_kv_cache_summary_amd import harness as hz
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    w = W["llama8b_32k"].replace(B=3, ctx=16 * 200)
+    announce("out-of-range sequence lengths and selection entries")
+    layer = hz.DeviceLayer(w, summaries="synthetic", seq_lens=[w.ctx, 0, w.ctx - 37])
+    q = hz.queries_device(w)
+    ref = hz.StepBuffers(w, with_S=True)
+    hz.whole_step(layer, q, ref)
+    good = layer.seq_lens.clone()
+    layer.seq_lens = torch.tensor([w.ctx + 1000, -5, w.ctx - 37], dtype=torch.int32, device="cuda")
+    odd = hz.StepBuffers(w, with_S=True)
+    hz.whole_step(layer, q, odd)
+    layer.seq_lens = good
+    torch.cuda.synchronize()
+    for name in ("sel", "sel_count"):
+        np.testing.assert_array_equal(getattr(odd, name).cpu().numpy(), getattr(ref, name).cpu().numpy())
+    for name in ("head_scores", "out", "lse"):
+        np.testing.assert_array_equal(getattr(odd, name).cpu().numpy().view(np.uint32),
+                                      getattr(ref, name).cpu().numpy().view(np.uint32))
+    assert np.all(odd.out.cpu().numpy()[1] == 0) and np.all(np.isneginf(odd.lse.cpu().numpy()[1]))
+
+    # attention over a selection with invalid entries and an oversized count
+    k_max = ref.sel.shape[-1]
+    sel = ref.sel.clone()
+    cnt = ref.sel_count.clone()
+    k0 = int(cnt[0, 0].item())
+    sel[0, 0, 1] = -1
+    sel[0, 0, 3] = w.Np + 7
+    bad = torch.tensor([int(sel[0, 0, 1].item()), int(sel[0, 0, 3].item())])
+    assert bad.tolist() == [-1, w.Np + 7]
+    cnt[0, 1] = k_max + 50                       # clamped to k_max; entries past the row's k are -1
+    out_a = torch.empty_like(ref.out)
+    lse_a = torch.empty_like(ref.lse)
+    kv.sparse_decode_attn(layer.L, q, layer.pages, layer.bt, layer.seq_lens, sel, cnt, out_a, lse_a, ref.ws)
+    # the same attention on the valid entries alone
+    keep = [i for i in range(k0) if i not in (1, 3)]
+    sel_b = ref.sel.clone()
+    cnt_b = ref.sel_count.clone()
+    sel_b[0, 0, :len(keep)] = ref.sel[0, 0, keep]
+    sel_b[0, 0, len(keep):] = -1
+    cnt_b[0, 0] = len(keep)
+    out_b = torch.empty_like(ref.out)
+    lse_b = torch.empty_like(ref.lse)
+    kv.sparse_decode_attn(layer.L, q, layer.pages, layer.bt, layer.seq_lens, sel_b, cnt_b, out_b, lse_b, ref.ws)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out_a.cpu().numpy(), out_b.cpu().numpy(), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(lse_a.cpu().numpy(), lse_b.cpu().numpy(), rtol=0, atol=1e-5)
+    layer.release()
