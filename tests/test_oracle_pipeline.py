@@ -86,3 +86,9 @@ def test_worked_step_closed_forms():
         np.testing.assert_allclose(r["lse"], case["lse"], rtol=0, atol=1e-7)
     # with every page selected the attention's lse is the score's normaliser L_h
     np.testing.assert_allclose(fx["cases"][2]["lse"], fx["L"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(np.exp(fx["S"]), fx["masses"], rtol=1e-12)
+    # coverage mode: the shortest prefix of the S order whose mass reaches the target
+    for case in fx["coverage_cases"]:
+        r = decode_row(q, keys, values, fx["seq_len"], fx["page_size"], fx["rank"], fx["tau"],
+                       coverage=case["coverage"])
+        assert r["k"] == case["k"] and r["sel"].tolist() == case["sel"], case
