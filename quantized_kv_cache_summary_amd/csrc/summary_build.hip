@@ -21,6 +21,68 @@
 
 namespace kvs {
 
+// Cyclic Jacobi on the m x m matrix A (LDS, symmetric), accumulating the
+// rotations into V.  MM > 0 fixes m at compile time (a full page, the common
+// case), so the schedule's index arithmetic folds to constants.
+template <int PS, int MM>
+__device__ __forceinline__ void jacobi_sweeps(float (*A)[PS + 1], float (*V)[PS + 1], float* rot_c, float* rot_s,
+                                              int* rot_p, int* rot_q, int m_rt, float tiny) {
+  const int lane = threadIdx.x;
+  const int m = MM > 0 ? MM : m_rt;
+  const int half = m / 2;
+  for (int sweep = 0; sweep < 16; ++sweep) {
+    bool rotated = false;   // any rotation this sweep (the block is one wave)
+    for (int step = 0; step < m - 1; ++step) {
+      bool rot = false;
+      if (lane < half) {
+        // circle method: player 0 fixed, players 1..m-1 rotate
+        int x, y;
+        if (lane == 0) { x = 0; y = 1 + (step % (m - 1)); }
+        else {
+          x = 1 + ((step + lane) % (m - 1));
+          y = 1 + ((step + m - 1 - lane) % (m - 1));
+        }
+        const int p = x < y ? x : y, qq = x < y ? y : x;
+        const float app = A[p][p], aqq = A[qq][qq], apq = A[p][qq];
+        float c = 1.f, s = 0.f;
+        if (fabsf(apq) > 1e-7f * sqrtf(fabsf(app * aqq)) + tiny) {
+          const float theta = (aqq - app) / (2.f * apq);
+          const float t = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
+          c = 1.f / sqrtf(t * t + 1.f);
+          s = t * c;
+          rot = true;
+        }
+        rot_p[lane] = p; rot_q[lane] = qq; rot_c[lane] = c; rot_s[lane] = s;
+      }
+      rotated = rotated || __any(rot);
+      __syncthreads();
+      for (int blk = lane; blk < half * half; blk += 64) {
+        const int a = blk / half, bb = blk - a * half;
+        const int pa = rot_p[a], qa = rot_q[a], pb = rot_p[bb], qb = rot_q[bb];
+        const float ca = rot_c[a], sa = rot_s[a], cb = rot_c[bb], sb = rot_s[bb];
+        const float b00 = A[pa][pb], b01 = A[pa][qb], b10 = A[qa][pb], b11 = A[qa][qb];
+        const float t00 = ca * b00 - sa * b10, t01 = ca * b01 - sa * b11;
+        const float t10 = sa * b00 + ca * b10, t11 = sa * b01 + ca * b11;
+        A[pa][pb] = t00 * cb - t01 * sb;
+        A[pa][qb] = t00 * sb + t01 * cb;
+        A[qa][pb] = t10 * cb - t11 * sb;
+        A[qa][qb] = t10 * sb + t11 * cb;
+      }
+      for (int idx = lane; idx < m * half; idx += 64) {
+        const int r = idx / half, bb = idx - r * half;
+        const int pb = rot_p[bb], qb = rot_q[bb];
+        const float cb = rot_c[bb], sb = rot_s[bb];
+        const float vp = V[r][pb], vq = V[r][qb];
+        V[r][pb] = cb * vp - sb * vq;
+        V[r][qb] = sb * vp + cb * vq;
+      }
+      __syncthreads();
+    }
+    if (!rotated) break;
+  }
+
+}
+
 template <int D, int PS, bool F16>
 __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __restrict__ k16,
                                                            const int32_t* __restrict__ block_table,
@@ -36,7 +98,6 @@ __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __res
   __shared__ float rot_c[PS / 2], rot_s[PS / 2];
   __shared__ int rot_p[PS / 2], rot_q[PS / 2];
   __shared__ int order[PS];
-  __shared__ int n_rot;
 
   const int lane = threadIdx.x;
   const int i = blockIdx.x / Hkv, g = blockIdx.x - (blockIdx.x / Hkv) * Hkv;
@@ -54,17 +115,25 @@ __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __res
     return;
   }
 
-  // mean (token order, float32) and centred keys
+  // mean (token order, float32) and centred keys.  Every slot of a page is
+  // allocated, so all PS keys are requested at once and slots past n masked.
+  uint16_t raw[CPL][PS];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int t = 0; t < PS; ++t) raw[c][t] = src[(size_t)t * D + lane + 64 * c];
   float mu[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int e = lane + 64 * c;
     float s = 0.f;
-    for (int t = 0; t < nv; ++t) s += h16_to_f32<F16>(src[(size_t)t * D + e]);
+#pragma unroll
+    for (int t = 0; t < PS; ++t)
+      if (t < nv) s += h16_to_f32<F16>(raw[c][t]);
     mu[c] = s / (float)nv;
     dst[e] = (uint16_t)f32_to_bf16_rne(mu[c]);
-    for (int t = 0; t < PS; ++t)
-      X[t][e] = t < nv ? h16_to_f32<F16>(src[(size_t)t * D + e]) - mu[c] : 0.f;
+#pragma unroll
+    for (int t = 0; t < PS; ++t) X[t][e] = t < nv ? h16_to_f32<F16>(raw[c][t]) - mu[c] : 0.f;
   }
   int m = nv + (nv & 1);
   if (m < 2) m = 2;
@@ -89,57 +158,8 @@ __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __res
   for (int a = 0; a < m; ++a) trace += A[a][a];
   const float tiny = 1e-12f * trace;
 
-  for (int sweep = 0; sweep < 16; ++sweep) {
-    if (lane == 0) n_rot = 0;
-    __syncthreads();
-    for (int step = 0; step < m - 1; ++step) {
-      if (lane < half) {
-        // circle method: player 0 fixed, players 1..m-1 rotate
-        int x, y;
-        if (lane == 0) { x = 0; y = 1 + (step % (m - 1)); }
-        else {
-          x = 1 + ((step + lane) % (m - 1));
-          y = 1 + ((step + m - 1 - lane) % (m - 1));
-        }
-        const int p = x < y ? x : y, qq = x < y ? y : x;
-        const float app = A[p][p], aqq = A[qq][qq], apq = A[p][qq];
-        float c = 1.f, s = 0.f;
-        if (fabsf(apq) > 1e-7f * sqrtf(fabsf(app * aqq)) + tiny) {
-          const float theta = (aqq - app) / (2.f * apq);
-          const float t = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
-          c = 1.f / sqrtf(t * t + 1.f);
-          s = t * c;
-          atomicAdd(&n_rot, 1);
-        }
-        rot_p[lane] = p; rot_q[lane] = qq; rot_c[lane] = c; rot_s[lane] = s;
-      }
-      __syncthreads();
-      for (int blk = lane; blk < half * half; blk += 64) {
-        const int a = blk / half, bb = blk - a * half;
-        const int pa = rot_p[a], qa = rot_q[a], pb = rot_p[bb], qb = rot_q[bb];
-        const float ca = rot_c[a], sa = rot_s[a], cb = rot_c[bb], sb = rot_s[bb];
-        const float b00 = A[pa][pb], b01 = A[pa][qb], b10 = A[qa][pb], b11 = A[qa][qb];
-        const float t00 = ca * b00 - sa * b10, t01 = ca * b01 - sa * b11;
-        const float t10 = sa * b00 + ca * b10, t11 = sa * b01 + ca * b11;
-        A[pa][pb] = t00 * cb - t01 * sb;
-        A[pa][qb] = t00 * sb + t01 * cb;
-        A[qa][pb] = t10 * cb - t11 * sb;
-        A[qa][qb] = t10 * sb + t11 * cb;
-      }
-      for (int idx = lane; idx < m * half; idx += 64) {
-        const int r = idx / half, bb = idx - r * half;
-        const int pb = rot_p[bb], qb = rot_q[bb];
-        const float cb = rot_c[bb], sb = rot_s[bb];
-        const float vp = V[r][pb], vq = V[r][qb];
-        V[r][pb] = cb * vp - sb * vq;
-        V[r][qb] = sb * vp + cb * vq;
-      }
-      __syncthreads();
-    }
-    const int applied = n_rot;
-    __syncthreads();
-    if (applied == 0) break;
-  }
+  if (m == PS) jacobi_sweeps<PS, PS>(A, V, rot_c, rot_s, rot_p, rot_q, m, tiny);
+  else jacobi_sweeps<PS, 0>(A, V, rot_c, rot_s, rot_p, rot_q, m, tiny);
 
   // eigenvalues descending (ties by index) -> order[rank] = column
   if (lane < m) {
