@@ -14,7 +14,8 @@
 // ("circle") pair schedule, so the n/2 rotations of a step are disjoint and
 // the whole step is a set of independent 2x2 block updates A <- J^T A J plus
 // the column update V <- V J.  A sweep applies every pair once; sweeps stop
-// when no off-diagonal element is above float32 noise (at most 16 sweeps).
+// when no off-diagonal element is above float32 noise (at most 16 sweeps);
+// that test is one pass over all pairs before each sweep.
 
 #include "device.h"
 #include "launch.h"
@@ -31,9 +32,16 @@ __device__ __forceinline__ void jacobi_sweeps(float (*A)[PS + 1], float (*V)[PS 
   const int m = MM > 0 ? MM : m_rt;
   const int half = m / 2;
   for (int sweep = 0; sweep < 16; ++sweep) {
-    bool rotated = false;   // any rotation this sweep (the block is one wave)
+    // A sweep whose pairs all fail the rotation test leaves A unchanged, so
+    // testing every pair on the current A at once decides the stop exactly as
+    // a sweep of no-op steps would (the block is one wave: a vote suffices).
+    bool any = false;
+    for (int idx = lane; idx < m * m; idx += 64) {
+      const int a = idx / m, b = idx - (idx / m) * m;
+      if (a < b) any = any || fabsf(A[a][b]) > 1e-7f * sqrtf(fabsf(A[a][a] * A[b][b])) + tiny;
+    }
+    if (!__any(any)) break;
     for (int step = 0; step < m - 1; ++step) {
-      bool rot = false;
       if (lane < half) {
         // circle method: player 0 fixed, players 1..m-1 rotate
         int x, y;
@@ -50,11 +58,9 @@ __device__ __forceinline__ void jacobi_sweeps(float (*A)[PS + 1], float (*V)[PS 
           const float t = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
           c = 1.f / sqrtf(t * t + 1.f);
           s = t * c;
-          rot = true;
         }
         rot_p[lane] = p; rot_q[lane] = qq; rot_c[lane] = c; rot_s[lane] = s;
       }
-      rotated = rotated || __any(rot);
       __syncthreads();
       for (int blk = lane; blk < half * half; blk += 64) {
         const int a = blk / half, bb = blk - a * half;
@@ -78,7 +84,6 @@ __device__ __forceinline__ void jacobi_sweeps(float (*A)[PS + 1], float (*V)[PS 
       }
       __syncthreads();
     }
-    if (!rotated) break;
   }
 
 }
