@@ -527,6 +527,23 @@ def main():
                                              "only, not the path"}
         log(f"[bench] dense attention (k = Np): {dense_us:.1f} us, {dense_b / (dense_us * 1e3):.0f} GB/s")
         del dsel, dws
+    # append-time summary build, for context (not in the step): the newest
+    # page of every sequence rebuilt from its keys, one call per layer; the
+    # rebuild writes the same record, so the layers are unchanged
+    if not args.no_extras and getattr(layers[0], "summary", None) is not None and layers[0].seq_lens_np.min() >= 1:
+        last = (layers[0].seq_lens_np - 1) // w.P
+        ent = torch.from_numpy(np.stack([np.arange(w.B), last], 1).astype(np.int32)).cuda()
+        nval = torch.from_numpy((layers[0].seq_lens_np - last * w.P).astype(np.int32)).cuda()
+        sb_us, _ = graph_avg_us(lambda li, q: kv.summary_build(layers[li].L, layers[li].k_src, layers[li].bt, ent,
+                                                                nval, layers[li].summary, layers[li].log_n))
+        result["append_summary_build"] = {
+            "avg_launch_us": sb_us, "page_heads": w.B * w.Hkv, "page_size": w.P,
+            "amortized_us_per_step": sb_us / w.P,
+            "note": "kv_summary_build of the newest page of every sequence (one page per sequence per P "
+                    "decode steps); append-time work, not in the timed step"}
+        log(f"[bench] append-time summary build ({w.B * w.Hkv} page-heads): {sb_us:.1f} us per call, "
+            f"{sb_us / w.P:.1f} us per step amortised")
+        del ent, nval
     # coverage-mode selection (k per row from the mass prefix) on the headline
     # layers' scores: its kernel time and the k it picks, for context
     from quantized_kv_cache_summary_amd import kvsparse as kvs
