@@ -22,6 +22,14 @@
 
 namespace kvs {
 
+// Whether the pair (p, q) is rotated: its off-diagonal element is above
+// float32 noise relative to the diagonal (tiny: an absolute floor).  The
+// hardware square root (about 1 ulp) serves: only the same test must be used
+// by the stop check and the steps.
+__device__ __forceinline__ bool rotation_wanted(float app, float aqq, float apq, float tiny) {
+  return fabsf(apq) > 1e-7f * __builtin_amdgcn_sqrtf(fabsf(app * aqq)) + tiny;
+}
+
 // Cyclic Jacobi on the m x m matrix A (LDS, symmetric), accumulating the
 // rotations into V.  MM > 0 fixes m at compile time (a full page, the common
 // case), so the schedule's index arithmetic folds to constants.
@@ -38,7 +46,7 @@ __device__ __forceinline__ void jacobi_sweeps(float (*A)[PS + 1], float (*V)[PS 
     bool any = false;
     for (int idx = lane; idx < m * m; idx += 64) {
       const int a = idx / m, b = idx - (idx / m) * m;
-      if (a < b) any = any || fabsf(A[a][b]) > 1e-7f * sqrtf(fabsf(A[a][a] * A[b][b])) + tiny;
+      if (a < b) any = any || rotation_wanted(A[a][a], A[b][b], A[a][b], tiny);
     }
     if (!__any(any)) break;
     for (int step = 0; step < m - 1; ++step) {
@@ -53,10 +61,14 @@ __device__ __forceinline__ void jacobi_sweeps(float (*A)[PS + 1], float (*V)[PS 
         const int p = x < y ? x : y, qq = x < y ? y : x;
         const float app = A[p][p], aqq = A[qq][qq], apq = A[p][qq];
         float c = 1.f, s = 0.f;
-        if (fabsf(apq) > 1e-7f * sqrtf(fabsf(app * aqq)) + tiny) {
-          const float theta = (aqq - app) / (2.f * apq);
-          const float t = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
-          c = 1.f / sqrtf(t * t + 1.f);
+        if (rotation_wanted(app, aqq, apq, tiny)) {
+          // the rotation that zeroes A[p][q] (smaller angle), with the
+          // hardware reciprocal, square root and reciprocal square root: an
+          // ulp in c or s only changes how fast the sweeps converge
+          const float theta = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
+          const float t = (theta >= 0.f ? 1.f : -1.f) *
+                          __builtin_amdgcn_rcpf(fabsf(theta) + __builtin_amdgcn_sqrtf(theta * theta + 1.f));
+          c = __builtin_amdgcn_rsqf(t * t + 1.f);
           s = t * c;
         }
         rot_p[lane] = p; rot_q[lane] = qq; rot_c[lane] = c; rot_s[lane] = s;
