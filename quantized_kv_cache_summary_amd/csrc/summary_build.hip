@@ -30,47 +30,64 @@ __device__ __forceinline__ bool rotation_wanted(float app, float aqq, float apq,
   return fabsf(apq) > 1e-7f * __builtin_amdgcn_sqrtf(fabsf(app * aqq)) + tiny;
 }
 
+// Pair k of a step of the round-robin ("circle") schedule over m players:
+// player 0 stays, players 1..m-1 rotate; p < q.
+__device__ __forceinline__ void circle_pair(int step, int k, int m, int& p, int& q) {
+  int x, y;
+  if (k == 0) { x = 0; y = 1 + (step % (m - 1)); }
+  else {
+    x = 1 + ((step + k) % (m - 1));
+    y = 1 + ((step + m - 1 - k) % (m - 1));
+  }
+  p = x < y ? x : y;
+  q = x < y ? y : x;
+}
+
+// The rotation (c, s) that zeroes A[p][q] (smaller angle), or the identity
+// when the pair fails the test.  Hardware reciprocal, square root and
+// reciprocal square root: an ulp in c or s only changes how fast the sweeps
+// converge.
+__device__ __forceinline__ void jacobi_rotation(float app, float aqq, float apq, float tiny, float& c, float& s) {
+  c = 1.f;
+  s = 0.f;
+  if (rotation_wanted(app, aqq, apq, tiny)) {
+    const float theta = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
+    const float t = (theta >= 0.f ? 1.f : -1.f) *
+                    __builtin_amdgcn_rcpf(fabsf(theta) + __builtin_amdgcn_sqrtf(theta * theta + 1.f));
+    c = __builtin_amdgcn_rsqf(t * t + 1.f);
+    s = t * c;
+  }
+}
+
+// A sweep whose pairs all fail the rotation test leaves A unchanged, so
+// testing every pair on the current A at once decides the stop exactly as a
+// sweep of no-op steps would (the block is one wave: a vote suffices).
+template <int PS>
+__device__ __forceinline__ bool jacobi_converged(float (*A)[PS + 1], int m, float tiny) {
+  bool any = false;
+  for (int idx = threadIdx.x; idx < m * m; idx += 64) {
+    const int a = idx / m, b = idx - (idx / m) * m;
+    if (a < b) any = any || rotation_wanted(A[a][a], A[b][b], A[a][b], tiny);
+  }
+  return !__any(any);
+}
+
 // Cyclic Jacobi on the m x m matrix A (LDS, symmetric), accumulating the
-// rotations into V.  MM > 0 fixes m at compile time (a full page, the common
-// case), so the schedule's index arithmetic folds to constants.
-template <int PS, int MM>
+// rotations into V.  Any m: the n/2 rotations of a step are computed by the
+// first lanes and handed to the update through LDS.
+template <int PS>
 __device__ __forceinline__ void jacobi_sweeps(float (*A)[PS + 1], float (*V)[PS + 1], float* rot_c, float* rot_s,
-                                              int* rot_p, int* rot_q, int m_rt, float tiny) {
+                                              int* rot_p, int* rot_q, int m, float tiny) {
   const int lane = threadIdx.x;
-  const int m = MM > 0 ? MM : m_rt;
   const int half = m / 2;
   for (int sweep = 0; sweep < 16; ++sweep) {
-    // A sweep whose pairs all fail the rotation test leaves A unchanged, so
-    // testing every pair on the current A at once decides the stop exactly as
-    // a sweep of no-op steps would (the block is one wave: a vote suffices).
-    bool any = false;
-    for (int idx = lane; idx < m * m; idx += 64) {
-      const int a = idx / m, b = idx - (idx / m) * m;
-      if (a < b) any = any || rotation_wanted(A[a][a], A[b][b], A[a][b], tiny);
-    }
-    if (!__any(any)) break;
+    if (jacobi_converged<PS>(A, m, tiny)) break;
     for (int step = 0; step < m - 1; ++step) {
       if (lane < half) {
-        // circle method: player 0 fixed, players 1..m-1 rotate
-        int x, y;
-        if (lane == 0) { x = 0; y = 1 + (step % (m - 1)); }
-        else {
-          x = 1 + ((step + lane) % (m - 1));
-          y = 1 + ((step + m - 1 - lane) % (m - 1));
-        }
-        const int p = x < y ? x : y, qq = x < y ? y : x;
-        const float app = A[p][p], aqq = A[qq][qq], apq = A[p][qq];
-        float c = 1.f, s = 0.f;
-        if (rotation_wanted(app, aqq, apq, tiny)) {
-          // the rotation that zeroes A[p][q] (smaller angle), with the
-          // hardware reciprocal, square root and reciprocal square root: an
-          // ulp in c or s only changes how fast the sweeps converge
-          const float theta = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
-          const float t = (theta >= 0.f ? 1.f : -1.f) *
-                          __builtin_amdgcn_rcpf(fabsf(theta) + __builtin_amdgcn_sqrtf(theta * theta + 1.f));
-          c = __builtin_amdgcn_rsqf(t * t + 1.f);
-          s = t * c;
-        }
+        int p, qq;
+        circle_pair(step, lane, m, p, qq);
+        float c, s;
+        jacobi_rotation(A[p][p], A[qq][qq], A[p][qq], tiny, c, s);
         rot_p[lane] = p; rot_q[lane] = qq; rot_c[lane] = c; rot_s[lane] = s;
       }
       __syncthreads();
@@ -97,7 +114,70 @@ __device__ __forceinline__ void jacobi_sweeps(float (*A)[PS + 1], float (*V)[PS 
       __syncthreads();
     }
   }
+}
 
+// The same sweeps for a full page (m = PS = 16 or 32), with no LDS handoff:
+// every lane owns the 2x2 blocks (a, bb) with bb = lane mod PS/2 fixed, and
+// the V entries of the same column pair bb, and computes the rotations of its
+// own pairs itself from the current A.  All of a step's LDS reads precede its
+// writes (one wave: LDS serves them in program order), so each step is one
+// round trip.  The rotations and updates are those of the general path (the
+// compiler may fuse a product into a multiply-add differently, so the last
+// bit can differ).
+template <int PS>
+__device__ __forceinline__ void jacobi_sweeps_full(float (*A)[PS + 1], float (*V)[PS + 1], float tiny) {
+  constexpr int M = PS, H = PS / 2;
+  constexpr int AS = 64 / H;           // the lane's blocks are rows a0, a0 + AS, ...
+  constexpr int NB = H * H / 64;       // blocks per lane
+  constexpr int NV = M * H / 64;       // V entry pairs per lane
+  static_assert(64 % H == 0 && NB >= 1 && NV >= 1, "full-page Jacobi needs PS = 16 or 32");
+  const int lane = threadIdx.x;
+  const int bb = lane % H, a0 = lane / H;
+  for (int sweep = 0; sweep < 16; ++sweep) {
+    if (jacobi_converged<PS>(A, M, tiny)) break;
+    for (int step = 0; step < M - 1; ++step) {
+      int pb, qb, pa[NB], qa[NB];
+      circle_pair(step, bb, M, pb, qb);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) circle_pair(step, a0 + AS * i, M, pa[i], qa[i]);
+      // reads
+      const float bpp = A[pb][pb], bqq = A[qb][qb], bpq = A[pb][qb];
+      float app[NB], aqq[NB], apq[NB], b00[NB], b01[NB], b10[NB], b11[NB], vp[NV], vq[NV];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        app[i] = A[pa[i]][pa[i]]; aqq[i] = A[qa[i]][qa[i]]; apq[i] = A[pa[i]][qa[i]];
+        b00[i] = A[pa[i]][pb]; b01[i] = A[pa[i]][qb]; b10[i] = A[qa[i]][pb]; b11[i] = A[qa[i]][qb];
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int r = a0 + AS * i;
+        vp[i] = V[r][pb];
+        vq[i] = V[r][qb];
+      }
+      // rotations of the lane's pairs
+      float cb, sb;
+      jacobi_rotation(bpp, bqq, bpq, tiny, cb, sb);
+      // writes
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        float ca, sa;
+        jacobi_rotation(app[i], aqq[i], apq[i], tiny, ca, sa);
+        const float t00 = ca * b00[i] - sa * b10[i], t01 = ca * b01[i] - sa * b11[i];
+        const float t10 = sa * b00[i] + ca * b10[i], t11 = sa * b01[i] + ca * b11[i];
+        A[pa[i]][pb] = t00 * cb - t01 * sb;
+        A[pa[i]][qb] = t00 * sb + t01 * cb;
+        A[qa[i]][pb] = t10 * cb - t11 * sb;
+        A[qa[i]][qb] = t10 * sb + t11 * cb;
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int r = a0 + AS * i;
+        V[r][pb] = cb * vp[i] - sb * vq[i];
+        V[r][qb] = sb * vp[i] + cb * vq[i];
+      }
+      __syncthreads();
+    }
+  }
 }
 
 template <int D, int PS, bool F16>
@@ -175,8 +255,8 @@ __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __res
   for (int a = 0; a < m; ++a) trace += A[a][a];
   const float tiny = 1e-12f * trace;
 
-  if (m == PS) jacobi_sweeps<PS, PS>(A, V, rot_c, rot_s, rot_p, rot_q, m, tiny);
-  else jacobi_sweeps<PS, 0>(A, V, rot_c, rot_s, rot_p, rot_q, m, tiny);
+  if (m == PS) jacobi_sweeps_full<PS>(A, V, tiny);
+  else jacobi_sweeps<PS>(A, V, rot_c, rot_s, rot_p, rot_q, m, tiny);
 
   // eigenvalues descending (ties by index) -> order[rank] = column
   if (lane < m) {
