@@ -24,7 +24,9 @@ SMALL = {
     "llama_small": W["llama8b_32k"].replace(B=2, ctx=16 * 300 + 7),        # 301 pages, 7-token tail
     "qwen_small": W["qwen3b_128k"].replace(B=2, ctx=16 * 400),             # G = 8
     "heavy_small": W["heavy70b_128k"].replace(B=2, Hq=16, Hkv=2, ctx=32 * 150 + 5, v_host=False),  # P = 32
-    # summary builder only: clustered (low-rank) keys, and float16 keys at P = 32
+}
+# summary builder only: clustered (low-rank) keys, and float16 keys at P = 32
+SUMMARY_ONLY = {
     "gmm_small": W["tiers_64k"].replace(B=2, ctx=16 * 120 + 9, keys="gmm", gmm_centers=64, gmm_std=0.5),
     "heavy_f16_small": W["heavy70b_128k"].replace(B=2, Hq=16, Hkv=2, ctx=32 * 60 + 17, v_host=False,
                                                   dtype="f16"),
@@ -358,7 +360,7 @@ def test_attention_edge_cases(hz):
 
 @pytest.mark.parametrize("name", ["tiny", "llama_small", "heavy_small", "gmm_small", "heavy_f16_small"])
 def test_summary_builder_invariants(hz, name):
-    w = SMALL[name]
+    w = SMALL[name] if name in SMALL else SUMMARY_ONLY[name]
     lens = [w.ctx, w.ctx - w.P - 3] if w.B == 2 else [w.ctx]
     announce(f"summary build {name}")
     layer = hz.DeviceLayer(w, summaries="build", seq_lens=lens)
