@@ -83,7 +83,10 @@ enum { KV_TIER_NATIVE = 0, KV_TIER_I8 = 1, KV_TIER_I4 = 2, KV_TIER_I2 = 3, KV_TI
 
 /* One layer's paged cache geometry.
  * Supported: head_dim in {64, 128}; page_size in {16, 32}; rank in {1, 2, 4, 8};
- * num_q_heads a multiple of num_kv_heads with G = Hq / Hkv <= 16;
+ * num_q_heads a multiple of num_kv_heads with G = Hq / Hkv <= 16 for the
+ * summary, score and selection calls, and G <= 8 for every call that runs the
+ * attention (kv_sparse_decode_attn, kv_topk_sparse_decode_attn and the
+ * whole-step call kv_sparse_decode_step: KV_ERR_UNSUPPORTED above);
  * kv_dtype KV_F16 or KV_BF16.  softmax_scale <= 0 selects 1/sqrt(head_dim). */
 typedef struct kv_layout {
   int32_t num_q_heads;
@@ -313,10 +316,14 @@ int kv_page_topk_coverage(const kv_layout* layout, const float* head_scores, con
  * Split-K: num_splits > 0 fixes the number of partial results per row (at
  * most 256); 0 lets the library choose.  Results agree across split counts to
  * float32 rounding.  ws/ws_bytes: kv_sparse_decode_attn_workspace_size() with
- * the same num_splits.  The workspace ends with one counter per row that must
- * be zero when a call starts: zero it once after allocating; every completed
- * call leaves the counters at zero.  Calls that share a workspace must not
- * overlap in time.
+ * the same num_splits (or more).  The workspace starts with one uint32 counter
+ * per row (B * Hkv of them) that must be zero when a call starts: zero it once
+ * after allocating; every completed call leaves the counters at zero.  The
+ * split partials follow from the first 256-byte boundary after the counters,
+ * so one workspace serves calls over the same B * Hkv rows with any split
+ * count up to the one it was sized for, native or packed pages alike; reused
+ * for a different number of rows it must be zeroed again.  Calls that share a
+ * workspace must not overlap in time.
  * --------------------------------------------------------------------------- */
 int kv_sparse_decode_attn(const kv_layout* layout, const void* q, const kv_pages* pages,
                           const int32_t* block_table, const int32_t* seq_lens, int32_t B,

@@ -35,7 +35,7 @@ per-step error bounds.
 
 import numpy as np
 
-from .codec import TIER_NATIVE, TIER_FP8, TIER_I8, TIER_I4, TIER_I2, TIER_B1, encode_vector, decode_vector
+from .codec import TIER_NATIVE, TIER_FP8, TIER_I8, TIER_I4, TIER_I2, TIER_B1, encode_vector
 
 TIER_OF_LEVEL = (TIER_NATIVE, TIER_FP8, TIER_I8, TIER_I4, TIER_I2, TIER_B1)
 LEVEL_OF_TIER = {t: l for l, t in enumerate(TIER_OF_LEVEL)}
@@ -85,7 +85,3 @@ def retier_vectors(x, old_tier, new_tier, d):
     assert new_tier != TIER_NATIVE and LEVEL_OF_TIER[new_tier] > LEVEL_OF_TIER[old_tier]
     return encode_vector(np.asarray(x, dtype=np.float32), new_tier)
 
-
-def decoded(packed, scale_zero, tier, d):
-    """float32 values of packed token vectors (the attention kernel's decode)."""
-    return decode_vector(packed, scale_zero, tier, d)

@@ -27,6 +27,13 @@ int check_layout(const kv_layout* L) {
   return KV_OK;
 }
 
+// Attention (and every call that runs it) takes at most eight query heads per
+// KV head; scoring and selection take up to sixteen.
+constexpr int kMaxAttnGroup = 8;
+int check_attn_group(const kv_layout* L) {
+  return L->num_q_heads / L->num_kv_heads > kMaxAttnGroup ? KV_ERR_UNSUPPORTED : KV_OK;
+}
+
 float scale_of(const kv_layout* L) {
   return L->softmax_scale > 0.f ? L->softmax_scale : 1.0f / std::sqrt((float)L->head_dim);
 }
@@ -283,6 +290,7 @@ int kv_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages* pg,
                           int32_t k_max, int32_t num_splits, float* out, float* lse, void* ws,
                           size_t ws_bytes, void* stream) {
   int rc = check_layout(L);
+  if (!rc) rc = check_attn_group(L);
   if (rc) return rc;
   if (B < 0 || max_pages < 0 || k_max < 0 || num_splits < 0) return KV_ERR_INVALID_ARG;
   if (num_splits > kvs::kMaxSplits) return KV_ERR_UNSUPPORTED;
@@ -298,13 +306,13 @@ int kv_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages* pg,
   const size_t need = kv_sparse_decode_attn_workspace_size(L, B, k_max, s);
   if (!ws || ws_bytes < need) return KV_ERR_WORKSPACE;
   return from_hip(kvs::launch_sparse_attn(*L, q, *pg, block_table, seq_lens, B, max_pages, sel,
-                                          sel_count, k_max, s, scale_of(L), out, lse, (float*)ws,
-                                          (hipStream_t)stream));
+                                          sel_count, k_max, s, scale_of(L), out, lse,
+                                          kvs::attn_scratch_in(ws, rows), (hipStream_t)stream));
 }
 
 int32_t kv_topk_sparse_decode_attn_supported(const kv_layout* L, int32_t max_pages, int32_t k_max,
                                              int32_t num_splits) {
-  if (check_layout(L) || max_pages < 0 || k_max < 0 || num_splits <= 0 || num_splits > kvs::kMaxSplits) return 0;
+  if (check_layout(L) || check_attn_group(L) || max_pages < 0 || k_max < 0 || num_splits <= 0 || num_splits > kvs::kMaxSplits) return 0;
   if (max_pages > kvs::kMaxTopkPages) return 0;
   return kvs::topk_attn_dyn_lds_bytes(*L, max_pages, k_max, num_splits) <= kvs::kTopkAttnMaxLds ? 1 : 0;
 }
@@ -317,6 +325,7 @@ int kv_topk_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages
                                float* page_S, int32_t num_splits, float* out, float* lse, void* ws,
                                size_t ws_bytes, void* stream) {
   int rc = check_layout(L);
+  if (!rc) rc = check_attn_group(L);
   if (rc) return rc;
   if (B < 0 || max_pages < 0 || k_max < 0 || k_fixed < 0 || n_force_first < 0 || n_force_last < 0 ||
       num_splits < 0)
@@ -344,8 +353,8 @@ int kv_topk_sparse_decode_attn(const kv_layout* L, const void* q, const kv_pages
   return from_hip(kvs::launch_topk_sparse_attn(*L, q, *pg, block_table, seq_lens, B, max_pages, head_scores,
                                                lse_partial, cov ? 0.f : keep_frac, cov ? 0 : k_fixed,
                                                cov ? coverage : -1.f, n_force_first, n_force_last, sel,
-                                               sel_count, k_max, page_S, s, scale_of(L), out, lse, (float*)ws,
-                                               (hipStream_t)stream));
+                                               sel_count, k_max, page_S, s, scale_of(L), out, lse,
+                                               kvs::attn_scratch_in(ws, rows), (hipStream_t)stream));
 }
 
 size_t kv_sparse_decode_step_workspace_size(const kv_layout* L, int32_t B, int32_t k_max, int32_t num_splits) {
@@ -354,7 +363,8 @@ size_t kv_sparse_decode_step_workspace_size(const kv_layout* L, int32_t B, int32
 
 int32_t kv_sparse_decode_step_supported(const kv_layout* L, int32_t B, int32_t max_pages, int32_t k_max,
                                         int32_t num_splits) {
-  if (check_layout(L) || B < 0 || max_pages < 1 || k_max < 0 || num_splits < 0 || num_splits > kvs::kMaxSplits)
+  if (check_layout(L) || check_attn_group(L) || B < 0 || max_pages < 1 || k_max < 0 || num_splits < 0 ||
+      num_splits > kvs::kMaxSplits)
     return 0;
   return max_pages <= kvs::kMaxTopkPages ? 1 : 0;
 }
@@ -371,13 +381,19 @@ int32_t kv_sparse_decode_step_fused(const kv_layout* L, const kv_pages* pages, i
   return kvs::topk_attn_dyn_lds_bytes(*L, max_pages, k_max, s) <= kvs::kTopkAttnMaxLds ? 1 : 0;
 }
 
-int kv_sparse_decode_step(const kv_layout* L, const void* q, const void* summary, const float* log_n,
-                          const kv_pages* pg, const int32_t* block_table, const int32_t* seq_lens, int32_t B,
-                          int32_t max_pages, float keep_frac, int32_t k_fixed, float coverage,
-                          int32_t n_force_first, int32_t n_force_last, float* head_scores, float* lse_partial,
-                          int32_t* sel, int32_t* sel_count, int32_t k_max, float* page_S, int32_t num_splits,
-                          float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation of kv_sparse_decode_step's arguments other than its workspace;
+// sets the split count the call uses.
+int check_step(const kv_layout* L, const void* q, const void* summary, const float* log_n, const kv_pages* pg,
+               const int32_t* block_table, const int32_t* seq_lens, int32_t B, int32_t max_pages, float keep_frac,
+               int32_t k_fixed, float coverage, int32_t n_force_first, int32_t n_force_last,
+               const float* head_scores, const float* lse_partial, const int32_t* sel, const int32_t* sel_count,
+               int32_t k_max, int32_t num_splits, const float* out, const float* lse, int* splits) {
   int rc = check_layout(L);
+  if (!rc) rc = check_attn_group(L);
   if (rc) return rc;
   if (B < 0 || max_pages < 0 || k_max < 0 || k_fixed < 0 || n_force_first < 0 || n_force_last < 0 ||
       num_splits < 0)
@@ -387,6 +403,7 @@ int kv_sparse_decode_step(const kv_layout* L, const void* q, const void* summary
   if (!cov && (!(keep_frac >= 0.f) || !std::isfinite(keep_frac))) return KV_ERR_INVALID_ARG;
   if (cov && k_max < 1) return KV_ERR_INVALID_ARG;
   if (num_splits > kvs::kMaxSplits) return KV_ERR_UNSUPPORTED;
+  *splits = 1;
   if (B == 0) return KV_OK;
   if (max_pages == 0) return KV_ERR_INVALID_ARG;
   if (max_pages > kvs::kMaxTopkPages) return KV_ERR_UNSUPPORTED;
@@ -400,26 +417,68 @@ int kv_sparse_decode_step(const kv_layout* L, const void* q, const void* summary
   if (rc) return rc;
   const int rows = B * L->num_kv_heads;
   if ((int64_t)rows > 65535) return KV_ERR_UNSUPPORTED;
-  const bool tiered = pg->page_entry != nullptr;
-  const int s = num_splits > 0 ? num_splits : auto_splits(rows, k_max, tiered);
+  *splits = num_splits > 0 ? num_splits : auto_splits(rows, k_max, pg->page_entry != nullptr);
+  return KV_OK;
+}
+
+// The whole step's launches (arguments already validated).
+int enqueue_step(const kv_layout* L, const void* q, const void* summary, const float* log_n, const kv_pages* pg,
+                 const int32_t* block_table, const int32_t* seq_lens, int32_t B, int32_t max_pages, float keep_frac,
+                 int32_t k_fixed, float coverage, int32_t n_force_first, int32_t n_force_last, float* head_scores,
+                 float* lse_partial, int32_t* sel, int32_t* sel_count, int32_t k_max, float* page_S, int s,
+                 float* out, float* lse, kvs::AttnScratch sc, hipStream_t st);
+
+}  // namespace
+
+extern "C" {
+
+int kv_sparse_decode_step(const kv_layout* L, const void* q, const void* summary, const float* log_n,
+                          const kv_pages* pg, const int32_t* block_table, const int32_t* seq_lens, int32_t B,
+                          int32_t max_pages, float keep_frac, int32_t k_fixed, float coverage,
+                          int32_t n_force_first, int32_t n_force_last, float* head_scores, float* lse_partial,
+                          int32_t* sel, int32_t* sel_count, int32_t k_max, float* page_S, int32_t num_splits,
+                          float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int s = 1;
+  const int rc = check_step(L, q, summary, log_n, pg, block_table, seq_lens, B, max_pages, keep_frac, k_fixed,
+                            coverage, n_force_first, n_force_last, head_scores, lse_partial, sel, sel_count, k_max,
+                            num_splits, out, lse, &s);
+  if (rc || B == 0) return rc;
   if (!ws || ws_bytes < kv_sparse_decode_attn_workspace_size(L, B, k_max, s)) return KV_ERR_WORKSPACE;
-  const hipStream_t st = (hipStream_t)stream;
+  return enqueue_step(L, q, summary, log_n, pg, block_table, seq_lens, B, max_pages, keep_frac, k_fixed, coverage,
+                      n_force_first, n_force_last, head_scores, lse_partial, sel, sel_count, k_max, page_S, s, out,
+                      lse, kvs::attn_scratch_in(ws, B * L->num_kv_heads), (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int enqueue_step(const kv_layout* L, const void* q, const void* summary, const float* log_n, const kv_pages* pg,
+                 const int32_t* block_table, const int32_t* seq_lens, int32_t B, int32_t max_pages, float keep_frac,
+                 int32_t k_fixed, float coverage, int32_t n_force_first, int32_t n_force_last, float* head_scores,
+                 float* lse_partial, int32_t* sel, int32_t* sel_count, int32_t k_max, float* page_S, int s,
+                 float* out, float* lse, kvs::AttnScratch sc, hipStream_t st) {
+  const bool cov = coverage >= 0.f;
   const float tau = scale_of(L);
   const float kf = cov ? 0.f : keep_frac, cv = cov ? coverage : -1.f;
   const int kx = cov ? 0 : k_fixed;
-  rc = from_hip(kvs::launch_page_score(*L, q, summary, log_n, seq_lens, B, max_pages, tau, head_scores,
-                                       lse_partial, st));
+  int rc = from_hip(kvs::launch_page_score(*L, q, summary, log_n, seq_lens, B, max_pages, tau, head_scores,
+                                           lse_partial, st));
   if (rc) return rc;
   if (kv_sparse_decode_step_fused(L, pg, B, max_pages, k_max, s))
     return from_hip(kvs::launch_topk_sparse_attn(*L, q, *pg, block_table, seq_lens, B, max_pages, head_scores,
                                                  lse_partial, kf, kx, cv, n_force_first, n_force_last, sel,
-                                                 sel_count, k_max, page_S, s, tau, out, lse, (float*)ws, st));
+                                                 sel_count, k_max, page_S, s, tau, out, lse, sc, st));
   rc = from_hip(kvs::launch_page_topk(*L, head_scores, lse_partial, seq_lens, B, max_pages, kf, kx, cv,
                                       n_force_first, n_force_last, sel, sel_count, k_max, page_S, st));
   if (rc) return rc;
   return from_hip(kvs::launch_sparse_attn(*L, q, *pg, block_table, seq_lens, B, max_pages, sel, sel_count, k_max,
-                                          s, tau, out, lse, (float*)ws, st));
+                                          s, tau, out, lse, sc, st));
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t kv_hot_admit_workspace_size(int32_t n_slots) {
   return n_slots > 0 ? kvs::hot_admit_workspace_bytes(n_slots) : 0;

@@ -18,14 +18,27 @@ constexpr int kMaxSplits = 256;
 
 inline int score_tiles(int max_pages) { return (max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock; }
 
-// Attention workspace: per (row, split, head) partials [d + 2] floats, then one
-// uint32 counter per row (zero between calls).
-inline size_t attn_partial_floats(int rows, int splits, int G, int d) {
-  const size_t n = (size_t)rows * splits * G * (d + 2);
-  return (n + 3) & ~(size_t)3;   // keeps the counters 16-byte aligned
+// Attention workspace: one uint32 counter per row first (zero between calls),
+// then per (row, split, head) partials [d + 2] floats from a 256-byte boundary.
+// The counters sit at a fixed offset whatever the split count or page kind, so
+// one workspace serves calls with different split counts over the same rows.
+inline size_t attn_counter_bytes(int rows) { return ((size_t)rows * sizeof(unsigned) + 255) & ~(size_t)255; }
+inline size_t attn_partial_bytes(int rows, int splits, int G, int d) {
+  return (size_t)rows * splits * G * (d + 2) * sizeof(float);
 }
 inline size_t attn_workspace_bytes(int rows, int splits, int G, int d) {
-  return attn_partial_floats(rows, splits, G, d) * sizeof(float) + (size_t)rows * sizeof(unsigned);
+  return attn_counter_bytes(rows) + attn_partial_bytes(rows, splits, G, d);
+}
+
+// Where the attention keeps its cross-block state: one counter per row (zero
+// between calls) and the split partials.
+struct AttnScratch {
+  unsigned* counters;
+  float* partials;
+};
+inline AttnScratch attn_scratch_in(void* ws, int rows) {
+  return AttnScratch{reinterpret_cast<unsigned*>(ws),
+                     reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + attn_counter_bytes(rows))};
 }
 
 // Shared-basis build: covariance statistics per (row, chunk of pages), then
@@ -86,7 +99,7 @@ hipError_t launch_page_topk(const kv_layout& L, const float* head_scores, const 
 hipError_t launch_sparse_attn(const kv_layout& L, const void* q, const kv_pages& pg,
                               const int32_t* block_table, const int32_t* seq_lens, int B,
                               int max_pages, const int32_t* sel, const int32_t* sel_count, int k_max,
-                              int n_splits, float tau, float* out, float* lse, float* partials,
+                              int n_splits, float tau, float* out, float* lse, AttnScratch sc,
                               hipStream_t st);
 
 // Fused selector + attention: every block of a row selects the row's pages
@@ -101,7 +114,7 @@ hipError_t launch_topk_sparse_attn(const kv_layout& L, const void* q, const kv_p
                                    const float* head_scores, const float* lse_partial, float keep, int k_fixed,
                                    float coverage, int n_force_first, int n_force_last, int32_t* sel,
                                    int32_t* sel_count, int k_max, float* page_S, int n_splits, float tau,
-                                   float* out, float* lse, float* partials, hipStream_t st);
+                                   float* out, float* lse, AttnScratch sc, hipStream_t st);
 
 hipError_t launch_dequant_tier(const kv_layout& L, const kv_pages& pg, const int32_t* pages, int n,
                                float* out, hipStream_t st);

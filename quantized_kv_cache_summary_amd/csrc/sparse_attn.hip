@@ -156,7 +156,7 @@ struct AttnLaunch {
   float tau;
   float* out;
   float* lse;
-  float* partials;
+  AttnScratch sc;
   SelArgs sa;
   size_t dyn_lds;
 };
@@ -165,20 +165,19 @@ template <int D, int GM, bool F16, bool TIERED, bool SEL>
 static hipError_t launch_attn_t(const kv_layout& L, const AttnLaunch& a, hipStream_t st) {
   const int G = L.num_q_heads / L.num_kv_heads;
   const int rows = a.B * L.num_kv_heads;
-  unsigned* counters = reinterpret_cast<unsigned*>(a.partials + attn_partial_floats(rows, a.n_splits, G, D));
   hipLaunchKernelGGL((sparse_attn_kernel<D, GM, F16, TIERED, SEL>), dim3(a.n_splits, rows),
                      dim3(64 * attn_waves<GM, SEL>()), a.dyn_lds, st, (const uint16_t*)a.q, a.pd, a.bt, a.sl,
                      L.num_kv_heads, G, L.page_size, a.max_pages, a.sel, a.cnt, a.k_max, a.n_splits,
-                     a.tau * kLog2e, a.partials, counters, a.out, a.lse, a.sa);
+                     a.tau * kLog2e, a.sc.partials, a.sc.counters, a.out, a.lse, a.sa);
   return hipGetLastError();
 }
 
 template <int D, bool F16, bool TIERED, bool SEL>
 static hipError_t launch_attn_g(const kv_layout& L, const AttnLaunch& a, hipStream_t st) {
   const int G = L.num_q_heads / L.num_kv_heads;
+  // the C ABI refuses groups wider than eight query heads for attention
   if (G <= 4) return launch_attn_t<D, 4, F16, TIERED, SEL>(L, a, st);
-  if (G <= 8) return launch_attn_t<D, 8, F16, TIERED, SEL>(L, a, st);
-  return launch_attn_t<D, 16, F16, TIERED, SEL>(L, a, st);
+  return launch_attn_t<D, 8, F16, TIERED, SEL>(L, a, st);
 }
 
 template <bool SEL>
@@ -198,10 +197,10 @@ static hipError_t launch_attn_any(const kv_layout& L, const AttnLaunch& a, bool 
 hipError_t launch_sparse_attn(const kv_layout& L, const void* q, const kv_pages& pg,
                               const int32_t* block_table, const int32_t* seq_lens, int B,
                               int max_pages, const int32_t* sel, const int32_t* sel_count, int k_max,
-                              int n_splits, float tau, float* out, float* lse, float* partials,
+                              int n_splits, float tau, float* out, float* lse, AttnScratch sc,
                               hipStream_t st) {
   AttnLaunch a{q, to_dev(pg), block_table, seq_lens, B, max_pages, sel, sel_count, k_max, n_splits,
-               tau, out, lse, partials, SelArgs{}, 0};
+               tau, out, lse, sc, SelArgs{}, 0};
   return launch_attn_any<false>(L, a, pg.page_entry != nullptr, st);
 }
 
@@ -216,10 +215,8 @@ static size_t sel_dyn_bytes(int max_pages, int k_max, int n_splits) {
 size_t topk_attn_dyn_lds_bytes(const kv_layout& L, int max_pages, int k_max, int n_splits) {
   const int G = L.num_q_heads / L.num_kv_heads;
   if (L.head_dim == 64)
-    return G <= 4 ? sel_dyn_bytes<64, 4>(max_pages, k_max, n_splits)
-                  : (G <= 8 ? sel_dyn_bytes<64, 8>(max_pages, k_max, n_splits) : sel_dyn_bytes<64, 16>(max_pages, k_max, n_splits));
-  return G <= 4 ? sel_dyn_bytes<128, 4>(max_pages, k_max, n_splits)
-                : (G <= 8 ? sel_dyn_bytes<128, 8>(max_pages, k_max, n_splits) : sel_dyn_bytes<128, 16>(max_pages, k_max, n_splits));
+    return G <= 4 ? sel_dyn_bytes<64, 4>(max_pages, k_max, n_splits) : sel_dyn_bytes<64, 8>(max_pages, k_max, n_splits);
+  return G <= 4 ? sel_dyn_bytes<128, 4>(max_pages, k_max, n_splits) : sel_dyn_bytes<128, 8>(max_pages, k_max, n_splits);
 }
 
 hipError_t launch_topk_sparse_attn(const kv_layout& L, const void* q, const kv_pages& pg,
@@ -227,11 +224,11 @@ hipError_t launch_topk_sparse_attn(const kv_layout& L, const void* q, const kv_p
                                    const float* head_scores, const float* lse_partial, float keep, int k_fixed,
                                    float coverage, int n_force_first, int n_force_last, int32_t* sel,
                                    int32_t* sel_count, int k_max, float* page_S, int n_splits, float tau,
-                                   float* out, float* lse, float* partials, hipStream_t st) {
+                                   float* out, float* lse, AttnScratch sc, hipStream_t st) {
   SelArgs sa{head_scores, lse_partial, keep, k_fixed, coverage, n_force_first, n_force_last,
              score_tiles(max_pages), sel, sel_count, page_S};
   AttnLaunch a{q, to_dev(pg), block_table, seq_lens, B, max_pages, nullptr, nullptr, k_max, n_splits,
-               tau, out, lse, partials, sa, topk_attn_dyn_lds_bytes(L, max_pages, k_max, n_splits)};
+               tau, out, lse, sc, sa, topk_attn_dyn_lds_bytes(L, max_pages, k_max, n_splits)};
   return launch_attn_any<true>(L, a, pg.page_entry != nullptr, st);
 }
 

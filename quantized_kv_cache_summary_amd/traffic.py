@@ -18,14 +18,29 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 PROFILES = os.path.join(ROOT, "profiles")
-SCORE_SOURCES = ("page_score.hip", "score_tile.h", "device.h", "launch.h")
+# the sources each kernel family is compiled from: a counter reading stays
+# valid while their hash is unchanged
+KERNEL_SOURCES = {
+    "page_score_kernel": ("page_score.hip", "score_tile.h", "device.h", "launch.h"),
+    "page_topk_kernel": ("page_topk.hip", "select.h", "device.h", "launch.h"),
+    "sparse_attn_kernel": ("sparse_attn.hip", "attn_split.h", "select.h", "tiers.h", "device.h", "launch.h"),
+    "summary_build_kernel": ("summary_build.hip", "device.h", "launch.h"),
+}
 COPY_BYTES = 3 * (512 << 20)
 
 
-def score_kernel_hash():
+def kernel_family(name):
+    return name.replace("void ", "").replace("kvs::", "").split("<")[0].split("(")[0].strip()
+
+
+def kernel_sources_hash(name):
+    """sha256 over the sources of the kernel's family (None for other kernels)."""
+    srcs = KERNEL_SOURCES.get(kernel_family(name))
+    if srcs is None:
+        return None
     h = hashlib.sha256()
-    for name in SCORE_SOURCES:
-        h.update(open(os.path.join(PKG, "csrc", name), "rb").read())
+    for f in srcs:
+        h.update(open(os.path.join(PKG, "csrc", f), "rb").read())
     return h.hexdigest()
 
 
@@ -49,7 +64,7 @@ def traffic(args):
     f_factor = COPY_BYTES / (copy_f * 1024.0)
     w_factor = COPY_BYTES / (copy_w * 1024.0)
     rows = []
-    score = None
+    entries = {}
     for k in sorted(fetch, key=lambda k: -sum(fetch[k]) / len(fetch[k])):
         if not k.startswith("void kvs::") and not k.startswith("kvs::"):
             continue
@@ -57,8 +72,9 @@ def traffic(args):
         wk = sum(write.get(k, [0.0])) / max(1, len(write.get(k, [])))
         fb, wb = fk * 1024 * f_factor, wk * 1024 * w_factor
         rows.append((_short(k), len(fetch[k]), fk, wk, fb, wb))
-        if "page_score_kernel" in k:
-            score = (fb, wb)
+        entries[_short(k)] = {"dispatches": len(fetch[k]), "hbm_read_bytes_per_launch": fb,
+                              "hbm_write_bytes_per_launch": wb, "hbm_bytes_per_launch": fb + wb,
+                              "sources_sha256": kernel_sources_hash(_short(k))}
     os.makedirs(PROFILES, exist_ok=True)
     md = [f"# HBM traffic per dispatch, {args.workload}", "",
           f"Command (two passes, one counter each): `{args.command}`", "",
@@ -70,13 +86,9 @@ def traffic(args):
     for name, n, fk, wk, fb, wb in rows:
         md.append(f"| {name} | {n} | {fk:.1f} | {wk:.1f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
     open(os.path.join(PROFILES, f"traffic_{args.workload}.md"), "w").write("\n".join(md) + "\n")
-    if score is not None:
-        json.dump({"kernel": "page_score_kernel", "workload": args.workload,
-                   "kernel_source_sha256": score_kernel_hash(),
-                   "hbm_read_bytes_per_launch": score[0], "hbm_write_bytes_per_launch": score[1],
-                   "hbm_bytes_per_launch": score[0] + score[1],
-                   "fetch_factor": f_factor, "write_factor": w_factor, "command": args.command},
-                  open(os.path.join(PROFILES, f"page_score_{args.workload}_traffic.json"), "w"), indent=1)
+    json.dump({"workload": args.workload, "command": args.command, "fetch_factor": f_factor,
+               "write_factor": w_factor, "kernels": entries},
+              open(os.path.join(PROFILES, f"traffic_{args.workload}.json"), "w"), indent=1)
     print("\n".join(md))
 
 

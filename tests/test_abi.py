@@ -177,7 +177,8 @@ def test_fused_topk_attention_validation():
     assert call(max_pages=15361, k_max=15361) == kv.KV_ERR_UNSUPPORTED
     # the row's keys and a split's share of the selection must fit one block's LDS
     assert kv.topk_attn_supported(L, 2048, 164, s)
-    assert kv.topk_attn_supported(_L(num_q_heads=128), 2048, 2048, 1)
+    assert kv.topk_attn_supported(_L(num_q_heads=64), 2048, 2048, 1)        # G = 8, the widest group
+    assert not kv.topk_attn_supported(_L(num_q_heads=128), 2048, 2048, 1)   # G = 16: refused
     assert not kv.topk_attn_supported(L, 15360, 15360, 1)
     assert call(max_pages=15360, k_max=15360, keep=1.0, splits=1,
                 ws_bytes=kv.attn_workspace_size(L, 8, 15360, 1)) == kv.KV_ERR_UNSUPPORTED
@@ -353,3 +354,26 @@ def test_lowrank_validation():
     assert sc(B=0) == kv.KV_OK
     assert lib.kv_page_score_lowrank(ctypes.byref(_L(rank=3)), FAKE, FAKE, FAKE, FAKE, FAKE, 2, 300, FAKE, FAKE,
                                      None) == kv.KV_ERR_UNSUPPORTED
+
+
+def test_attention_refuses_groups_wider_than_eight():
+    """Score and selection take up to 16 query heads per KV head; every call
+    that runs the attention refuses more than 8 before any HIP call."""
+    L16 = _L(num_q_heads=128)                       # G = 16
+    pg = kv.KvPages()
+    pg.k16 = pg.v16 = FAKE
+    ws = kv.attn_workspace_size(L16, 8, 164)
+    rc = kv.lib().kv_sparse_decode_attn(ctypes.byref(L16), FAKE, ctypes.byref(pg), FAKE, FAKE, 8, 2048, FAKE, FAKE,
+                                        164, 0, FAKE, FAKE, FAKE, ws, None)
+    assert rc == kv.KV_ERR_UNSUPPORTED
+    rc = kv.lib().kv_topk_sparse_decode_attn(ctypes.byref(L16), FAKE, ctypes.byref(pg), FAKE, FAKE, 8, 2048, FAKE,
+                                             FAKE, 0.08, 0, -1.0, 0, 0, FAKE, FAKE, 164, None, 0, FAKE, FAKE, FAKE,
+                                             ws, None)
+    assert rc == kv.KV_ERR_UNSUPPORTED
+    rc = kv.lib().kv_sparse_decode_step(ctypes.byref(L16), FAKE, FAKE, FAKE, ctypes.byref(pg), FAKE, FAKE, 8, 2048,
+                                        0.08, 0, -1.0, 0, 0, FAKE, FAKE, FAKE, FAKE, 164, None, 0, FAKE, FAKE, FAKE,
+                                        ws, None)
+    assert rc == kv.KV_ERR_UNSUPPORTED
+    assert not kv.step_supported(L16, 8, 2048, 164)
+    assert not kv.topk_attn_supported(L16, 2048, 164, 4)
+    assert kv.step_supported(_L(num_q_heads=64), 8, 2048, 164)        # G = 8

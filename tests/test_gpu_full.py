@@ -12,6 +12,9 @@ The host-mapped value pool (pinned host memory with an HBM hot buffer) is
 exercised in both its hot and its host-read branch.
 """
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -29,9 +32,25 @@ def announce(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def sample_rows(w, n=3):
+def sample_rows(w, n=6):
+    """Every row of the 8 x 32 K workload (64 rows); n seeded rows of the larger ones."""
+    if w.name == "llama8b_32k":
+        return [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     rows = [(0, 0), (w.B // 2, w.Hkv - 1), (w.B - 1, w.Hkv // 2)]
-    return rows[:n]
+    rng = np.random.default_rng(7 + w.wid)
+    while len(rows) < min(n, w.rows):
+        r = (int(rng.integers(w.B)), int(rng.integers(w.Hkv)))
+        if r not in rows:
+            rows.append(r)
+    return rows
+
+
+def for_rows(rows, fn):
+    """Runs fn(b, g) for every row in a thread pool (numpy releases the GIL);
+    re-raises the first failure."""
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        for f in [ex.submit(fn, b, g) for b, g in rows]:
+            f.result()
 
 
 def _q(w, b, g, layer=0):
@@ -49,14 +68,17 @@ def _score_select_check(w, layer, bufs, rows):
     S_gpu = bufs.page_S
     rec_bits, n_valid = wl.synthetic_summary(w)
     log_n = np.log(n_valid.astype(np.float64)).astype(np.float32).astype(np.float64)
-    for b, g in rows:
+    hs, S_gpu, sel = hs.cpu().numpy(), S_gpu.cpu().numpy(), bufs.sel.cpu().numpy()
+
+    def one(b, g):
         rec = bits_to_f64(rec_bits[b, g])
         s_ref = oracle.page_score(_q(w, b, g), rec[:, 0], rec[:, 1:], log_n[b], w.tau)
-        assert_scores_close(hs[b, g].cpu().numpy(), s_ref)
+        assert_scores_close(hs[b, g], s_ref)
         S_ref = oracle.group_aggregate(s_ref)
-        assert_scores_close(S_gpu[b, g].cpu().numpy(), S_ref, what="S")
+        assert_scores_close(S_gpu[b, g], S_ref, what="S")
         k = oracle.selection_count(w.Np, w.keep, w.k_fixed)
-        check_selection(S_ref, k, bufs.sel[b, g, :k].cpu().numpy())
+        check_selection(S_ref, k, sel[b, g, :k])
+    for_rows(rows, one)
 
 
 @pytest.mark.parametrize("name", ["llama8b_32k", "tiers_64k", "tiers_fp8_64k", "qwen3b_128k"])
@@ -79,7 +101,8 @@ def test_full_size_score_select_and_attention(hz, name):
     torch.cuda.synchronize()
     out, lse = bufs.out.cpu().numpy(), bufs.lse.cpu().numpy()
     tiers = wl.page_tiers(w)
-    for b, g in rows:
+
+    def one(b, g):
         K = wl.row_keys(w, 0, b, g)
         V = wl.row_values(w, 0, b, g)
         if tiers is not None:
@@ -88,6 +111,7 @@ def test_full_size_score_select_and_attention(hz, name):
         o_ref, l_ref = oracle.sparse_attention(_q(w, b, g), K, V, w.ctx, w.P, sel_np[b, g], w.tau)
         hs = slice(g * w.G, (g + 1) * w.G)
         assert_attn_close(out[b, hs], lse[b, hs], o_ref, l_ref)
+    for_rows(rows, one)
 
 
 def _e2e_check(w, layer, bufs, rows, band=1e-3):
@@ -96,19 +120,21 @@ def _e2e_check(w, layer, bufs, rows, band=1e-3):
     sel = bufs.sel.cpu().numpy()
     out, lse = bufs.out.cpu().numpy(), bufs.lse.cpu().numpy()
     tiers = wl.page_tiers(w)
-    compared = differing = 0
-    for b, g in rows:
+    same = {}
+
+    def one(b, g):
         r = oracle.decode_row(_q(w, b, g), wl.row_keys(w, 0, b, g), wl.row_values(w, 0, b, g), w.ctx, w.P,
                               w.rank, w.tau, w.keep, w.k_fixed,
                               page_tiers=None if tiers is None else tiers[b])
         k = r["k"]
         check_selection(r["S"], k, sel[b, g, :k], rel=band)
-        if set(sel[b, g, :k].tolist()) == set(r["sel"].tolist()):
+        same[b, g] = set(sel[b, g, :k].tolist()) == set(r["sel"].tolist())
+        if same[b, g]:
             hs = slice(g * w.G, (g + 1) * w.G)
             assert_attn_close(out[b, hs], lse[b, hs], r["out"], r["lse"])
-            compared += 1
-        else:
-            differing += 1
+    for_rows(rows, one)
+    compared = sum(same.values())
+    differing = len(same) - compared
     print(f"rows compared {compared}, rows with in-band set differences {differing}")
     assert compared >= 1
 
@@ -122,7 +148,7 @@ def test_full_size_end_to_end(hz, name):
     bufs = hz.StepBuffers(w)
     hz.decode_step(layer, q, bufs)
     torch.cuda.synchronize()
-    _e2e_check(w, layer, bufs, sample_rows(w))
+    _e2e_check(w, layer, bufs, sample_rows(w, 8))
 
 
 @pytest.mark.timeout(600)

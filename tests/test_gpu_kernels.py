@@ -217,7 +217,17 @@ def test_coverage_selection_crafted(G, max_pages):
     hs_d = torch.from_numpy(hs).cuda()
     part_d = torch.from_numpy(part).cuda()
     cases = [(0.95, max_pages, 0, 0), (0.5, max_pages, 0, 0), (0.0, max_pages, 0, 0), (1.0, max_pages, 0, 0),
-             (1.5, 40, 0, 0), (0.9, 25, 0, 0), (0.95, max_pages, 3, 2), (0.2, max_pages, 6, 0)]
+             (1.5, 40, 0, 0), (0.9, 25, 0, 0), (0.95, max_pages, 3, 2), (0.2, max_pages, 6, 0),
+             (0.6, max_pages, 0, 5), (0.99, 30, 2, 2)]
+    # the kernel's own float32 S of every page, forced ones included: page_S of
+    # a call without forced pages (S does not depend on forcing; forced pages
+    # count with their own mass and only rank first)
+    S_all = torch.zeros((8, max_pages), dtype=torch.float32, device="cuda")
+    kv.page_topk_coverage(L, hs_d, part_d, seq, max_pages, 0.5,
+                          torch.full((8, max_pages), -7, dtype=torch.int32, device="cuda"),
+                          torch.zeros(8, dtype=torch.int32, device="cuda"), page_S=S_all)
+    torch.cuda.synchronize()
+    S_all = S_all.cpu().numpy().astype(np.float64)
     seen = set()
     for cov, cap, nff, nfl in cases:
         sel = torch.full((8, cap), -7, dtype=torch.int32, device="cuda")
@@ -233,16 +243,15 @@ def test_coverage_selection_crafted(G, max_pages):
             if n == 0:
                 assert k == 0 and np.all(sel_h[r] == -1)
                 continue
-            # forced pages hold +inf in page_S and their own masses are not reported, so rows
-            # with forced pages are only checked for k's clamp range
+            # forced pages hold +inf in page_S; their masses come from the unforced call's S
             Sr = S_h[r].astype(np.float64)
-            if nff or nfl:
-                forced = [p for p in range(n) if p < nff or p >= n - nfl]
-                assert np.all(np.isposinf(Sr[forced]))
-                assert max(1, len(forced)) <= k <= min(cap, n)
-            else:
-                lo, hi = _coverage_bounds(Sr, n, cov, cap, 0, 0, 1e-6)
-                assert lo <= k <= hi, (cov, cap, r, k, lo, hi)
+            forced = [p for p in range(n) if p < nff or p >= n - nfl]
+            assert np.all(np.isposinf(Sr[forced]))
+            assert np.array_equal(np.delete(Sr[:n], forced).view(np.uint64),
+                                  np.delete(S_all[r, :n], forced).view(np.uint64))
+            lo, hi = _coverage_bounds(S_all[r], n, cov, cap, nff, nfl, 1e-6)
+            assert lo <= k <= hi, (cov, cap, nff, nfl, r, k, lo, hi)
+            assert max(1, len(forced)) <= k <= min(cap, n)
             seen.add(k)
             exp = _expected_selection(S_h[r], n, k)
             assert np.array_equal(sel_h[r, :k], exp), (cov, r)
@@ -264,21 +273,29 @@ def test_coverage_selection_on_scores(hz):
     rec_bits, n_valid = wl.synthetic_summary(w)
     rec = bits_to_f64(rec_bits)
     log_n = np.log(n_valid.astype(np.float64)).astype(np.float32).astype(np.float64)
-    for cov in (0.3, 0.8, 0.95):
-        sel = torch.full((w.B, w.Hkv, w.Np), -7, dtype=torch.int32, device="cuda")
+    S_ref = {}
+    for b in range(w.B):
+        Np = oracle.num_pages(lens[b], w.P)
+        for g in range(w.Hkv):
+            s_ref = oracle.page_score(_q_ref(w, b, g), rec[b, g, :Np, 0], rec[b, g, :Np, 1:], log_n[b, :Np], w.tau)
+            S_ref[b, g] = oracle.group_aggregate(s_ref)
+    for cov, cap, nff, nfl in ((0.3, w.Np, 0, 0), (0.8, w.Np, 0, 0), (0.95, w.Np, 0, 0), (0.8, w.Np, 3, 2),
+                               (0.5, w.Np, 0, 4), (0.95, 100, 2, 0)):
+        sel = torch.full((w.B, w.Hkv, cap), -7, dtype=torch.int32, device="cuda")
         cnt = torch.zeros((w.B, w.Hkv), dtype=torch.int32, device="cuda")
-        kv.page_topk_coverage(layer.L, bufs.head_scores, bufs.lse_partial, layer.seq_lens, w.Np, cov, sel, cnt)
+        kv.page_topk_coverage(layer.L, bufs.head_scores, bufs.lse_partial, layer.seq_lens, w.Np, cov, sel, cnt,
+                              n_force_first=nff, n_force_last=nfl)
         torch.cuda.synchronize()
         sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
         for b in range(w.B):
             Np = oracle.num_pages(lens[b], w.P)
             for g in range(w.Hkv):
-                s_ref = oracle.page_score(_q_ref(w, b, g), rec[b, g, :Np, 0], rec[b, g, :Np, 1:], log_n[b, :Np], w.tau)
-                S_ref = oracle.group_aggregate(s_ref)
                 k = int(cnt_h[b, g])
-                lo, hi = _coverage_bounds(S_ref, Np, cov, w.Np, 0, 0, 1e-5)
-                assert lo <= k <= hi, (cov, b, g, k, lo, hi)
-                check_selection(S_ref, k, sel_h[b, g, :k])
+                lo, hi = _coverage_bounds(S_ref[b, g], Np, cov, cap, nff, nfl, 1e-5)
+                assert lo <= k <= hi, (cov, cap, nff, nfl, b, g, k, lo, hi)
+                forced = [p for p in range(Np) if p < nff or p >= Np - nfl]
+                check_selection(S_ref[b, g], k, sel_h[b, g, :k], forced=forced)
+                assert np.all(sel_h[b, g, k:] == -1)
 
 
 # ---------------------------------------------------------------- attention

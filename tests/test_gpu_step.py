@@ -63,10 +63,9 @@ def _ragged(w):
     return [w.ctx] + [max(1, w.ctx - (3 + 2 * i) * w.P - 5) for i in range(1, w.B)]
 
 
-def _ws_tail_words(kv, bufs, w, L):
-    """The workspace's per-row split counters (zero between calls)."""
-    need = kv.step_workspace_size(L, w.B, bufs.sel.shape[-1], bufs.num_splits)
-    return bufs.ws.view(torch.int32)[need // 4 - w.rows:need // 4].cpu().numpy()
+def _ws_counters(bufs, w):
+    """The workspace's per-row split counters (its first B * Hkv words; zero between calls)."""
+    return bufs.ws.view(torch.int32)[:w.rows].cpu().numpy()
 
 
 def _reference(hz, layer, q, w, splits, **sel_args):
@@ -99,8 +98,8 @@ def _assert_same(a, f):
 
 
 def _assert_ws_clean(kv, bufs, w, L):
-    tail = _ws_tail_words(kv, bufs, w, L)
-    assert np.all(tail == 0), f"workspace words not reset: {np.nonzero(tail)[0][:10]}"
+    ctr = _ws_counters(bufs, w)
+    assert np.all(ctr == 0), f"workspace counters not reset: {np.nonzero(ctr)[0][:10]}"
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -119,7 +118,7 @@ def test_step_equals_score_and_fused(hz, kv, name, splits):
     _assert_ws_clean(kv, f, w, layer.L)
 
 
-@pytest.mark.parametrize("name", ["llama_small", "llama_r8_f16", "heavy_g4", "qwen_small"])
+@pytest.mark.parametrize("name", ["llama_small", "llama_r8_f16", "tiny_r1_long", "heavy_g4", "qwen_small"])
 def test_step_matches_oracle(hz, name):
     """Scores, selection and attention of the step against the oracle."""
     w = SMALL[name]
@@ -272,7 +271,7 @@ def test_step_full_size(hz, kv):
     out, lse = f.out.cpu().numpy(), f.lse.cpu().numpy()
     rec_bits, n_valid = wl.synthetic_summary(w)
     log_n = np.log(n_valid.astype(np.float64)).astype(np.float32).astype(np.float64)
-    for b, g in [(0, 0), (w.B - 1, w.Hkv - 1), (3, 5)]:
+    for b, g in [(b, g) for b in range(w.B) for g in range(w.Hkv)]:       # all 64 rows
         rec = bits_to_f64(rec_bits[b, g])
         qg = wl.queries(w, 0, b, g).astype(np.float64)
         S_ref = oracle.group_aggregate(oracle.page_score(qg, rec[:, 0], rec[:, 1:], log_n[b], w.tau))
@@ -283,3 +282,60 @@ def test_step_full_size(hz, kv):
                                                sel[b, g, :k], w.tau)
         heads = slice(g * w.G, (g + 1) * w.G)
         assert_attn_close(out[b, heads], lse[b, heads], o_ref, l_ref)
+
+
+@pytest.mark.parametrize("name", ["llama_small", "qwen_small", "tiers_small"])
+@pytest.mark.parametrize("coverage,nff,nfl", [(0.5, 0, 0), (0.95, 0, 0), (0.8, 2, 3)])
+def test_step_coverage_matches_oracle(hz, name, coverage, nff, nfl):
+    """A coverage-mode step (selection by attention-mass coverage, then the
+    attention) against the oracle's decode of each row on the same stored
+    summary: k within the counts for coverages +-1e-5, the set band-exact, and
+    the attention within 2e-3 (over the oracle's own set where the two agree,
+    else over the GPU's set)."""
+    w = SMALL[name]
+    lens = _ragged(w)
+    announce(f"step coverage={coverage} forced=({nff},{nfl}) vs oracle {name} seq_lens={lens}")
+    layer = hz.DeviceLayer(w, summaries="synthetic", seq_lens=lens)
+    q = hz.queries_device(w)
+    bufs = hz.StepBuffers(w, with_S=True)
+    bufs.sel = torch.full((w.B, w.Hkv, w.Np), -7, dtype=torch.int32, device="cuda")   # cap = Np
+    bufs.ws = torch.zeros(max(1, hz.kv.attn_workspace_size(layer.L, w.B, w.Np) // 4), dtype=torch.float32,
+                          device="cuda")
+    f = _step(hz, layer, q, w, 0, bufs=bufs, coverage=coverage, n_force_first=nff, n_force_last=nfl)
+    torch.cuda.synchronize()
+    sel, cnt = f.sel.cpu().numpy(), f.sel_count.cpu().numpy()
+    out, lse = f.out.cpu().numpy(), f.lse.cpu().numpy()
+    rec_bits, n_valid = wl.synthetic_summary(w)
+    rec = bits_to_f64(rec_bits)
+    log_n = np.log(n_valid.astype(np.float64)).astype(np.float32).astype(np.float64)
+    tiers = wl.page_tiers(w)
+    same = 0
+    for b in range(w.B):
+        Np = oracle.num_pages(lens[b], w.P)
+        for g in range(w.Hkv):
+            qg = wl.queries(w, 0, b, g).astype(np.float64)
+            r = oracle.decode_row(qg, wl.row_keys(w, 0, b, g), wl.row_values(w, 0, b, g), lens[b], w.P, w.rank,
+                                  w.tau, n_force_first=nff, n_force_last=nfl,
+                                  page_tiers=None if tiers is None else tiers[b],
+                                  summary=(rec[b, g, :Np, 0], rec[b, g, :Np, 1:], log_n[b, :Np]),
+                                  coverage=coverage, k_cap=w.Np)
+            k = int(cnt[b, g])
+            lo = oracle.coverage_count(r["S"], max(0.0, coverage - 1e-5), w.Np, nff, nfl)
+            hi = oracle.coverage_count(r["S"], coverage + 1e-5, w.Np, nff, nfl)
+            assert lo <= r["k"] <= hi and lo <= k <= hi, (b, g, k, r["k"], lo, hi)
+            forced = [p for p in range(Np) if p < nff or p >= Np - nfl]
+            check_selection(r["S"], k, sel[b, g, :k], forced=forced)
+            assert np.all(sel[b, g, k:] == -1)
+            heads = slice(g * w.G, (g + 1) * w.G)
+            if k == r["k"] and np.array_equal(sel[b, g, :k], r["sel"]):
+                same += 1
+                assert_attn_close(out[b, heads], lse[b, heads], r["out"], r["lse"])
+            else:
+                K, V = wl.row_keys(w, 0, b, g), wl.row_values(w, 0, b, g)
+                if tiers is not None:
+                    K = oracle.pipeline.reconstruct_tiers(K, lens[b], w.P, tiers[b])
+                    V = oracle.pipeline.reconstruct_tiers(V, lens[b], w.P, tiers[b])
+                o_ref, l_ref = oracle.sparse_attention(qg, K, V, lens[b], w.P, sel[b, g, :k], w.tau)
+                assert_attn_close(out[b, heads], lse[b, heads], o_ref, l_ref)
+    print(f"rows whose set equals the oracle's: {same} of {w.rows}")
+    assert same >= 1
