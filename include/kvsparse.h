@@ -86,7 +86,8 @@ enum { KV_TIER_NATIVE = 0, KV_TIER_I8 = 1, KV_TIER_I4 = 2, KV_TIER_I2 = 3, KV_TI
  * num_q_heads a multiple of num_kv_heads with G = Hq / Hkv <= 16 for the
  * summary, score and selection calls, and G <= 8 for every call that runs the
  * attention (kv_sparse_decode_attn, kv_topk_sparse_decode_attn and the
- * whole-step call kv_sparse_decode_step: KV_ERR_UNSUPPORTED above);
+ * whole-step calls kv_sparse_decode_step and kv_sparse_decode_step_noalloc:
+ * KV_ERR_UNSUPPORTED above);
  * kv_dtype KV_F16 or KV_BF16.  softmax_scale <= 0 selects 1/sqrt(head_dim). */
 typedef struct kv_layout {
   int32_t num_q_heads;
@@ -398,6 +399,30 @@ int kv_sparse_decode_step(const kv_layout* layout, const void* q, const void* su
                           int32_t n_force_first, int32_t n_force_last, float* head_scores, float* lse_partial,
                           int32_t* sel, int32_t* sel_count, int32_t k_max, float* page_S, int32_t num_splits,
                           float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_sparse_decode_step_noalloc -- kv_sparse_decode_step without a workspace,
+ * for callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments (minus ws / ws_bytes), same launches, and
+ * outputs bit-identical to kv_sparse_decode_step with the same num_splits.
+ * The attention's split counters and partials live in a 32 MiB array of
+ * device memory inside the library (one copy per GPU, kept until the process
+ * ends): 256 KiB of counters for up to 65535 rows, then room for
+ * B * Hkv * splits * G * (head_dim + 2) float32 partials, at most
+ * 33292288 bytes; a larger call returns KV_ERR_WORKSPACE without launching.
+ * The first call on a device looks the array up and clears its counters with
+ * a kernel on `stream`; every completed call leaves them at zero.  The call
+ * allocates nothing.  All calls on one GPU share the array, so calls that
+ * overlap in time on one GPU (on different streams or from different host
+ * threads) race and must be serialised by the caller.
+ * --------------------------------------------------------------------------- */
+int kv_sparse_decode_step_noalloc(const kv_layout* layout, const void* q, const void* summary, const float* log_n,
+                                  const kv_pages* pages, const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t B, int32_t max_pages, float keep_frac, int32_t k_fixed, float coverage,
+                                  int32_t n_force_first, int32_t n_force_last, float* head_scores,
+                                  float* lse_partial, int32_t* sel, int32_t* sel_count, int32_t k_max,
+                                  float* page_S, int32_t num_splits, float* out, float* lse, void* stream);
 
 /* Bytes of workspace for kv_sparse_decode_step: kv_sparse_decode_attn's for
  * the same arguments; 0 for invalid arguments. */

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/kvsparse.h"
 #include "launch.h"
@@ -479,6 +480,81 @@ int enqueue_step(const kv_layout* L, const void* q, const void* summary, const f
 }  // namespace
 
 extern "C" {
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- whole step without a workspace
+//
+// For callers that cannot allocate: the attention's cross-block state lives
+// in this file-scope device array instead of a caller workspace.  Counters
+// for up to 65535 rows sit at a fixed offset in front (so calls over
+// different numbers of rows never overwrite each other's counters), the split
+// partials after them.  Every GPU the library runs on holds its own copy until
+// the process ends; its device address is looked up once per device.
+
+namespace {
+constexpr size_t kNoAllocBytes = (size_t)32 << 20;
+constexpr size_t kNoAllocCounterBytes = (size_t)65536 * sizeof(unsigned);
+constexpr size_t kNoAllocPartialBytes = kNoAllocBytes - kNoAllocCounterBytes;
+constexpr int kNoAllocMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices];
+
+__global__ void clear_words_kernel(unsigned* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's copy of `scratch` (looked up on its first use, with its
+// counters then cleared on `st` by a fill kernel).  KV_ERR_HIP on failure.
+int scratch_on_current_device(hipStream_t st, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return KV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KV_ERR_HIP;
+    const int n = (int)(kNoAllocCounterBytes / sizeof(unsigned));
+    hipLaunchKernelGGL(clear_words_kernel, dim3(64), dim3(256), 0, st, reinterpret_cast<unsigned*>(ptr), n);
+    if (hipGetLastError() != hipSuccess) return KV_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = reinterpret_cast<char*>(g_scratch_ptr[dev]);
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_sparse_decode_step_noalloc(const kv_layout* L, const void* q, const void* summary, const float* log_n,
+                                  const kv_pages* pg, const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t B, int32_t max_pages, float keep_frac, int32_t k_fixed, float coverage,
+                                  int32_t n_force_first, int32_t n_force_last, float* head_scores,
+                                  float* lse_partial, int32_t* sel, int32_t* sel_count, int32_t k_max,
+                                  float* page_S, int32_t num_splits, float* out, float* lse, void* stream) {
+  int s = 1;
+  int rc = check_step(L, q, summary, log_n, pg, block_table, seq_lens, B, max_pages, keep_frac, k_fixed, coverage,
+                      n_force_first, n_force_last, head_scores, lse_partial, sel, sel_count, k_max, num_splits, out,
+                      lse, &s);
+  if (rc || B == 0) return rc;
+  const int rows = B * L->num_kv_heads;
+  if (kvs::attn_partial_bytes(rows, s, L->num_q_heads / L->num_kv_heads, L->head_dim) > kNoAllocPartialBytes)
+    return KV_ERR_WORKSPACE;
+  char* base = nullptr;
+  rc = scratch_on_current_device((hipStream_t)stream, &base);
+  if (rc) return rc;
+  const kvs::AttnScratch sc{reinterpret_cast<unsigned*>(base),
+                            reinterpret_cast<float*>(base + kNoAllocCounterBytes)};
+  return enqueue_step(L, q, summary, log_n, pg, block_table, seq_lens, B, max_pages, keep_frac, k_fixed, coverage,
+                      n_force_first, n_force_last, head_scores, lse_partial, sel, sel_count, k_max, page_S, s, out,
+                      lse, sc, (hipStream_t)stream);
+}
 
 size_t kv_hot_admit_workspace_size(int32_t n_slots) {
   return n_slots > 0 ? kvs::hot_admit_workspace_bytes(n_slots) : 0;

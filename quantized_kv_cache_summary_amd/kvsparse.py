@@ -30,7 +30,7 @@ SYMBOLS = (
     "kv_page_topk_coverage", "kv_hot_admit", "kv_hot_admit_workspace_size", "kv_tier_plan", "kv_tier_demote",
     "kv_lowrank_coords", "kv_page_score_lowrank", "kv_topk_sparse_decode_attn",
     "kv_topk_sparse_decode_attn_supported", "kv_sparse_decode_step", "kv_sparse_decode_step_workspace_size",
-    "kv_sparse_decode_step_supported", "kv_sparse_decode_step_fused",
+    "kv_sparse_decode_step_supported", "kv_sparse_decode_step_fused", "kv_sparse_decode_step_noalloc",
 )
 
 
@@ -97,6 +97,9 @@ def lib():
             "kv_sparse_decode_step": (_I, [_LP, _P, _P, _P, _PP, _P, _P, _I, _I, ctypes.c_float, _I,
                                            ctypes.c_float, _I, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P,
                                            _SZ, _P]),
+            "kv_sparse_decode_step_noalloc": (_I, [_LP, _P, _P, _P, _PP, _P, _P, _I, _I, ctypes.c_float, _I,
+                                                   ctypes.c_float, _I, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P,
+                                                   _P]),
             "kv_sparse_decode_step_workspace_size": (_SZ, [_LP, _I, _I, _I]),
             "kv_sparse_decode_step_supported": (_I, [_LP, _I, _I, _I, _I]),
             "kv_sparse_decode_step_fused": (_I, [_LP, _PP, _I, _I, _I, _I]),
@@ -366,6 +369,21 @@ def sparse_decode_step(L, q, summary, log_n, pages, block_table, seq_lens, head_
         int(num_splits), _p(out), _p(lse), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
     _check(rc, "kv_sparse_decode_step")
+
+
+def sparse_decode_step_noalloc(L, q, summary, log_n, pages, block_table, seq_lens, head_scores, lse_partial, sel,
+                               sel_count, out, lse, keep_frac=0.0, k_fixed=0, coverage=-1.0, n_force_first=0,
+                               n_force_last=0, page_S=None, num_splits=0, stream=None):
+    """kv_sparse_decode_step with the attention's cross-block state in the
+    library's own device array instead of a workspace (allocates nothing)."""
+    B, max_pages = block_table.shape
+    k_max = sel.shape[-1]
+    rc = lib().kv_sparse_decode_step_noalloc(
+        ctypes.byref(L), _p(q), _p(summary), _p(log_n), ctypes.byref(pages), _p(block_table), _p(seq_lens),
+        int(B), int(max_pages), float(keep_frac), int(k_fixed), float(coverage), int(n_force_first),
+        int(n_force_last), _p(head_scores), _p(lse_partial), _p(sel), _p(sel_count), int(k_max), _p(page_S),
+        int(num_splits), _p(out), _p(lse), _stream(stream))
+    _check(rc, "kv_sparse_decode_step_noalloc")
 
 
 def dequant_tier(L, pages, page_ids, out, stream=None):

@@ -377,3 +377,26 @@ def test_attention_refuses_groups_wider_than_eight():
     assert not kv.step_supported(L16, 8, 2048, 164)
     assert not kv.topk_attn_supported(L16, 2048, 164, 4)
     assert kv.step_supported(_L(num_q_heads=64), 8, 2048, 164)        # G = 8
+
+
+def test_noalloc_step_validation():
+    """The whole step without a workspace: the same argument rules as the
+    workspace call, and calls whose partials exceed the library's array are
+    refused with KV_ERR_WORKSPACE, all before any HIP call."""
+    L = _L()
+    pg = kv.KvPages()
+    pg.k16 = pg.v16 = FAKE
+    f = kv.lib().kv_sparse_decode_step_noalloc
+
+    def call(L=L, B=8, max_pages=2048, k_max=164, splits=0, sel=FAKE, summary=FAKE):
+        return f(ctypes.byref(L), FAKE, summary, FAKE, ctypes.byref(pg), FAKE, FAKE, B, max_pages, 0.08, 0, -1.0,
+                 0, 0, FAKE, FAKE, sel, FAKE, k_max, None, splits, FAKE, FAKE, None)
+
+    assert call(B=0) == kv.KV_OK
+    assert call(k_max=163) == kv.KV_ERR_INVALID_ARG
+    assert call(sel=None) == kv.KV_ERR_INVALID_ARG
+    assert call(summary=FAKE + 8) == kv.KV_ERR_INVALID_ARG
+    assert call(splits=300) == kv.KV_ERR_UNSUPPORTED
+    assert call(L=_L(num_q_heads=128)) == kv.KV_ERR_UNSUPPORTED                  # G = 16
+    # 64 rows x 256 splits x 4 heads x 130 floats = 34 MB: more than the 33292288 bytes of partials
+    assert call(splits=256) == kv.KV_ERR_WORKSPACE
