@@ -218,11 +218,14 @@ def cpu_baseline(w, budget_s):
 
 # ---------------------------------------------------------------- GPU timing helpers
 
-def timed_region(step, n_layers, nq, K, stream, eager=False):
+def timed_region(step, n_layers, nq, K, stream, eager=False, dist_replays=8):
     """K steps, HIP events on the launch stream around them.  Graph mode: one
-    graph per query index holding one step per rotated layer, replayed with an
-    event after every replay (the last replay holds the remainder, so exactly
-    K steps run).  Returns (ms per step, per-replay ms per step samples)."""
+    graph holding a pass over every rotated layer with every query (n_layers x
+    nq steps), replayed back to back with an event after every replay; the last
+    replay holds the remainder, so exactly K steps are timed.  The per-step
+    time of each full replay is a distribution sample; when K covers fewer than
+    `dist_replays` full replays, further replays after the timed region add
+    samples.  Returns (ms per step over the K timed steps, samples)."""
     import numpy as np
     import torch
     if eager:
@@ -234,30 +237,41 @@ def timed_region(step, n_layers, nq, K, stream, eager=False):
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / K, None
-    R = math.ceil(K / n_layers)
-    last = K - (R - 1) * n_layers
+    n_cap = n_layers * nq
 
-    def capture(j, n):
+    def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for li in range(n):
-                step(li, j)
+            for i in range(n):
+                step(i % n_layers, (i // n_layers) % nq)
         return g
 
-    graphs = [capture(j, n_layers) for j in range(nq)]
-    tail = graphs[(R - 1) % nq] if last == n_layers else capture((R - 1) % nq, last)
-    for g in graphs + [tail]:
+    R = math.ceil(K / n_cap)
+    last = K - (R - 1) * n_cap
+    full_g = capture(n_cap)
+    tail = full_g if last == n_cap else capture(last)
+    for g in (full_g, tail):
         g.replay()
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
     ev[0].record(stream)
     for r in range(R):
-        (graphs[r % nq] if r < R - 1 else tail).replay()
+        (full_g if r < R - 1 else tail).replay()
         ev[r + 1].record(stream)
     torch.cuda.synchronize()
-    full = R if last == n_layers else R - 1
-    per = np.array([ev[r].elapsed_time(ev[r + 1]) / n_layers for r in range(full)])
-    return ev[0].elapsed_time(ev[R]) / K, per
+    ms = ev[0].elapsed_time(ev[R]) / K
+    full = R if last == n_cap else R - 1
+    per = [ev[r].elapsed_time(ev[r + 1]) / n_cap for r in range(full)]
+    extra = max(0, dist_replays - full)
+    if extra:
+        ex = [torch.cuda.Event(enable_timing=True) for _ in range(extra + 1)]
+        ex[0].record(stream)
+        for r in range(extra):
+            full_g.replay()
+            ex[r + 1].record(stream)
+        torch.cuda.synchronize()
+        per += [ex[r].elapsed_time(ex[r + 1]) / n_cap for r in range(extra)]
+    return ms, np.array(per)
 
 
 def graph_avg_us(launch, n_layers, nq, K, stream):
@@ -287,7 +301,8 @@ def distribution(per):
     import numpy as np
     if per is None or len(per) == 0:
         return None
-    return {"over": f"{len(per)} graph replays (one step per rotated layer each)",
+    return {"over": f"{len(per)} graph replays of one pass over every rotated layer and query (per-step time "
+                    f"of each replay)",
             "median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
             "p90": float(np.percentile(per, 90)), "min": float(np.min(per)), "max": float(np.max(per))}
 

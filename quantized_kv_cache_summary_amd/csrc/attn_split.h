@@ -25,6 +25,12 @@ template <int GM, bool SEL>
 constexpr int attn_waves() { return SEL && GM <= 4 ? 8 : 4; }
 constexpr int kStreamWaves = 4;
 
+// Waves per SIMD a block must leave room for: the packed-tier kernel runs two
+// 4-wave blocks per CU (its decode work hides the other block's latency), so
+// its registers must fit two waves per SIMD.
+template <int GM, bool TIERED, bool SEL>
+constexpr int attn_min_waves_per_simd() { return (TIERED && !SEL && GM <= 4) ? 2 : 1; }
+
 // The attention's LDS: per-wave probability tiles and the wave merge.
 template <int W, int GM, int D>
 struct AttnLds {
@@ -101,8 +107,9 @@ constexpr int tier_bits() {
 
 // Raw code words of one 16-token chunk of a page in packed tier T as the
 // attention lanes read it: per MFMA k-step the codes of the lane's 8 key
-// elements and their group's (scale, zero) word; per value slot j the codes of
-// the lane's D/16 value elements and their (scale, zero) word.
+// elements (key row `col`) and the (scale, zero) word of that row's group;
+// per value slot j the codes of the lane's D/16 value elements and their
+// (scale, zero) word.
 template <int D, int T>
 struct TierChunk {
   static constexpr int BITS = tier_bits<T>();
@@ -116,6 +123,114 @@ struct TierChunk {
   uint32_t vo[4];
 };
 
+// Exact 16-bit MFMA operand of two small values (codes, or E4M3 values): both
+// have at most 8 significant bits, so bfloat16 truncation and float16
+// conversion keep them exactly.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+  if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  else return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// byte i of w as float32 (one conversion instruction)
+template <int I>
+__device__ __forceinline__ float ubyte(uint32_t w) { return (float)((w >> (8 * I)) & 0xFFu); }
+
+// The lane's 8 key codes of one k-step (elements 8 grp .. 8 grp + 7 of a
+// 32-element group; their first bit is byte aligned) as the MFMA A operand:
+// the codes themselves for the integer tiers (0 .. 2^b - 1) and the 1-bit
+// tier (0, 1), the E4M3 values for FP8.  The group's scale and zero are
+// applied to the MFMA result instead (tier_logits).
+template <int T, bool F16>
+__device__ __forceinline__ u32x4_t key_codes(const uint32_t* w) {
+  u32x4_t a;
+  if constexpr (T == KV_TIER_FP8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+      a[2 * i] = pack_exact<F16>(lo[0], lo[1]);
+      a[2 * i + 1] = pack_exact<F16>(hi[0], hi[1]);
+    }
+  } else if constexpr (T == KV_TIER_I8) {
+    a[0] = pack_exact<F16>(ubyte<0>(w[0]), ubyte<1>(w[0]));
+    a[1] = pack_exact<F16>(ubyte<2>(w[0]), ubyte<3>(w[0]));
+    a[2] = pack_exact<F16>(ubyte<0>(w[1]), ubyte<1>(w[1]));
+    a[3] = pack_exact<F16>(ubyte<2>(w[1]), ubyte<3>(w[1]));
+  } else if constexpr (T == KV_TIER_I4) {
+    const uint32_t lo = w[0] & 0x0F0F0F0Fu, hi = (w[0] >> 4) & 0x0F0F0F0Fu;   // elements 2i, 2i + 1
+    a[0] = pack_exact<F16>(ubyte<0>(lo), ubyte<0>(hi));
+    a[1] = pack_exact<F16>(ubyte<1>(lo), ubyte<1>(hi));
+    a[2] = pack_exact<F16>(ubyte<2>(lo), ubyte<2>(hi));
+    a[3] = pack_exact<F16>(ubyte<3>(lo), ubyte<3>(hi));
+  } else if constexpr (T == KV_TIER_I2) {
+    float f[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {                  // byte 0: element k, byte 1: element 4 + k
+      const uint32_t m = (w[0] >> (2 * k)) & 0x0303u;
+      f[k] = ubyte<0>(m);
+      f[4 + k] = ubyte<1>(m);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = pack_exact<F16>(f[2 * i], f[2 * i + 1]);
+  } else {                                         // 1-bit: 1.0 where the bit is set
+    constexpr uint32_t one = F16 ? 0x3C00u : 0x3F80u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = (((w[0] >> (2 * i)) & 1u) | (((w[0] >> (2 * i + 1)) & 1u) << 16)) * one;
+  }
+  return a;
+}
+
+// Scale and zero of a packed group's codes from its (scale, zero) float16
+// word: x = sc * c + ze, so (s, z) for the integer tiers and FP8 and (2 s,
+// z - s) for the 1-bit tier (x = z - s + 2 s c).
+template <int T>
+__device__ __forceinline__ void group_scale_zero(uint32_t szw, float& sc, float& ze) {
+  const float s = f16_bits_to_f32(szw & 0xFFFFu), z = f16_bits_to_f32(szw >> 16);
+  if constexpr (T == KV_TIER_B1) {
+    sc = 2.f * s;
+    ze = z - s;
+  } else {
+    sc = s;
+    ze = z;
+  }
+}
+
+// 1-bit outlier side table on the key side: the kept element (index in bits
+// 0..4 of `word`, float16 value in bits 16..31) of the group, if it is one of
+// the lane's 8 elements (8 grp .. 8 grp + 7), is given in code units of the
+// group, c' = (v - (z - s)) / (2 s), as a 16-bit hi part (replacing its code
+// in `a`) and a 16-bit lo remainder (`lo`, zero elsewhere), so the group's
+// scale and zero turn the MFMA result into the kept value.  A group with
+// s = 0 keeps its code: then every element is within 2^-20 of z, the kept
+// value too.
+template <bool F16>
+__device__ __forceinline__ void outlier_operand(u32x4_t& a, u32x4_t& lo, uint32_t word, uint32_t szw, int grp) {
+  const int idx = (int)(word & 31u) - 8 * grp;
+  float sc, ze;
+  group_scale_zero<KV_TIER_B1>(szw, sc, ze);
+  const float v = f16_bits_to_f32(word >> 16);
+  const bool mine = idx >= 0 && idx < 8 && sc != 0.f;
+  const float c = mine ? (v - ze) * __builtin_amdgcn_rcpf(sc) : 0.f;
+  uint32_t h16, l16;
+  if constexpr (F16) {
+    const _Float16 h = (_Float16)c;
+    h16 = __builtin_bit_cast(uint16_t, h);
+    l16 = __builtin_bit_cast(uint16_t, (_Float16)(c - (float)h));
+  } else {
+    h16 = f32_to_bf16_rne(c);
+    l16 = f32_to_bf16_rne(c - __uint_as_float(h16 << 16));
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t m = !mine ? 0u : (idx == 2 * w ? 0x0000FFFFu : (idx == 2 * w + 1 ? 0xFFFF0000u : 0u));
+    const uint32_t hv = h16 | (h16 << 16), lv = l16 | (l16 << 16);
+    a[w] = (a[w] & ~m) | (hv & m);
+    lo[w] = lv & m;
+  }
+}
+
 // Requests the codes of EL elements from e0 of token row `tokrow` of packed
 // tier T and the group's (scale, zero) word.
 template <int D, int EL, int T>
@@ -128,13 +243,40 @@ __device__ __forceinline__ void tier_load(const uint8_t* codes, const uint16_t* 
 }
 
 // Decodes what tier_load requested: int-b x = c*s + z (one FMA), 1-bit
-// x = z +- s, FP8 x = e4m3(c)*s + z.
+// x = z +- s, FP8 x = e4m3(c)*s + z.  Codes are taken out of their words a
+// byte at a time where the run's first bit is byte aligned.
 template <int EL, int T>
 __device__ __forceinline__ void tier_decode(const uint32_t* w, uint32_t szw, int e0, float* x) {
   constexpr int BITS = tier_bits<T>();
   const float s = f16_bits_to_f32(szw & 0xFFFFu), z = f16_bits_to_f32(szw >> 16);
-  const int sh = (e0 * BITS) & 7;
-  if constexpr (T == KV_TIER_FP8) {
+  constexpr bool aligned = (EL * BITS) % 8 == 0;   // runs start at multiples of EL
+  const int sh = aligned ? 0 : (e0 * BITS) & 7;
+  if constexpr (T == KV_TIER_I8 && EL % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < EL / 4; ++i) {
+      x[4 * i + 0] = __builtin_fmaf(ubyte<0>(w[i]), s, z);
+      x[4 * i + 1] = __builtin_fmaf(ubyte<1>(w[i]), s, z);
+      x[4 * i + 2] = __builtin_fmaf(ubyte<2>(w[i]), s, z);
+      x[4 * i + 3] = __builtin_fmaf(ubyte<3>(w[i]), s, z);
+    }
+  } else if constexpr (T == KV_TIER_I4 && EL == 8) {
+    const uint32_t lo = w[0] & 0x0F0F0F0Fu, hi = (w[0] >> 4) & 0x0F0F0F0Fu;
+    x[0] = __builtin_fmaf(ubyte<0>(lo), s, z);
+    x[1] = __builtin_fmaf(ubyte<0>(hi), s, z);
+    x[2] = __builtin_fmaf(ubyte<1>(lo), s, z);
+    x[3] = __builtin_fmaf(ubyte<1>(hi), s, z);
+    x[4] = __builtin_fmaf(ubyte<2>(lo), s, z);
+    x[5] = __builtin_fmaf(ubyte<2>(hi), s, z);
+    x[6] = __builtin_fmaf(ubyte<3>(lo), s, z);
+    x[7] = __builtin_fmaf(ubyte<3>(hi), s, z);
+  } else if constexpr (T == KV_TIER_I2 && EL == 8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t m = (w[0] >> (2 * k)) & 0x0303u;
+      x[k] = __builtin_fmaf(ubyte<0>(m), s, z);
+      x[4 + k] = __builtin_fmaf(ubyte<1>(m), s, z);
+    }
+  } else if constexpr (T == KV_TIER_FP8) {
 #pragma unroll
     for (int i = 0; i < EL / 4; ++i) {
       const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
@@ -151,22 +293,6 @@ __device__ __forceinline__ void tier_decode(const uint32_t* w, uint32_t szw, int
   } else {
 #pragma unroll
     for (int e = 0; e < EL; ++e) x[e] = __builtin_fmaf((float)code_at<BITS>(w, sh, e), s, z);
-  }
-}
-
-// Exact split of float32 values into a 16-bit hi part and a 16-bit lo part.
-template <bool F16>
-__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  if constexpr (F16) {
-    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-    const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-    hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-  } else {
-    const uint32_t u0 = __float_as_uint(x0) & 0xFFFF0000u, u1 = __float_as_uint(x1) & 0xFFFF0000u;
-    hi = (u0 >> 16) | u1;
-    const uint32_t r0 = __float_as_uint(x0 - __uint_as_float(u0)), r1 = __float_as_uint(x1 - __uint_as_float(u1));
-    lo = (r0 >> 16) | (r1 & 0xFFFF0000u);
   }
 }
 
@@ -314,6 +440,21 @@ __device__ __forceinline__ void attend_split(const PagesDev& pg, const int32_t* 
   for (int h = 0; h < GM; ++h)
 #pragma unroll
     for (int e = 0; e < EV; ++e) st.acc[h][e] = 0.f;
+
+  // tiered kernels: sum of each 32-element group of the lane's query head
+  // (column col), for the zero terms of packed keys
+  float qsum[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    float t = 0.f;
+    if constexpr (TIERED) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) t += lo16<F16>(qop[s][w]) + hi16<F16>(qop[s][w]);
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+    }
+    qsum[s] = t;
+  }
 
   const int32_t* bt = block_table + (size_t)b * max_pages;
   const size_t page_elems = (size_t)P * D;
@@ -464,10 +605,20 @@ __device__ __forceinline__ void attend_split(const PagesDev& pg, const int32_t* 
             const uint16_t* vbase = hot >= 0 ? pg.v_hot + hr : pg.v16 + pr * page_elems;
             load_native_chunk<D>(r, kbase, vbase, c, col, grp);
           } else {
+            constexpr int BITS = tier_bits<T>();
             const size_t tok = pr * P + c * 16;
+            const uint8_t* kc = pg.kq[T - 1] + (tok + col) * (D * BITS / 8);
+            const uint16_t* ks = pg.ksz[T - 1];
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-              tier_load<D, 8, T>(pg.kq[T - 1], pg.ksz[T - 1], tok + col, 32 * s + 8 * grp, r.k[s], r.ksz[s]);
+            for (int s = 0; s < KS; ++s) {
+              int sh;   // 0: the lane's 8 codes start on a byte boundary
+              load_code_words<8, BITS>(kc, 32 * s + 8 * grp, r.k[s], sh);
+            }
+            {
+              const uint32_t* w = reinterpret_cast<const uint32_t*>(ks + (tok + col) * (D / 32) * 2);
+#pragma unroll
+              for (int s = 0; s < KS; ++s) r.ksz[s] = w[s];
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               tier_load<D, EV, T>(pg.vq[T - 1], pg.vsz[T - 1], tok + 4 * j + grp, col * EV, r.v[j], r.vsz[j]);
@@ -489,22 +640,34 @@ __device__ __forceinline__ void attend_split(const PagesDev& pg, const int32_t* 
 #pragma unroll
             for (int s = 0; s < KS; ++s) zacc = mfma16<F16>(r.k[s], qop[s], zacc);
           } else {
+            // q.k of a packed key: per 32-element group, s q.c + z sum(q) (1-bit:
+            // 2 s q.c + (z - s) sum(q)), the codes c exact in the 16-bit MFMA
+            // operand, one MFMA per group, scale and zero applied to its result
+            // the MFMA leaves token 4 grp + i in this lane: its (scale, zero)
+            // word comes from lane 4 grp + i (key row 4 grp + i) by a permute
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-              float x[8];
-              tier_decode<8, T>(r.k[s], r.ksz[s], 32 * s + 8 * grp, x);
-              if constexpr (T == KV_TIER_B1)
-                if (pg.kout) apply_outlier<8>(x, 32 * s + 8 * grp, r.ko[s]);
-              u32x4_t ah, al;
-#pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                uint32_t hw, lw;
-                split_pair<F16>(x[2 * w], x[2 * w + 1], hw, lw);
-                ah[w] = hw;
-                al[w] = lw;
+              u32x4_t a = key_codes<T, F16>(r.k[s]);
+              const f32x4_t z0 = {0.f, 0.f, 0.f, 0.f};
+              f32x4_t part;
+              if constexpr (T == KV_TIER_B1) {
+                if (pg.kout) {
+                  u32x4_t alo;
+                  outlier_operand<F16>(a, alo, r.ko[s], r.ksz[s], grp);
+                  part = mfma16<F16>(alo, qop[s], mfma16<F16>(a, qop[s], z0));
+                } else {
+                  part = mfma16<F16>(a, qop[s], z0);
+                }
+              } else {
+                part = mfma16<F16>(a, qop[s], z0);
               }
-              zacc = mfma16<F16>(ah, qop[s], zacc);
-              zacc = mfma16<F16>(al, qop[s], zacc);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((4 * grp + i) * 4, (int)r.ksz[s]);
+                float sc, ze;
+                group_scale_zero<T>(w, sc, ze);
+                zacc[i] = __builtin_fmaf(sc, part[i], __builtin_fmaf(ze, qsum[s], zacc[i]));
+              }
             }
           }
           softmax_chunk<D, GM>(st, zacc, tok0, L, true, scale_log2, pt, grp, col);

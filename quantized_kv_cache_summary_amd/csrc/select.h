@@ -85,7 +85,12 @@ __device__ __forceinline__ float key_to_score(uint32_t key) {
 template <int NT, int GM>
 struct SelectLoads {
   static constexpr int NW = NT / 64;
-  static constexpr int U0 = 2048 / NT, U1 = 32 / GM;
+  // pages per thread per round: 2048 pages per round for blocks under 1024
+  // threads (the fused kernel's register budget); the 1024-thread selector of
+  // long rows keeps up to 64 scores per thread in flight (4096 pages a round
+  // at up to eight heads), so a 4096-page row is one round and an 8192-page
+  // row two
+  static constexpr int U0 = (NT >= 1024 ? 4096 : 2048) / NT, U1 = (NT >= 1024 && GM <= 8 ? 64 : 32) / GM;
   static constexpr int U = U0 < U1 ? U0 : U1;
   static constexpr int HJ = (GM + NW - 1) / NW;
   static constexpr int TI = 4;   // up to 256 score tiles per row

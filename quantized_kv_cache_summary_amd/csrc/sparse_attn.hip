@@ -36,7 +36,8 @@
 namespace kvs {
 
 template <int D, int GM, bool F16, bool TIERED, bool SEL>
-__global__ __launch_bounds__((64 * attn_waves<GM, SEL>())) void sparse_attn_kernel(
+__global__ __launch_bounds__((64 * attn_waves<GM, SEL>()))
+__attribute__((amdgpu_waves_per_eu(attn_min_waves_per_simd<GM, TIERED, SEL>()))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, PagesDev pg, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int Hkv, int G, int P, int max_pages,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int k_max, int n_splits,
