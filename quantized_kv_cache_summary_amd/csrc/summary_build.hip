@@ -3,19 +3,31 @@
 // selector keeps a tiny per-page summary with r' eigen-quantities instead of
 // the per-key coordinates.  Per (physical page, KV head), over n valid keys:
 //   mu = mean key, Xc = keys - mu, Gram = Xc Xc^T / n (n <= 32),
-//   eigenpairs of Gram by cyclic Jacobi in float32, lam descending,
+//   the top R eigenpairs of Gram in float32, lam descending,
 //   w_j = Xc^T v_j / sqrt(n) (= sqrt(lam_j) u_j), zero when j > n-1 or
 //   lam_j <= 1e-6 lam_1;
 // stored as bfloat16 [mu, w_1..w_R] and float32 log n at the page's logical
 // position (sequence, KV head, page), where the scorer streams them in order.
 //
-// One wave per (page, KV head).  The keys are centred into LDS once; the
-// n x n Gram comes from LDS dot products; Jacobi runs with the round-robin
-// ("circle") pair schedule, so the n/2 rotations of a step are disjoint and
-// the whole step is a set of independent 2x2 block updates A <- J^T A J plus
-// the column update V <- V J.  A sweep applies every pair once; sweeps stop
-// when no off-diagonal element is above float32 noise (at most 16 sweeps);
-// that test is one pass over all pairs before each sweep.
+// One wave per (page, KV head).  The keys are centred into LDS once and the
+// n x n Gram comes from the float32 MFMA (16 x 16 tiles of X X^T).  The top R
+// eigenpairs are found without sweeping the whole spectrum:
+//   1. Householder reduction of the Gram to tridiagonal form T = Q^T G Q
+//      (n - 2 reflections, each a rank-2 update of the trailing block);
+//   2. the R largest eigenvalues of T by multisection on Sturm counts (the
+//      lanes of a group evaluate the count at evenly spaced points of the
+//      eigenvalue's bracket, so each round shrinks it lp + 1 times);
+//   3. each eigenvector of T from the twisted factorisation of T - lam I
+//      (forward and backward LDL^T, twisted where |gamma| is smallest), then
+//      modified Gram-Schmidt among the R vectors and the back-transform by
+//      the reflections.
+// A kept eigenvector that Gram-Schmidt leaves (almost) empty means an
+// eigenvalue repeated inside the top R (T splits, and the twisted solves
+// return the same vector); such a page is redone by cyclic Jacobi on the
+// whole Gram with the round-robin ("circle") pair schedule, so the n/2
+// rotations of a step are disjoint and a step is a set of independent 2x2
+// block updates A <- J^T A J plus the column update V <- V J; sweeps stop when
+// no off-diagonal element is above float32 noise (at most 16 sweeps).
 
 #include "device.h"
 #include "launch.h"
@@ -180,6 +192,260 @@ __device__ __forceinline__ void jacobi_sweeps_full(float (*A)[PS + 1], float (*V
   }
 }
 
+// Gram / n of the centred keys X (rows past n are zero) into A, on the float32
+// MFMA: a 16 x 16 tile of X X^T takes D/4 steps of 16x16x4, lane l feeding
+// X[row l%16][4 st + l/16] of both row blocks.  One writer per symmetric pair,
+// so A is exactly symmetric.
+template <int D, int PS>
+__device__ __forceinline__ void gram_mfma(const float (*X)[D + 1], float (*A)[PS + 1], float inv_n) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  constexpr int NT16 = PS / 16;
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int ta = 0; ta < NT16; ++ta)
+#pragma unroll
+    for (int tb = ta; tb < NT16; ++tb) {
+      f32x4v acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int st = 0; st < D / 4; ++st) {
+        const float xa = X[16 * ta + r16][4 * st + kq];
+        const float xb = X[16 * tb + r16][4 * st + kq];
+        acc[st & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, xb, acc[st & 3], 0, 0, 0);
+      }
+      const f32x4v t = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ia = 16 * ta + 4 * kq + r, jb = 16 * tb + r16;
+        if (ta < tb || ia <= jb) {
+          const float v = t[r] * inv_n;
+          A[ia][jb] = v;
+          A[jb][ia] = v;
+        }
+      }
+    }
+}
+
+// Sum over lanes 0..PS-1 of a layout in which lanes repeat every PS (16 or
+// 32): DPP inside 16-lane rows, then across the row pair.  Uniform result.
+template <int PS>
+__device__ __forceinline__ float copy_sum(float x) {
+  auto add = [](int a, int b) { return __float_as_int(__int_as_float(a) + __int_as_float(b)); };
+  int v = __float_as_int(x);
+  v = add(v, dpp<0x111, 0xF>(0, v));   // row_shr:1
+  v = add(v, dpp<0x112, 0xF>(0, v));   // row_shr:2
+  v = add(v, dpp<0x114, 0xF>(0, v));   // row_shr:4
+  v = add(v, dpp<0x118, 0xF>(0, v));   // row_shr:8
+  if constexpr (PS == 32) v = add(v, dpp<0x142, 0xA>(0, v));   // row_bcast:15
+  return __int_as_float(__builtin_amdgcn_readlane(v, PS - 1));
+}
+
+// Householder reduction of the symmetric PS x PS matrix whose row i sits in
+// a[] of the lanes i, i + PS, ...: T = Q^T A Q tridiagonal with diagonal d
+// and off-diagonal e (uniform), Q = H_0 .. H_{PS-3} accumulated row-wise in
+// qr[].  Reflection k takes v over rows k+1.. (v_{k+1} = x_{k+1} - alpha),
+// beta = 2 / |v|^2 = 1 / (sig2 - x_{k+1} alpha), and the trailing block gets
+// A <- A - v q^T - q v^T with p = beta A v, q = p - (beta/2)(p.v) v.  A column
+// already zero below the subdiagonal (to tiny2) is left alone.
+template <int PS>
+__device__ __forceinline__ void householder_rows(float (&a)[PS], float (&qr)[PS], float (&d)[PS], float (&e)[PS],
+                                                 float tiny2) {
+  const int i = threadIdx.x & (PS - 1);
+#pragma unroll
+  for (int j = 0; j < PS; ++j) qr[j] = i == j ? 1.f : 0.f;
+#pragma unroll
+  for (int k = 0; k + 2 < PS; ++k) {
+    const float xi = i > k ? a[k] : 0.f;
+    const float sig2 = copy_sum<PS>(xi * xi);
+    const float x0 = readlane_f(a[k], k + 1);
+    d[k] = readlane_f(a[k], k);
+    if (!(sig2 - x0 * x0 > tiny2)) {   // uniform
+      e[k] = x0;
+      continue;
+    }
+    const float sg = __builtin_amdgcn_sqrtf(sig2);
+    const float alpha = x0 >= 0.f ? -sg : sg;
+    const float bt = __builtin_amdgcn_rcpf(sig2 - x0 * alpha);
+    e[k] = alpha;
+    const float vi = i == k + 1 ? x0 - alpha : xi;
+    float vj[PS];
+#pragma unroll
+    for (int j = k + 1; j < PS; ++j) vj[j] = j == k + 1 ? x0 - alpha : readlane_f(a[k], j);
+    float p = 0.f, qv = 0.f;
+#pragma unroll
+    for (int j = k + 1; j < PS; ++j) {
+      p = fmaf(a[j], vj[j], p);
+      qv = fmaf(qr[j], vj[j], qv);
+    }
+    p = i > k ? p * bt : 0.f;
+    qv *= bt;
+    const float K = 0.5f * bt * copy_sum<PS>(p * vi);
+    const float qi = p - K * vi;
+#pragma unroll
+    for (int j = k + 1; j < PS; ++j) {
+      const float qj = readlane_f(qi, j);
+      a[j] = fmaf(-vi, qj, fmaf(-qi, vj[j], a[j]));
+      qr[j] = fmaf(-qv, vj[j], qr[j]);
+    }
+  }
+  d[PS - 2] = readlane_f(a[PS - 2], PS - 2);
+  d[PS - 1] = readlane_f(a[PS - 1], PS - 1);
+  e[PS - 2] = readlane_f(a[PS - 2], PS - 1);
+  e[PS - 1] = 0.f;
+}
+
+// The R (1, 2, 4 or 8) largest eigenpairs of the tridiagonal T (d, e) whose
+// Householder product Q is in qr[] (row i = lane mod PS).  Returns
+// u[j] = (Q z_j)_i in lane i and lam[j] (uniform); false when an eigenvector
+// that the summary keeps (j + 1 <= kept and lam_j above 1e-6 lam_0) is, to
+// half its length, a combination of the ones before it (an eigenvalue
+// repeated inside the top R).
+template <int PS>
+__device__ __forceinline__ bool tridiag_top_eigen(const float (&d)[PS], const float (&e)[PS], const float (&qr)[PS],
+                                                  int R, int kept, float (&u)[8], float (&lam)[8]) {
+  const int lane = threadIdx.x;
+  float e2[PS];
+#pragma unroll
+  for (int j = 0; j < PS; ++j) e2[j] = e[j] * e[j];
+  float e2max = 0.f, glo = INFINITY, ghi = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < PS; ++j) {
+    e2max = fmaxf(e2max, e2[j]);
+    const float r = fabsf(e[j]) + (j > 0 ? fabsf(e[j - 1]) : 0.f);
+    glo = fminf(glo, d[j] - r);
+    ghi = fmaxf(ghi, d[j] + r);
+  }
+  const float pivmin = 1e-30f * fmaxf(1.f, e2max);
+  {
+    const float span = fmaxf(ghi - glo, fabsf(ghi) * 1e-6f + 1e-30f);
+    glo -= 1e-6f * span;
+    ghi += 1e-6f * span;
+  }
+  auto guard = [&](float x) { return fabsf(x) < pivmin ? (x >= 0.f ? pivmin : -pivmin) : x; };
+
+  // 1. multisection: lp lanes per eigenvalue t (index PS-1-t ascending) count
+  //    the eigenvalues below lp evenly spaced points of its bracket
+  const int lp = 64 / R;
+  const int t = lane / lp, l = lane - t * lp;
+  const int target = PS - 1 - t;
+  const float step_den = 1.f / (float)(lp + 1);
+  float blo = glo, bhi = ghi;
+  const int rounds = lp >= 32 ? 5 : (lp >= 16 ? 6 : 7);
+  for (int rd = 0; rd < rounds; ++rd) {
+    const float w = bhi - blo;
+    const float sigma = blo + w * ((float)(l + 1) * step_den);
+    float q = guard(d[0] - sigma);
+    int c = q < 0.f;
+#pragma unroll
+    for (int j = 1; j < PS; ++j) {
+      q = guard((d[j] - sigma) - e2[j - 1] * __builtin_amdgcn_rcpf(q));
+      c += q < 0.f;
+    }
+    const unsigned long long ball = __ballot(c >= target + 1);
+    const unsigned long long gm = lp == 64 ? ball : (ball >> (t * lp)) & ((1ull << lp) - 1ull);
+    if (gm) {
+      const int f = __ffsll((long long)gm) - 1;
+      const float nhi = blo + w * ((float)(f + 1) * step_den);
+      blo = f > 0 ? blo + w * ((float)f * step_den) : blo;
+      bhi = nhi;
+    } else {
+      blo = blo + w * ((float)lp * step_den);
+    }
+  }
+  // lane t (< R) takes eigenvalue t's estimate
+  const float lm = __shfl(0.5f * (blo + bhi), (lane * lp) & 63);
+
+  // 2. twisted factorisation of T - lm I: forward pivots Dp, backward Dm,
+  //    twist index r where |gamma_r| = |Dp_r + Dm_r - (d_r - lm)| is least;
+  //    z_r = 1, z_i = -(e_i / Dp_i) z_{i+1} below, z_i = -(e_{i-1} / Dm_i) z_{i-1} above
+  float Dp[PS], Ub[PS];
+  Dp[0] = guard(d[0] - lm);
+#pragma unroll
+  for (int j = 0; j + 1 < PS; ++j) Dp[j + 1] = guard(fmaf(-e[j] * __builtin_amdgcn_rcpf(Dp[j]), e[j], d[j + 1] - lm));
+  float Dm = guard(d[PS - 1] - lm);
+  float best = fabsf(Dp[PS - 1]);
+  int r = PS - 1;
+#pragma unroll
+  for (int j = PS - 2; j >= 0; --j) {
+    Ub[j] = e[j] * __builtin_amdgcn_rcpf(Dm);
+    Dm = guard(fmaf(-Ub[j], e[j], d[j] - lm));
+    const float gam = fabsf(Dp[j] + Dm - (d[j] - lm));
+    if (gam < best) {
+      best = gam;
+      r = j;
+    }
+  }
+  float z[PS];
+  {
+    float zd = r == PS - 1 ? 1.f : 0.f;
+    z[PS - 1] = zd;
+#pragma unroll
+    for (int j = PS - 2; j >= 0; --j) {
+      zd = j == r ? 1.f : -(e[j] * __builtin_amdgcn_rcpf(Dp[j])) * zd;
+      z[j] = zd;
+    }
+    float zu = r == 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int j = 1; j < PS; ++j) {
+      zu = j == r ? 1.f : -Ub[j - 1] * zu;
+      if (j > r) z[j] = zu;
+    }
+  }
+  // normalise; the Rayleigh quotient z^T T z is the eigenvalue estimate
+  float nz = 0.f;
+#pragma unroll
+  for (int j = 0; j < PS; ++j) nz = fmaf(z[j], z[j], nz);
+  const float inz = __builtin_amdgcn_rsqf(fmaxf(nz, 1e-37f));
+#pragma unroll
+  for (int j = 0; j < PS; ++j) z[j] *= inz;
+  float rq = 0.f;
+#pragma unroll
+  for (int j = 0; j < PS; ++j) {
+    float tz = d[j] * z[j];
+    if (j > 0) tz = fmaf(e[j - 1], z[j - 1], tz);
+    if (j + 1 < PS) tz = fmaf(e[j], z[j + 1], tz);
+    rq = fmaf(z[j], tz, rq);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lam[j] = j < R ? readlane_f(rq, j) : 0.f;
+
+  // 3. modified Gram-Schmidt over lanes 0..R-1, z_s broadcast to the lanes after it
+  bool good = true;
+  const float lam_floor = 1e-6f * fmaxf(lam[0], 0.f);
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) {
+    if (s2 >= R) break;
+    float n2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < PS; ++j) n2 = fmaf(z[j], z[j], n2);
+    const float n2s = readlane_f(n2, s2);
+    if (!(n2s >= 0.25f) && s2 + 1 <= kept && lam[s2] > lam_floor) good = false;
+    const float sc = __builtin_amdgcn_rsqf(fmaxf(n2s, 1e-37f));
+    float zs[PS];
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < PS; ++j) {
+      zs[j] = readlane_f(z[j], s2) * sc;
+      dot = fmaf(z[j], zs[j], dot);
+    }
+    dot = lane > s2 ? dot : 0.f;
+#pragma unroll
+    for (int j = 0; j < PS; ++j) z[j] = lane == s2 ? zs[j] : fmaf(-dot, zs[j], z[j]);
+  }
+
+  // 4. back-transform: u_j = Q z_j, row i of Q in this lane
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float acc = 0.f;
+    if (j < R) {
+#pragma unroll
+      for (int k = 0; k < PS; ++k) acc = fmaf(qr[k], readlane_f(z[k], j), acc);
+    }
+    u[j] = acc;
+  }
+  return good;
+}
+
 template <int D, int PS, bool F16>
 __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __restrict__ k16,
                                                            const int32_t* __restrict__ block_table,
@@ -232,59 +498,86 @@ __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __res
 #pragma unroll
     for (int t = 0; t < PS; ++t) X[t][e] = t < nv ? h16_to_f32<F16>(raw[c][t]) - mu[c] : 0.f;
   }
-  int m = nv + (nv & 1);
-  if (m < 2) m = 2;
-  const int half = m / 2;
   __syncthreads();
 
-  // Gram / n
+  const int row = lane & (PS - 1);
   const float inv_n = 1.f / (float)nv;
-  for (int idx = lane; idx < m * m; idx += 64) {
-    const int a = idx / m, bb = idx - a * m;
-    if (a <= bb) {
-      float s = 0.f;
-      for (int e = 0; e < D; ++e) s += X[a][e] * X[bb][e];
-      s *= inv_n;
-      A[a][bb] = s;
-      A[bb][a] = s;
-    }
-    V[a][bb] = a == bb ? 1.f : 0.f;
-  }
+  gram_mfma<D, PS>(X, A, inv_n);
   __syncthreads();
-  float trace = 0.f;
-  for (int a = 0; a < m; ++a) trace += A[a][a];
+  const float trace = copy_sum<PS>(A[row][row]);
   const float tiny = 1e-12f * trace;
-
-  if (m == PS) jacobi_sweeps_full<PS>(A, V, tiny);
-  else jacobi_sweeps<PS>(A, V, rot_c, rot_s, rot_p, rot_q, m, tiny);
-
-  // eigenvalues descending (ties by index) -> order[rank] = column
-  if (lane < m) {
-    const float lj = A[lane][lane];
-    int pos = 0;
-    for (int j = 0; j < m; ++j) {
-      const float li = A[j][j];
-      pos += (li > lj) || (li == lj && j < lane);
-    }
-    order[pos] = lane;
-  }
-  __syncthreads();
-  const float lam1 = fmaxf(A[order[0]][order[0]], 0.f);
-  const float inv_sqrt_n = 1.f / sqrtf((float)nv);
-  for (int j = 0; j < R; ++j) {
-    float lam = 0.f;
-    int colj = 0;
-    if (j < m) { colj = order[j]; lam = fmaxf(A[colj][colj], 0.f); }
-    const bool zero = (j + 1 > nv - 1) || !(lam > 1e-6f * lam1);
+  float u[8], lam[8];
+  bool good;
+  {
+    float a[PS], qr[PS], d[PS], e[PS];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int e = lane + 64 * c;
-      float w = 0.f;
-      if (!zero) {
-        for (int t = 0; t < nv; ++t) w += X[t][e] * V[t][colj];
-        w *= inv_sqrt_n;
+    for (int j = 0; j < PS; ++j) a[j] = A[row][j];
+    householder_rows<PS>(a, qr, d, e, tiny * tiny);
+    good = tridiag_top_eigen<PS>(d, e, qr, R, nv - 1, u, lam);   // w_j is kept only for j + 1 <= n - 1
+  }
+  if (!good) {
+    // an eigenvalue repeated inside the top R: cyclic Jacobi on the whole Gram
+    int m = nv + (nv & 1);
+    if (m < 2) m = 2;
+    __syncthreads();
+    gram_mfma<D, PS>(X, A, inv_n);
+    __syncthreads();
+    for (int idx = lane; idx < m * m; idx += 64) {
+      const int a = idx / m, bb = idx - a * m;
+      V[a][bb] = a == bb ? 1.f : 0.f;
+    }
+    __syncthreads();
+    if (m == PS) jacobi_sweeps_full<PS>(A, V, tiny);
+    else jacobi_sweeps<PS>(A, V, rot_c, rot_s, rot_p, rot_q, m, tiny);
+    // eigenvalues descending (ties by index) -> order[rank] = column
+    if (lane < m) {
+      const float lj = A[lane][lane];
+      int pos = 0;
+      for (int j = 0; j < m; ++j) {
+        const float li = A[j][j];
+        pos += (li > lj) || (li == lj && j < lane);
       }
-      dst[(size_t)(1 + j) * D + e] = (uint16_t)f32_to_bf16_rne(w);
+      order[pos] = lane;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = j < m ? order[j] : 0;
+      lam[j] = j < R && j < m ? A[col][col] : 0.f;
+      u[j] = j < R && j < m && row < m ? V[row][col] : 0.f;
+    }
+  }
+
+  // w_j = Xc^T u_j / sqrt(n): keys of the lane's columns from LDS, u_j[t]
+  // broadcast from lane t
+  const float lam1 = fmaxf(lam[0], 0.f);
+  const float inv_sqrt_n = 1.f / sqrtf((float)nv);
+  float wacc[8][CPL];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) wacc[j][c] = 0.f;
+#pragma unroll
+  for (int t = 0; t < PS; ++t) {
+    float xv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) xv[c] = X[t][lane + 64 * c];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < R) {
+        const float ut = readlane_f(u[j], t);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) wacc[j][c] = fmaf(xv[c], ut, wacc[j][c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < R) {
+      const bool zero = (j + 1 > nv - 1) || !(fmaxf(lam[j], 0.f) > 1e-6f * lam1);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        dst[(size_t)(1 + j) * D + lane + 64 * c] = (uint16_t)f32_to_bf16_rne(zero ? 0.f : wacc[j][c] * inv_sqrt_n);
     }
   }
   if (g == 0 && lane == 0) *ln = logf((float)nv);

@@ -375,6 +375,75 @@ def test_attention_edge_cases(hz):
 
 # ---------------------------------------------------------------- summary builder
 
+def check_page_summary(keys, rec, rank, counts):
+    """One page's stored summary (rec: (1 + rank, d) float64 of the bf16
+    record) against the oracle over its valid keys (n, d).
+
+    The mean is unique: within half a bf16 ulp (plus slack).  The eigenvalues
+    are unique, the eigenvectors only up to rotations inside a repeated (or
+    nearly repeated) eigenvalue, so each kept w_j is checked by what holds for
+    any valid choice: |w_j|^2 = lam_j (skipped within 1e-3 lam_1 of another
+    eigenvalue), C w_j = lam_j w_j for the key covariance C = Xc^T Xc / n,
+    w_i . w_j = 0 for i != j, and, where lam_R is clear of lam_{R+1}, the
+    projector sum_j w_j w_j^T (= sum_j lam_j u_j u_j^T, unique then) against
+    the oracle's.  Directions the oracle zeroes are zero."""
+    n = keys.shape[0]
+    mu, wv, lam, _ = oracle.summarize_page(keys, rank)
+    mu_b = oracle.round_bf16(mu)
+    ulp = np.maximum(np.abs(mu_b), 2.0 ** -126) * 2.0 ** -7
+    assert np.all(np.abs(rec[0] - mu_b) <= ulp * 1.01)
+    wg = rec[1:]
+    Xc = keys.astype(np.float64) - mu
+    C = Xc.T @ Xc / n
+    lam_all = np.sort(np.linalg.eigvalsh(Xc @ Xc.T / n))[::-1]
+    lam1 = lam_all[0]
+    kept = [j for j in range(rank) if lam[j] != 0]
+    for j in range(rank):
+        if lam[j] == 0:
+            assert not wg[j].any(), f"direction {j} should be zero (n = {n})"
+            continue
+        nw = np.linalg.norm(wg[j])
+        assert np.linalg.norm(C @ wg[j] - lam[j] * wg[j]) <= 2e-2 * lam1 * nw, f"direction {j} is no eigenvector"
+        for i in kept:
+            if i < j:
+                assert abs(wg[i] @ wg[j]) <= 1e-2 * lam1, f"directions {i}, {j} not orthogonal"
+        gap_lo = lam_all[j - 1] - lam_all[j] if j > 0 else np.inf
+        gap_hi = lam_all[j] - lam_all[j + 1] if j + 1 < len(lam_all) else np.inf
+        if min(gap_lo, gap_hi) < 1e-3 * lam1:
+            counts["skipped"] += 1
+            continue
+        counts["checked"] += 1
+        assert abs(wg[j] @ wg[j] - lam[j]) <= 1e-2 * lam[j]
+    cut = lam_all[rank - 1] - lam_all[rank] if rank < len(lam_all) else np.inf
+    if cut >= 1e-3 * lam1 and lam1 > 0:
+        Pg = wg.T @ wg
+        Po = wv.T @ wv
+        assert np.linalg.norm(Pg - Po) <= 2e-2 * np.linalg.norm(Po)
+        counts["projectors"] += 1
+
+
+def check_layer_summaries(w, layer, lens, row_keys, pages=None):
+    rec = layer.summary.float().cpu().numpy().astype(np.float64).reshape(w.B, w.Hkv, w.Np, 1 + w.rank, w.d)
+    log_n = layer.log_n.cpu().numpy()
+    nv = layer.valid_tokens()
+    counts = {"checked": 0, "skipped": 0, "projectors": 0}
+    for b in range(w.B):
+        Np = oracle.num_pages(lens[b], w.P)
+        assert np.all(log_n[b, Np:] == -np.inf) and not rec[b, :, Np:].any()
+        for g in range(w.Hkv):
+            K = row_keys(b, g)
+            for p in (range(Np) if pages is None else [p for p in pages if p < Np]):
+                keys = K[p * w.P: min((p + 1) * w.P, lens[b])]
+                n = keys.shape[0]
+                assert nv[b, p] == n
+                ln = log_n[b, p]
+                assert ln == np.float32(math.log(n)) or abs(ln - math.log(n)) <= 2 ** -22 * max(1.0, math.log(n))
+                check_page_summary(keys, rec[b, g, p], w.rank, counts)
+    print(f"directions checked {counts['checked']}, skipped (near-degenerate) {counts['skipped']}, "
+          f"projectors {counts['projectors']}")
+    return counts
+
+
 @pytest.mark.parametrize("name", ["tiny", "llama_small", "heavy_small", "gmm_small", "heavy_f16_small"])
 def test_summary_builder_invariants(hz, name):
     w = SMALL[name] if name in SMALL else SUMMARY_ONLY[name]
@@ -382,48 +451,67 @@ def test_summary_builder_invariants(hz, name):
     announce(f"summary build {name}")
     layer = hz.DeviceLayer(w, summaries="build", seq_lens=lens)
     torch.cuda.synchronize()
-    rec = layer.summary.float().cpu().numpy().astype(np.float64).reshape(w.B, w.Hkv, w.Np, 1 + w.rank, w.d)
-    log_n = layer.log_n.cpu().numpy()
-    nv = layer.valid_tokens()
-    skipped = checked = 0
-    for b in range(w.B):
-        Np = oracle.num_pages(lens[b], w.P)
-        assert np.all(log_n[b, Np:] == -np.inf) and not rec[b, :, Np:].any()
-        for g in range(w.Hkv):
-            K = wl.row_keys(w, 0, b, g)
-            for p in range(Np):
-                keys = K[p * w.P: min((p + 1) * w.P, lens[b])]
-                n = keys.shape[0]
-                assert nv[b, p] == n
-                ln = log_n[b, p]
-                assert ln == np.float32(math.log(n)) or abs(ln - math.log(n)) <= 2 ** -22 * max(1.0, math.log(n))
-                mu, wv, lam, _ = oracle.summarize_page(keys, w.rank)
-                mu_b = oracle.round_bf16(mu)
-                ulp = np.maximum(np.abs(mu_b), 2.0 ** -126) * 2.0 ** -7
-                assert np.all(np.abs(rec[b, g, p, 0] - mu_b) <= ulp * 1.01)
-                wg = rec[b, g, p, 1:]
-                # full spectrum for the gap test
-                Xc = keys.astype(np.float64) - mu
-                lam_all = np.sort(np.linalg.eigvalsh(Xc @ Xc.T / n))[::-1]
-                lam1 = lam_all[0]
-                for j in range(w.rank):
-                    if lam[j] == 0:
-                        assert not wg[j].any()
-                        continue
-                    gap_lo = lam_all[j - 1] - lam_all[j] if j > 0 else np.inf
-                    gap_hi = lam_all[j] - lam_all[j + 1] if j + 1 < len(lam_all) else np.inf
-                    if min(gap_lo, gap_hi) < 1e-3 * lam1:
-                        skipped += 1
-                        continue
-                    checked += 1
-                    assert abs(wg[j] @ wg[j] - lam[j]) <= 1e-2 * lam[j]
-                cut = lam_all[w.rank - 1] - lam_all[w.rank] if w.rank < len(lam_all) else np.inf
-                if cut >= 1e-3 * lam1 and lam1 > 0:
-                    Pg = wg.T @ wg
-                    Po = wv.T @ wv
-                    assert np.linalg.norm(Pg - Po) <= 2e-2 * np.linalg.norm(Po)
-    print(f"directions checked {checked}, skipped (near-degenerate) {skipped}")
-    assert checked > 0
+    counts = check_layer_summaries(w, layer, lens, lambda b, g: wl.row_keys(w, 0, b, g))
+    assert counts["checked"] > 0
+
+
+def crafted_page(kind, P, d, rng):
+    """(P, d) float32 keys, exact in bfloat16 and float16, of a page whose
+    spectrum is degenerate on purpose: keys +-a along a few coordinate axes
+    (each axis gets as many + as - keys, so the centred keys are those
+    offsets) on top of a shared random integer vector."""
+    base = rng.integers(-3, 4, d).astype(np.float32)
+    x = np.tile(base, (P, 1))
+    def axes(amps):
+        per = P // len(amps)
+        for a, amp in enumerate(amps):
+            for t in range(per):
+                x[a * per + t, 5 + 7 * a] += amp * (1 if t % 2 == 0 else -1)
+    if kind == "four_equal":          # one eigenvalue of multiplicity 4
+        axes([2.0] * 4)
+    elif kind == "two_pairs":         # two eigenvalues of multiplicity 2
+        axes([3.0, 3.0, 2.0, 2.0])
+    elif kind == "eight_equal":       # multiplicity 8: top-4 space not unique
+        axes([2.0] * 8)
+    elif kind == "rank_two":          # two non-zero eigenvalues, the rest zero
+        axes([3.0, 2.0])
+    elif kind == "identical":         # all keys equal: no spread
+        pass
+    elif kind == "doubled":           # random keys, each twice
+        r = rng.integers(-4, 5, (P // 2, d)).astype(np.float32)
+        x = np.repeat(r, 2, axis=0)
+    return x
+
+
+CRAFTED = ("four_equal", "two_pairs", "eight_equal", "rank_two", "identical", "doubled")
+
+
+@pytest.mark.parametrize("name", ["llama_small", "heavy_small"])
+def test_summary_builder_repeated_eigenvalues(hz, name):
+    """Pages with repeated top eigenvalues, rank below R, no spread at all, and
+    duplicated keys, written into the K pool and summarised again; a partial
+    last page of each kind as well."""
+    w = SMALL[name].replace(B=1, ctx=SMALL[name].P * 40 + 6)
+    lens = [w.ctx]
+    announce(f"summary build on crafted pages {name}")
+    layer = hz.DeviceLayer(w, summaries=None, seq_lens=lens)
+    layer.summary = torch.empty((w.B, w.Hkv, w.Np, (1 + w.rank) * w.d), dtype=torch.bfloat16, device="cuda")
+    rng = np.random.default_rng(7)
+    dt = layer.k16.dtype
+    pages = []
+    for i, kind in enumerate(CRAFTED):
+        for p in (3 + i, w.Np - 1 if i == 0 else 10 + i):
+            phys = int(layer.bt_np[0, p])
+            for g in range(w.Hkv):
+                layer.k16[phys, g] = torch.from_numpy(crafted_page(kind, w.P, w.d, rng)).to(dt)
+            pages.append(p)
+    layer.build_summaries()
+    torch.cuda.synchronize()
+    pool = layer.k16.float().cpu().numpy()
+    def row_keys(b, g):
+        return pool[layer.bt_np[b], g].reshape(-1, w.d)
+    counts = check_layer_summaries(w, layer, lens, row_keys, pages=sorted(set(pages)) + [0, 1, 2])
+    assert counts["projectors"] > 0
 
 
 # ---------------------------------------------------------------- codec
