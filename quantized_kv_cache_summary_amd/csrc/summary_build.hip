@@ -307,21 +307,22 @@ __device__ __forceinline__ bool tridiag_top_eigen(const float (&d)[PS], const fl
   float e2[PS];
 #pragma unroll
   for (int j = 0; j < PS; ++j) e2[j] = e[j] * e[j];
-  float e2max = 0.f, glo = INFINITY, ghi = -INFINITY;
+  float glo = INFINITY, ghi = -INFINITY;
 #pragma unroll
   for (int j = 0; j < PS; ++j) {
-    e2max = fmaxf(e2max, e2[j]);
     const float r = fabsf(e[j]) + (j > 0 ? fabsf(e[j - 1]) : 0.f);
     glo = fminf(glo, d[j] - r);
     ghi = fmaxf(ghi, d[j] + r);
   }
-  const float pivmin = 1e-30f * fmaxf(1.f, e2max);
   {
     const float span = fmaxf(ghi - glo, fabsf(ghi) * 1e-6f + 1e-30f);
     glo -= 1e-6f * span;
     ghi += 1e-6f * span;
   }
-  auto guard = [&](float x) { return fabsf(x) < pivmin ? (x >= 0.f ? pivmin : -pivmin) : x; };
+  // Pivots of the LDL^T recurrences use the reciprocal clamped to +-1e30: a
+  // zero pivot (+0 or -0) acts as a pivot of that sign and size, so the next
+  // pivot is +-inf or huge, never NaN, even where e_j = 0 (T splits).
+  auto rc = [](float x) { return __builtin_amdgcn_fmed3f(__builtin_amdgcn_rcpf(x), -1e30f, 1e30f); };
 
   // 1. multisection: lp lanes per eigenvalue t (index PS-1-t ascending) count
   //    the eigenvalues below lp evenly spaced points of its bracket
@@ -334,14 +335,15 @@ __device__ __forceinline__ bool tridiag_top_eigen(const float (&d)[PS], const fl
   for (int rd = 0; rd < rounds; ++rd) {
     const float w = bhi - blo;
     const float sigma = blo + w * ((float)(l + 1) * step_den);
-    float q = guard(d[0] - sigma);
-    int c = q < 0.f;
+    // negative pivots, counted by sign bit (-0 counts as negative, as its reciprocal does)
+    float q = d[0] - sigma;
+    unsigned c = __float_as_uint(q) >> 31;
 #pragma unroll
     for (int j = 1; j < PS; ++j) {
-      q = guard((d[j] - sigma) - e2[j - 1] * __builtin_amdgcn_rcpf(q));
-      c += q < 0.f;
+      q = fmaf(-e2[j - 1], rc(q), d[j] - sigma);
+      c += __float_as_uint(q) >> 31;
     }
-    const unsigned long long ball = __ballot(c >= target + 1);
+    const unsigned long long ball = __ballot((int)c >= target + 1);
     const unsigned long long gm = lp == 64 ? ball : (ball >> (t * lp)) & ((1ull << lp) - 1ull);
     if (gm) {
       const int f = __ffsll((long long)gm) - 1;
@@ -359,16 +361,16 @@ __device__ __forceinline__ bool tridiag_top_eigen(const float (&d)[PS], const fl
   //    twist index r where |gamma_r| = |Dp_r + Dm_r - (d_r - lm)| is least;
   //    z_r = 1, z_i = -(e_i / Dp_i) z_{i+1} below, z_i = -(e_{i-1} / Dm_i) z_{i-1} above
   float Dp[PS], Ub[PS];
-  Dp[0] = guard(d[0] - lm);
+  Dp[0] = d[0] - lm;
 #pragma unroll
-  for (int j = 0; j + 1 < PS; ++j) Dp[j + 1] = guard(fmaf(-e[j] * __builtin_amdgcn_rcpf(Dp[j]), e[j], d[j + 1] - lm));
-  float Dm = guard(d[PS - 1] - lm);
+  for (int j = 0; j + 1 < PS; ++j) Dp[j + 1] = fmaf(-e[j] * rc(Dp[j]), e[j], d[j + 1] - lm);
+  float Dm = d[PS - 1] - lm;
   float best = fabsf(Dp[PS - 1]);
   int r = PS - 1;
 #pragma unroll
   for (int j = PS - 2; j >= 0; --j) {
-    Ub[j] = e[j] * __builtin_amdgcn_rcpf(Dm);
-    Dm = guard(fmaf(-Ub[j], e[j], d[j] - lm));
+    Ub[j] = e[j] * rc(Dm);
+    Dm = fmaf(-Ub[j], e[j], d[j] - lm);
     const float gam = fabsf(Dp[j] + Dm - (d[j] - lm));
     if (gam < best) {
       best = gam;
@@ -381,7 +383,7 @@ __device__ __forceinline__ bool tridiag_top_eigen(const float (&d)[PS], const fl
     z[PS - 1] = zd;
 #pragma unroll
     for (int j = PS - 2; j >= 0; --j) {
-      zd = j == r ? 1.f : -(e[j] * __builtin_amdgcn_rcpf(Dp[j])) * zd;
+      zd = j == r ? 1.f : -(e[j] * rc(Dp[j])) * zd;
       z[j] = zd;
     }
     float zu = r == 0 ? 1.f : 0.f;
@@ -552,33 +554,27 @@ __global__ __launch_bounds__(64) void summary_build_kernel(const uint16_t* __res
   // broadcast from lane t
   const float lam1 = fmaxf(lam[0], 0.f);
   const float inv_sqrt_n = 1.f / sqrtf((float)nv);
-  float wacc[8][CPL];
+  float xv[PS][CPL];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int t = 0; t < PS; ++t)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) wacc[j][c] = 0.f;
-#pragma unroll
-  for (int t = 0; t < PS; ++t) {
-    float xv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) xv[c] = X[t][lane + 64 * c];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < R) {
-        const float ut = readlane_f(u[j], t);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) wacc[j][c] = fmaf(xv[c], ut, wacc[j][c]);
-      }
-    }
-  }
+    for (int c = 0; c < CPL; ++c) xv[t][c] = X[t][lane + 64 * c];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if (j < R) {
-      const bool zero = (j + 1 > nv - 1) || !(fmaxf(lam[j], 0.f) > 1e-6f * lam1);
+    if (j >= R) break;   // uniform
+    const bool zero = (j + 1 > nv - 1) || !(fmaxf(lam[j], 0.f) > 1e-6f * lam1);
+    float w[CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        dst[(size_t)(1 + j) * D + lane + 64 * c] = (uint16_t)f32_to_bf16_rne(zero ? 0.f : wacc[j][c] * inv_sqrt_n);
+    for (int c = 0; c < CPL; ++c) w[c] = 0.f;
+#pragma unroll
+    for (int t = 0; t < PS; ++t) {
+      const float ut = readlane_f(u[j], t);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) w[c] = fmaf(xv[t][c], ut, w[c]);
     }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      dst[(size_t)(1 + j) * D + lane + 64 * c] = (uint16_t)f32_to_bf16_rne(zero ? 0.f : w[c] * inv_sqrt_n);
   }
   if (g == 0 && lane == 0) *ln = logf((float)nv);
 }
