@@ -425,6 +425,30 @@ def release(state):
     torch.cuda.empty_cache()
 
 
+def append_summary_build(w, args, st):
+    """Append-time summary build, for context (not in the step): the newest
+    page of every sequence rebuilt from its keys, one call per layer.  The
+    rebuild writes the same record, so the layers are unchanged."""
+    import numpy as np
+    import torch
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    layers = st["layers"]
+    if layers[0].summary is None or layers[0].seq_lens_np.min() < 1:
+        return None
+    last = (layers[0].seq_lens_np - 1) // w.P
+    ent = torch.from_numpy(np.stack([np.arange(w.B), last], 1).astype(np.int32)).cuda()
+    nval = torch.from_numpy((layers[0].seq_lens_np - last * w.P).astype(np.int32)).cuda()
+    sb_us = graph_avg_us(lambda li, j: kv.summary_build(layers[li].L, layers[li].k_src, layers[li].bt, ent, nval,
+                                                        layers[li].summary, layers[li].log_n),
+                         st["n_layers"], st["nq"], args.steps, st["stream"])[0]
+    log(f"[bench] append-time summary build ({w.B * w.Hkv} page-heads, P = {w.P}, rank {w.rank}): "
+        f"{sb_us:.1f} us per call, {sb_us / w.P:.2f} us per step amortised")
+    return {"avg_launch_us": sb_us, "page_heads": w.B * w.Hkv, "page_size": w.P, "rank": w.rank,
+            "amortized_us_per_step": sb_us / w.P,
+            "note": "kv_summary_build of the newest page of every sequence (one page per sequence per P "
+                    "decode steps); append-time work, not in the timed step"}
+
+
 def headline_extras(w, args, res, st):
     """Context lines of the headline workload (not part of the step)."""
     import numpy as np
@@ -489,23 +513,9 @@ def headline_extras(w, args, res, st):
                                           "not the path"}
         log(f"[bench] dense attention (k = Np): {dense_us:.1f} us, {dense_b / (dense_us * 1e3):.0f} GB/s")
         del dsel, dws
-    # append-time summary build, for context (not in the step): the newest
-    # page of every sequence rebuilt from its keys, one call per layer; the
-    # rebuild writes the same record, so the layers are unchanged
-    if layers[0].summary is not None and layers[0].seq_lens_np.min() >= 1:
-        last = (layers[0].seq_lens_np - 1) // w.P
-        ent = torch.from_numpy(np.stack([np.arange(w.B), last], 1).astype(np.int32)).cuda()
-        nval = torch.from_numpy((layers[0].seq_lens_np - last * w.P).astype(np.int32)).cuda()
-        sb_us = gavg(lambda li, j: kv.summary_build(layers[li].L, layers[li].k_src, layers[li].bt, ent, nval,
-                                                    layers[li].summary, layers[li].log_n))
-        res["append_summary_build"] = {
-            "avg_launch_us": sb_us, "page_heads": w.B * w.Hkv, "page_size": w.P,
-            "amortized_us_per_step": sb_us / w.P,
-            "note": "kv_summary_build of the newest page of every sequence (one page per sequence per P "
-                    "decode steps); append-time work, not in the timed step"}
-        log(f"[bench] append-time summary build ({w.B * w.Hkv} page-heads): {sb_us:.1f} us per call, "
-            f"{sb_us / w.P:.1f} us per step amortised")
-        del ent, nval
+    sb = append_summary_build(w, args, st)
+    if sb is not None:
+        res["append_summary_build"] = sb
     # coverage-mode selection (k per row from the mass prefix) on the headline
     # layers' scores: its kernel time and the k it picks, for context
     cov_sel = [torch.empty((w.B, w.Hkv, w.Np), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
@@ -651,6 +661,9 @@ def other_config(name, args):
     else:
         w = wl.WORKLOADS[name]
     res, st = measure_step(w, args, extras=False, label=name)
+    sb = append_summary_build(w, args, st)
+    if sb is not None:
+        res["append_summary_build"] = sb
     if name == "heavy70b_128k_v_in_hbm":
         res["note"] = "the 70B-shaped workload with K and V resident in HBM (no host link)"
     release(st)
