@@ -673,9 +673,11 @@ def other_config(name, args):
 
 def heavy_host_v(w, args):
     """The 70B-shaped workload as stated: K in HBM, V in pinned device-mapped
-    host memory with an HBM hot buffer of 10 % of the pages (a seeded random
-    set, as a cold buffer); eager steps.  Its bound is the larger of HBM bytes
-    / 8 TB/s and host-link bytes / the link's nominal rate."""
+    host memory with an HBM hot buffer of 10 % of the (page, KV head) units;
+    eager steps, first with the buffer left as set up (a seeded random set:
+    the reported value), then with LRU admission before every attention.  Its
+    bound is the larger of HBM bytes / 8 TB/s and host-link bytes / the link's
+    nominal rate."""
     import torch
     from quantized_kv_cache_summary_amd import harness as hz
     steps = max(1, min(args.steps, 10))
@@ -683,21 +685,40 @@ def heavy_host_v(w, args):
     layer = hz.DeviceLayer(w, summaries="build", hot_mode="cold")
     log(f"[bench] heavy70b_128k_host_v: set-up {time.time() - t0:.1f}s")
     try:
-        static, sel_counts = mem_run(w, layer, False, steps, min(args.warmup, 3), max(args.queries, 2))
+        runs, sel_counts = mem_runs(w, layer, steps, min(args.warmup, 3), max(args.queries, 2))
     finally:
         layer.release()
         torch.cuda.empty_cache()
+    static = runs["iid"]["static"]
     summary_b, selected_b = algorithmic_bytes(w, sel_counts)
     cb = combined_bound(summary_b, selected_b, static)
-    log(f"[bench] heavy70b_128k_host_v: {static['ms_per_step'] * 1e3:.0f} us/step, bound {cb['bound_ms'] * 1e3:.0f} us")
     return {"value": static["value"], "unit": "steps/s", "ms_per_step": static["ms_per_step"], "steps": steps,
             "algorithmic_bytes_per_step": {"summaries": summary_b, "selected_kv": selected_b},
-            "combined_bound": cb, "hot_share_of_pages_read": static["hot_share_of_pages_read"],
+            "combined_bound": cb,
             "host_link": {"bytes_per_step": static["host_bytes_read_by_attention"],
                           "achieved_GBps": static["host_bytes_read_by_attention"] / (static["attention_us"] * 1e3),
                           "link_peak_GBps": HOST_LINK_GBS},
-            "note": "K in HBM, V in pinned device-mapped host memory, HBM hot buffer of 10 % of the pages "
-                    "(seeded random set); eager steps, HIP events; never the headline value"}
+            "hot_buffer": mem_summary(w, runs, summary_b, selected_b),
+            "note": "K in HBM, V in pinned device-mapped host memory, HBM hot buffer of 10 % of the (page, KV "
+                    "head) units; value: independent queries with the buffer as set up (seeded random set); "
+                    "hot_buffer: static against LRU admission before every attention, with independent and "
+                    "with drifting queries; eager steps, HIP events; never the headline value"}
+
+
+def mem_summary(w, runs, summary_b, selected_b):
+    """Static buffer against admission, per query kind: step times, hot shares,
+    link bytes and each run's combined bound."""
+    out = {"buffer_unit": "(physical page, KV head)", "drift_cosine": DRIFT_COS}
+    for kind, r in runs.items():
+        st, ad = r["static"], r["admission"]
+        out[kind] = {"static": st, "admission": ad,
+                     "admission_over_static": ad["ms_per_step"] / st["ms_per_step"],
+                     "static_bound": combined_bound(summary_b, selected_b, st),
+                     "admission_bound": combined_bound(summary_b, selected_b, ad)}
+    out["iid"]["queries"] = "independent draws used in turn"
+    out["drift"]["queries"] = (f"q_t = c q_(t-1) + sqrt(1 - c^2) xi_t, c = {DRIFT_COS}: consecutive selections "
+                               "share most pages, as decode steps do")
+    return out
 
 
 def main():
@@ -755,105 +776,139 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def selected_pages(sel, sel_count, bt, seq_lens, P):
-    """Physical page of every valid selection entry of one step (one per
-    (row, page) read, so a page appears once per KV head that selected it)."""
+def selected_units(sel, sel_count, bt, seq_lens, P):
+    """Hot-buffer unit phys * Hkv + g of every valid selection entry of one
+    step (one per (row, page) the attention reads)."""
     import numpy as np
     B, Hkv, k_max = sel.shape
     npg = np.minimum(bt.shape[1], -(-seq_lens.astype(np.int64) // P))
     idx = np.arange(k_max)[None, None, :]
     ok = (idx < np.clip(sel_count, 0, k_max)[:, :, None]) & (sel >= 0) & (sel < npg[:, None, None])
     b = np.broadcast_to(np.arange(B)[:, None, None], sel.shape)
-    return bt[b[ok], sel[ok]]
+    g = np.broadcast_to(np.arange(Hkv)[None, :, None], sel.shape)
+    return bt[b[ok], sel[ok]].astype(np.int64) * Hkv + g[ok]
 
 
 HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction, nominal
 
 
 def combined_bound(summary_b, selected_b, run):
-    """The step's bound when V of cold pages crosses the host link: the larger
-    of (HBM bytes / 8 TB/s) and (host-link bytes / the link's nominal rate)."""
-    host_b = run["host_bytes_read_by_attention"]
-    hbm_b = summary_b + selected_b - host_b
+    """The step's bound when K or V of cold units crosses the host link: the
+    larger of (HBM bytes / 8 TB/s) and (host-link bytes / the link's nominal
+    rate).  Host-link bytes are those the attention reads over the link plus
+    those admission copies in."""
+    host_b = run["host_bytes_read_by_attention"] + run["host_bytes_copied_by_admission"]
+    hbm_b = summary_b + selected_b - run["host_bytes_read_by_attention"]
     t = max(hbm_b / (HBM_PEAK_GBS * 1e9), host_b / (HOST_LINK_GBS * 1e9))
     return {"hbm_bytes": hbm_b, "host_bytes": host_b, "bound_ms": t * 1e3,
             "frac": t * 1e3 / run["ms_per_step"]}
 
 
-def mem_run(w, layer, admit, K, W, nq):
-    """Steps over a host-resident pool with a static hot buffer or LRU
-    admission after every step (hz.MemStep); timed, then an untimed pass that
-    measures attention and admission per step and the hot share of the pages read."""
+DRIFT_COS = 0.95   # cosine of consecutive queries in the step-to-step locality runs
+
+
+def mem_queries(w, kind, n):
+    """Queries of a host-resident run: "iid", a few independent draws used in
+    turn, or "drift", a sequence of n with consecutive cosine DRIFT_COS."""
+    from quantized_kv_cache_summary_amd import harness as hz
+    if kind == "iid":
+        return [hz.queries_device(w, 0, j) for j in range(n)]
+    return hz.drift_queries_device(w, n, DRIFT_COS)
+
+
+def mem_runs(w, layer, K, W, nq):
+    """Static buffer and LRU admission, with independent queries and then with
+    drifting ones (the buffer reset to its seeded contents in between)."""
+    import numpy as np
+    iid = mem_queries(w, "iid", nq)
+    out = {"iid": {}, "drift": {}}
+    out["iid"]["static"], sel_counts = mem_run(w, layer, False, K, W, iid)
+    out["iid"]["admission"], _ = mem_run(w, layer, True, K, W, iid)
+    layer.set_hot_units(np.zeros(0, np.int64))
+    drift = mem_queries(w, "drift", W + K + 6)
+    out["drift"]["static"], _ = mem_run(w, layer, False, K, W, drift)
+    out["drift"]["admission"], _ = mem_run(w, layer, True, K, W, drift)
+    for kind in ("iid", "drift"):
+        st, ad = out[kind]["static"], out[kind]["admission"]
+        log(f"[bench] {w.name} {kind} queries: static {st['ms_per_step'] * 1e3:.0f} us/step "
+            f"(hot share {st['hot_share_of_units_called']:.3f}), admission {ad['ms_per_step'] * 1e3:.0f} us/step "
+            f"(hot share {ad['hot_share_of_units_called']:.3f}, {ad['units_copied_per_step']:.0f} units copied)")
+    return out, sel_counts
+
+
+def mem_run(w, layer, admit, K, W, qs):
+    """Steps over a host-resident pool with the hot buffer as set up (static)
+    or with LRU admission of (page, KV head) units before every attention
+    (hz.MemStep), step i using qs[i mod len(qs)]; timed, then an untimed pass
+    that measures admission and attention per step and the hot share of the
+    units the selection calls."""
     import numpy as np
     import torch
     from quantized_kv_cache_summary_amd import harness as hz
     stream = torch.cuda.current_stream()
-    qs = [hz.queries_device(w, 0, j) for j in range(nq)]
+    nq = len(qs)
     ms = hz.MemStep(layer, admit=admit)
     for i in range(W):
         ms(qs[i % nq])
-    ms.finish()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for i in range(K):
         ms(qs[(W + i) % nq])
-    ms.finish()
     b.record(stream)
     torch.cuda.synchronize()
     ms_step = a.elapsed_time(b) / K
-    # untimed pass: attention and admission per step, hot share of the pages read
+    # untimed pass: admission and attention per step, hot share of the units
+    # called (before this step's admission), units read over the link
+    unit_b = w.P * w.d * 2 * (2 if layer.host_k is not None else 1)
     att, adm, hit, n_sel, cold, copies = [], [], [], [], [], []
     for i in range(min(K, 6)):
         bufs = ms.bufs[ms.t & 1]
         q = qs[(W + K + i) % nq]
         hz.score(layer, q, bufs)
         hz.topk(layer, bufs)
-        ms.finish()
         torch.cuda.synchronize()
-        reads = selected_pages(bufs.sel.cpu().numpy(), bufs.sel_count.cpu().numpy(), layer.bt_np,
+        reads = selected_units(bufs.sel.cpu().numpy(), bufs.sel_count.cpu().numpy(), layer.bt_np,
                                layer.seq_lens_np, w.P)
-        hot_map = layer.v_hot_slot.cpu().numpy()
         U = np.unique(reads)
-        hit.append(float((hot_map[U] >= 0).mean()) if U.size else 0.0)
+        hot_before = layer.v_hot_slot.cpu().numpy()
+        hit.append(float((hot_before[U] >= 0).mean()) if U.size else 0.0)
         n_sel.append(int(U.size))
-        cold.append(int((hot_map[reads] < 0).sum()))
+        ms.t += 1
+        ea0, ea1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if admit:
+            ea0.record(stream)
+            ms.admit_step(bufs)
+            ea1.record(stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         hz.attend(layer, q, bufs)
         e1.record(stream)
-        ms.t += 1
-        if admit:
-            ms.side.wait_stream(stream)
-            ms.admit_start.record(ms.side)
-            from quantized_kv_cache_summary_amd import kvsparse as kv
-            kv.hot_admit(layer.L, layer.host_v.dev.value, layer.v_hot, layer.v_hot_slot, ms.slot_page,
-                         ms.slot_stamp, layer.bt, layer.seq_lens, bufs.sel, bufs.sel_count, ms.t, ms.ws, ms.side,
-                         k16_ptr=layer.host_k.dev.value if layer.host_k is not None else None,
-                         k_hot=layer.k_hot)
-            ms.admitted.record(ms.side)
         torch.cuda.synchronize()
         att.append(e0.elapsed_time(e1) * 1e3)
+        hot_after = layer.v_hot_slot.cpu().numpy()
+        cold.append(int((hot_after[reads] < 0).sum()))
         if admit:
-            adm.append(ms.admit_start.elapsed_time(ms.admitted) * 1e3)
+            adm.append(ea0.elapsed_time(ea1) * 1e3)
             copies.append(int(ms.ws[0].item()))
     sel_counts = ms.bufs[0].sel_count.cpu().numpy()
     return {"ms_per_step": ms_step, "value": 1e3 / ms_step, "unit": "steps/s", "steps": K,
             "attention_us": float(np.median(att)), "admission_us": float(np.median(adm)) if adm else None,
-            "pages_copied_per_step": float(np.mean(copies)) if copies else 0.0,
-            "hot_share_of_pages_read": float(np.mean(hit)), "distinct_pages_read": float(np.mean(n_sel)),
-            "host_bytes_read_by_attention": float(np.mean(cold)) * w.P * w.d * 2 *
-            (2 if layer.host_k is not None else 1),
-            "hot_slots": int(layer.v_hot.shape[0])}, sel_counts
-
+            "units_copied_per_step": float(np.mean(copies)) if copies else 0.0,
+            "hot_share_of_units_called": float(np.mean(hit)), "distinct_units_called": float(np.mean(n_sel)),
+            "host_bytes_read_by_attention": float(np.mean(cold)) * unit_b,
+            "host_bytes_copied_by_admission": (float(np.mean(copies)) if copies else 0.0) * unit_b,
+            "hot_slots": int(layer.v_hot.shape[0]), "buffer_unit": "(physical page, KV head)",
+            "unit_bytes": unit_b}, sel_counts
 
 
 def mem_main(args, w):
     """The host-resident workload: V (and with --mem-kv K too) in pinned,
     device-mapped host memory with an HBM hot buffer of a fixed share of the
-    pages.  One layer; each step uses a different query.  Timed: steps with the
-    hot buffer left as set up (the headline value), steps with LRU admission
-    after every step on a side stream (kv_hot_admit), and the same for mem-kv."""
+    (page, KV head) units.  One layer.  Timed: steps with the hot buffer left
+    as set up (the headline value: independent queries), steps with LRU
+    admission before every attention (kv_hot_admit), both again with drifting
+    queries, and static and admission for mem-kv."""
     import numpy as np
     import torch
     from quantized_kv_cache_summary_amd import harness as hz
@@ -866,23 +921,21 @@ def mem_main(args, w):
     t0 = time.time()
     layer = hz.DeviceLayer(w, summaries="build", hot_mode="cold")
     log(f"[bench] {w.name}: set-up {time.time() - t0:.1f}s")
-    static, sel_counts = mem_run(w, layer, False, K, W, nq)
-    log(f"[bench] static hot buffer: {static}")
-    admitted, _ = mem_run(w, layer, True, K, W, nq)
-    log(f"[bench] with admission: {admitted}")
+    runs, sel_counts = mem_runs(w, layer, K, W, nq)
+    static, admitted = runs["iid"]["static"], runs["iid"]["admission"]
     layer.release()
     memkv = None
     if args.mem_kv:
         t0 = time.time()
         layer = hz.DeviceLayer(w, summaries="build", hot_mode="cold", host_k=True)
         log(f"[bench] {w.name} mem-kv: set-up {time.time() - t0:.1f}s")
-        memkv = {"static": mem_run(w, layer, False, K, W, nq)[0], "admission": mem_run(w, layer, True, K, W, nq)[0]}
+        iid = mem_queries(w, "iid", nq)
+        memkv = {"static": mem_run(w, layer, False, K, W, iid)[0], "admission": mem_run(w, layer, True, K, W, iid)[0]}
         log(f"[bench] mem-kv: {memkv}")
         layer.release()
 
     # the same step with V resident in HBM: the bound a hot buffer holding every
-    # page read would approach (the workload's 8 KV heads read 57 % of the pool
-    # per step, more than a 10 % buffer can hold)
+    # unit read would approach
     t0 = time.time()
     hl = hz.DeviceLayer(w, summaries="build", host_v=False)
     hb = hz.StepBuffers(w)
@@ -910,7 +963,6 @@ def mem_main(args, w):
     torch.cuda.empty_cache()
 
     summary_b, selected_b = algorithmic_bytes(w, sel_counts)
-    page_v = w.Hkv * w.P * w.d * 2
     result = {
         "metric": METRIC,
         "value": static["value"],
@@ -930,18 +982,17 @@ def mem_main(args, w):
                    "value_pool": "pinned device-mapped host memory"},
         "algorithmic_bytes_per_step": {"summaries": summary_b, "selected_kv": selected_b},
         "host_link": {
-            "note": "V of selected pages not in the hot buffer is read over the host link by the attention "
-                    "kernel (one KV head's part per selecting row)",
+            "note": "V of selected (page, KV head) units not in the hot buffer is read over the host link by "
+                    "the attention kernel",
             "bytes_per_step": static["host_bytes_read_by_attention"],
             "achieved_GBps": static["host_bytes_read_by_attention"] / (static["attention_us"] * 1e3),
-            "admission_copy_GBps": (admitted["pages_copied_per_step"] * page_v / (admitted["admission_us"] * 1e3)
+            "admission_copy_GBps": (admitted["host_bytes_copied_by_admission"] / (admitted["admission_us"] * 1e3)
                                     if admitted["admission_us"] else None),
             "link_peak_GBps": HOST_LINK_GBS,
         },
         "combined_bound": combined_bound(summary_b, selected_b, static),
         "v_in_hbm": v_in_hbm,
-        "static_hot_buffer": static,
-        "lru_admission": admitted,
+        "hot_buffer": mem_summary(w, runs, summary_b, selected_b),
         "mem_kv": memkv,
         "cpu_baseline": None,
     }

@@ -112,16 +112,18 @@ typedef struct kv_layout {
  *     FP8 x = e4m3(c)*s + z (exact).  Every one of the five tiers' pointers
  *     must be set when page_entry is (a tier with no pages may point to a
  *     one-slot dummy).
- *   v_hot_slot != NULL: V of physical page phys is read from
- *     v_hot[v_hot_slot[phys]] ([hot][Hkv][P][d] 16-bit, device memory) when
- *     v_hot_slot[phys] >= 0, else from v16[slot]; v16 may then be pinned host
- *     memory mapped into the device address space (zero-copy reads over the
- *     host link).  AMASS page, section "What is in the box" item 2 (the DRAM
- *     value tier with a bounded resident hot buffer).
+ *   v_hot_slot != NULL: the hot buffer, whose unit is one (physical page,
+ *     KV head), u = phys * Hkv + g.  Row (b, g)'s V of physical page phys is
+ *     read from v_hot[v_hot_slot[u]] ([n_slots][P][d] 16-bit, device memory)
+ *     when v_hot_slot[u] >= 0, else from v16[slot]; v16 may then be pinned
+ *     host memory mapped into the device address space (zero-copy reads over
+ *     the host link).  v_hot_slot holds n_phys * Hkv int32.  AMASS page,
+ *     section "What is in the box" item 2 (the DRAM value tier with a bounded
+ *     resident hot buffer).
  *   k_hot != NULL (needs v_hot_slot): the mem-kv variant (AMASS page, table
  *     "Two variants, one algorithm": K and V both offloaded).  A hot slot holds
- *     the page's K as well, K of page phys is read from k_hot[v_hot_slot[phys]]
- *     ([hot][Hkv][P][d] 16-bit) when that slot is >= 0, else from k16[slot],
+ *     the unit's K as well: K of unit u is read from k_hot[v_hot_slot[u]]
+ *     ([n_slots][P][d] 16-bit) when that slot is >= 0, else from k16[slot],
  *     which may then be device-mapped host memory too.  Native pages only: a
  *     packed tier's codes stay where kq/vq point.
  *   kout/vout != NULL (both or neither, with page_entry): the 1-bit tier's
@@ -443,37 +445,45 @@ int32_t kv_sparse_decode_step_fused(const kv_layout* layout, const kv_pages* pag
  * kv_hot_admit -- hot-buffer admission for a host-resident V pool (AMASS page,
  * "What is in the box" item 2 and the AMASS-mem variant: V in pinned,
  * device-mapped host memory, a bounded resident hot buffer plus a staging
- * pool).  Run once per step after its attention, on a stream the next step's
- * attention waits for.  With U = the physical pages of the step's selection
- * (entries i < sel_count, clamped to [0, k_max], of pages 0 <= p < Np_b,
- * through block_table; duplicates removed):
- *   1. a page of U already hot (v_hot_slot[p] = s >= 0) stamps its slot:
+ * pool).  The buffer's unit is one (physical page, KV head), u = phys * Hkv
+ * + g: the P x d values one row's attention reads of a page.  Run once per
+ * step after its selection and before its attention, on the attention's
+ * stream: the attention then reads every admitted unit from device memory.
+ * With U = the units of the step's selection (entries i < sel_count of row
+ * (b, g), clamped to [0, k_max], of pages 0 <= p < Np_b, through block_table,
+ * as block_table[b][p] * Hkv + g; duplicates removed):
+ *   1. a unit of U already hot (v_hot_slot[u] = s >= 0) stamps its slot:
  *      slot_stamp[s] = step;
- *   2. the pages of U that are not hot, ascending by page id, are admitted
+ *   2. the units of U that are not hot, ascending by unit id, are admitted
  *      into the slots least recently used before this step -- the smallest
- *      (slot_stamp, slot index) among slots with slot_stamp < step -- one page
+ *      (slot_stamp, slot index) among slots with slot_stamp < step -- one unit
  *      per slot, paired in ascending slot order; with fewer such slots than
- *      pages the lowest page ids are admitted;
- *   3. an admitted slot s drops its old page (v_hot_slot[old] = -1), takes p
- *      (slot_page[s] = p, v_hot_slot[p] = s, slot_stamp[s] = step) and p's V
- *      for every KV head, [Hkv][P][d] 16-bit, is copied from v16 (the pool,
- *      [n_phys][Hkv][P][d], device-mapped host memory or device memory) into
- *      v_hot ([n_slots][Hkv][P][d]); with k16 and k_hot given (the mem-kv
- *      variant, both or neither) p's K is copied from k16 into k_hot the same
- *      way.
- * State, device memory owned by the caller: v_hot_slot int32 [n_phys],
- * slot_page int32 [n_slots], slot_stamp uint32 [n_slots] (0 = never used).
- * Initialise them consistently (all -1 / 0 for an empty buffer).  step >= 1
- * and increasing across calls.  n_phys <= 2^19, n_slots <= 2^14.
- * ws/ws_bytes: kv_hot_admit_workspace_size(n_slots).
+ *      units the lowest unit ids are admitted;
+ *   3. an admitted slot s drops its old unit (v_hot_slot[old] = -1), takes u
+ *      (slot_page[s] = u, v_hot_slot[u] = s, slot_stamp[s] = step) and u's V,
+ *      [P][d] 16-bit at v16 + u * P * d (the pool [n_phys][Hkv][P][d],
+ *      device-mapped host memory or device memory), is copied to
+ *      v_hot + s * P * d ([n_slots][P][d]); with k16 and k_hot given (the
+ *      mem-kv variant, both or neither) u's K is copied from k16 into k_hot the
+ *      same way.
+ * State, device memory owned by the caller: v_hot_slot int32 [n_units] with
+ * n_units = n_phys * Hkv, slot_page int32 [n_slots], slot_stamp uint32
+ * [n_slots] (0 = never used).  Initialise them consistently (all -1 / 0 for an
+ * empty buffer).  step >= 1 and increasing across calls.  n_units <= 2^24 and
+ * a multiple of Hkv, n_slots <= 2^22 (else KV_ERR_UNSUPPORTED).
+ * ws/ws_bytes: kv_hot_admit_workspace_size(n_slots, n_units) bytes of device
+ * memory, 4-byte aligned; no contents carry over between calls.  After the
+ * call ws[0] (int32) is the number of units copied and ws[1 + 2i], ws[2 + 2i]
+ * the i-th (unit, slot) pair, ascending by slot.
  * --------------------------------------------------------------------------- */
 int kv_hot_admit(const kv_layout* layout, const void* v16, void* v_hot, const void* k16, void* k_hot,
-                 int32_t* v_hot_slot, int32_t n_phys, int32_t* slot_page, uint32_t* slot_stamp, int32_t n_slots,
+                 int32_t* v_hot_slot, int32_t n_units, int32_t* slot_page, uint32_t* slot_stamp, int32_t n_slots,
                  const int32_t* block_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,
                  const int32_t* sel, const int32_t* sel_count, int32_t k_max, uint32_t step,
                  void* ws, size_t ws_bytes, void* stream);
 
-size_t kv_hot_admit_workspace_size(int32_t n_slots);
+/* Workspace bytes of kv_hot_admit (0 for sizes it does not support). */
+size_t kv_hot_admit_workspace_size(int32_t n_slots, int32_t n_units);
 
 /* ---------------------------------------------------------------------------
  * kv_dequant_tier -- the attention kernel's in-register tier decoding as a

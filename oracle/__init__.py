@@ -41,7 +41,7 @@ from .codec import (
     encode_vector, decode_vector, outlier_words, apply_outliers,
     pack_codes, unpack_codes,
 )
-from .hotbuffer import HotBuffer, selected_physical_pages
+from .hotbuffer import HotBuffer, selected_physical_pages, selected_units
 from .lowrank import row_mean, store_mean, key_coords, row_lowrank, page_score_lowrank
 from .cascade import (TIER_OF_LEVEL, LEVEL_OF_TIER, page_importance, rank_pages, desired_levels, plan_row,
                       retier_vectors)
@@ -60,7 +60,7 @@ __all__ = [
     "encode_group_int", "encode_group_1bit", "encode_group_fp8", "e4m3_magnitudes", "e4m3_value",
     "round_e4m3", "encode_vector", "decode_vector", "outlier_words", "apply_outliers",
     "pack_codes", "unpack_codes",
-    "HotBuffer", "selected_physical_pages",
+    "HotBuffer", "selected_physical_pages", "selected_units",
     "row_mean", "store_mean", "key_coords", "row_lowrank", "page_score_lowrank",
     "TIER_OF_LEVEL", "LEVEL_OF_TIER", "page_importance", "rank_pages", "desired_levels", "plan_row",
     "retier_vectors",

@@ -474,7 +474,7 @@ __device__ __forceinline__ void attend_split(const PagesDev& pg, const int32_t* 
           l_p = p;
           const int phys = bt[p];
           l_slot = (uint32_t)phys;
-          if (pg.v_hot_slot) l_hot = pg.v_hot_slot[phys];
+          if (pg.v_hot_slot) l_hot = pg.v_hot_slot[(size_t)phys * Hkv + g];
         }
       }
       const unsigned long long valid = __ballot(l_p >= 0);
@@ -499,7 +499,7 @@ __device__ __forceinline__ void attend_split(const PagesDev& pg, const int32_t* 
           const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)l_slot, jj);
           const int hot = __builtin_amdgcn_readlane(l_hot, jj);
           const size_t pr = (size_t)slot * Hkv + g;
-          const size_t hr = ((size_t)hot * Hkv + g) * page_elems;
+          const size_t hr = (size_t)hot * page_elems;
           const uint16_t* kb = hot >= 0 && pg.k_hot ? pg.k_hot + hr : pg.k16 + pr * page_elems;
           const uint16_t* vb = hot >= 0 ? pg.v_hot + hr : pg.v16 + pr * page_elems;
           load_native_chunk<D>(r[u], kb, vb, ci - jj * cpp, col, grp);
@@ -568,7 +568,7 @@ __device__ __forceinline__ void attend_split(const PagesDev& pg, const int32_t* 
             l_tier = e >> 29;
             l_slot = e & 0x1FFFFFFFu;
           }
-          if (pg.v_hot_slot) l_hot = pg.v_hot_slot[phys];
+          if (pg.v_hot_slot) l_hot = pg.v_hot_slot[(size_t)phys * Hkv + g];
         }
       }
       auto run_tier = [&](auto tc) {
@@ -600,7 +600,7 @@ __device__ __forceinline__ void attend_split(const PagesDev& pg, const int32_t* 
           const size_t pr = (size_t)slot * Hkv + g;
           if constexpr (T == KV_TIER_NATIVE) {
             const int hot = __builtin_amdgcn_readlane(l_hot, jj);
-            const size_t hr = ((size_t)hot * Hkv + g) * page_elems;
+            const size_t hr = (size_t)hot * page_elems;
             const uint16_t* kbase = hot >= 0 && pg.k_hot ? pg.k_hot + hr : pg.k16 + pr * page_elems;
             const uint16_t* vbase = hot >= 0 ? pg.v_hot + hr : pg.v16 + pr * page_elems;
             load_native_chunk<D>(r, kbase, vbase, c, col, grp);

@@ -71,13 +71,26 @@ hipError_t launch_page_score_basis(const kv_layout& L, const void* q, const void
                                    int max_pages, float tau, float* head_scores, float* lse_partial,
                                    hipStream_t st);
 
-// Hot-buffer admission: limits of the one-block plan (bitmap and slot keys in LDS).
-constexpr int kAdmitMaxPhys = 1 << 19;
-constexpr int kAdmitMaxSlots = 1 << 14;
-inline size_t hot_admit_workspace_bytes(int n_slots) { return (size_t)(1 + 3 * n_slots) * sizeof(int32_t); }
+// Hot-buffer admission: units u = phys * Hkv + g, limits of the one-block
+// plan, and its workspace (int32 words): count, (unit, slot) pairs, miss list,
+// then the unit bitmap and the slot keys, each at a 64-word boundary.
+constexpr int kAdmitMaxUnits = 1 << 24;
+constexpr int kAdmitMaxSlots = 1 << 22;
+struct HotAdmitWs { size_t bits, keys, words; };
+inline HotAdmitWs hot_admit_ws_layout(int n_slots, int n_units) {
+  auto up64 = [](size_t x) { return (x + 63) & ~(size_t)63; };
+  HotAdmitWs l;
+  l.bits = up64(1 + 3 * (size_t)n_slots);
+  l.keys = up64(l.bits + (((size_t)n_units + 31) >> 5));
+  l.words = l.keys + (size_t)n_slots;
+  return l;
+}
+inline size_t hot_admit_workspace_bytes(int n_slots, int n_units) {
+  return hot_admit_ws_layout(n_slots, n_units).words * sizeof(int32_t);
+}
 
 hipError_t launch_hot_admit(const kv_layout& L, const void* v16, void* v_hot, const void* k16, void* k_hot,
-                            int32_t* hot, int n_phys,
+                            int32_t* hot, int n_units,
                             int32_t* slot_page, uint32_t* slot_stamp, int n_slots, const int32_t* block_table,
                             const int32_t* seq_lens, int B, int max_pages, const int32_t* sel,
                             const int32_t* sel_count, int k_max, uint32_t step, int32_t* ws, hipStream_t st);

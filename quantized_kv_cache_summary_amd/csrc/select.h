@@ -469,8 +469,9 @@ __device__ int select_coverage_k(SelectLds<NT>& sh, const uint32_t* keys, int Np
 
 // Calls emit(p, pos) for every kept page p of [0, Np), pos = its rank in
 // ascending page order.  Each thread walks a contiguous run of pages.
-// Uses sh.wave_tot once (no barrier after it).
-template <int NT, typename Emit>
+// Uses sh.wave_tot (and with WIDE sh.wpos) once (no barrier after it).  The
+// two counts share one scan for Np < 2^15; WIDE scans them apart, for any Np.
+template <int NT, bool WIDE = false, typename Emit>
 __device__ __forceinline__ void select_compact(SelectLds<NT>& sh, const uint32_t* keys, int Np, uint32_t T,
                                                int take, Emit&& emit) {
   constexpr int NW = NT / 64;
@@ -490,16 +491,35 @@ __device__ __forceinline__ void select_compact(SelectLds<NT>& sh, const uint32_t
       n_eq += kv[i] == T;
     }
   }
-  // one scan of both counts (each total is at most Np < 2^15)
-  const int v = (n_gt << 16) | n_eq;
-  const int incl = wave_incl_sum(v);
-  if (lane == 63) sh.wave_tot[wave] = incl;
-  __syncthreads();
-  int before = incl - v;
+  int gt_before, eq_before;
+  if constexpr (!WIDE) {
+    // one scan of both counts (each total is at most Np < 2^15)
+    const int v = (n_gt << 16) | n_eq;
+    const int incl = wave_incl_sum(v);
+    if (lane == 63) sh.wave_tot[wave] = incl;
+    __syncthreads();
+    int before = incl - v;
 #pragma unroll
-  for (int w = 0; w < NW; ++w)
-    if (w < wave) before += sh.wave_tot[w];
-  const int gt_before = before >> 16, eq_before = before & 0xFFFF;
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) before += sh.wave_tot[w];
+    gt_before = before >> 16;
+    eq_before = before & 0xFFFF;
+  } else {
+    const int ig = wave_incl_sum(n_gt), ie = wave_incl_sum(n_eq);
+    if (lane == 63) {
+      sh.wave_tot[wave] = ig;
+      sh.wpos[wave] = ie;
+    }
+    __syncthreads();
+    gt_before = ig - n_gt;
+    eq_before = ie - n_eq;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) {
+        gt_before += sh.wave_tot[w];
+        eq_before += sh.wpos[w];
+      }
+  }
   int take_eq = take - eq_before;
   take_eq = take_eq < 0 ? 0 : (take_eq > n_eq ? n_eq : take_eq);
   int pos = gt_before + (eq_before < take ? eq_before : take);

@@ -261,8 +261,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(PagesDev pg, const int32_t
     if (tier == KV_TIER_NATIVE) {
       const uint16_t* src = (kv == 0 ? pg.k16 : pg.v16) + prow * D;
       if (pg.v_hot_slot && (kv == 1 || pg.k_hot)) {
-        const int hs = pg.v_hot_slot[phys];
-        if (hs >= 0) src = (kv == 0 ? pg.k_hot : pg.v_hot) + (((size_t)hs * Hkv + g) * P + tk) * D;
+        const int hs = pg.v_hot_slot[(size_t)phys * Hkv + g];
+        if (hs >= 0) src = (kv == 0 ? pg.k_hot : pg.v_hot) + ((size_t)hs * P + tk) * D;
       }
       const u32x4_t w = ld16(src + run * RUN);
 #pragma unroll

@@ -262,29 +262,32 @@ class DeviceLayer:
         self.page_entry = torch.from_numpy(entry.view(np.int32)).to(self.device)
         self.tiers = tier_phys
 
-    def _init_hot_buffer(self, hot_mode, sel_pages=None):
+    def _init_hot_buffer(self, hot_mode):
+        """HBM hot buffer of hot_buffer_frac of the (physical page, KV head)
+        units, seeded random contents."""
         w = self.w
-        n_slots = max(1, int(round(w.hot_buffer_frac * w.n_phys)))
+        n_slots = max(1, int(round(w.hot_buffer_frac * w.n_phys * w.Hkv)))
         self.n_hot = n_slots
-        self.v_hot = torch.empty((n_slots, w.Hkv, w.P, w.d), dtype=TORCH16[w.dtype], device=self.device)
+        self.v_hot = torch.empty((n_slots, w.P, w.d), dtype=TORCH16[w.dtype], device=self.device)
         if self.host_k is not None:
             self.k_hot = torch.empty_like(self.v_hot)
-        self.set_hot_pages(np.zeros(0, np.int64) if sel_pages is None else sel_pages, fill_random=True)
+        self.set_hot_units(np.zeros(0, np.int64), fill_random=True)
 
-    def set_hot_pages(self, must_include, fill_random=True):
-        """Hot buffer = must_include pages (then a seeded random fill); copies their V."""
+    def set_hot_units(self, must_include, fill_random=True):
+        """Hot buffer = must_include units u = phys * Hkv + g (then a seeded
+        random fill); copies their V (and K with a host K pool)."""
         w = self.w
         slot, chosen = wl.hot_buffer_slots(w, self.n_hot if fill_random else min(self.n_hot, len(must_include)),
                                            self.layer, must_include)
         self.v_hot_slot = torch.from_numpy(slot).to(self.device)
-        vh = self.host_v.numpy(np.uint16, (w.n_phys, w.Hkv, w.P, w.d))
+        vh = self.host_v.numpy(np.uint16, (w.n_phys * w.Hkv, w.P, w.d))
         stage = torch.from_numpy(np.ascontiguousarray(vh[chosen]).view(np.int16)).view(TORCH16[w.dtype])
         self.v_hot[: len(chosen)].copy_(stage.to(self.device))
         if self.host_k is not None:
-            kh = self.host_k.numpy(np.uint16, (w.n_phys, w.Hkv, w.P, w.d))
+            kh = self.host_k.numpy(np.uint16, (w.n_phys * w.Hkv, w.P, w.d))
             stage = torch.from_numpy(np.ascontiguousarray(kh[chosen]).view(np.int16)).view(TORCH16[w.dtype])
             self.k_hot[: len(chosen)].copy_(stage.to(self.device))
-        self.hot_pages = chosen
+        self.hot_units = chosen
         self.pages = self._make_pages()
 
     def _make_pages(self):
@@ -329,6 +332,14 @@ class StepBuffers:
 
 def queries_device(w: wl.Workload, layer=0, qidx=0, device="cuda"):
     return to_device16(wl.query_tensor(w, layer, qidx), w.dtype, device)
+
+
+def drift_queries_device(w: wl.Workload, n_steps: int, c: float, layer=0, device="cuda"):
+    """n_steps [B, Hq, d] 16-bit device tensors of wl.drift_queries (every row)."""
+    rows = np.stack([np.stack([wl.drift_queries(w, layer, b, g, n_steps, c) for g in range(w.Hkv)], 1)
+                     for b in range(w.B)], 1)           # (n_steps, B, Hkv, G, d)
+    rows = rows.reshape(n_steps, w.B, w.Hq, w.d)
+    return [to_device16(wl.to_bits(rows[t], w.dtype), w.dtype, device) for t in range(n_steps)]
 
 
 def score(layer: DeviceLayer, q, bufs: StepBuffers, stream=None):
@@ -489,16 +500,16 @@ class SplitStep:
 # ------------------------------------------------------------------ host-resident pool with admission
 
 class MemStep:
-    """Decode steps over a host-resident V (or K and V) pool with hot-buffer
-    admission after every step (kv_hot_admit).
+    """Decode steps over a layer whose V (and, with a host K pool, K) lives in
+    device-mapped host memory behind an HBM hot buffer of (page, KV head)
+    units.
 
-    Per step, on the caller's stream: score, top-k, then attention once the
-    previous step's admission has finished (the hot map and the buffer must be
-    consistent while attention reads them).  This step's admission then runs
-    on a side stream (default priority) and overlaps the next step's score and
-    top-k.  Two step buffers alternate, so the admission reads a selection the
-    next top-k does not overwrite.  With admit=False the hot buffer stays as
-    the layer set it up."""
+    Per step, on the caller's stream: score, top-k, then (with admit=True)
+    kv_hot_admit, which stamps the units the selection calls that are hot and
+    copies the others into the least recently used slots, then attention,
+    which so reads every admitted unit from HBM.  With admit=False the hot
+    buffer stays as the layer set it up and attention reads the units that
+    are not hot over the host link."""
 
     def __init__(self, layer: DeviceLayer, admit=True):
         w = layer.w
@@ -508,36 +519,29 @@ class MemStep:
         self.bufs = [StepBuffers(w, layer.device), StepBuffers(w, layer.device)]
         n_slots = layer.v_hot.shape[0]
         sp = np.full(n_slots, -1, dtype=np.int32)
-        sp[: len(layer.hot_pages)] = np.asarray(layer.hot_pages, dtype=np.int32)
+        sp[: len(layer.hot_units)] = np.asarray(layer.hot_units, dtype=np.int32)
         self.slot_page = torch.from_numpy(sp).to(layer.device)
         self.slot_stamp = torch.zeros(n_slots, dtype=torch.int32, device=layer.device)
-        self.ws = torch.zeros(kv.hot_admit_workspace_size(n_slots) // 4, dtype=torch.int32, device=layer.device)
-        self.side = torch.cuda.Stream()
-        self.admitted = torch.cuda.Event(enable_timing=True)
+        self.ws = torch.zeros(kv.hot_admit_workspace_size(n_slots, layer.v_hot_slot.shape[0]) // 4,
+                              dtype=torch.int32, device=layer.device)
         self.admit_start = torch.cuda.Event(enable_timing=True)
+        self.admitted = torch.cuda.Event(enable_timing=True)
         self.t = 0
+
+    def admit_step(self, bufs, stream=None):
+        layer = self.layer
+        kv.hot_admit(layer.L, layer.host_v.dev.value, layer.v_hot, layer.v_hot_slot, self.slot_page,
+                     self.slot_stamp, layer.bt, layer.seq_lens, bufs.sel, bufs.sel_count, self.t, self.ws, stream,
+                     k16_ptr=layer.host_k.dev.value if layer.host_k is not None else None, k_hot=layer.k_hot)
 
     def __call__(self, q):
         layer = self.layer
         bufs = self.bufs[self.t & 1]
-        main = torch.cuda.current_stream()
         score(layer, q, bufs)
         topk(layer, bufs)
-        if self.t > 0 and self.admit:
-            main.wait_event(self.admitted)
-        attend(layer, q, bufs)
         self.t += 1
         if self.admit:
-            self.side.wait_stream(main)
-            self.admit_start.record(self.side)
-            kv.hot_admit(layer.L, layer.host_v.dev.value, layer.v_hot, layer.v_hot_slot, self.slot_page,
-                         self.slot_stamp, layer.bt, layer.seq_lens, bufs.sel, bufs.sel_count, self.t, self.ws,
-                         self.side, k16_ptr=layer.host_k.dev.value if layer.host_k is not None else None,
-                         k_hot=layer.k_hot)
-            self.admitted.record(self.side)
+            self.admit_step(bufs)
+        attend(layer, q, bufs)
         return bufs
 
-    def finish(self):
-        """Makes the caller's stream wait for the last admission."""
-        if self.admit and self.t > 0:
-            torch.cuda.current_stream().wait_event(self.admitted)

@@ -82,7 +82,7 @@ def lib():
             "kv_page_topk_workspace_size": (_SZ, [_LP, _I, _I]),
             "kv_hot_admit": (_I, [_LP, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, ctypes.c_uint32,
                                   _P, _SZ, _P]),
-            "kv_hot_admit_workspace_size": (_SZ, [_I]),
+            "kv_hot_admit_workspace_size": (_SZ, [_I, _I]),
             "kv_tier_plan": (_I, [_LP, _P, _P, _I, _I, _P, _P, ctypes.POINTER(ctypes.c_int32), _I, _I, _P, _P, _P]),
             "kv_tier_demote": (_I, [_LP, ctypes.POINTER(KvPages), _P, _I, _I, _P, _P, _P]),
             "kv_page_topk_coverage": (_I, [_LP, _P, _P, _P, _I, _I, ctypes.c_float, _I, _I, _P, _P, _I, _P,
@@ -248,14 +248,15 @@ def page_topk_coverage(L, head_scores, lse_partial, seq_lens, max_pages, coverag
     _check(rc, "kv_page_topk_coverage")
 
 
-def hot_admit_workspace_size(n_slots):
-    return int(lib().kv_hot_admit_workspace_size(int(n_slots)))
+def hot_admit_workspace_size(n_slots, n_units):
+    return int(lib().kv_hot_admit_workspace_size(int(n_slots), int(n_units)))
 
 
 def hot_admit(L, v16_ptr, v_hot, v_hot_slot, slot_page, slot_stamp, block_table, seq_lens, sel, sel_count, step,
               ws, stream=None, k16_ptr=None, k_hot=None):
     """v16_ptr / k16_ptr: device addresses (int) of the V / K pools, which may be
-    device-mapped host memory; K is admitted only with k16_ptr and k_hot."""
+    device-mapped host memory; K is admitted only with k16_ptr and k_hot.
+    v_hot_slot: int32 [n_phys * Hkv], one entry per (physical page, KV head)."""
     B, max_pages = block_table.shape
     rc = lib().kv_hot_admit(ctypes.byref(L), ctypes.c_void_p(v16_ptr), _p(v_hot),
                             None if k16_ptr is None else ctypes.c_void_p(k16_ptr), _p(k_hot), _p(v_hot_slot),

@@ -27,7 +27,7 @@ import numpy as np
 
 SEED = 2026
 
-T_Q, T_K, T_V, T_HOT, T_TABLE, T_TIER, T_SEL, T_SUMMARY, T_CENTERS, T_HOTBUF, T_BASIS, T_LOWRANK = range(12)
+T_Q, T_K, T_V, T_HOT, T_TABLE, T_TIER, T_SEL, T_SUMMARY, T_CENTERS, T_HOTBUF, T_BASIS, T_LOWRANK, T_DRIFT = range(13)
 
 TIER_NAMES = ("native", "int8", "int4", "int2", "1bit", "fp8")
 
@@ -153,6 +153,22 @@ def queries(w: Workload, layer: int, b: int, g: int, qidx: int = 0):
     return round16(x, w.dtype)
 
 
+def drift_queries(w: Workload, layer: int, b: int, g: int, n_steps: int, c: float):
+    """(n_steps, G, d) float32 decode-step queries with step-to-step locality:
+    q_0 is query draw 0 and q_t = c q_{t-1} + sqrt(1 - c^2) xi_t with seeded
+    xi_t ~ N(0, 1), so every q_t is N(0, 1) per element and consecutive
+    queries have cosine about c; each rounded to the pool dtype."""
+    rng = rng_for(w, layer, b, g, T_DRIFT)
+    x = queries(w, layer, b, g, 0).astype(np.float64)
+    s = np.sqrt(max(0.0, 1.0 - c * c))
+    out = np.empty((n_steps, w.G, w.d), dtype=np.float32)
+    for t in range(n_steps):
+        if t > 0:
+            x = c * x + s * rng.standard_normal((w.G, w.d))
+        out[t] = round16(x.astype(np.float32), w.dtype)
+    return out
+
+
 def hot_pages(w: Workload, layer: int, b: int):
     """Sorted logical pages that carry planted high-mass keys in sequence b."""
     rng = rng_for(w, layer, b, 0, T_HOT)
@@ -233,15 +249,17 @@ def page_tiers(w: Workload, layer: int = 0):
 
 
 def hot_buffer_slots(w: Workload, n_slots: int, layer: int = 0, must_include=()):
-    """Physical pages resident in the V hot buffer: must_include first, then a
-    seeded random fill, at most n_slots.  Returns (slot_of_page[n_phys] int32, pages)."""
+    """Units u = phys * Hkv + g (one physical page of one KV head) resident in
+    the V hot buffer: must_include first, then a seeded random fill, at most
+    n_slots.  Returns (slot_of_unit[n_phys * Hkv] int32, units)."""
+    n_units = w.n_phys * w.Hkv
     rng = rng_for(w, layer, 0, 0, T_HOTBUF)
-    chosen = list(dict.fromkeys(int(p) for p in must_include))[:n_slots]
+    chosen = list(dict.fromkeys(int(u) for u in must_include))[:n_slots]
     if len(chosen) < n_slots:
-        rest = np.setdiff1d(rng.permutation(w.n_phys), np.array(chosen, dtype=np.int64), assume_unique=False)
+        rest = np.setdiff1d(rng.permutation(n_units), np.array(chosen, dtype=np.int64), assume_unique=False)
         rest = rng.permutation(rest)[: n_slots - len(chosen)]
-        chosen += [int(p) for p in rest]
-    slot = np.full(w.n_phys, -1, dtype=np.int32)
+        chosen += [int(u) for u in rest]
+    slot = np.full(n_units, -1, dtype=np.int32)
     slot[np.array(chosen, dtype=np.int64)] = np.arange(len(chosen), dtype=np.int32)
     return slot, np.array(chosen, dtype=np.int64)
 

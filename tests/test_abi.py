@@ -282,26 +282,33 @@ def test_shared_basis_validation():
 def test_hot_admit_validation_and_workspace():
     L = _L()
     f = kv.lib().kv_hot_admit
-    assert kv.hot_admit_workspace_size(100) == (1 + 3 * 100) * 4
-    assert kv.hot_admit_workspace_size(0) == 0
+    # count + 100 (unit, slot) pairs + 100 misses = 301 words, padded to 320; the
+    # bitmap of 1000 units (32 words) ends at 352, padded to 384; then 100 slot keys
+    assert kv.hot_admit_workspace_size(100, 1000) == (384 + 100) * 4
+    assert kv.hot_admit_workspace_size(0, 1000) == 0
+    assert kv.hot_admit_workspace_size(100, 0) == 0
+    assert kv.hot_admit_workspace_size((1 << 22) + 1, 1000) == 0
 
-    def call(v16=FAKE, v_hot=FAKE, k16=None, k_hot=None, hot=FAKE, n_phys=1000, n_slots=100, step=1,
+    def call(v16=FAKE, v_hot=FAKE, k16=None, k_hot=None, hot=FAKE, n_units=1000, n_slots=100, step=1,
              ws=FAKE, ws_bytes=1 << 20, sel=FAKE, B=2):
-        return f(ctypes.byref(L), v16, v_hot, k16, k_hot, hot, n_phys, FAKE, FAKE, n_slots, FAKE, FAKE, B, 64,
+        return f(ctypes.byref(L), v16, v_hot, k16, k_hot, hot, n_units, FAKE, FAKE, n_slots, FAKE, FAKE, B, 64,
                  sel, FAKE, 12, step, ws, ws_bytes, None)
 
+    assert L.num_kv_heads == 8
     assert call(step=0) == kv.KV_ERR_INVALID_ARG                     # steps start at 1
     assert call(n_slots=0) == kv.KV_ERR_INVALID_ARG
-    assert call(n_slots=(1 << 14) + 1) == kv.KV_ERR_UNSUPPORTED
-    assert call(n_phys=(1 << 19) + 1) == kv.KV_ERR_UNSUPPORTED
+    assert call(n_units=1004) == kv.KV_ERR_INVALID_ARG               # not n_phys * Hkv
+    assert call(n_slots=(1 << 22) + 1) == kv.KV_ERR_UNSUPPORTED
+    assert call(n_units=(1 << 24) + 8) == kv.KV_ERR_UNSUPPORTED
     assert call(v16=None) == kv.KV_ERR_INVALID_ARG
     assert call(v_hot=FAKE + 8) == kv.KV_ERR_INVALID_ARG
     assert call(hot=None) == kv.KV_ERR_INVALID_ARG
     assert call(k16=FAKE) == kv.KV_ERR_INVALID_ARG                   # K pool without a K hot buffer
     assert call(k_hot=FAKE) == kv.KV_ERR_INVALID_ARG                 # and the reverse
     assert call(sel=None) == kv.KV_ERR_INVALID_ARG
-    assert call(ws_bytes=(1 + 3 * 100) * 4 - 1) == kv.KV_ERR_WORKSPACE
+    assert call(ws_bytes=(384 + 100) * 4 - 1) == kv.KV_ERR_WORKSPACE
     assert call(ws=None) == kv.KV_ERR_WORKSPACE
+    assert call(ws=FAKE + 2) == kv.KV_ERR_WORKSPACE                  # not 4-byte aligned
 
 
 def test_tier_plan_and_demote_validation():

@@ -179,17 +179,19 @@ def test_heavy_host_mapped_values(hz):
         torch.cuda.synchronize()
         sel = bufs.sel.cpu().numpy()
         rows = sample_rows(w)
-        # warm: the hot buffer holds the pages the sampled rows selected (then a
-        # seeded fill); every other V page is read through the host mapping
-        must = np.unique(np.concatenate([layer.bt_np[b, sel[b, g]] for b, g in rows]))
-        layer.set_hot_pages(must)
-        announce(f"heavy70b_128k: attention, {len(must)} pages forced hot")
+        # warm: the hot buffer holds the (page, KV head) units the sampled rows
+        # selected (then a seeded fill); every other unit is read through the
+        # host mapping
+        must = np.unique(np.concatenate([layer.bt_np[b, sel[b, g]].astype(np.int64) * w.Hkv + g
+                                         for b, g in rows]))
+        layer.set_hot_units(must)
+        announce(f"heavy70b_128k: attention, {len(must)} units forced hot")
         hz.attend(layer, q, bufs)
         torch.cuda.synchronize()
         out_warm = bufs.out.cpu().numpy().copy()
         _e2e_check(w, layer, bufs, rows)
         # cold: a seeded random hot set; results must not change
-        layer.set_hot_pages(np.zeros(0, np.int64))
+        layer.set_hot_units(np.zeros(0, np.int64))
         announce("heavy70b_128k: attention with a random hot buffer")
         hz.attend(layer, q, bufs)
         torch.cuda.synchronize()

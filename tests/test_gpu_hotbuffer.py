@@ -1,10 +1,11 @@
 """GPU parity of hot-buffer admission (kv_hot_admit) against the oracle's rule.
 
-Over a sequence of steps with seeded selections, after every step the three
-state arrays (page -> slot, slot -> page, slot stamps) must equal the oracle's
-exactly, and every hot slot must hold its page's V bit for bit.  With the V pool
-in pinned, device-mapped host memory, attention results must not depend on
-which pages are hot (the same bits are read from either place).
+The buffer's unit is one (physical page, KV head), u = phys * Hkv + g.  Over a
+sequence of steps with seeded selections, after every step the three state
+arrays (unit -> slot, slot -> unit, slot stamps) and the copy list must equal
+the oracle's exactly, and every hot slot must hold its unit's V bit for bit.
+With the V pool in pinned, device-mapped host memory, attention results must
+not depend on which units are hot (the same bits are read from either place).
 """
 
 import numpy as np
@@ -43,7 +44,8 @@ def _step_selection(w, rng, k_max, lens):
     return sel, cnt
 
 
-@pytest.mark.parametrize("name,n_slots", [("llama_small", 40), ("heavy_small", 13), ("heavy_small", 400)])
+@pytest.mark.parametrize("name,n_slots", [("llama_small", 40), ("heavy_small", 13), ("heavy_small", 400),
+                                          ("llama_small", 40000)])
 def test_admission_matches_oracle(hz, name, n_slots):
     from quantized_kv_cache_summary_amd import kvsparse as kv
     w = {"llama_small": W["llama8b_32k"].replace(B=2, ctx=16 * 300 + 7),
@@ -52,22 +54,22 @@ def test_admission_matches_oracle(hz, name, n_slots):
     lens = [w.ctx, w.ctx - 7 * w.P]
     layer = hz.DeviceLayer(w, summaries=None, seq_lens=lens)
     L = layer.L
-    n_phys = w.n_phys
-    hot = torch.full((n_phys,), -1, dtype=torch.int32, device="cuda")
+    n_units = w.n_phys * w.Hkv
+    hot = torch.full((n_units,), -1, dtype=torch.int32, device="cuda")
     slot_page = torch.full((n_slots,), -1, dtype=torch.int32, device="cuda")
     slot_stamp = torch.zeros((n_slots,), dtype=torch.int32, device="cuda")
-    v_hot = torch.zeros((n_slots, w.Hkv, w.P, w.d), dtype=layer.v16.dtype, device="cuda")
-    ws = torch.zeros(kv.hot_admit_workspace_size(n_slots) // 4, dtype=torch.int32, device="cuda")
-    ref = oracle.HotBuffer(n_phys, n_slots)
+    v_hot = torch.zeros((n_slots, w.P, w.d), dtype=layer.v16.dtype, device="cuda")
+    ws = torch.full((kv.hot_admit_workspace_size(n_slots, n_units) // 4,), -7, dtype=torch.int32, device="cuda")
+    ref = oracle.HotBuffer(n_units, n_slots)
     rng = np.random.default_rng(41 + n_slots)
-    k_max = 12
-    v_all = layer.v16.view(torch.int16).cpu().numpy().reshape(n_phys, -1)
+    k_max = 12 if n_slots < 1000 else 160
+    v_all = layer.v16.view(torch.int16).cpu().numpy().reshape(n_units, -1)
     for t in range(1, 16):
         sel, cnt = _step_selection(w, rng, k_max, lens)
         kv.hot_admit(L, layer.v16.data_ptr(), v_hot, hot, slot_page, slot_stamp, layer.bt, layer.seq_lens,
                      torch.from_numpy(sel).cuda(), torch.from_numpy(cnt).cuda(), t, ws)
         torch.cuda.synchronize()
-        U = oracle.selected_physical_pages(sel, cnt, layer.bt_np, w.Hkv, np.array(lens), w.P)
+        U = oracle.selected_units(sel, cnt, layer.bt_np, w.Hkv, np.array(lens), w.P)
         copies = ref.step(U, t)
         assert np.array_equal(hot.cpu().numpy(), ref.hot), t
         assert np.array_equal(slot_page.cpu().numpy(), ref.slot_page), t
@@ -75,9 +77,9 @@ def test_admission_matches_oracle(hz, name, n_slots):
         wsn = ws.cpu().numpy()
         assert wsn[0] == len(copies) and [tuple(x) for x in wsn[1:1 + 2 * len(copies)].reshape(-1, 2)] == copies
         vh = v_hot.view(torch.int16).cpu().numpy().reshape(n_slots, -1)
-        for s, p in enumerate(ref.slot_page):
-            if p >= 0:
-                assert np.array_equal(vh[s], v_all[p]), (t, s, p)
+        for s, u in enumerate(ref.slot_page):
+            if u >= 0:
+                assert np.array_equal(vh[s], v_all[u]), (t, s, u)
 
 
 def test_admission_from_host_mapped_pool_keeps_attention(hz):
@@ -94,21 +96,21 @@ def test_admission_from_host_mapped_pool_keeps_attention(hz):
         torch.cuda.synchronize()
         out0, lse0 = bufs.out.cpu().numpy().copy(), bufs.lse.cpu().numpy().copy()
         n_slots = layer.v_hot.shape[0]
-        slot_page = torch.from_numpy(np.array(layer.hot_pages, dtype=np.int32)).cuda()
+        slot_page = torch.from_numpy(np.array(layer.hot_units, dtype=np.int32)).cuda()
         if slot_page.numel() < n_slots:
             slot_page = torch.cat([slot_page, torch.full((n_slots - slot_page.numel(),), -1, dtype=torch.int32,
                                                           device="cuda")])
         slot_stamp = torch.zeros(n_slots, dtype=torch.int32, device="cuda")
         hot = layer.v_hot_slot.clone()
-        ws = torch.zeros(kv.hot_admit_workspace_size(n_slots) // 4, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(kv.hot_admit_workspace_size(n_slots, hot.shape[0]) // 4, dtype=torch.int32, device="cuda")
         kv.hot_admit(layer.L, layer.host_v.dev.value, layer.v_hot, hot, slot_page, slot_stamp, layer.bt,
                      layer.seq_lens, bufs.sel, bufs.sel_count, 1, ws)
         torch.cuda.synchronize()
         layer.v_hot_slot = hot
         layer.pages = layer._make_pages()
-        # every selected page is hot now (the step fits the buffer) ...
+        # every selected unit is hot now (the step fits the buffer) ...
         sel, cnt = bufs.sel.cpu().numpy(), bufs.sel_count.cpu().numpy()
-        U = oracle.selected_physical_pages(sel, cnt, layer.bt_np, w.Hkv, layer.seq_lens_np, w.P)
+        U = oracle.selected_units(sel, cnt, layer.bt_np, w.Hkv, layer.seq_lens_np, w.P)
         if U.size <= n_slots:
             assert np.all(hot.cpu().numpy()[U] >= 0)
         # ... and attention reads the same bits from the buffer
@@ -122,9 +124,9 @@ def test_admission_from_host_mapped_pool_keeps_attention(hz):
 
 def test_mem_kv_pool_with_admission_matches_resident(hz):
     """K and V both in device-mapped host memory (mem-kv) with a hot buffer for
-    each, driven step by step with admission on a side stream: every step's
-    selection and attention are bit-identical to the same layer held in HBM,
-    and every hot slot holds its page's K and V."""
+    each, driven step by step with admission before every attention: every
+    step's selection and attention are bit-identical to the same layer held in
+    HBM, and every hot slot holds its unit's K and V."""
     from parity import assert_attn_close, check_selection
     base = W["heavy70b_128k"].replace(B=2, Hq=16, Hkv=2, ctx=32 * 150 + 5)
     announce("mem-kv pool (K and V host-mapped) against the resident layer")
@@ -141,24 +143,23 @@ def test_mem_kv_pool_with_admission_matches_resident(hz):
             q = hz.queries_device(w, 0, t % 2)          # steps repeat, so later ones hit the buffer
             hz.decode_step(res, q, rbufs)
             mb = ms(q)
-            ms.finish()
             torch.cuda.synchronize()
             np.testing.assert_array_equal(mb.sel_count.cpu().numpy(), rbufs.sel_count.cpu().numpy())
             np.testing.assert_array_equal(mb.sel.cpu().numpy(), rbufs.sel.cpu().numpy())
             np.testing.assert_array_equal(mb.out.cpu().numpy(), rbufs.out.cpu().numpy())
             np.testing.assert_array_equal(mb.lse.cpu().numpy(), rbufs.lse.cpu().numpy())
         # the buffer's contents follow its map, for K and V
-        kh = mem.host_k.numpy(np.uint16, (w.n_phys, w.Hkv, w.P, w.d))
-        vh = mem.host_v.numpy(np.uint16, (w.n_phys, w.Hkv, w.P, w.d))
+        kh = mem.host_k.numpy(np.uint16, (w.n_phys * w.Hkv, w.P, w.d))
+        vh = mem.host_v.numpy(np.uint16, (w.n_phys * w.Hkv, w.P, w.d))
         k_hot = mem.k_hot.view(torch.int16).cpu().numpy().view(np.uint16)
         v_hot = mem.v_hot.view(torch.int16).cpu().numpy().view(np.uint16)
         slot_page = ms.slot_page.cpu().numpy()
         hot = mem.v_hot_slot.cpu().numpy()
         assert (slot_page >= 0).sum() == k_hot.shape[0]
-        for s, p in enumerate(slot_page):
-            assert hot[p] == s
-            np.testing.assert_array_equal(k_hot[s], kh[p])
-            np.testing.assert_array_equal(v_hot[s], vh[p])
+        for s, u in enumerate(slot_page):
+            assert hot[u] == s
+            np.testing.assert_array_equal(k_hot[s], kh[u])
+            np.testing.assert_array_equal(v_hot[s], vh[u])
         # and the last step against the oracle on every row
         sel, out, lse = mb.sel.cpu().numpy(), mb.out.cpu().numpy(), mb.lse.cpu().numpy()
         for b in range(w.B):

@@ -3,11 +3,11 @@ invariants over seeded random sequences."""
 
 import numpy as np
 
-from oracle.hotbuffer import HotBuffer, selected_physical_pages
+from oracle.hotbuffer import HotBuffer, selected_physical_pages, selected_units
 
 
 def test_hand_worked_sequence():
-    h = HotBuffer(n_phys=10, n_slots=3)
+    h = HotBuffer(n_ids=10, n_slots=3)
     assert h.step([5, 2, 5], 1) == [(2, 0), (5, 1)]                 # fill: free slots by index
     assert h.step([5, 7, 9], 2) == [(7, 0), (9, 2)]                 # 5 hits; LRU slot 2 (never) then 0
     assert list(h.hot[[2, 5, 7, 9]]) == [-1, 1, 0, 2]
@@ -48,3 +48,17 @@ def test_selected_pages_follow_counts_and_lengths():
     # row (0,0): pages 0,2,3 -> 7,5,1; row (0,1): 1,3 -> 3,1; sequence 1 has 2 pages:
     # row (1,0): 3 (skipped), 1 -> 2; row (1,1): 2 (skipped), 0,0,0 -> 0
     assert list(got) == [0, 1, 2, 3, 5, 7]
+
+
+def test_selected_units_follow_counts_lengths_and_heads():
+    bt = np.array([[7, 3, 5, 1], [0, 2, 4, 6]])
+    sel = np.array([[[0, 2, 3, -1], [1, 3, 0, 0]], [[3, 1, 0, 0], [2, 0, 0, 0]]])
+    cnt = np.array([[3, 2], [2, 9]])                                # 9 clamps to k_max = 4
+    got = selected_units(sel, cnt, bt, 2, seq_lens=np.array([64, 30]), page_size=16)
+    # u = phys * 2 + g.  Row (0,0): phys 7,5,1 -> 14,10,2; row (0,1): phys 3,1 -> 7,3;
+    # row (1,0): page 3 past the 2 pages, page 1 -> phys 2 -> 4; row (1,1): pages 0,0,0 -> phys 0 -> 1
+    assert list(got) == [1, 2, 3, 4, 7, 10, 14]
+    # the same physical page selected by both heads is two units
+    sel2 = np.array([[[1], [1]]])
+    got2 = selected_units(sel2, np.array([[1, 1]]), np.array([[4, 9]]), 2, seq_lens=np.array([32]), page_size=16)
+    assert list(got2) == [18, 19]
