@@ -386,7 +386,7 @@ def measure_step(w, args, extras, label=None):
               "attention": (selected_b, "K and V of the selected pages (codes and scale/zero for packed tiers)"),
               "topk_attention": (selected_b + head_scores_b,
                                  "K and V of the selected pages plus the head scores read once per row")}
-    kernels = {role: roofline_entry(kn[role], kbytes[role][0], us, w.name, kbytes[role][1])
+    kernels = {role: roofline_entry(kn[role], kbytes[role][0], us, label, kbytes[role][1])
                for role, us in kus.items()}
     dominant = max(kernels, key=lambda r: kernels[r]["avg_launch_us"])
     roofline = dict(kernels[dominant])
@@ -401,7 +401,7 @@ def measure_step(w, args, extras, label=None):
         "algorithmic_bytes_per_step": {"summaries": summary_b, "selected_kv": selected_b},
         "step_ms_distribution": distribution(per),
         "config": {
-            "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+            "workload": label, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
             "page_size": w.P, "ctx": w.ctx, "rank": w.rank, "keep": w.keep, "k_per_row": int(sel_counts.max()),
             "tiers": None if tiers is None else dict(zip([wl.TIER_NAMES[t] for t in w.tier_order], w.tier_fracs)),
             "rotated_layers": n_layers, "queries": nq, "row_groups_on_streams": args.groups,
@@ -730,7 +730,10 @@ def main():
     import torch
     from quantized_kv_cache_summary_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
+    if args.workload == "heavy70b_128k_v_in_hbm":
+        w = wl.WORKLOADS["heavy70b_128k"].replace(v_host=False, hot_buffer_frac=0.0)
+    else:
+        w = wl.WORKLOADS[args.workload]
     if w.v_host:
         return mem_main(args, w)
     torch.cuda.set_device(0)
@@ -740,7 +743,7 @@ def main():
         configs = []
     else:
         configs = [c for c in args.configs.split(",") if c]
-    res, st = measure_step(w, args, extras=not args.no_extras)
+    res, st = measure_step(w, args, extras=not args.no_extras, label=args.workload)
     if not args.no_extras:
         headline_extras(w, args, res, st)
     release(st)
