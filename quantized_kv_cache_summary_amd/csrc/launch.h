@@ -71,18 +71,24 @@ hipError_t launch_page_score_basis(const kv_layout& L, const void* q, const void
                                    int max_pages, float tau, float* head_scores, float* lse_partial,
                                    hipStream_t st);
 
-// Hot-buffer admission: units u = phys * Hkv + g, limits of the one-block
-// plan, and its workspace (int32 words): count, (unit, slot) pairs, miss list,
-// then the unit bitmap and the slot keys, each at a 64-word boundary.
+// Hot-buffer admission: units u = phys * Hkv + g, limits, and the workspace
+// (int32 words): count, (unit, slot) pairs, miss list, then at 64-word
+// boundaries the unit bitmap, the slot keys, the per-block miss counts, the
+// per-block victim counts and three scalars.
 constexpr int kAdmitMaxUnits = 1 << 24;
 constexpr int kAdmitMaxSlots = 1 << 22;
-struct HotAdmitWs { size_t bits, keys, words; };
+struct HotAdmitWs { size_t bits, keys, wcnt, vcnt, scal, words; };
 inline HotAdmitWs hot_admit_ws_layout(int n_slots, int n_units) {
   auto up64 = [](size_t x) { return (x + 63) & ~(size_t)63; };
+  const size_t n_words = ((size_t)n_units + 31) >> 5;
+  const size_t n_wblocks = (n_words + 255) / 256, n_sblocks = ((size_t)n_slots + 255) / 256;
   HotAdmitWs l;
   l.bits = up64(1 + 3 * (size_t)n_slots);
-  l.keys = up64(l.bits + (((size_t)n_units + 31) >> 5));
-  l.words = l.keys + (size_t)n_slots;
+  l.keys = up64(l.bits + n_words);
+  l.wcnt = up64(l.keys + (size_t)n_slots);
+  l.vcnt = up64(l.wcnt + n_wblocks);
+  l.scal = up64(l.vcnt + 2 * n_sblocks);
+  l.words = l.scal + 4;
   return l;
 }
 inline size_t hot_admit_workspace_bytes(int n_slots, int n_units) {

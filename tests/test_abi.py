@@ -283,8 +283,10 @@ def test_hot_admit_validation_and_workspace():
     L = _L()
     f = kv.lib().kv_hot_admit
     # count + 100 (unit, slot) pairs + 100 misses = 301 words, padded to 320; the
-    # bitmap of 1000 units (32 words) ends at 352, padded to 384; then 100 slot keys
-    assert kv.hot_admit_workspace_size(100, 1000) == (384 + 100) * 4
+    # bitmap of 1000 units (32 words) ends at 352, padded to 384; 100 slot keys end
+    # at 484, padded to 512; one word block's miss count ends at 513, padded to
+    # 576; one slot block's two victim counts end at 578, padded to 640; 4 scalars
+    assert kv.hot_admit_workspace_size(100, 1000) == 644 * 4
     assert kv.hot_admit_workspace_size(0, 1000) == 0
     assert kv.hot_admit_workspace_size(100, 0) == 0
     assert kv.hot_admit_workspace_size((1 << 22) + 1, 1000) == 0
@@ -306,7 +308,7 @@ def test_hot_admit_validation_and_workspace():
     assert call(k16=FAKE) == kv.KV_ERR_INVALID_ARG                   # K pool without a K hot buffer
     assert call(k_hot=FAKE) == kv.KV_ERR_INVALID_ARG                 # and the reverse
     assert call(sel=None) == kv.KV_ERR_INVALID_ARG
-    assert call(ws_bytes=(384 + 100) * 4 - 1) == kv.KV_ERR_WORKSPACE
+    assert call(ws_bytes=644 * 4 - 1) == kv.KV_ERR_WORKSPACE
     assert call(ws=None) == kv.KV_ERR_WORKSPACE
     assert call(ws=FAKE + 2) == kv.KV_ERR_WORKSPACE                  # not 4-byte aligned
 
