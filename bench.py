@@ -932,9 +932,9 @@ def mem_main(args, w):
         t0 = time.time()
         layer = hz.DeviceLayer(w, summaries="build", hot_mode="cold", host_k=True)
         log(f"[bench] {w.name} mem-kv: set-up {time.time() - t0:.1f}s")
-        iid = mem_queries(w, "iid", nq)
-        memkv = {"static": mem_run(w, layer, False, K, W, iid)[0], "admission": mem_run(w, layer, True, K, W, iid)[0]}
-        log(f"[bench] mem-kv: {memkv}")
+        kv_runs, kv_counts = mem_runs(w, layer, K, W, nq)
+        sb_k, selb_k = algorithmic_bytes(w, kv_counts)
+        memkv = mem_summary(w, kv_runs, sb_k, selb_k)
         layer.release()
 
     # the same step with V resident in HBM: the bound a hot buffer holding every
