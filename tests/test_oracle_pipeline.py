@@ -2,8 +2,9 @@
 
 A sanity check, not parity: on the tiny workload (4 planted high-mass pages per
 sequence, keys = 3 u_g + noise) the oracle's top-8 pages per KV head contain
-every planted page, with per-page summaries and with the shared-basis ones; and
-the generator reproduces any row on its own.
+every planted page, with per-page summaries and with the shared-basis ones; the
+generator reproduces any row on its own; and the drifting-query recipe of the
+host-resident runs has the stated statistics.
 """
 
 import numpy as np
@@ -92,3 +93,17 @@ def test_worked_step_closed_forms():
         r = decode_row(q, keys, values, fx["seq_len"], fx["page_size"], fx["rank"], fx["tau"],
                        coverage=case["coverage"])
         assert r["k"] == case["k"] and r["sel"].tolist() == case["sel"], case
+
+
+def test_drift_queries_recipe():
+    """The host-resident runs' drifting queries: q_0 is query draw 0, every
+    step keeps N(0, 1) marginals, and consecutive queries have cosine about c."""
+    w = wl.WORKLOADS["heavy70b_128k"]
+    c = 0.95
+    q = wl.drift_queries(w, 0, 3, 5, 40, c).astype(np.float64)
+    assert np.array_equal(q[0], wl.queries(w, 0, 3, 5, 0))
+    cos = [float(np.sum(q[t] * q[t + 1]) / np.linalg.norm(q[t]) / np.linalg.norm(q[t + 1])) for t in range(39)]
+    assert abs(np.mean(cos) - c) < 0.01
+    assert abs(q.std() - 1.0) < 0.05
+    iid = np.stack([wl.queries(w, 0, 3, 5, j) for j in range(2)]).astype(np.float64)
+    assert abs(float(np.sum(iid[0] * iid[1]) / np.linalg.norm(iid[0]) / np.linalg.norm(iid[1]))) < 0.2
