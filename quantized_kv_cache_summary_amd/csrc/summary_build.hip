@@ -10,17 +10,20 @@
 // position (sequence, KV head, page), where the scorer streams them in order.
 //
 // One wave per (page, KV head).  The keys are centred into LDS once and the
-// n x n Gram comes from the float32 MFMA (16 x 16 tiles of X X^T).  The top R
-// eigenpairs are found without sweeping the whole spectrum:
-//   1. Householder reduction of the Gram to tridiagonal form T = Q^T G Q
-//      (n - 2 reflections, each a rank-2 update of the trailing block);
+// Gram comes from the float32 MFMA (16 x 16 tiles of X X^T), padded to P x P
+// with zero rows (which only adds zero eigenvalues).  The top R eigenpairs are
+// found without sweeping the whole spectrum, in registers: lane i (and its
+// copies i + P, ...) holds row i of the Gram and of Q.
+//   1. Householder reduction to tridiagonal form T = Q^T G Q (P - 2
+//      reflections, each a rank-2 update of the trailing block), with Q
+//      accumulated row by row;
 //   2. the R largest eigenvalues of T by multisection on Sturm counts (the
 //      lanes of a group evaluate the count at evenly spaced points of the
 //      eigenvalue's bracket, so each round shrinks it lp + 1 times);
-//   3. each eigenvector of T from the twisted factorisation of T - lam I
-//      (forward and backward LDL^T, twisted where |gamma| is smallest), then
-//      modified Gram-Schmidt among the R vectors and the back-transform by
-//      the reflections.
+//   3. each eigenvector z of T from the twisted factorisation of T - lam I
+//      (forward and backward LDL^T, twisted where |gamma| is smallest), its
+//      Rayleigh quotient as the eigenvalue, modified Gram-Schmidt among the R
+//      vectors, then u = Q z.
 // A kept eigenvector that Gram-Schmidt leaves (almost) empty means an
 // eigenvalue repeated inside the top R (T splits, and the twisted solves
 // return the same vector); such a page is redone by cyclic Jacobi on the
