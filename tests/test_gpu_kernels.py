@@ -30,6 +30,11 @@ SUMMARY_ONLY = {
     "gmm_small": W["tiers_64k"].replace(B=2, ctx=16 * 120 + 9, keys="gmm", gmm_centers=64, gmm_std=0.5),
     "heavy_f16_small": W["heavy70b_128k"].replace(B=2, Hq=16, Hkv=2, ctx=32 * 60 + 17, v_host=False,
                                                   dtype="f16"),
+    # the solver's other group widths: rank 8 (8 lanes per eigenvalue) at page
+    # sizes 16 and 32 and rank 1 (one group of 64 lanes); the tiny workload has rank 2
+    "r8_p16": W["llama8b_32k"].replace(B=2, Hq=8, Hkv=2, ctx=16 * 90 + 11, rank=8),
+    "r8_p32": W["heavy70b_128k"].replace(B=2, Hq=16, Hkv=2, ctx=32 * 45 + 21, v_host=False, rank=8),
+    "r1_p16": W["llama8b_32k"].replace(B=2, Hq=8, Hkv=2, ctx=16 * 90 + 5, rank=1),
 }
 
 
@@ -444,7 +449,8 @@ def check_layer_summaries(w, layer, lens, row_keys, pages=None):
     return counts
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama_small", "heavy_small", "gmm_small", "heavy_f16_small"])
+@pytest.mark.parametrize("name", ["tiny", "llama_small", "heavy_small", "gmm_small", "heavy_f16_small", "r8_p16",
+                                  "r8_p32", "r1_p16"])
 def test_summary_builder_invariants(hz, name):
     w = SMALL[name] if name in SMALL else SUMMARY_ONLY[name]
     lens = [w.ctx, w.ctx - w.P - 3] if w.B == 2 else [w.ctx]
