@@ -492,12 +492,13 @@ def crafted_page(kind, P, d, rng):
 CRAFTED = ("four_equal", "two_pairs", "eight_equal", "rank_two", "identical", "doubled")
 
 
-@pytest.mark.parametrize("name", ["llama_small", "heavy_small"])
+@pytest.mark.parametrize("name", ["llama_small", "heavy_small", "r8_p16", "r8_p32"])
 def test_summary_builder_repeated_eigenvalues(hz, name):
     """Pages with repeated top eigenvalues, rank below R, no spread at all, and
     duplicated keys, written into the K pool and summarised again; a partial
     last page of each kind as well."""
-    w = SMALL[name].replace(B=1, ctx=SMALL[name].P * 40 + 6)
+    base = SMALL[name] if name in SMALL else SUMMARY_ONLY[name]
+    w = base.replace(B=1, ctx=base.P * 40 + 6)
     lens = [w.ctx]
     announce(f"summary build on crafted pages {name}")
     layer = hz.DeviceLayer(w, summaries=None, seq_lens=lens)
