@@ -5,7 +5,8 @@ sequence of steps with seeded selections, after every step the three state
 arrays (unit -> slot, slot -> unit, slot stamps) and the copy list must equal
 the oracle's exactly, and every hot slot must hold its unit's V bit for bit.
 With the V pool in pinned, device-mapped host memory, attention results must
-not depend on which units are hot (the same bits are read from either place).
+not depend on which units are hot (the same bits are read from either place),
+and the standalone decode reads every page's K and V through the buffer.
 """
 
 import numpy as np
@@ -174,3 +175,30 @@ def test_mem_kv_pool_with_admission_matches_resident(hz):
                     assert_attn_close(out[b, hs], lse[b, hs], r["out"], r["lse"])
     finally:
         mem.release()
+
+
+@pytest.mark.parametrize("host_k", [False, True])
+def test_dequant_reads_through_the_hot_buffer(hz, host_k):
+    """kv_dequant_tier over a layer whose V (and, mem-kv, K) sit in device-mapped
+    host memory behind a buffer of (page, KV head) units: every page's K and V
+    come out equal to the pool's values, whichever of its units are hot."""
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    w = W["heavy70b_128k"].replace(B=2, Hq=16, Hkv=2, ctx=32 * 150 + 5, k_host=host_k)
+    announce(f"dequant through the hot buffer, K in host memory: {host_k}")
+    layer = hz.DeviceLayer(w, summaries=None, hot_mode="cold")
+    try:
+        ids_np = np.arange(w.n_phys, dtype=np.int32)
+        out = torch.empty((w.n_phys, 2, w.Hkv, w.P, w.d), dtype=torch.float32, device="cuda")
+        kv.dequant_tier(layer.L, layer.pages, torch.from_numpy(ids_np).cuda(), out)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        shape = (w.n_phys, w.Hkv, w.P, w.d)
+        kpool = (layer.host_k.numpy(np.uint16, shape) if host_k
+                 else layer.k16.view(torch.int16).cpu().numpy().view(np.uint16).reshape(shape))
+        vpool = layer.host_v.numpy(np.uint16, shape)
+        np.testing.assert_array_equal(out[:, 0], wl.bits_to_f32(kpool, w.dtype))
+        np.testing.assert_array_equal(out[:, 1], wl.bits_to_f32(vpool, w.dtype))
+        hot = layer.v_hot_slot.cpu().numpy()
+        assert (hot >= 0).any() and (hot < 0).any()      # both kinds of unit were read
+    finally:
+        layer.release()
