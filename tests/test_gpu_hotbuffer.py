@@ -202,3 +202,42 @@ def test_dequant_reads_through_the_hot_buffer(hz, host_k):
         assert (hot >= 0).any() and (hot < 0).any()      # both kinds of unit were read
     finally:
         layer.release()
+
+
+def test_tiered_layout_reads_native_values_through_the_hot_buffer(hz):
+    """A tiered layout with a unit hot buffer: the native pages' values are read
+    from the buffer where their unit is hot, and the attention is bit-identical
+    to the same layout without a buffer (packed tiers keep their own pools)."""
+    from quantized_kv_cache_summary_amd import kvsparse as kv
+    w = W["tiers_64k"].replace(B=2, ctx=16 * 300 + 7)
+    announce("tiered layout with a hot buffer of native units")
+    layer = hz.DeviceLayer(w, summaries=None)
+    q = hz.queries_device(w)
+    sel_np, cnt_np = wl.synthetic_selection(w, w.k_of(w.Np), ragged=True)
+    sel, cnt = torch.from_numpy(sel_np).cuda(), torch.from_numpy(cnt_np).cuda()
+    bufs = hz.StepBuffers(w)
+    hz.attend(layer, q, bufs, sel=sel, sel_count=cnt)
+    torch.cuda.synchronize()
+    out0, lse0 = bufs.out.cpu().numpy().copy(), bufs.lse.cpu().numpy().copy()
+    n_units = w.n_phys * w.Hkv
+    native_units = np.nonzero(np.repeat(layer.tier_phys == 0, w.Hkv))[0]
+    units = native_units[::2]
+    assert units.size > 0
+    slot = np.full(n_units, -1, dtype=np.int32)
+    slot[units] = np.arange(units.size, dtype=np.int32)
+    # the buffer holds copies of the units' values; the pool keeps them too
+    layer.v_hot = layer.v16.view(n_units, w.P, w.d)[torch.from_numpy(units).cuda()].contiguous()
+    layer.v_hot_slot = torch.from_numpy(slot).cuda()
+    layer.pages = layer._make_pages()
+    bufs.out.fill_(float("nan"))
+    hz.attend(layer, q, bufs, sel=sel, sel_count=cnt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bufs.out.cpu().numpy(), out0)
+    np.testing.assert_array_equal(bufs.lse.cpu().numpy(), lse0)
+    # with the pool's values zeroed where the unit is hot, the result still holds
+    # only because those units are read from the buffer
+    pool = layer.v16.view(n_units, w.P, w.d)
+    pool[torch.from_numpy(units).cuda()] = 0
+    hz.attend(layer, q, bufs, sel=sel, sel_count=cnt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bufs.out.cpu().numpy(), out0)
